@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Throughput of data-parallel gradient synchronisation on one MI355X.
+
+Default workload (one JSON line): K=8 data-parallel ranks emulated as 8 HBM
+buffers, each holding the bf16 gradients of one transformer layer (GQA q/o
+4096x4096, k/v 4096x1024, SwiGLU 3 x 4096x14336: 218,103,808 values,
+N(0, 1e-3)), cut into 9 buckets of at most 25,000,000 elements. A step is, for
+every bucket in order, an averaged ReduceScatter (fp32 accumulation in ring
+order) into per-rank shards followed by an AllGather back to every rank.
+`value` is algorithmic HBM bytes per step (ReduceScatter reads K*n and writes
+n, AllGather reads n and writes K*n, per bucket of n elements) times steps,
+over the wall time of the timed steps, in GB/s.
+
+Other measurements (each prints its own JSON line):
+  --config ring1m    K=4, 1,048,576 fp32 and int32, S=4, AllReduce
+  --config fsdp      FSDP layer step, K=8, x[1024,512], w[512,512]
+  --config weighted  token-weighted AllReduce, K=8, 10,000,019 fp32
+  --config c3        RS+AG of 1 GiB/rank fp32 (K=8) concurrent with a bf16
+                     8192^3 GEMM on another stream
+  --config all       the default line, then all of the above
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F32_TFLOPS = 157.3        # dense fp32 matrix
+MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def host_cores() -> int:
+    return min(len(os.sched_getaffinity(0)), 16)
+
+
+def bf16_bits(t):
+    import numpy as np
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------- headline
+
+def bench_layer(args):
+    import torch
+
+    import gen
+    from gradient_sync_amd.buckets import BucketedSync
+
+    k = 8
+    total = gen.LAYER_PARAMS
+    log(f"[bench] generating {k} x {total} bf16 gradients on the GPU")
+    grads = gen.layer_grads_bf16(3, k, device="cuda")
+    out = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
+    step_bytes = sync.algorithmic_bytes()
+
+    for _ in range(args.warmup):
+        sync.step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    events = []
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        sync.step(events=events)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    value = step_bytes * args.steps / wall / 1e9
+
+    # per-launch durations of full-size buckets, per kernel
+    full = gen.BUCKET_ELEMS
+    per = {"rs": [], "ag": []}
+    tot = {"rs": 0.0, "ag": 0.0}
+    for kind, b, e0, e1 in events:
+        ms = e0.elapsed_time(e1)
+        tot[kind] += ms
+        if sync.plan[b][1] == full:
+            per[kind].append(ms)
+    launch_bytes = (k + 1) * full * 2
+    kern = {kind: {"avg_us": 1e3 * statistics.mean(v), "median_us": 1e3 * statistics.median(v),
+                   "gbs": launch_bytes / (statistics.mean(v) * 1e-3) / 1e9, "launches": len(v)}
+            for kind, v in per.items()}
+    dom = max(tot, key=tot.get)
+    achieved = kern[dom]["gbs"]
+    names = {"rs": "rs_kernel<bf16, avg, K=8>", "ag": "ag_kernel<2-byte, K=8>"}
+    line = {
+        "metric": "reduce-scatter+all-gather HBM GB/s (% of peak), K=8 bf16 25M-elem buckets",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "K=8 emulated ranks, one GQA+SwiGLU layer (hidden 4096) of bf16 "
+                               "grads = 218,103,808 per rank, 9 buckets of <=25,000,000, "
+                               "averaged ReduceScatter then AllGather per bucket",
+                   "ranks": k, "params_per_rank": total, "bucket_elems": gen.BUCKET_ELEMS,
+                   "buckets": len(sync.plan), "op": "avg", "accumulate": "fp32, ring order"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "bytes_per_step": step_bytes,
+        "kernels": {names[k_]: {kk: (round(v, 2) if isinstance(v, float) else v)
+                                for kk, v in d.items()} for k_, d in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "bytes_per_launch": launch_bytes,
+                     "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_layer(grads, k, args.cpu_seconds)
+    return line
+
+
+def cpu_baseline_layer(grads, k, seconds):
+    """The oracle's ReduceScatter + AllGather of one 25,000,000-element bf16
+    bucket (the first bucket of the same inputs), repeated for ~`seconds`."""
+    import numpy as np
+
+    import gen
+    import oracle
+
+    n = gen.BUCKET_ELEMS
+    xs = [np.ascontiguousarray(bf16_bits(g[:n])) for g in grads]
+    cores = host_cores()
+    reps, t = 0, 0.0
+    while reps == 0 or t < seconds:
+        t0 = time.perf_counter()
+        sh = oracle.reduce_scatter(xs, op="avg", nthreads=cores)
+        oracle.all_gather(sh, n, nthreads=cores)
+        t += time.perf_counter() - t0
+        reps += 1
+    b = 2 * (k + 1) * n * 2
+    return {"value": round(reps * b / t / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x (ReduceScatter avg + AllGather) of bucket 0 "
+                      f"(K=8 x 25,000,000 bf16), {t:.1f} s"}
+
+
+# ------------------------------------------------------------ other configs
+
+def _time_ms(fn, warm=6, reps=9, stream=None):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def bench_ring1m(args):
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, n, s = 4, 1_048_576, 4
+    xf = gen.ring_uniform_inputs(1, k, n, device="cuda")
+    xi = [gen.int_copy(x) for x in xf]
+    res = {}
+    for name, xs, op in (("f32_avg", xf, "avg"), ("i32_sum", xi, "sum")):
+        out = [torch.empty_like(x) for x in xs]
+        ms = _time_ms(lambda: dps.dp_all_reduce(xs, out, op=op, s_chunks=s))
+        med = statistics.median(ms)
+        b = 2 * (k + 1) * n * 4
+        res[name] = {"median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
+                     "gbs": round(b / (med * 1e-3) / 1e9, 1)}
+    return {"metric": "ring AllReduce K=4 N=1,048,576 S=4 (cache-resident, launch-bound)",
+            "unit": "us", "results": res, "config": {"workload": "K=4, 1,048,576 fp32/int32, S=4"}}
+
+
+def bench_fsdp(args):
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, m, d, f = 8, 1024, 512, 512
+    fx = gen.fsdp_fixture(seed=2, k=k, device="cuda")
+    ml, R = m // k, d // k
+    xl = [fx["x"][r * ml:(r + 1) * ml].contiguous() for r in range(k)]
+    dyl = [fx["dy"][r * ml:(r + 1) * ml].contiguous() for r in range(k)]
+    ws = [fx["w"][c * R:(c + 1) * R].contiguous() for c in range(k)]
+    wf = [torch.empty(d, f, device="cuda") for _ in range(k)]
+    y = [torch.empty(ml, f, device="cuda") for _ in range(k)]
+    dwf = [torch.empty(d, f, device="cuda") for _ in range(k)]
+    dws = [torch.empty(R, f, device="cuda") for _ in range(k)]
+    ms = _time_ms(lambda: dps.dp_fsdp_layer(xl, ws, dyl, wf, y, dwf, dws), warm=10, reps=50)
+    med = statistics.median(ms)
+    flops = 2 * (2 * k * ml * d * f)
+    return {"metric": "FSDP layer step (AG w, y=xW, dW=x^T dy, RS dW), K=8",
+            "unit": "us", "median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
+            "gemm_flops": flops,
+            "effective_tflops": round(flops / (med * 1e-3) / 1e12, 2),
+            "mfma_peak_tflops": MFMA_F32_TFLOPS,
+            "config": {"workload": "K=8, x[1024,512] N(0,1), w[512,512] N(0,0.02^2), "
+                                   "dy[1024,512] N(0,1), fp32"}}
+
+
+def bench_weighted(args):
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, n = 8, 10_000_019
+    xs = gen.ring_uniform_inputs(4, k, n, device="cuda")
+    toks = gen.token_counts(4, k)
+    out = [torch.empty(n, device="cuda") for _ in range(k)]
+    # rotate between two input sets so the working set exceeds the cache
+    xs2 = gen.ring_uniform_inputs(6, k, n, device="cuda")
+    out2 = [torch.empty(n, device="cuda") for _ in range(k)]
+    flip = [0]
+
+    def go():
+        a, o = (xs, out) if flip[0] == 0 else (xs2, out2)
+        flip[0] ^= 1
+        dps.dp_weighted_reduce(a, o, toks)
+    ms = _time_ms(go)
+    med = statistics.median(ms)
+    b = 2 * (k + 1) * n * 4
+    return {"metric": "token-weighted AllReduce K=8 N=10,000,019 fp32", "unit": "GB/s",
+            "value": round(b / (med * 1e-3) / 1e9, 1), "median_us": round(1e3 * med, 2),
+            "tokens": toks, "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "config": {"workload": "K=8, 10,000,019 fp32 uniform[-1,1), log-normal(7,1) "
+                                   "token counts, 2 docs/rank"}}
+
+
+def bench_c3(args):
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, n = 8, 268_435_456
+    log("[c3] generating 8 x 1 GiB fp32 and 2 x 8192^2 bf16")
+    xs = gen.ring_uniform_inputs(5, k, n, device="cuda")
+    L = dps.dp_shard_len(n, k)
+    sh = [torch.empty(L, device="cuda") for _ in range(k)]
+    out = [torch.empty(n, device="cuda") for _ in range(k)]
+    a, b = gen.gemm_bf16_inputs(5, 8192, 8192, 8192, device="cuda")
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def comm(stream=None):
+        dps.dp_reduce_scatter(xs, sh, op="sum", stream=stream)
+        dps.dp_all_gather(sh, out, stream=stream)
+
+    def gemm(stream=None):
+        dps.dp_gemm_bf16(a, b, c, stream=stream)
+
+    t_comm = statistics.median(_time_ms(comm))
+    t_gemm = statistics.median(_time_ms(gemm))
+
+    def concurrent(first):
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        start.record(cur)
+        sa.wait_event(start)
+        sb.wait_event(start)
+        order = [(comm, sa, ea), (gemm, sb, eb)] if first == "comm" else [(gemm, sb, eb), (comm, sa, ea)]
+        for fn, st, ev in order:
+            fn(stream=st)
+            ev.record(st)
+        torch.cuda.synchronize()
+        return max(start.elapsed_time(ea), start.elapsed_time(eb))
+
+    res = {}
+    for first in ("gemm", "comm"):
+        for _ in range(6):
+            concurrent(first)
+        tc = statistics.median([concurrent(first) for _ in range(9)])
+        s = (t_comm + t_gemm) / tc
+        s_ideal = (t_comm + t_gemm) / max(t_comm, t_gemm)
+        res[f"{first}_first"] = {"t_concurrent_ms": round(tc, 4), "S": round(s, 4),
+                                 "S_ideal": round(s_ideal, 4),
+                                 "S_over_S_ideal": round(s / s_ideal, 4),
+                                 "pct_of_ideal_gain": round(100 * (s - 1) / (s_ideal - 1), 1)
+                                 if s_ideal > 1 else None}
+    comm_bytes = 2 * (k + 1) * n * 4
+    flops = 2 * 8192 ** 3
+    return {"metric": "C3: RS+AG (K=8, 1 GiB/rank fp32) concurrent with bf16 GEMM 8192^3",
+            "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
+            "comm_gbs": round(comm_bytes / (t_comm * 1e-3) / 1e9, 1),
+            "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+            "gemm_frac_of_bf16_peak": round(flops / (t_gemm * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
+            "results": res,
+            "config": {"workload": "K=8 x 268,435,456 fp32 RS(sum)+AG on stream A, "
+                                   "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}
+
+
+CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="layer", choices=["layer", "all", *CONFIGS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU (K ranks are emulated as K buffers in "
+              f"one MI355X's HBM); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import gradient_sync_amd  # noqa: F401  (fails loudly if the library is not built)
+    if args.config in ("layer", "all"):
+        print(json.dumps(bench_layer(args)), flush=True)
+    for name, fn in CONFIGS.items():
+        if args.config in (name, "all"):
+            log(f"[bench] config {name}")
+            print(json.dumps(fn(args)), flush=True)
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

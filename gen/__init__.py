@@ -151,11 +151,6 @@ LAYER_PARAMS = sum(a * b for _, a, b in LAYER_MATRICES)   # 218,103,808
 BUCKET_ELEMS = 25_000_000
 
 
-def bucket_plan(total: int = LAYER_PARAMS, cap: int = BUCKET_ELEMS) -> list[tuple[int, int]]:
-    """(offset, length) of consecutive buckets of at most `cap` elements."""
-    return [(o, min(cap, total - o)) for o in range(0, total, cap)]
-
-
 def layer_grads_bf16(seed: int, k: int, device="cpu", total: int = LAYER_PARAMS,
                      std: float = 1e-3) -> list[torch.Tensor]:
     """K flat bf16 gradient vectors of one layer, N(0, std^2), tensor id 3."""
@@ -172,7 +167,7 @@ def fsdp_fixture(seed: int = 2, k: int = 8, m: int = 1024, d: int = 512, f: int 
 
 
 def gemm_bf16_inputs(seed: int, m: int, n: int, kk: int, device="cpu"):
-    """A[m,kk], B[kk,n] bf16 from N(0,1)."""
+    """A[m,kk] and B[n,kk] (k-contiguous weight layout, C = A B^T), bf16 from N(0,1)."""
     a = bf16_normal(seed, 30, 0, m * kk, 1.0, device=device).view(m, kk)
-    b = bf16_normal(seed, 31, 0, kk * n, 1.0, device=device).view(kk, n)
+    b = bf16_normal(seed, 31, 0, n * kk, 1.0, device=device).view(n, kk)
     return a, b

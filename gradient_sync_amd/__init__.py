@@ -1,0 +1,267 @@
+"""gradient_sync_amd: data-parallel gradient and parameter synchronisation on
+one MI355X, with K data-parallel ranks emulated as K buffers in HBM.
+
+This module is a thin ctypes binding over libdpsync.so (include/dpsync.h).
+It only marshals arguments: torch tensors become device pointers, the current
+torch stream becomes the hipStream_t, and a non-zero status becomes a
+DpsyncError. Every step of the computation runs in the library's HIP kernels;
+there is no fallback path. If libdpsync.so has not been built this import
+fails loudly.
+
+Calls (same names and meaning as the C ABI):
+  dp_reduce_scatter(send, recv, op="sum", s_chunks=1, stream=None)
+  dp_all_gather(send, recv, n=None, s_chunks=1, stream=None)
+  dp_all_reduce(send, recv, op="sum", s_chunks=1, stream=None)
+  dp_weighted_reduce(send, recv, tokens, s_chunks=1, stream=None)
+  dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full, dw_shard, stream=None)
+  dp_gemm_bf16(a, b, c, stream=None)          # c = a @ b.T
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+__all__ = [
+    "DpsyncError", "lib", "dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
+    "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
+    "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdpsync.so")
+
+DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_ALIAS, DP_ERR_HIP = range(5)
+DP_F32, DP_BF16, DP_I32 = 0, 1, 2
+DP_SUM, DP_AVG = 0, 1
+DP_MAX_K = 64
+
+# every symbol include/dpsync.h declares
+EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
+           "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
+           "dp_fsdp_layer", "dp_gemm_bf16")
+
+_DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
+_OPS = {"sum": DP_SUM, "avg": DP_AVG}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+_lib = None
+
+
+class DpsyncError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = dp_status_string(code)
+        if code == DP_ERR_HIP:
+            msg += f" (hipError {dp_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def lib():
+    """The loaded libdpsync (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.dp_shard_len.restype = _sz
+        L.dp_shard_len.argtypes = [_sz, _int]
+        L.dp_status_string.restype = ctypes.c_char_p
+        L.dp_status_string.argtypes = [_int]
+        L.dp_last_hip_error.restype = _int
+        L.dp_last_hip_error.argtypes = []
+        L.dp_version.restype = _int
+        L.dp_version.argtypes = []
+        L.dp_reduce_scatter.restype = _int
+        L.dp_reduce_scatter.argtypes = [_vp, _vp, _sz, _int, _int, _int, _int, _vp]
+        L.dp_all_gather.restype = _int
+        L.dp_all_gather.argtypes = [_vp, _vp, _sz, _int, _int, _int, _vp]
+        L.dp_all_reduce.restype = _int
+        L.dp_all_reduce.argtypes = [_vp, _vp, _sz, _int, _int, _int, _int, _vp]
+        L.dp_weighted_reduce.restype = _int
+        L.dp_weighted_reduce.argtypes = [_vp, _vp, _vp, _sz, _int, _int, _int, _vp]
+        L.dp_fsdp_layer.restype = _int
+        L.dp_fsdp_layer.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.dp_gemm_bf16.restype = _int
+        L.dp_gemm_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
+        _lib = L
+    return _lib
+
+
+def dp_shard_len(n: int, k: int) -> int:
+    return int(lib().dp_shard_len(n, k))
+
+
+def dp_status_string(code: int) -> str:
+    return lib().dp_status_string(code).decode()
+
+
+def dp_last_hip_error() -> int:
+    return int(lib().dp_last_hip_error())
+
+
+def dp_version() -> int:
+    return int(lib().dp_version())
+
+
+# ----------------------------------------------------------------- marshalling
+
+def ptr_array(ptrs):
+    """Host array of device pointers (ints), as the ABI's `const void* const*`."""
+    arr = (_vp * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+    return arr
+
+
+def _stream(stream):
+    if stream is None:
+        return _vp(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return _vp(stream.cuda_stream)
+    return _vp(int(stream))
+
+
+def _check(code: int, where: str):
+    if code != DP_OK:
+        raise DpsyncError(code, where)
+
+
+def _tensors(ts, what, dtype=None):
+    ts = list(ts)
+    if not ts:
+        raise ValueError(f"{what}: need at least one rank")
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{what}: expected torch tensors")
+        if t.device.type != "cuda":
+            raise ValueError(f"{what}: tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: tensors must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if len({t.dtype for t in ts}) != 1:
+        raise TypeError(f"{what}: all ranks must share one dtype")
+    return ts
+
+
+def _dt(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _numel_check(ts, n, what):
+    for t in ts:
+        if t.numel() < n:
+            raise ValueError(f"{what}: buffer of {t.numel()} elements, need {n}")
+
+
+# ----------------------------------------------------------------- the calls
+
+def dp_reduce_scatter(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
+    """recv[c] (ceil(n/K) elements) <- shard c of the ring-order sum of send[r]."""
+    send = _tensors(send, "send")
+    recv = _tensors(recv, "recv", send[0].dtype)
+    k = len(send)
+    n = send[0].numel() if n is None else n
+    _numel_check(send, n, "send")
+    _numel_check(recv, dp_shard_len(n, k), "recv")
+    if len(recv) != k:
+        raise ValueError("send and recv need one buffer per rank")
+    _check(lib().dp_reduce_scatter(ptr_array([t.data_ptr() for t in send]),
+                                   ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
+                                   _OPS[op], s_chunks, _stream(stream)), "dp_reduce_scatter")
+
+
+def dp_all_gather(send, recv, n=None, s_chunks: int = 1, stream=None):
+    """recv[r][c*L + j] <- send[c][j] for the valid elements of every shard."""
+    send = _tensors(send, "send")
+    recv = _tensors(recv, "recv", send[0].dtype)
+    k = len(send)
+    n = recv[0].numel() if n is None else n
+    _numel_check(recv, n, "recv")
+    L = dp_shard_len(n, k)
+    for c, t in enumerate(send):
+        _numel_check([t], max(0, min(L, n - c * L)), f"send[{c}]")
+    if len(recv) != k:
+        raise ValueError("send and recv need one buffer per rank")
+    _check(lib().dp_all_gather(ptr_array([t.data_ptr() for t in send]),
+                               ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
+                               s_chunks, _stream(stream)), "dp_all_gather")
+
+
+def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
+    send = _tensors(send, "send")
+    recv = _tensors(recv, "recv", send[0].dtype)
+    k = len(send)
+    n = send[0].numel() if n is None else n
+    _numel_check(send, n, "send")
+    _numel_check(recv, n, "recv")
+    if len(recv) != k:
+        raise ValueError("send and recv need one buffer per rank")
+    _check(lib().dp_all_reduce(ptr_array([t.data_ptr() for t in send]),
+                               ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
+                               _OPS[op], s_chunks, _stream(stream)), "dp_all_reduce")
+
+
+def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=None):
+    send = _tensors(send, "send")
+    recv = _tensors(recv, "recv", send[0].dtype)
+    k = len(send)
+    n = send[0].numel() if n is None else n
+    _numel_check(send, n, "send")
+    _numel_check(recv, n, "recv")
+    if len(recv) != k or len(tokens) != k:
+        raise ValueError("send, recv and tokens need one entry per rank")
+    toks = (ctypes.c_int64 * k)(*[int(t) for t in tokens])
+    _check(lib().dp_weighted_reduce(ptr_array([t.data_ptr() for t in send]),
+                                    ptr_array([t.data_ptr() for t in recv]), toks, n, k,
+                                    _dt(send[0]), s_chunks, _stream(stream)),
+           "dp_weighted_reduce")
+
+
+def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_shard=None,
+                  stream=None):
+    """FSDP layer step over K ranks (fp32): gather W, y = x W, dW = x^T dy, RS(dW)."""
+    f32 = torch.float32
+    x_local = _tensors(x_local, "x_local", f32)
+    w_shard = _tensors(w_shard, "w_shard", f32)
+    w_full = _tensors(w_full, "w_full", f32)
+    y_local = _tensors(y_local, "y_local", f32)
+    k = len(x_local)
+    m_local, d = x_local[0].shape
+    f = w_full[0].shape[1]
+    bwd = dy_local is not None
+    if bwd:
+        dy_local = _tensors(dy_local, "dy_local", f32)
+        dw_full = _tensors(dw_full, "dw_full", f32)
+        dw_shard = _tensors(dw_shard, "dw_shard", f32)
+    R = dp_shard_len(d, k)
+    for name, ts, shape in (("x_local", x_local, (m_local, d)), ("w_shard", w_shard, (R, f)),
+                            ("w_full", w_full, (d, f)), ("y_local", y_local, (m_local, f))) + (
+            (("dy_local", dy_local, (m_local, f)), ("dw_full", dw_full, (d, f)),
+             ("dw_shard", dw_shard, (R, f))) if bwd else ()):
+        if len(ts) != k or any(tuple(t.shape) != shape for t in ts):
+            raise ValueError(f"{name}: expected {k} tensors of shape {shape}")
+    P = lambda ts: ptr_array([t.data_ptr() for t in ts])
+    _check(lib().dp_fsdp_layer(k, m_local, d, f, P(x_local), P(w_shard),
+                               P(dy_local) if bwd else None, P(w_full), P(y_local),
+                               P(dw_full) if bwd else None, P(dw_shard) if bwd else None,
+                               _stream(stream)), "dp_fsdp_layer")
+
+
+def dp_gemm_bf16(a, b, c, stream=None):
+    """c[m,n] = a[m,kk] @ b[n,kk]^T in bf16 with fp32 accumulation."""
+    for name, t in (("a", a), ("b", b), ("c", c)):
+        _tensors([t], name, torch.bfloat16)
+    m, kk = a.shape
+    n = b.shape[0]
+    if b.shape[1] != kk or tuple(c.shape) != (m, n):
+        raise ValueError("dp_gemm_bf16: shapes must be a[m,k], b[n,k], c[m,n]")
+    _check(lib().dp_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), m, n, kk,
+                              _stream(stream)), "dp_gemm_bf16")

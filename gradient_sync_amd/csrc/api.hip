@@ -1,0 +1,354 @@
+// extern "C" entry points of libdpsync: argument validation, shard planning
+// and kernel dispatch on the caller's stream. The contract of every call is
+// stated in include/dpsync.h.
+#include <stdint.h>
+#include <string.h>
+
+#include "dps_internal.h"
+#include "dpsync.h"
+
+static_assert(dps::kMaxK == DP_MAX_K, "kernel and ABI rank limits differ");
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+dp_status_t hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return DP_OK;
+    g_last_hip_error = (int)e;
+    return DP_ERR_HIP;
+}
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range span(const void *p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Range a, Range b) { return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi; }
+
+bool valid_k(int k) { return k >= 1 && k <= DP_MAX_K; }
+
+bool valid_dtype(int dt) { return dt == DP_F32 || dt == DP_BF16 || dt == DP_I32; }
+
+// every element non-null and element-aligned
+bool ptrs_ok(const void *const *a, int k, int es)
+{
+    if (!a) return false;
+    for (int i = 0; i < k; ++i)
+        if (!a[i] || ((uintptr_t)a[i] % (uintptr_t)es) != 0) return false;
+    return true;
+}
+
+// n elements of size es per rank must fit comfortably in a signed 64-bit byte count
+bool size_ok(size_t n, int es) { return n <= ((size_t)1 << 58) / (size_t)es; }
+
+bool pairwise_disjoint(void *const *a, int k, size_t bytes)
+{
+    for (int i = 0; i < k; ++i)
+        for (int j = i + 1; j < k; ++j)
+            if (overlap(span(a[i], bytes), span(a[j], bytes))) return false;
+    return true;
+}
+
+int64_t shard_valid(int64_t n, int64_t L, int c)
+{
+    const int64_t lo = (int64_t)c * L;
+    if (lo >= n) return 0;
+    return n - lo < L ? n - lo : L;
+}
+
+// epilogue for DP_SUM / DP_AVG; AVG by a power-of-two K multiplies by the
+// exact reciprocal, which rounds the same real number as the division
+void pick_epilogue(int op, int k, int &ep, float &scale)
+{
+    if (op == DP_SUM) {
+        ep = dps::kSum;
+        scale = 1.0f;
+    } else if ((k & (k - 1)) == 0) {
+        ep = dps::kMul;
+        scale = 1.0f / (float)k;
+    } else {
+        ep = dps::kDiv;
+        scale = (float)k;
+    }
+}
+
+dp_status_t validate_rs_ag_common(const void *const *send, void *const *recv, size_t n, int k,
+                                  int dt, int s_chunks)
+{
+    if (!valid_k(k) || s_chunks < 1) return DP_ERR_INVALID_ARG;
+    if (!valid_dtype(dt)) return DP_ERR_UNSUPPORTED;
+    const int es = dps::elem_size(dt);
+    if (!size_ok(n, es)) return DP_ERR_INVALID_ARG;
+    if (n == 0) return (send && recv) ? DP_OK : DP_ERR_INVALID_ARG;
+    if (!ptrs_ok(send, k, es) || !ptrs_ok((const void *const *)recv, k, es)) return DP_ERR_INVALID_ARG;
+    return DP_OK;
+}
+
+// ReduceScatter launch shared by the RS and AR entry points.
+// out[c] = element 0 of shard c's output region.
+dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t L, int k, int dt,
+                   int ep, float scale, const float *w, int write_pads, int s_chunks,
+                   hipStream_t st)
+{
+    dps::RsParams p;
+    memset(&p, 0, sizeof(p));
+    for (int r = 0; r < k; ++r) {
+        p.src[r] = (const char *)send[r];
+        p.dst[r] = out[r];
+        p.w[r] = w ? w[r] : 1.0f;
+    }
+    p.scale = scale;
+    p.write_pads = write_pads;
+    p.n = n;
+    p.L = L;
+    p.k = k;
+    p.S = s_chunks;
+    return hip_status(dps::launch_rs(p, dt, ep, st));
+}
+
+dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_t L, int k, int dt,
+                   int skip_own, int s_chunks, hipStream_t st)
+{
+    dps::AgParams p;
+    memset(&p, 0, sizeof(p));
+    for (int r = 0; r < k; ++r) {
+        p.src[r] = (const char *)shard[r];
+        p.dst[r] = out[r];
+    }
+    p.skip_own = skip_own;
+    p.n = n;
+    p.L = L;
+    p.k = k;
+    p.S = s_chunks;
+    return hip_status(dps::launch_ag(p, dt, st));
+}
+
+// AllReduce-shaped validation: for every r, recv[r] either equals send[r] or
+// overlaps no send buffer; receive buffers are pairwise disjoint.
+dp_status_t check_ar_alias(const void *const *send, void *const *recv, size_t n, int k, int es)
+{
+    const size_t bytes = n * (size_t)es;
+    for (int r = 0; r < k; ++r) {
+        if (recv[r] == send[r]) continue;
+        for (int q = 0; q < k; ++q)
+            if (overlap(span(recv[r], bytes), span(send[q], bytes))) return DP_ERR_ALIAS;
+    }
+    return pairwise_disjoint(recv, k, bytes) ? DP_OK : DP_ERR_ALIAS;
+}
+
+dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, int dt, int ep,
+                   float scale, const float *w, int s_chunks, hipStream_t st)
+{
+    const int es = dps::elem_size(dt);
+    const int64_t L = (int64_t)dp_shard_len(n, k);
+    char *rs_out[DP_MAX_K];
+    for (int c = 0; c < k; ++c) rs_out[c] = (char *)recv[c] + (size_t)c * (size_t)L * (size_t)es;
+    dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st);
+    if (s != DP_OK) return s;
+    return run_ag((const void *const *)rs_out, (char *const *)recv, (int64_t)n, L, k, dt, 1,
+                  s_chunks, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dp_shard_len(size_t n, int k)
+{
+    if (n == 0 || k < 1) return 0;
+    return (n + (size_t)k - 1) / (size_t)k;
+}
+
+const char *dp_status_string(int status)
+{
+    switch (status) {
+    case DP_OK: return "DP_OK: success";
+    case DP_ERR_INVALID_ARG: return "DP_ERR_INVALID_ARG: invalid argument";
+    case DP_ERR_UNSUPPORTED: return "DP_ERR_UNSUPPORTED: unsupported dtype or op";
+    case DP_ERR_ALIAS: return "DP_ERR_ALIAS: buffers overlap outside the in-place forms";
+    case DP_ERR_HIP: return "DP_ERR_HIP: HIP launch failed";
+    default: return "unknown dpsync status";
+    }
+}
+
+int dp_last_hip_error(void) { return g_last_hip_error; }
+
+int dp_version(void) { return 100; }
+
+dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                              int op, int s_chunks, void *stream)
+{
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK || n == 0) return s;
+    if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
+    if (dt == DP_I32 && op != DP_SUM) return DP_ERR_UNSUPPORTED;
+    const int es = dps::elem_size(dt);
+    const size_t L = dp_shard_len(n, k);
+    bool in_place = n == L * (size_t)k;
+    for (int c = 0; c < k && in_place; ++c)
+        in_place = (const char *)recv[c] == (const char *)send[c] + (size_t)c * L * (size_t)es;
+    if (!in_place) {
+        for (int c = 0; c < k; ++c)
+            for (int r = 0; r < k; ++r)
+                if (overlap(span(recv[c], L * es), span(send[r], n * es))) return DP_ERR_ALIAS;
+        if (!pairwise_disjoint(recv, k, L * es)) return DP_ERR_ALIAS;
+    }
+    int ep;
+    float scale;
+    pick_epilogue(op, k, ep, scale);
+    return run_rs(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, ep, scale, nullptr, 1,
+                  s_chunks, (hipStream_t)stream);
+}
+
+dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                          int s_chunks, void *stream)
+{
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK || n == 0) return s;
+    const int es = dps::elem_size(dt);
+    const size_t L = dp_shard_len(n, k);
+    if (!pairwise_disjoint(recv, k, n * es)) return DP_ERR_ALIAS;
+    bool in_place = true;
+    for (int c = 0; c < k && in_place; ++c)
+        in_place = (const char *)send[c] == (const char *)recv[c] + (size_t)c * L * (size_t)es;
+    if (!in_place) {
+        for (int c = 0; c < k; ++c) {
+            const size_t nc = (size_t)shard_valid((int64_t)n, (int64_t)L, c);
+            for (int r = 0; r < k; ++r)
+                if (overlap(span(send[c], nc * es), span(recv[r], n * es))) return DP_ERR_ALIAS;
+        }
+    }
+    return run_ag(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, in_place ? 1 : 0,
+                  s_chunks, (hipStream_t)stream);
+}
+
+dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                          int op, int s_chunks, void *stream)
+{
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK || n == 0) return s;
+    if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
+    if (dt == DP_I32 && op != DP_SUM) return DP_ERR_UNSUPPORTED;
+    s = check_ar_alias(send, recv, n, k, dps::elem_size(dt));
+    if (s != DP_OK) return s;
+    int ep;
+    float scale;
+    pick_epilogue(op, k, ep, scale);
+    return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream);
+}
+
+dp_status_t dp_weighted_reduce(const void *const *send, void *const *recv, const int64_t *tokens,
+                               size_t n, int k, int dt, int s_chunks, void *stream)
+{
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK) return s;
+    if (dt == DP_I32) return DP_ERR_UNSUPPORTED;
+    if (!tokens) return DP_ERR_INVALID_ARG;
+    float w[DP_MAX_K];
+    int64_t total = 0;
+    for (int r = 0; r < k; ++r) {
+        if (tokens[r] < 0 || tokens[r] > ((int64_t)1 << 56)) return DP_ERR_INVALID_ARG;
+        total += tokens[r];
+        w[r] = (float)tokens[r];
+    }
+    if (total <= 0) return DP_ERR_INVALID_ARG;
+    if (n == 0) return DP_OK;
+    s = check_ar_alias(send, recv, n, k, dps::elem_size(dt));
+    if (s != DP_OK) return s;
+    return run_ar(send, recv, n, k, dt, dps::kWeighted, (float)total, w, s_chunks,
+                  (hipStream_t)stream);
+}
+
+dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
+                          const float *const *x_local, const float *const *w_shard,
+                          const float *const *dy_local, float *const *w_full,
+                          float *const *y_local, float *const *dw_full, float *const *dw_shard,
+                          void *stream)
+{
+    if (!valid_k(k) || m_local < 1 || d < 1 || f < 1) return DP_ERR_INVALID_ARG;
+    if (m_local > (1 << 24) || d > (1 << 24) || f > (1 << 24)) return DP_ERR_INVALID_ARG;
+    if (!ptrs_ok((const void *const *)x_local, k, 4) || !ptrs_ok((const void *const *)w_shard, k, 4) ||
+        !ptrs_ok((const void *const *)w_full, k, 4) || !ptrs_ok((const void *const *)y_local, k, 4))
+        return DP_ERR_INVALID_ARG;
+    const bool bwd = dy_local != nullptr;
+    if (bwd && (!ptrs_ok((const void *const *)dy_local, k, 4) ||
+                !ptrs_ok((const void *const *)dw_full, k, 4) ||
+                !ptrs_ok((const void *const *)dw_shard, k, 4)))
+        return DP_ERR_INVALID_ARG;
+    const int64_t R = (d + k - 1) / k;
+    const size_t bx = (size_t)(m_local * d) * 4, bws = (size_t)(R * f) * 4, bdy = (size_t)(m_local * f) * 4;
+    const size_t bwf = (size_t)(d * f) * 4, by = (size_t)(m_local * f) * 4;
+    // outputs must be disjoint from every input and from each other
+    Range ins[3 * DP_MAX_K], outs[4 * DP_MAX_K];
+    int ni = 0, no = 0;
+    for (int r = 0; r < k; ++r) {
+        ins[ni++] = span(x_local[r], bx);
+        ins[ni++] = span(w_shard[r], bws);
+        if (bwd) ins[ni++] = span(dy_local[r], bdy);
+        outs[no++] = span(w_full[r], bwf);
+        outs[no++] = span(y_local[r], by);
+        if (bwd) {
+            outs[no++] = span(dw_full[r], bwf);
+            outs[no++] = span(dw_shard[r], bws);
+        }
+    }
+    for (int a = 0; a < no; ++a) {
+        for (int b = 0; b < ni; ++b)
+            if (overlap(outs[a], ins[b])) return DP_ERR_ALIAS;
+        for (int b = a + 1; b < no; ++b)
+            if (overlap(outs[a], outs[b])) return DP_ERR_ALIAS;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    // 1. forward: all-gather the weight row shards into every rank's W
+    dp_status_t s = run_ag((const void *const *)w_shard, (char *const *)w_full, d * f, R * f, k,
+                           DP_F32, 0, 1, st);
+    if (s != DP_OK) return s;
+    // 2. local dot y_r = x_r . W
+    dps::GemmF32Batch g;
+    memset(&g, 0, sizeof(g));
+    for (int r = 0; r < k; ++r) {
+        g.a[r] = x_local[r];
+        g.b[r] = w_full[r];
+        g.c[r] = y_local[r];
+    }
+    g.nb = k;
+    g.M = m_local;
+    g.N = f;
+    g.Kd = d;
+    g.trans_a = 0;
+    s = hip_status(dps::launch_gemm_f32(g, st));
+    if (s != DP_OK || !bwd) return s;
+    // 3. backward: dW_r = x_r^T . dy_r
+    for (int r = 0; r < k; ++r) {
+        g.a[r] = x_local[r];
+        g.b[r] = dy_local[r];
+        g.c[r] = dw_full[r];
+    }
+    g.M = d;
+    g.N = f;
+    g.Kd = m_local;
+    g.trans_a = 1;
+    s = hip_status(dps::launch_gemm_f32(g, st));
+    if (s != DP_OK) return s;
+    // 4. reduce-scatter dW back to the row shards (sum, pad rows zero)
+    return run_rs((const void *const *)dw_full, (char *const *)dw_shard, d * f, R * f, k, DP_F32,
+                  dps::kSum, 1.0f, nullptr, 1, 1, st);
+}
+
+dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n, int64_t kk,
+                         void *stream)
+{
+    if (!a || !b || !c || m < 1 || n < 1 || kk < 1) return DP_ERR_INVALID_ARG;
+    if (m > (1 << 24) || n > (1 << 24) || kk > (1 << 24)) return DP_ERR_INVALID_ARG;
+    if (kk % 8 != 0 || ((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)c & 1))
+        return DP_ERR_UNSUPPORTED;
+    const Range rc = span(c, (size_t)(m * n) * 2);
+    if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
+        return DP_ERR_ALIAS;
+    return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the libdpsync translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dps {
+
+constexpr int kMaxK = 64;          // must equal DP_MAX_K in include/dpsync.h
+constexpr int kBlock = 256;        // threads per workgroup of the sync kernels
+
+enum Dtype { kF32 = 0, kBF16 = 1, kI32 = 2 };
+
+// Reduction epilogues. kMul multiplies by an exactly representable 1/K (K a
+// power of two), which gives the same correctly rounded result as dividing.
+enum Epilogue { kSum = 0, kMul = 1, kDiv = 2, kWeighted = 3 };
+
+inline int elem_size(int dt) { return dt == kBF16 ? 2 : 4; }
+
+// ReduceScatter kernel arguments. Shard c's fold reads element (c*L + j) of
+// every rank and writes element j of dst[c].
+struct RsParams {
+    const char *src[kMaxK];     // rank r input, element 0
+    char *dst[kMaxK];           // shard c output, element 0 of the shard
+    float w[kMaxK];             // per-rank weights f32(t_r) (kWeighted)
+    unsigned char fast[kMaxK];  // shard c: all inputs and the output share a 16-byte phase
+    unsigned char ph0[kMaxK];   // that phase (bytes) at shard element 0
+    float scale;                // 1/K (kMul), K (kDiv), sum of tokens (kWeighted)
+    int write_pads;             // write zero into elements n_c..L-1 of every shard
+    long long n, L;             // elements per rank, shard length
+    long long sub;              // elements per sub-chunk, ceil(L/S)
+    long long tiles_per_seg;    // workgroups per (sub-chunk, shard) segment
+    int k, S;
+};
+
+// AllGather kernel arguments. Shard c's valid elements go to element c*L + j
+// of every rank's output.
+struct AgParams {
+    const char *src[kMaxK];     // shard c, element 0
+    char *dst[kMaxK];           // rank r output, element 0
+    unsigned char fast[kMaxK];
+    unsigned char ph0[kMaxK];
+    int skip_own;               // do not copy shard c to rank c (already in place)
+    long long n, L, sub, tiles_per_seg;
+    int k, S;
+};
+
+// Fill the phase table and tiling of the parameter blocks; returns the grid size.
+long long plan_rs(RsParams &p, int dt);
+long long plan_ag(AgParams &p, int dt);
+
+hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t stream);
+hipError_t launch_ag(const AgParams &p, int dt, hipStream_t stream);
+
+// Batched fp32 GEMM on MFMA: for each batch b < nb,
+// C_b[M,N] = op(A_b)[M,Kd] * B_b[Kd,N], row-major; op(A) = A ([M,Kd]) or, with
+// trans_a, A^T where A_b is stored [Kd,M].
+struct GemmF32Batch {
+    const float *a[kMaxK];
+    const float *b[kMaxK];
+    float *c[kMaxK];
+    int nb;
+    long long M, N, Kd;
+    int trans_a;
+};
+hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t stream);
+
+// bf16 GEMM, C[M,N] = A[M,Kd] * B[Kd,N], row-major, fp32 accumulation.
+hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
+                            long long Kd, hipStream_t stream);
+
+}  // namespace dps

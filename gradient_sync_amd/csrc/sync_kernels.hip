@@ -1,0 +1,447 @@
+// ReduceScatter and AllGather kernels for K ranks emulated as K HBM buffers.
+//
+// ReduceScatter (CMU 11-868 L14-L15 notes, "Ring AllReduce: ReduceScatter,
+// then AllGather", phase 1; "Sharding and Parallelism", "The cost of the
+// inserted collectives", T_RS,ring): shard c of the result is the sum over
+// ranks of elements [cL, cL + n_c). On one GPU the ring's K-1 hops become K
+// streaming reads of the same element range, folded in the order the ring
+// would add them: rho_c = (c+1, ..., c+K-1, c) mod K, left fold, fp32
+// accumulation (wrapping uint32 for int32).
+//
+// AllGather (same sources, phase 2 and T_AG,ring): every rank receives every
+// shard's valid elements at their global offset.
+//
+// Both are HBM-bound streams: per 16-byte vector of shard elements the
+// ReduceScatter reads K vectors and writes one; the AllGather reads one and
+// writes K. Each workgroup handles one tile of one (sub-chunk, shard)
+// segment, so the fold order rho_c and the alignment decision are uniform per
+// workgroup. Where the K inputs and the output of a shard share their address
+// phase modulo 16 bytes, the body of the tile moves 128-bit vectors (one
+// global_load/store_dwordx4 per lane, consecutive lanes on consecutive
+// vectors) and the unaligned head and the tail are done element by element;
+// otherwise the tile is done element by element with consecutive lanes on
+// consecutive elements (still coalesced).
+#include "dps_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace dps {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Tr;
+template <> struct Tr<kF32>  { using Acc = float;    static constexpr int ES = 4, V = 4; };
+template <> struct Tr<kBF16> { using Acc = float;    static constexpr int ES = 2, V = 8; };
+template <> struct Tr<kI32>  { using Acc = unsigned; static constexpr int ES = 4, V = 4; };
+
+// vectors per thread per tile
+template <int DT> struct RsU { static constexpr int U = 2; };
+constexpr int kAgU = 2;
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN (sign kept).
+__device__ __forceinline__ unsigned f32_to_bf16_bits(float f)
+{
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <int DT>
+__device__ __forceinline__ typename Tr<DT>::Acc load1(const char *p)
+{
+    if constexpr (DT == kF32) return *reinterpret_cast<const float *>(p);
+    else if constexpr (DT == kBF16) return bf16_bits_to_f32(*reinterpret_cast<const unsigned short *>(p));
+    else return *reinterpret_cast<const unsigned *>(p);
+}
+
+template <int DT>
+__device__ __forceinline__ void store1(char *p, typename Tr<DT>::Acc v)
+{
+    if constexpr (DT == kF32) *reinterpret_cast<float *>(p) = v;
+    else if constexpr (DT == kBF16) *reinterpret_cast<unsigned short *>(p) = (unsigned short)f32_to_bf16_bits(v);
+    else *reinterpret_cast<unsigned *>(p) = v;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 v, typename Tr<DT>::Acc (&o)[Tr<DT>::V])
+{
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+    } else if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(v[i] << 16);
+            o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = v[i];
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const typename Tr<DT>::Acc (&a)[Tr<DT>::V])
+{
+    u32x4 v;
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(a[i]);
+    } else if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = f32_to_bf16_bits(a[2 * i]) | (f32_to_bf16_bits(a[2 * i + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = a[i];
+    }
+    return v;
+}
+
+// operand m of shard c's fold is rank (c + 1 + m) mod K
+__device__ __forceinline__ int fold_rank(int c, int m, int K)
+{
+    int r = c + 1 + m;
+    return r >= K ? r - K : r;
+}
+
+template <int EP, typename A>
+__device__ __forceinline__ A term(A x, float w)
+{
+    if constexpr (EP == kWeighted) return x * w;
+    else return x;
+}
+
+template <int EP, typename A>
+__device__ __forceinline__ A finish(A acc, float scale)
+{
+    if constexpr (EP == kMul) return acc * scale;
+    else if constexpr (EP == kDiv || EP == kWeighted) return acc / scale;
+    else return acc;
+}
+
+// One element of shard c, shard-local index j (< n_c).
+template <int DT, int EP, int KT>
+__device__ __forceinline__ void rs_elem(const RsParams &p, int K, int c, long long g, char *out)
+{
+    using A = typename Tr<DT>::Acc;
+    constexpr int ES = Tr<DT>::ES;
+    const int r0 = fold_rank(c, 0, K);
+    A acc = term<EP>(load1<DT>(p.src[r0] + g * ES), p.w[r0]);
+#pragma unroll
+    for (int m = 1; m < (KT ? KT : kMaxK); ++m) {
+        if (!KT && m >= K) break;
+        const int r = fold_rank(c, m, K);
+        acc = acc + term<EP>(load1<DT>(p.src[r] + g * ES), p.w[r]);
+    }
+    store1<DT>(out, finish<EP>(acc, p.scale));
+}
+
+template <int DT, int EP, int KT>
+__device__ __forceinline__ void rs_scalar_range(const RsParams &p, int K, int c, long long base,
+                                                long long nc, long long lo, long long hi)
+{
+    constexpr int ES = Tr<DT>::ES;
+    char *dst = p.dst[c];
+    for (long long j = lo + threadIdx.x; j < hi; j += kBlock) {
+        if (j < nc) rs_elem<DT, EP, KT>(p, K, c, base + j, dst + j * ES);
+        else if (p.write_pads) store1<DT>(dst + j * ES, typename Tr<DT>::Acc(0));
+    }
+}
+
+template <int DT, int EP, int KT, int U>
+__global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
+{
+    using A = typename Tr<DT>::Acc;
+    constexpr int ES = Tr<DT>::ES, V = Tr<DT>::V;
+    constexpr long long TE = (long long)kBlock * U * V;
+    const int K = KT ? KT : p.k;
+    const long long bid = blockIdx.x;
+    const long long seg = bid / p.tiles_per_seg;
+    const long long t = bid - seg * p.tiles_per_seg;
+    const int s = (int)(seg / K);
+    const int c = (int)(seg - (long long)s * K);
+    const long long j0 = (long long)s * p.sub;
+    const long long j1 = min(j0 + p.sub, p.L);
+    if (j0 >= j1) return;
+    const long long base = (long long)c * p.L;
+    const long long nc = max(0LL, min(p.L, p.n - base));
+    const bool fast = p.fast[c] != 0;
+    const long long head = fast ? (long long)(((16 - ((p.ph0[c] + j0 * ES) & 15)) & 15) / ES) : 0;
+    const long long body = min(j0 + head, j1);
+    const long long e0 = body + t * TE;
+    const long long e1 = min(e0 + TE, j1);
+
+    if (t == 0 && body > j0) rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, j0, body);
+    if (e0 >= e1) return;
+    if (!fast) {
+        rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, e0, e1);
+        return;
+    }
+    const long long ve = min(e1, nc);
+    const long long nv = ve > e0 ? (ve - e0) / V : 0;
+    if (nv > 0) {
+        const int tid = threadIdx.x;
+        char *dst = p.dst[c] + e0 * ES;
+        const long long off = (base + e0) * ES;
+        A acc[U][V];
+        if constexpr (KT != 0) {
+            // issue all U*K loads, then fold in ring order
+            u32x4 v[U][KT];
+#pragma unroll
+            for (int m = 0; m < KT; ++m) {
+                const char *ps = p.src[fold_rank(c, m, KT)] + off;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const long long q = min((long long)tid + u * kBlock, nv - 1);
+                    v[u][m] = *reinterpret_cast<const u32x4 *>(ps + q * 16);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < KT; ++m) {
+                const float w = p.w[fold_rank(c, m, KT)];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    A x[V];
+                    unpack<DT>(v[u][m], x);
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
+                }
+            }
+        } else {
+            for (int m = 0; m < K; ++m) {
+                const int r = fold_rank(c, m, K);
+                const char *ps = p.src[r] + off;
+                const float w = p.w[r];
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const long long q = min((long long)tid + u * kBlock, nv - 1);
+                    v[u] = *reinterpret_cast<const u32x4 *>(ps + q * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    A x[V];
+                    unpack<DT>(v[u], x);
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long q = (long long)tid + u * kBlock;
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[u][e] = finish<EP>(acc[u][e], p.scale);
+            if (q < nv) *reinterpret_cast<u32x4 *>(dst + q * 16) = pack<DT>(acc[u]);
+        }
+    }
+    rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, e0 + nv * V, e1);
+}
+
+// ------------------------------------------------------------------ AllGather
+
+template <int ES>
+__device__ __forceinline__ void copy1(char *d, const char *s)
+{
+    if constexpr (ES == 2) *reinterpret_cast<unsigned short *>(d) = *reinterpret_cast<const unsigned short *>(s);
+    else *reinterpret_cast<unsigned *>(d) = *reinterpret_cast<const unsigned *>(s);
+}
+
+template <int ES, int KT>
+__device__ __forceinline__ void ag_scalar_range(const AgParams &p, int K, int c, long long base,
+                                                long long lo, long long hi)
+{
+    const char *src = p.src[c];
+    for (long long j = lo + threadIdx.x; j < hi; j += kBlock) {
+        unsigned short h = 0;
+        unsigned w = 0;
+        if constexpr (ES == 2) h = *reinterpret_cast<const unsigned short *>(src + j * ES);
+        else w = *reinterpret_cast<const unsigned *>(src + j * ES);
+#pragma unroll
+        for (int r = 0; r < (KT ? KT : kMaxK); ++r) {
+            if (!KT && r >= K) break;
+            if (p.skip_own && r == c) continue;
+            char *d = p.dst[r] + (base + j) * ES;
+            if constexpr (ES == 2) *reinterpret_cast<unsigned short *>(d) = h;
+            else *reinterpret_cast<unsigned *>(d) = w;
+        }
+    }
+}
+
+template <int ES, int KT, int U>
+__global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
+{
+    constexpr int V = 16 / ES;
+    constexpr long long TE = (long long)kBlock * U * V;
+    const int K = KT ? KT : p.k;
+    const long long bid = blockIdx.x;
+    const long long seg = bid / p.tiles_per_seg;
+    const long long t = bid - seg * p.tiles_per_seg;
+    const int s = (int)(seg / K);
+    const int c = (int)(seg - (long long)s * K);
+    const long long base = (long long)c * p.L;
+    const long long nc = max(0LL, min(p.L, p.n - base));
+    const long long j0 = (long long)s * p.sub;
+    const long long j1 = min(min(j0 + p.sub, p.L), nc);   // valid elements only
+    if (j0 >= j1) return;
+    const bool fast = p.fast[c] != 0;
+    const long long head = fast ? (long long)(((16 - ((p.ph0[c] + j0 * ES) & 15)) & 15) / ES) : 0;
+    const long long body = min(j0 + head, j1);
+    const long long e0 = body + t * TE;
+    const long long e1 = min(e0 + TE, j1);
+
+    if (t == 0 && body > j0) ag_scalar_range<ES, KT>(p, K, c, base, j0, body);
+    if (e0 >= e1) return;
+    if (!fast) {
+        ag_scalar_range<ES, KT>(p, K, c, base, e0, e1);
+        return;
+    }
+    const long long nv = (e1 - e0) / V;
+    if (nv > 0) {
+        const int tid = threadIdx.x;
+        const char *src = p.src[c] + e0 * ES;
+        const long long off = (base + e0) * ES;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long q = min((long long)tid + u * kBlock, nv - 1);
+            v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
+        }
+#pragma unroll
+        for (int r = 0; r < (KT ? KT : kMaxK); ++r) {
+            if (!KT && r >= K) break;
+            if (p.skip_own && r == c) continue;
+            char *d = p.dst[r] + off;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const long long q = (long long)tid + u * kBlock;
+                if (q < nv) *reinterpret_cast<u32x4 *>(d + q * 16) = v[u];
+            }
+        }
+    }
+    ag_scalar_range<ES, KT>(p, K, c, base, e0 + nv * V, e1);
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int DT, int EP, int KT>
+hipError_t rs_go(const RsParams &p, long long grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int DT, int EP>
+hipError_t rs_k(const RsParams &p, long long grid, hipStream_t st)
+{
+    switch (p.k) {
+    case 2: return rs_go<DT, EP, 2>(p, grid, st);
+    case 4: return rs_go<DT, EP, 4>(p, grid, st);
+    case 8: return rs_go<DT, EP, 8>(p, grid, st);
+    default: return rs_go<DT, EP, 0>(p, grid, st);
+    }
+}
+
+template <int ES, int KT>
+hipError_t ag_go(const AgParams &p, long long grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int ES>
+hipError_t ag_k(const AgParams &p, long long grid, hipStream_t st)
+{
+    switch (p.k) {
+    case 2: return ag_go<ES, 2>(p, grid, st);
+    case 4: return ag_go<ES, 4>(p, grid, st);
+    case 8: return ag_go<ES, 8>(p, grid, st);
+    default: return ag_go<ES, 0>(p, grid, st);
+    }
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+int rs_vectors_per_thread(int dt)
+{
+    return dt == kF32 ? RsU<kF32>::U : dt == kBF16 ? RsU<kBF16>::U : RsU<kI32>::U;
+}
+
+}  // namespace
+
+long long plan_rs(RsParams &p, int dt)
+{
+    const int es = elem_size(dt);
+    for (int c = 0; c < p.k; ++c) {
+        const unsigned ph = (unsigned)((uintptr_t)p.dst[c] & 15);
+        bool same = true;
+        for (int r = 0; r < p.k; ++r)
+            same = same && (unsigned)(((uintptr_t)p.src[r] + (uintptr_t)(c * p.L * es)) & 15) == ph;
+        p.fast[c] = same ? 1 : 0;
+        p.ph0[c] = (unsigned char)ph;
+    }
+    p.sub = ceil_div(p.L, p.S);
+    const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
+    p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
+    return (long long)p.S * p.k * p.tiles_per_seg;
+}
+
+long long plan_ag(AgParams &p, int dt)
+{
+    const int es = elem_size(dt);
+    for (int c = 0; c < p.k; ++c) {
+        const unsigned ph = (unsigned)((uintptr_t)p.src[c] & 15);
+        bool same = true;
+        for (int r = 0; r < p.k; ++r)
+            same = same && (unsigned)(((uintptr_t)p.dst[r] + (uintptr_t)(c * p.L * es)) & 15) == ph;
+        p.fast[c] = same ? 1 : 0;
+        p.ph0[c] = (unsigned char)ph;
+    }
+    p.sub = ceil_div(p.L, p.S);
+    const long long te = (long long)kBlock * kAgU * (16 / es);
+    p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
+    return (long long)p.S * p.k * p.tiles_per_seg;
+}
+
+hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t st)
+{
+    RsParams q = p;
+    const long long grid = plan_rs(q, dt);
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (dt == kF32) {
+        switch (ep) {
+        case kSum: return rs_k<kF32, kSum>(q, grid, st);
+        case kMul: return rs_k<kF32, kMul>(q, grid, st);
+        case kDiv: return rs_k<kF32, kDiv>(q, grid, st);
+        default: return rs_k<kF32, kWeighted>(q, grid, st);
+        }
+    }
+    if (dt == kBF16) {
+        switch (ep) {
+        case kSum: return rs_k<kBF16, kSum>(q, grid, st);
+        case kMul: return rs_k<kBF16, kMul>(q, grid, st);
+        case kDiv: return rs_k<kBF16, kDiv>(q, grid, st);
+        default: return rs_k<kBF16, kWeighted>(q, grid, st);
+        }
+    }
+    return rs_k<kI32, kSum>(q, grid, st);
+}
+
+hipError_t launch_ag(const AgParams &p, int dt, hipStream_t st)
+{
+    AgParams q = p;
+    const long long grid = plan_ag(q, dt);
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return elem_size(dt) == 2 ? ag_k<2>(q, grid, st) : ag_k<4>(q, grid, st);
+}
+
+}  // namespace dps

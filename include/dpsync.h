@@ -1,0 +1,189 @@
+/*
+ * dpsync.h -- C ABI of libdpsync: data-parallel gradient and parameter
+ * synchronisation on one MI355X, with K data-parallel ranks emulated as K
+ * buffers in the GPU's HBM.
+ *
+ * Interface model: one call per collective taking (send buffers, receive
+ * buffers, element count, data type, reduction op, stream), with every
+ * operation bound to a stream that the caller synchronises (CMU 11-868
+ * L14-L15 notes, sections "NCCL's five building blocks" and the ncclAllReduce
+ * listing that follows "Ring AllReduce: ReduceScatter, then AllGather"). The
+ * communicator is replaced by explicit host arrays of K device pointers, one
+ * per emulated rank.
+ *
+ * Common conventions
+ *   - Pointer arrays (send, recv, ...) are HOST arrays of K DEVICE pointers.
+ *     They are read during the call only (copied into kernel arguments).
+ *   - Every device buffer belongs to the caller; the library never allocates,
+ *     frees or synchronises in these calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream of
+ *     the current device) and the call returns at once. Completion is the
+ *     caller's stream synchronisation or event.
+ *   - Arguments are validated before anything is enqueued. On any error
+ *     nothing runs and outputs are untouched. The library never aborts or
+ *     prints.
+ *   - Element counts are per rank. n == 0 is a no-op returning DP_OK.
+ *   - Every pointer must be aligned to its element size. A faster path is
+ *     taken where the K inputs and the output of a shard share their address
+ *     phase modulo 16 bytes.
+ *   - Shards: L = dp_shard_len(n, k) = ceil(n / k). Shard c covers elements
+ *     [c*L, min((c+1)*L, n)) of every rank; the last shards are short, or
+ *     empty when n < k*L, and are padded to L ("Sharding and Parallelism",
+ *     section "Global arrays and device-local shards": the local shard is
+ *     A[d/q] and non-divisible sizes need padding).
+ *   - Reduction order: the element of shard c is the left fold of the K rank
+ *     values in ring order rho_c = (c+1, c+2, ..., c+K-1, c) mod K, the order
+ *     in which a unidirectional ring r -> r+1 accumulates chunk c when rank c
+ *     ends up owning it (CMU notes, "Ring AllReduce: ReduceScatter, then
+ *     AllGather"). Sums are accumulated in fp32 (wrapping uint32 for int32)
+ *     and results are bit-identical for any s_chunks, stream or run.
+ *   - s_chunks (S >= 1): each shard is cut into S contiguous sub-chunks of
+ *     ceil(L/S) elements, processed in sub-chunk order, as messages are chopped
+ *     into S pieces for pipelining (CMU notes, "Why a ring: chop the data so
+ *     transfers pipeline"). It changes only the work decomposition.
+ */
+#ifndef DPSYNC_H
+#define DPSYNC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DP_MAX_K 64
+
+typedef enum {
+    DP_OK = 0,
+    DP_ERR_INVALID_ARG = 1,  /* null pointer, k out of [1, DP_MAX_K], s_chunks < 1,
+                                misaligned pointer, size overflow, bad token counts */
+    DP_ERR_UNSUPPORTED = 2,  /* dtype/op outside the enums, or AVG/weighted on DP_I32 */
+    DP_ERR_ALIAS = 3,        /* buffers overlap other than in the documented in-place forms */
+    DP_ERR_HIP = 4           /* a HIP launch failed; see dp_last_hip_error() */
+} dp_status_t;
+
+typedef enum { DP_F32 = 0, DP_BF16 = 1, DP_I32 = 2 } dp_dtype_t;
+
+typedef enum {
+    DP_SUM = 0,  /* plain sum */
+    DP_AVG = 1   /* sum, then one IEEE division of the fp32 sum by K (the average
+                    gradient of the data-parallel step, CMU notes section
+                    "Intuition: data parallelism has only one thing to
+                    synchronize", step 3) */
+} dp_op_t;
+
+/* ceil(n / k); 0 when n == 0 or k < 1. */
+size_t dp_shard_len(size_t n, int k);
+
+/* Static text for a status code (never NULL). */
+const char *dp_status_string(int status);
+
+/* hipError_t value behind the last DP_ERR_HIP returned on this thread (0 if none). */
+int dp_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dp_version(void);
+
+/*
+ * ReduceScatter ("Sharding and Parallelism", section "The cost of the
+ * inserted collectives", T_RS,ring: every rank starts with a reducible buffer
+ * and ends with its 1/K share; CMU notes, ring phase 1).
+ *   send[r] : n elements of rank r (dtype dt).
+ *   recv[c] : L = dp_shard_len(n,k) elements; receives shard c, the ring-order
+ *             fold over the K ranks of elements [c*L, c*L + n_c), then op's
+ *             epilogue (DP_AVG divides by K in fp32; bf16 is rounded once,
+ *             to nearest even, after the fp32 sum); elements n_c..L-1 are
+ *             written as zero.
+ *   In place: recv[c] == send[c] + c*L (in elements) for every c is allowed
+ *   when n == k*L; any other overlap of a recv range with a send or recv
+ *   range returns DP_ERR_ALIAS.
+ */
+dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t n, int k,
+                              int dt, int op, int s_chunks, void *stream);
+
+/*
+ * AllGather (same page and section, T_AG,ring: each rank starts with B/X and
+ * ends with all of B; CMU notes, ring phase 2).
+ *   send[c] : shard c, L elements of which the first n_c are read (pads ignored).
+ *   recv[r] : n elements; recv[r][c*L + j] = send[c][j] for every rank r.
+ *   In place: send[c] == recv[c] + c*L for every c is allowed (shard c is then
+ *   already at its place in rank c's output and is copied to the other ranks
+ *   only); other overlaps return DP_ERR_ALIAS.
+ */
+dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, int k,
+                          int dt, int s_chunks, void *stream);
+
+/*
+ * AllReduce = ReduceScatter followed by AllGather (CMU notes, section "NCCL's
+ * five building blocks"; T_AR,ring equation in "Sharding and Parallelism").
+ *   send[r], recv[r] : n elements. Every recv[r] receives the full reduced
+ *   vector, bit-identical to dp_all_gather(dp_reduce_scatter(send)).
+ *   Shard c is first reduced into recv[c] at offset c*L, then copied from
+ *   there to the other ranks; no workspace is used.
+ *   In place: recv[r] == send[r] for every r is allowed.
+ */
+dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k,
+                          int dt, int op, int s_chunks, void *stream);
+
+/*
+ * Token-weighted AllReduce for uneven per-rank token counts (the imbalance of
+ * variable-length SFT batches in "Using ODC to Accelerate AMD SFT Training",
+ * section "Why FSDP is Slow: ... Workload-imbalance Bubble"):
+ *   recv[r][i] = (sum_r f32(t_r) * send[r][i]) / f32(sum_r t_r)
+ * with the products folded in ring order without fused multiply-add and one
+ * IEEE division at the end. dt is DP_F32 or DP_BF16 (fp32 accumulation).
+ *   tokens : HOST array of k counts, each >= 0, with a positive int64 sum.
+ *   Buffers and in-place rule as dp_all_reduce.
+ */
+dp_status_t dp_weighted_reduce(const void *const *send, void *const *recv,
+                               const int64_t *tokens, size_t n, int k, int dt, int s_chunks,
+                               void *stream);
+
+/*
+ * FSDP layer step, fp32, row-major ("Sharding and Parallelism", section "Real
+ * HLO before and after partitioning", FSDP fixture: AllGather(w[64,512]) ->
+ * w[512,512] then the local dot; section "FSDP and ZeRO": the forward pass
+ * gathers W[D,F] before the dot and the backward pass reduce-scatters the
+ * gradient).
+ *   x_local[r]  : [m_local, d]   activations of rank r
+ *   w_shard[c]  : [R, f], R = ceil(d/k): rows c*R .. min((c+1)R, d) of W,
+ *                 pad rows ignored
+ *   dy_local[r] : [m_local, f] upstream gradient of rank r, or NULL for the
+ *                 forward step only
+ *   w_full[r]   : [d, f] workspace, receives the gathered W
+ *   y_local[r]  : [m_local, f] = x_local[r] . W   (fp32 MFMA)
+ *   dw_full[r]  : [d, f] workspace, receives x_local[r]^T . dy_local[r]
+ *                 (unused and may be NULL when dy_local is NULL)
+ *   dw_shard[c] : [R, f] receives rows c*R.. of sum_r dw_full[r] (ring-order
+ *                 fp32 ReduceScatter, DP_SUM), pad rows zero (may be NULL
+ *                 when dy_local is NULL)
+ *   All buffers must be pairwise disjoint (DP_ERR_ALIAS otherwise).
+ */
+dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
+                          const float *const *x_local, const float *const *w_shard,
+                          const float *const *dy_local, float *const *w_full,
+                          float *const *y_local, float *const *dw_full, float *const *dw_shard,
+                          void *stream);
+
+/*
+ * Dense bf16 GEMM used as the compute side of concurrent computation and
+ * communication (the GEMM kernel of a (GEMM, collective) pair, "Optimizing ML
+ * Concurrent Computation and Communication with GPU DMA Engines", section
+ * "Problem Formulation").
+ *   c[m,n] = a[m,kk] . b[n,kk]^T: a is [m,kk] and b is [n,kk] (both
+ *   k-contiguous, the linear-layer weight layout), c is [m,n]; all row-major
+ *   bf16 device buffers, fp32 accumulation on MFMA, result rounded to nearest
+ *   even bf16.
+ *   m, n, kk >= 1 (else DP_ERR_INVALID_ARG); kk must be a multiple of 8 and a,
+ *   b 16-byte aligned (else DP_ERR_UNSUPPORTED); c must not overlap a or b
+ *   (DP_ERR_ALIAS).
+ */
+dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n,
+                         int64_t kk, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPSYNC_H */

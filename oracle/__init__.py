@@ -64,6 +64,9 @@ def lib():
         for name in ("orc_rs_f32_at", "orc_rs_bf16_at"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [_vp, _vp, _i64, _i64, _int, _int, _int, _vp]
+        for name in ("orc_fold_f32_at", "orc_fold_bf16_at"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [_vp, _vp, _i64, _int, _int, _int, _vp]
         L.orc_ag.restype = None
         L.orc_ag.argtypes = [_int, _vp, _vp, _i64, _i64, _int, _int]
         L.orc_ar.restype = _int
@@ -168,6 +171,19 @@ def rs_at(xs, idx, op: str = "sum", order: str = "ring", L: int | None = None):
     out = np.zeros(idx.size, dtype=xs[0].dtype)
     fn = {0: lib().orc_rs_f32_at, 1: lib().orc_rs_bf16_at}[dt]
     fn(_ptrs(xs), idx.ctypes.data, idx.size, L, k, {"sum": SUM, "avg": AVG}[op],
+       ORDERS[order], out.ctypes.data)
+    return out
+
+
+def fold_at(xs_compact, shard_ids, op: str = "sum", order: str = "ring"):
+    """Reduced values of compact samples: xs_compact[r][s] is rank r's value of
+    sample s, which belongs to shard shard_ids[s]."""
+    k = len(xs_compact)
+    dt = _dtype_code(xs_compact)
+    sid = np.ascontiguousarray(shard_ids, dtype=np.int32)
+    out = np.zeros(sid.size, dtype=xs_compact[0].dtype)
+    fn = {0: lib().orc_fold_f32_at, 1: lib().orc_fold_bf16_at}[dt]
+    fn(_ptrs(xs_compact), sid.ctypes.data, sid.size, k, {"sum": SUM, "avg": AVG}[op],
        ORDERS[order], out.ctypes.data)
     return out
 

@@ -308,6 +308,28 @@ void orc_rs_bf16_at(const uint16_t *const *x, const int64_t *idx, int64_t count,
     }
 }
 
+/* Folds of compact samples: sample s has the K rank values x[r][s] and
+ * belongs to shard shard_id[s], whose ring order it is folded in. */
+void orc_fold_f32_at(const float *const *x, const int32_t *shard_id, int64_t count, int k,
+                     int op, int order, float *vals)
+{
+    for (int64_t s = 0; s < count; ++s) {
+        float acc = fold_f32(x, s, shard_id[s], k, order);
+        if (op == ORC_AVG) acc = acc / (float)k;
+        vals[s] = acc;
+    }
+}
+
+void orc_fold_bf16_at(const uint16_t *const *x, const int32_t *shard_id, int64_t count, int k,
+                      int op, int order, uint16_t *vals)
+{
+    for (int64_t s = 0; s < count; ++s) {
+        float acc = fold_bf16(x, s, shard_id[s], k, order);
+        if (op == ORC_AVG) acc = acc / (float)k;
+        vals[s] = orc_bf16_from_f32(acc);
+    }
+}
+
 /* -------------------------------------------------------------- AllGather
  * out[r][i] = shard[i / L][i mod L] for every rank r and 0 <= i < n. */
 

@@ -1,0 +1,176 @@
+"""The C-ABI library loads, exports every symbol include/dpsync.h declares, and
+rejects invalid arguments before enqueuing anything. CPU only: every call
+below fails validation (or is a no-op), so no device memory is touched and no
+kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gradient_sync_amd as dps
+from gradient_sync_amd.buckets import bucket_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dpsync.h")
+
+OK, INVALID, UNSUPPORTED, ALIAS = 0, 1, 2, 3
+F32, BF16, I32 = 0, 1, 2
+SUM, AVG = 0, 1
+P = dps.ptr_array
+MB = 1 << 20
+
+
+def fake(k, base=1 << 40, stride=MB):
+    """k distinct, 256-byte aligned, non-overlapping fake device addresses."""
+    return [base + i * stride for i in range(k)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dp_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dps.EXPORTS)
+    L = dps.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert dps.dp_version() == 100
+
+
+def test_shard_len_and_strings():
+    assert dps.dp_shard_len(0, 8) == 0
+    assert dps.dp_shard_len(10_000_019, 8) == 1_250_003
+    assert dps.dp_shard_len(1_048_576, 4) == 262_144
+    assert dps.dp_shard_len(5, 0) == 0
+    for code in range(5):
+        assert dps.dp_status_string(code).startswith("DP_")
+    assert "unknown" in dps.dp_status_string(99)
+    assert dps.dp_last_hip_error() == 0
+
+
+def rs(send, recv, n, k, dt=F32, op=SUM, s=1):
+    return dps.lib().dp_reduce_scatter(P(send), P(recv), n, k, dt, op, s, None)
+
+
+def ag(send, recv, n, k, dt=F32, s=1):
+    return dps.lib().dp_all_gather(P(send), P(recv), n, k, dt, s, None)
+
+
+def ar(send, recv, n, k, dt=F32, op=SUM, s=1):
+    return dps.lib().dp_all_reduce(P(send), P(recv), n, k, dt, op, s, None)
+
+
+def wr(send, recv, toks, n, k, dt=F32, s=1):
+    t = (ctypes.c_int64 * len(toks))(*toks)
+    return dps.lib().dp_weighted_reduce(P(send), P(recv), t, n, k, dt, s, None)
+
+
+def test_rank_count_and_chunks():
+    a, b = fake(65), fake(65, base=1 << 41)
+    assert rs(a[:2], b[:2], 100, 0) == INVALID
+    assert rs(a, b, 100, 65) == INVALID
+    assert rs(a[:2], b[:2], 100, 2, s=0) == INVALID
+    assert ag(a[:2], b[:2], 100, 2, s=-1) == INVALID
+    assert ar(a[:2], b[:2], 100, 2, s=0) == INVALID
+
+
+def test_null_and_misaligned_pointers():
+    L = dps.lib()
+    a, b = fake(4), fake(4, base=1 << 41)
+    assert L.dp_reduce_scatter(None, P(b), 100, 4, F32, SUM, 1, None) == INVALID
+    assert L.dp_all_gather(P(a), None, 100, 4, F32, 1, None) == INVALID
+    assert rs([a[0], 0, a[2], a[3]], b, 100, 4) == INVALID
+    assert rs([a[0] + 2] + a[1:], b, 100, 4, dt=F32) == INVALID       # 2-byte aligned f32
+    assert rs(a, [b[0] + 1] + b[1:], 100, 4, dt=BF16) == INVALID      # odd address bf16
+    assert rs(a, b, 1 << 62, 4) == INVALID                            # size overflow
+
+
+def test_unsupported_dtype_and_op():
+    a, b = fake(4), fake(4, base=1 << 41)
+    assert rs(a, b, 100, 4, dt=7) == UNSUPPORTED
+    assert rs(a, b, 100, 4, op=9) == UNSUPPORTED
+    assert rs(a, b, 100, 4, dt=I32, op=AVG) == UNSUPPORTED
+    assert ar(a, b, 100, 4, dt=I32, op=AVG) == UNSUPPORTED
+    assert wr(a, b, [1, 1, 1, 1], 100, 4, dt=I32) == UNSUPPORTED
+
+
+def test_token_validation():
+    a, b = fake(4), fake(4, base=1 << 41)
+    assert wr(a, b, [0, 0, 0, 0], 100, 4) == INVALID
+    assert wr(a, b, [5, -1, 0, 0], 100, 4) == INVALID
+    assert dps.lib().dp_weighted_reduce(P(a), P(b), None, 100, 4, F32, 1, None) == INVALID
+    assert wr(a, b, [1, 2, 3, 4], 0, 4) == OK                         # n == 0 is a no-op
+
+
+def test_alias_rules():
+    a = fake(4)
+    # recv overlapping a send buffer
+    assert rs(a, [a[1] + 64] + fake(3, base=1 << 41), 1000, 4) == ALIAS
+    # recv buffers overlapping each other
+    assert rs(a, [1 << 41, (1 << 41) + 16, 1 << 42, 1 << 43], 1000, 4) == ALIAS
+    # AllGather outputs overlapping each other
+    assert ag(fake(4, base=1 << 41), [a[0], a[0] + 400, a[2], a[3]], 1000, 4) == ALIAS
+    # AllGather source shard inside an output, not at the in-place position
+    assert ag([a[0] + 8, a[1], a[2], a[3]], fake(4, base=a[0]), 1000, 4) == ALIAS
+    # AllReduce: recv[r] may be send[r], but not overlap another send
+    assert ar(a, [a[1]] + fake(3, base=1 << 41), 1000, 4) == ALIAS
+    # ReduceScatter in-place form requires n == k*L
+    n = 1001
+    L = dps.dp_shard_len(n, 4)
+    assert rs(a, [a[c] + c * L * 4 for c in range(4)], n, 4) == ALIAS
+
+
+def test_zero_length_is_noop():
+    a, b = fake(3), fake(3, base=1 << 41)
+    assert rs(a, b, 0, 3) == OK
+    assert ag(a, b, 0, 3) == OK
+    assert ar(a, b, 0, 3, op=AVG) == OK
+
+
+def test_fsdp_validation():
+    L = dps.lib()
+    k = 2
+    x, ws, dy = fake(k, 1 << 40), fake(k, 1 << 41), fake(k, 1 << 42)
+    wf, y, dwf, dws = fake(k, 1 << 43), fake(k, 1 << 44), fake(k, 1 << 45), fake(k, 1 << 46)
+
+    def call(k_=k, m=8, d=8, f=8, x_=x, wf_=wf, y_=y, dy_=dy):
+        return L.dp_fsdp_layer(k_, m, d, f, P(x_), P(ws), P(dy_) if dy_ else None, P(wf_), P(y_),
+                               P(dwf), P(dws), None)
+    assert call(k_=0) == INVALID
+    assert call(m=0) == INVALID
+    assert call(d=-1) == INVALID
+    assert call(x_=[x[0], 0]) == INVALID
+    assert call(y_=[x[0], y[1]]) == ALIAS             # output on top of an input
+    assert call(wf_=[wf[0], wf[0] + 4]) == ALIAS      # outputs overlap each other
+
+
+def test_gemm_validation():
+    L = dps.lib()
+    a, b, c = 1 << 40, 1 << 41, 1 << 42
+    assert L.dp_gemm_bf16(a, b, c, 0, 8, 8, None) == INVALID
+    assert L.dp_gemm_bf16(None, b, c, 8, 8, 8, None) == INVALID
+    assert L.dp_gemm_bf16(a, b, c, 8, 8, 12, None) == UNSUPPORTED    # k not a multiple of 8
+    assert L.dp_gemm_bf16(a + 2, b, c, 8, 8, 8, None) == UNSUPPORTED
+    assert L.dp_gemm_bf16(a, b, a + 16, 8, 8, 8, None) == ALIAS
+
+
+def test_bucket_plan():
+    plan = bucket_plan(218_103_808, 25_000_000)
+    assert len(plan) == 9
+    assert plan[-1] == (200_000_000, 18_103_808)
+    assert sum(n for _, n in plan) == 218_103_808
+    assert all(o == i * 25_000_000 for i, (o, _) in enumerate(plan))
+    assert bucket_plan(0, 10) == []
+    with pytest.raises(ValueError):
+        bucket_plan(10, 0)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    t = [torch.zeros(10) for _ in range(2)]
+    with pytest.raises(ValueError):
+        dps.dp_all_reduce(t, t)

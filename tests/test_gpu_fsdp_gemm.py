@@ -1,0 +1,189 @@
+"""GPU parity of the FSDP layer step and of the bf16 GEMM, through the C ABI.
+
+The gathered weights are exact copies and must match bit for bit. The GEMMs
+run on MFMA with an accumulation order of their own, so each entry is checked
+against the oracle's fp64 value within the recursive-summation bound
+gamma_n * sum |a||b| (Higham, Accuracy and Stability of Numerical Algorithms,
+eq. 3.5); with small-integer inputs every step is exact and the comparison is
+bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import gradient_sync_amd as dps
+import oracle
+from tests.helpers import bits_equal, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+U32 = 2.0 ** -24
+U_BF16 = 2.0 ** -8
+
+
+def gamma(n, u=U32):
+    return n * u / (1 - n * u)
+
+
+def shard_rows(w, k):
+    d, f = w.shape
+    R = -(-d // k)
+    out = []
+    for c in range(k):
+        s = torch.zeros(R, f, dtype=w.dtype)
+        rows = w[c * R:(c + 1) * R]
+        s[:rows.shape[0]] = rows
+        out.append(s)
+    return out
+
+
+def run_fsdp(x, w, dy, k, backward=True):
+    m, d = x.shape
+    f = w.shape[1]
+    ml = m // k
+    R = -(-d // k)
+    xl = [x[r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    dyl = [dy[r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    ws = [s.to(DEV) for s in shard_rows(w, k)]
+    wf = [torch.full((d, f), float("nan"), device=DEV) for _ in range(k)]
+    y = [torch.full((ml, f), float("nan"), device=DEV) for _ in range(k)]
+    dwf = [torch.full((d, f), float("nan"), device=DEV) for _ in range(k)]
+    dws = [torch.full((R, f), float("nan"), device=DEV) for _ in range(k)]
+    dps.dp_fsdp_layer(xl, ws, dyl if backward else None, wf, y,
+                      dwf if backward else None, dws if backward else None)
+    torch.cuda.synchronize()
+    host = dict(xl=[to_np(t) for t in xl], ws=[to_np(t) for t in ws],
+                dyl=[to_np(t) for t in dyl])
+    return dict(wf=[to_np(t) for t in wf], y=[to_np(t) for t in y], dwf=[to_np(t) for t in dwf],
+                dws=[to_np(t) for t in dws]), host
+
+
+def check_fsdp(x, w, dy, k, exact=False):
+    m, d = x.shape
+    f = w.shape[1]
+    ml = m // k
+    R = -(-d // k)
+    got, host = run_fsdp(x, w, dy, k)
+    want = oracle.fsdp_layer(host["xl"], host["ws"], host["dyl"], d=d, nthreads=8)
+    wn, xn, dyn = w.numpy(), x.numpy(), dy.numpy()
+    for r in range(k):
+        assert bits_equal(got["wf"][r], want["w_full"][r])
+        yr = want["y"][r]
+        if exact:
+            assert bits_equal(got["y"][r], yr.astype(np.float32))
+        else:
+            _, ab = oracle.gemm_f64(host["xl"][r], wn)
+            err = np.abs(got["y"][r].astype(np.float64) - yr)
+            assert np.all(err <= gamma(d + 2) * ab), float((err / (ab + 1e-300)).max())
+    _, ab_dw = oracle.gemm_f64(xn, dyn, trans_a=True)      # sum over all ranks' rows
+    for c in range(k):
+        rows = min(R, max(0, d - c * R))
+        ws_ = want["dw_shard"][c]
+        g = got["dws"][c]
+        assert not g[rows:].any(), "pad rows must be zero"
+        if exact:
+            assert bits_equal(g[:rows], ws_[:rows].astype(np.float32))
+        else:
+            ab = ab_dw[c * R:c * R + rows]
+            err = np.abs(g[:rows].astype(np.float64) - ws_[:rows])
+            assert np.all(err <= gamma(ml + k + 2) * ab)
+    # global view: concatenated y is x @ w (normwise)
+    ycat = np.concatenate(got["y"]).astype(np.float64)
+    ref = xn.astype(np.float64) @ wn.astype(np.float64)
+    rel = np.linalg.norm(ycat - ref) / np.linalg.norm(ref)
+    assert rel < 1e-6, rel
+    return rel
+
+
+def test_fsdp_fixture_k8():
+    """x[1024,512] ~ N(0,1), w[512,512] ~ N(0,0.02^2) row-sharded over 8 ranks to
+    x_local[128,512] and w[64,512]; dy[1024,512] ~ N(0,1)."""
+    say("fsdp fixture k=8")
+    fx = gen.fsdp_fixture(seed=2, k=8)
+    check_fsdp(fx["x"], fx["w"], fx["dy"], 8)
+
+
+def test_fsdp_integer_values_exact():
+    say("fsdp integer fixture")
+    g = torch.Generator().manual_seed(0)
+    x = torch.randint(-4, 5, (1024, 512), generator=g).float()
+    w = torch.randint(-4, 5, (512, 512), generator=g).float()
+    dy = torch.randint(-4, 5, (1024, 512), generator=g).float()
+    check_fsdp(x, w, dy, 8, exact=True)
+
+
+@pytest.mark.parametrize("k,m,d,f", [(3, 111, 45, 29), (8, 64, 100, 70), (1, 5, 3, 2),
+                                     (5, 5 * 33, 64, 130), (2, 256, 96, 64)])
+def test_fsdp_ragged_shapes(k, m, d, f):
+    say(f"fsdp ragged k={k} m={m} d={d} f={f}")
+    g = torch.Generator().manual_seed(k * m + d)
+    x = torch.randn(m, d, generator=g)
+    w = torch.randn(d, f, generator=g) * 0.02
+    dy = torch.randn(m, f, generator=g)
+    check_fsdp(x, w, dy, k)
+    xi = torch.randint(-3, 4, (m, d), generator=g).float()
+    wi = torch.randint(-3, 4, (d, f), generator=g).float()
+    dyi = torch.randint(-3, 4, (m, f), generator=g).float()
+    check_fsdp(xi, wi, dyi, k, exact=True)
+
+
+def test_fsdp_forward_only():
+    fx = gen.fsdp_fixture(seed=7, k=8, m=256, d=128, f=64)
+    got, host = run_fsdp(fx["x"], fx["w"], fx["dy"], 8, backward=False)
+    want = oracle.fsdp_layer(host["xl"], host["ws"], None, d=128)
+    for r in range(8):
+        assert bits_equal(got["wf"][r], want["w_full"][r])
+        assert np.all(np.isnan(got["dws"][r]))      # untouched
+
+
+# ------------------------------------------------------------------ bf16 GEMM
+
+def _bits(t):
+    return to_np(t)
+
+
+def check_gemm(a, b, rows=None, cols=None, exact=False):
+    m, kk = a.shape
+    n = b.shape[0]
+    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dps.dp_gemm_bf16(a, b, c)
+    torch.cuda.synchronize()
+    if rows is None:
+        rows, cols = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        rows, cols = rows.ravel(), cols.ravel()
+    ab = _bits(a)
+    bt = np.ascontiguousarray(_bits(b).T)
+    ref, absr = oracle.gemm_bf16_at(ab, bt, rows, cols, nthreads=16)
+    got = oracle.bf16_to_f32(_bits(c)[rows, cols]).astype(np.float64)
+    if exact:
+        assert np.array_equal(got, ref)
+        return
+    g = gamma(kk + 1)
+    bound = U_BF16 * (np.abs(ref) + g * absr) + g * absr
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+
+
+@pytest.mark.parametrize("m,n,kk", [(128, 128, 32), (256, 384, 64), (200, 136, 40), (1, 1, 8),
+                                    (129, 255, 1000), (512, 512, 4096)])
+def test_gemm_bf16_small(m, n, kk):
+    say(f"gemm bf16 {m}x{n}x{kk}")
+    a, b = gen.gemm_bf16_inputs(8, m, n, kk, device=DEV)
+    check_gemm(a, b)
+    g = torch.Generator().manual_seed(m + n)
+    ai = torch.randint(-1, 2, (m, kk), generator=g).to(torch.bfloat16).to(DEV)
+    bi = torch.randint(-1, 2, (n, kk), generator=g).to(torch.bfloat16).to(DEV)
+    if kk <= 256:
+        check_gemm(ai, bi, exact=True)
+
+
+def test_gemm_bf16_8192_sampled():
+    """C = A B^T with A, B bf16 [8192,8192] ~ N(0,1): sampled entries."""
+    m = n = kk = 8192
+    say("gemm bf16 8192^3")
+    a, b = gen.gemm_bf16_inputs(5, m, n, kk, device=DEV)
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([rng.integers(0, m, 3000), [0, 0, m - 1, m - 1, 127, 128]])
+    cols = np.concatenate([rng.integers(0, n, 3000), [0, n - 1, 0, n - 1, 128, 127]])
+    check_gemm(a, b, rows.astype(np.int64), cols.astype(np.int64))

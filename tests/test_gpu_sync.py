@@ -1,0 +1,382 @@
+"""GPU parity of the sync kernels against the oracle, through the C ABI.
+
+Every comparison is bit-exact: with the ring fold order fixed on both sides,
+ReduceScatter, AllGather, AllReduce and the token-weighted reduction have one
+correct result for f32, bf16 and int32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import gradient_sync_amd as dps
+import oracle
+from gradient_sync_amd.buckets import BucketedSync
+from tests.helpers import bits_equal, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CANARY = 0x5A
+GUARD = 64          # guard elements on each side of an output
+
+
+class Guarded:
+    """A device buffer of `n` elements at element offset `off` inside a larger
+    allocation whose surroundings hold a canary pattern."""
+
+    def __init__(self, n, dtype, off=0):
+        self.full = torch.empty(n + off + 2 * GUARD, dtype=dtype, device=DEV)
+        self.full.view(torch.uint8).fill_(CANARY)
+        self.lo = GUARD + off
+        self.t = self.full[self.lo:self.lo + n]
+
+    def intact(self):
+        raw = self.full.view(torch.uint8).cpu().numpy()
+        es = self.full.element_size()
+        return bool(np.all(raw[:self.lo * es] == CANARY) and
+                    np.all(raw[(self.lo + self.t.numel()) * es:] == CANARY))
+
+
+def make_inputs(dtype, k, n, seed, off=0):
+    """K device input buffers (at element offset off) and their host copies."""
+    xs = []
+    for r in range(k):
+        u = gen.uniform_pm1(seed, 0, r, n)
+        if dtype == torch.int32:
+            # full-range values so that the sums wrap
+            v = gen.raw_u64(seed, 1, r, 0, n).to(torch.int32)
+        elif dtype == torch.bfloat16:
+            v = u.to(torch.bfloat16)
+        else:
+            v = u
+        g = Guarded(n, dtype, off)
+        g.t.copy_(v.to(DEV))
+        xs.append(g)
+    return xs, [to_np(g.t) for g in xs]
+
+
+def _magnitude(a):
+    """Bit pattern without the sign bit."""
+    if a.dtype == np.uint16:
+        return a & 0x7FFF
+    return a.view(np.uint32) & 0x7FFFFFFF
+
+
+# ------------------------------------------------------------ ReduceScatter
+
+CASES_K = [1, 2, 3, 4, 5, 7, 8, 16, 64]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_rs_bruteforce_small(dtype):
+    for k in CASES_K:
+        small = range(0, 3 * k + 3) if k <= 8 else [0, 1, k - 1, k, k + 1, 2 * k + 3, 3 * k + 2]
+        ns = sorted(set(list(small) + [97, 1000, 4099]))
+        for n in ns:
+            xs, hx = make_inputs(dtype, k, n, seed=1000 + k * 7 + n)
+            L = dps.dp_shard_len(n, k)
+            for op in (["sum"] if dtype == torch.int32 else ["sum", "avg"]):
+                for s in (1, 3):
+                    say(f"rs k={k} n={n} {dtype} {op} S={s}")
+                    outs = [Guarded(max(L, 0), dtype) for _ in range(k)]
+                    dps.dp_reduce_scatter([g.t for g in xs], [o.t for o in outs], op=op,
+                                          s_chunks=s, n=n)
+                    torch.cuda.synchronize()
+                    want = oracle.reduce_scatter(hx, op=op)
+                    for c in range(k):
+                        assert bits_equal(to_np(outs[c].t), want[c]), (k, n, op, s, c)
+                        assert outs[c].intact()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_rs_every_alignment(dtype):
+    """Input offsets shift the address phase of every shard; output offsets
+    make input and output phases differ (element-wise path)."""
+    k, n = 8, 3 * 4096 + 37
+    L = dps.dp_shard_len(n, k)
+    for in_off in (0, 1, 2, 3, 5, 7):
+        xs, hx = make_inputs(dtype, k, n, seed=77 + in_off, off=in_off)
+        want = oracle.reduce_scatter(hx, op="sum")
+        for out_off in (0, 1, 3, in_off):
+            say(f"rs-align {dtype} in_off={in_off} out_off={out_off}")
+            outs = [Guarded(L, dtype, out_off) for _ in range(k)]
+            dps.dp_reduce_scatter([g.t for g in xs], [o.t for o in outs], op="sum")
+            torch.cuda.synchronize()
+            for c in range(k):
+                assert bits_equal(to_np(outs[c].t), want[c]), (in_off, out_off, c)
+                assert outs[c].intact()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("k,n", [(2, 2 * 3 * 4096 + 5), (4, (1 << 20) + 3), (6, 123_457),
+                                 (8, 8 * 2048 * 5 - 1), (3, 1 << 16)])
+def test_rs_multi_tile_ragged(dtype, k, n):
+    xs, hx = make_inputs(dtype, k, n, seed=5)
+    L = dps.dp_shard_len(n, k)
+    for op in ("sum", "avg"):
+        say(f"rs-tiles k={k} n={n} {dtype} {op}")
+        outs = [Guarded(L, dtype) for _ in range(k)]
+        dps.dp_reduce_scatter([g.t for g in xs], [o.t for o in outs], op=op)
+        torch.cuda.synchronize()
+        want = oracle.reduce_scatter(hx, op=op, nthreads=8)
+        for c in range(k):
+            assert bits_equal(to_np(outs[c].t), want[c])
+            assert outs[c].intact()
+
+
+# --------------------------------------------------------------- AllGather
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_ag_bruteforce_and_alignment(dtype):
+    for k in (1, 2, 3, 8, 16):
+        for n in (0, 1, k - 1 if k > 1 else 1, k + 1, 3 * k + 2, 1000, 3 * 4096 + 37):
+            L = dps.dp_shard_len(n, k)
+            for sh_off, out_off in ((0, 0), (1, 0), (0, 3), (5, 5)):
+                say(f"ag k={k} n={n} {dtype} sh_off={sh_off} out_off={out_off}")
+                shards = []
+                for c in range(k):
+                    g = Guarded(L, dtype, sh_off)
+                    v = gen.raw_u64(9, 2, c, 0, L).to(torch.int32)
+                    g.t.copy_((v if dtype == torch.int32 else
+                               (v.to(torch.float32) * 2.0 ** -31).to(dtype)).to(DEV))
+                    shards.append(g)
+                outs = [Guarded(n, dtype, out_off) for _ in range(k)]
+                dps.dp_all_gather([g.t for g in shards], [o.t for o in outs], n=n)
+                torch.cuda.synchronize()
+                want = oracle.all_gather([to_np(g.t) for g in shards], n)
+                for r in range(k):
+                    assert bits_equal(to_np(outs[r].t), want[r]), (k, n, r)
+                    assert outs[r].intact()
+
+
+# --------------------------------------------------------------- AllReduce
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+@pytest.mark.parametrize("k,n", [(4, 10_001), (8, 8 * 4096 * 3 + 11), (5, 777), (1, 100),
+                                 (16, 50_000)])
+def test_ar_is_rs_then_ag(dtype, k, n):
+    xs, hx = make_inputs(dtype, k, n, seed=k + n)
+    op = "sum" if dtype == torch.int32 else "avg"
+    say(f"ar k={k} n={n} {dtype} {op}")
+    outs = [Guarded(n, dtype) for _ in range(k)]
+    dps.dp_all_reduce([g.t for g in xs], [o.t for o in outs], op=op, s_chunks=2)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(hx, op=op)
+    # the same through the two separate calls on the GPU
+    L = dps.dp_shard_len(n, k)
+    sh = [torch.empty(L, dtype=dtype, device=DEV) for _ in range(k)]
+    outs2 = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+    dps.dp_reduce_scatter([g.t for g in xs], sh, op=op)
+    dps.dp_all_gather(sh, outs2, n=n)
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(outs[r].t), want[r])
+        assert bits_equal(to_np(outs2[r]), want[r])
+        assert outs[r].intact()
+    # in place: recv == send
+    dps.dp_all_reduce([g.t for g in xs], [g.t for g in xs], op=op)
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(xs[r].t), want[r])
+        assert xs[r].intact()
+
+
+def test_rs_and_ag_in_place_forms():
+    k, n = 8, 8 * 5000
+    dtype = torch.float32
+    xs, hx = make_inputs(dtype, k, n, seed=3)
+    L = n // k
+    want = oracle.reduce_scatter(hx, op="avg")
+    # ReduceScatter with recv[c] = send[c] + c*L
+    dps.dp_reduce_scatter([g.t for g in xs], [g.t[c * L:(c + 1) * L] for c, g in enumerate(xs)],
+                          op="avg")
+    torch.cuda.synchronize()
+    for c in range(k):
+        assert bits_equal(to_np(xs[c].t[c * L:(c + 1) * L]), want[c])
+    # AllGather with send[c] = recv[c] + c*L
+    dps.dp_all_gather([g.t[c * L:(c + 1) * L] for c, g in enumerate(xs)], [g.t for g in xs], n=n)
+    torch.cuda.synchronize()
+    full = oracle.all_gather(want, n)
+    for r in range(k):
+        assert bits_equal(to_np(xs[r].t), full[r])
+
+
+def test_invariant_to_s_and_repeatable():
+    k, n = 8, 1_000_003
+    for dtype in (torch.float32, torch.bfloat16):
+        xs, hx = make_inputs(dtype, k, n, seed=11)
+        want = oracle.all_reduce(hx, op="avg", nthreads=8)
+        for s in (1, 2, 7, 64):
+            say(f"S-invariance {dtype} S={s}")
+            for rep in range(2):
+                outs = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+                dps.dp_all_reduce([g.t for g in xs], outs, op="avg", s_chunks=s)
+                torch.cuda.synchronize()
+                for r in (0, k - 1):
+                    assert bits_equal(to_np(outs[r]), want[r]), (dtype, s, rep)
+
+
+def test_side_stream():
+    k, n = 4, 300_000
+    xs, hx = make_inputs(torch.float32, k, n, seed=12)
+    st = torch.cuda.Stream()
+    outs = [torch.empty(n, device=DEV) for _ in range(k)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        dps.dp_all_reduce([g.t for g in xs], outs, op="sum")
+    st.synchronize()
+    want = oracle.all_reduce(hx, op="sum")
+    assert bits_equal(to_np(outs[2]), want[2])
+
+
+# ------------------------------------------------------------ weighted
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_weighted_special_cases(dtype):
+    k, n = 8, 77_777
+    xs, hx = make_inputs(dtype, k, n, seed=13)
+    outs = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+    ref = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+    say(f"weighted t=1 {dtype}")
+    dps.dp_weighted_reduce([g.t for g in xs], outs, [1] * k)
+    dps.dp_all_reduce([g.t for g in xs], ref, op="avg")
+    torch.cuda.synchronize()
+    assert bits_equal(to_np(outs[0]), to_np(ref[0]))
+    for j in (0, 5):
+        t = [0] * k
+        t[j] = 64
+        dps.dp_weighted_reduce([g.t for g in xs], outs, t)
+        torch.cuda.synchronize()
+        # one-hot power-of-two weight returns rank j's values (up to the sign of zero)
+        assert np.array_equal(_magnitude(to_np(outs[3])), _magnitude(hx[j]))
+    for toks in ([3, 1, 4, 1, 5, 9, 2, 6], [1000, 0, 0, 7, 123456, 1, 1, 2]):
+        say(f"weighted {toks} {dtype}")
+        dps.dp_weighted_reduce([g.t for g in xs], outs, toks, s_chunks=3)
+        torch.cuda.synchronize()
+        want = oracle.weighted_all_reduce(hx, toks)
+        for r in range(k):
+            assert bits_equal(to_np(outs[r]), want[r])
+
+
+# ------------------------------------------------------- workloads, full size
+
+def test_ring_allreduce_k4_1m_fp32_and_int32():
+    """K=4 ranks, 1,048,576 fp32 gradients uniform in [-1,1), S=4, averaged;
+    and the int32 copy round(1000 x), summed. Bit-exact, through RS+AG and AR."""
+    k, n, s = 4, 1_048_576, 4
+    xf = gen.ring_uniform_inputs(1, k, n, device=DEV)
+    xi = [gen.int_copy(x) for x in xf]
+    for xs, op in ((xf, "avg"), (xi, "sum"), ([x.to(torch.float32) for x in xi], "sum")):
+        say(f"k4-1m {xs[0].dtype} {op}")
+        hx = [to_np(x) for x in xs]
+        L = dps.dp_shard_len(n, k)
+        sh = [torch.empty(L, dtype=xs[0].dtype, device=DEV) for _ in range(k)]
+        out = [torch.empty(n, dtype=xs[0].dtype, device=DEV) for _ in range(k)]
+        dps.dp_reduce_scatter(xs, sh, op=op, s_chunks=s)
+        dps.dp_all_gather(sh, out, s_chunks=s)
+        out2 = [torch.empty(n, dtype=xs[0].dtype, device=DEV) for _ in range(k)]
+        dps.dp_all_reduce(xs, out2, op=op, s_chunks=s)
+        torch.cuda.synchronize()
+        want_sh = oracle.reduce_scatter(hx, op=op)
+        want = oracle.all_gather(want_sh, n)
+        for c in range(k):
+            assert bits_equal(to_np(sh[c]), want_sh[c])
+            assert bits_equal(to_np(out[c]), want[c])
+            assert bits_equal(to_np(out2[c]), want[c])
+    # integer-valued fp32 sums are exact, so they equal the int32 sums
+    a = [torch.empty(n, device=DEV) for _ in range(k)]
+    b = [torch.empty(n, dtype=torch.int32, device=DEV) for _ in range(k)]
+    dps.dp_all_reduce([x.to(torch.float32) for x in xi], a, op="sum")
+    dps.dp_all_reduce(xi, b, op="sum")
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1].to(torch.float32))
+
+
+def test_layer_buckets_k8_bf16_full_size():
+    """K=8 ranks, one GQA+SwiGLU layer of bf16 gradients (218,103,808 per rank,
+    N(0, 1e-3)), 9 buckets of at most 25,000,000, averaged ReduceScatter then
+    AllGather, in the bucketed launch configuration the benchmark times.
+    Compared bit-exactly with the oracle for every element."""
+    k, total = 8, gen.LAYER_PARAMS
+    say("layer-buckets: generating inputs")
+    grads = gen.layer_grads_bf16(3, k, device=DEV)
+    out = [torch.empty(total, dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
+    say("layer-buckets: step")
+    sync.step()
+    torch.cuda.synchronize()
+    host = [to_np(g) for g in grads]
+    say("layer-buckets: oracle")
+    for b, (off, n) in enumerate(sync.plan):
+        xs = [np.ascontiguousarray(h[off:off + n]) for h in host]
+        want = oracle.reduce_scatter(xs, op="avg", nthreads=16)
+        for c in range(k):
+            assert bits_equal(to_np(sync.shard_view(b, c)), want[c]), (b, c)
+        full = oracle.all_gather(want, n)
+        for r in (0, 3, 7):
+            assert bits_equal(to_np(out[r][off:off + n]), full[r]), (b, r)
+    for r in range(1, k):
+        assert torch.equal(out[0], out[r])
+
+
+def test_uneven_token_weighted_k8_10m():
+    """K=8 ranks, N=10,000,019 fp32 (not divisible by 8: shards of 1,250,003,
+    5 pads), token counts from sums of log-normal(7,1) document lengths,
+    out = sum_r t_r g_r / sum_r t_r. Bit-exact for every element."""
+    k, n = 8, 10_000_019
+    xs = gen.ring_uniform_inputs(4, k, n, device=DEV)
+    toks = gen.token_counts(4, k)
+    say(f"weighted-10m tokens={toks}")
+    out = [torch.empty(n, device=DEV) for _ in range(k)]
+    dps.dp_weighted_reduce(xs, out, toks)
+    torch.cuda.synchronize()
+    hx = [to_np(x) for x in xs]
+    want = oracle.weighted_all_reduce(hx, toks, nthreads=16)
+    for r in range(k):
+        assert bits_equal(to_np(out[r]), want[r])
+    # the separate calls at this size take the shard-phase-mismatch path
+    L = dps.dp_shard_len(n, k)
+    sh = [torch.empty(L, device=DEV) for _ in range(k)]
+    dps.dp_reduce_scatter(xs, sh, op="avg")
+    dps.dp_all_gather(sh, out)
+    torch.cuda.synchronize()
+    want_sh = oracle.reduce_scatter(hx, op="avg", nthreads=16)
+    for c in range(k):
+        assert bits_equal(to_np(sh[c]), want_sh[c])
+    want_full = oracle.all_gather(want_sh, n, nthreads=16)
+    for r in (0, 7):
+        assert bits_equal(to_np(out[r]), want_full[r])
+
+
+def test_one_gib_per_rank_k8_fp32_sampled():
+    """K=8 ranks of 268,435,456 fp32 (1 GiB each): ReduceScatter + AllGather.
+    Checked at sampled positions (every shard boundary, the ends, and random
+    indices) against the oracle's fold of the same input values, plus the
+    property that all K outputs are equal."""
+    k, n = 8, 268_435_456
+    say("1gib: generating inputs")
+    xs = gen.ring_uniform_inputs(5, k, n, device=DEV)
+    L = dps.dp_shard_len(n, k)
+    sh = [torch.empty(L, device=DEV) for _ in range(k)]
+    out = [torch.empty(n, device=DEV) for _ in range(k)]
+    say("1gib: rs+ag")
+    dps.dp_reduce_scatter(xs, sh, op="sum")
+    dps.dp_all_gather(sh, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([
+        rng.integers(0, n, 200_000), np.arange(k) * L, np.arange(1, k + 1) * L - 1,
+        np.arange(16), n - 1 - np.arange(16)]).astype(np.int64))
+    ti = torch.from_numpy(idx).to(DEV)
+    comp = [to_np(x[ti]) for x in xs]
+    want = oracle.fold_at(comp, idx // L, op="sum")
+    # shards at the sampled positions
+    shard_vals = np.empty(idx.size, np.float32)
+    for c in range(k):
+        m = (idx // L) == c
+        shard_vals[m] = to_np(sh[c][torch.from_numpy(idx[m] - c * L).to(DEV)])
+    assert bits_equal(shard_vals, want)
+    for r in range(k):
+        assert bits_equal(to_np(out[r][ti]), want)
+    for r in range(1, k):
+        assert torch.equal(out[0], out[r])

@@ -315,6 +315,17 @@ def test_rs_at_matches_full():
         assert got[s] == full[i // L][i % L]
 
 
+def test_fold_at_matches_full():
+    k, n = 8, 4001
+    xs = _rand_f32(k, n, 23)
+    full = oracle.reduce_scatter(xs, op="avg")
+    L = oracle.shard_len(n, k)
+    idx = np.array([0, 500, 501, 1999, 4000, 3500], np.int64)
+    comp = [np.ascontiguousarray(x[idx]) for x in xs]
+    got = oracle.fold_at(comp, idx // L, op="avg")
+    assert np.array_equal(got, np.array([full[i // L][i % L] for i in idx], np.float32))
+
+
 # ------------------------------------------------------------------ shapes
 
 def test_shard_shapes_from_the_pages():
@@ -344,13 +355,13 @@ def test_gemm_f64_matches_numpy():
 
 
 def test_gemm_bf16_at_matches_numpy():
-    a, b = gen.gemm_bf16_inputs(5, 40, 24, 96)
+    a, b = gen.gemm_bf16_inputs(5, 40, 24, 96)          # b is [n, k]
     ab = a.view(torch.int16).numpy().view(np.uint16)
-    bb = b.view(torch.int16).numpy().view(np.uint16)
+    bb = np.ascontiguousarray(b.view(torch.int16).numpy().view(np.uint16).T)
     rows = np.array([0, 3, 39, 17], np.int64)
     cols = np.array([0, 23, 5, 11], np.int64)
     vals, _ = oracle.gemm_bf16_at(ab, bb, rows, cols)
-    ref = a.double().numpy() @ b.double().numpy()
+    ref = a.double().numpy() @ b.double().numpy().T
     assert np.allclose(vals, ref[rows, cols], rtol=0, atol=1e-12)
 
 
