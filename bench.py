@@ -67,20 +67,27 @@ def bench_layer(args):
         sync.step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
-    events = []
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        sync.step(events=events)
+        sync.step()
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
     gpu_ms = ev0.elapsed_time(ev1)
     value = step_bytes * args.steps / wall / 1e9
+    # Per-kernel durations: the same steps again, with a pair of HIP events
+    # recorded on the launch stream around every launch. Kept out of the
+    # throughput loop above because 36 event records per step cost ~0.1 ms.
+    events = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        sync.step(events=events)
+    torch.cuda.synchronize()
 
     # per-launch durations of full-size buckets, per kernel
     full = gen.BUCKET_ELEMS
@@ -118,6 +125,7 @@ def bench_layer(args):
                    "buckets": len(sync.plan), "op": "avg", "accumulate": "fp32, ring order"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "kernel_timing": "HIP events around every launch in a second pass of the same steps",
         "bytes_per_step": step_bytes,
         "kernels": {names[k_]: {kk: (round(v, 2) if isinstance(v, float) else v)
                                 for kk, v in d.items()} for k_, d in kern.items()},

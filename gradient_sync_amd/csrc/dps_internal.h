@@ -23,13 +23,17 @@ struct RsParams {
     const char *src[kMaxK];     // rank r input, element 0
     char *dst[kMaxK];           // shard c output, element 0 of the shard
     float w[kMaxK];             // per-rank weights f32(t_r) (kWeighted)
-    unsigned char fast[kMaxK];  // shard c: all inputs and the output share a 16-byte phase
-    unsigned char ph0[kMaxK];   // that phase (bytes) at shard element 0
+    // shard c: bit 4 set when all inputs and the output share one address phase
+    // modulo 16 bytes; bits 0-3 hold that phase at shard element 0. 32-bit
+    // words so the kernel reads them with scalar loads.
+    int meta[kMaxK];
     float scale;                // 1/K (kMul), K (kDiv), sum of tokens (kWeighted)
     int write_pads;             // write zero into elements n_c..L-1 of every shard
     long long n, L;             // elements per rank, shard length
     long long sub;              // elements per sub-chunk, ceil(L/S)
-    long long tiles_per_seg;    // workgroups per (sub-chunk, shard) segment
+    long long tiles_per_seg;    // tiles per (sub-chunk, shard) segment
+    long long total_tiles;      // S * K * tiles_per_seg
+    int max_blocks;             // persistent grid size (0: library default)
     int k, S;
 };
 
@@ -38,14 +42,16 @@ struct RsParams {
 struct AgParams {
     const char *src[kMaxK];     // shard c, element 0
     char *dst[kMaxK];           // rank r output, element 0
-    unsigned char fast[kMaxK];
-    unsigned char ph0[kMaxK];
+    int meta[kMaxK];            // as RsParams::meta, for shard c and the K outputs
     int skip_own;               // do not copy shard c to rank c (already in place)
-    long long n, L, sub, tiles_per_seg;
+    long long n, L, sub, tiles_per_seg, total_tiles;
+    int max_blocks;
     int k, S;
 };
 
 // Fill the phase table and tiling of the parameter blocks; returns the grid size.
+// The kernels are persistent: each workgroup walks tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... of the flat (sub-chunk, shard, tile) space.
 long long plan_rs(RsParams &p, int dt);
 long long plan_ag(AgParams &p, int dt);
 

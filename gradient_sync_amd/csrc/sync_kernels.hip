@@ -13,9 +13,13 @@
 //
 // Both are HBM-bound streams: per 16-byte vector of shard elements the
 // ReduceScatter reads K vectors and writes one; the AllGather reads one and
-// writes K. Each workgroup handles one tile of one (sub-chunk, shard)
-// segment, so the fold order rho_c and the alignment decision are uniform per
-// workgroup. Where the K inputs and the output of a shard share their address
+// writes K. The work is cut into tiles of one (sub-chunk, shard) segment, so
+// the fold order rho_c and the alignment decision are uniform per tile; a
+// persistent grid of workgroups walks the tiles. ReduceScatter inputs are read
+// once, so they are loaded with the nontemporal hint. The per-shard phase
+// table is kept in 32-bit words so that it is read with scalar loads.
+//
+// Where the K inputs and the output of a shard share their address
 // phase modulo 16 bytes, the body of the tile moves 128-bit vectors (one
 // global_load/store_dwordx4 per lane, consecutive lanes on consecutive
 // vectors) and the unaligned head and the tail are done element by element;
@@ -38,6 +42,33 @@ template <> struct Tr<kI32>  { using Acc = unsigned; static constexpr int ES = 4
 // vectors per thread per tile
 template <int DT> struct RsU { static constexpr int U = 2; };
 constexpr int kAgU = 2;
+// persistent grid: workgroups per CU and the CU count the default assumes
+// Default grid: one workgroup per tile (a wave that finishes its tile exits
+// instead of waiting for its stores before loading the next tile). A positive
+// DPS_BLOCKS_PER_CU caps the grid at that many workgroups per CU instead.
+#ifndef DPS_BLOCKS_PER_CU
+#define DPS_BLOCKS_PER_CU 0
+#endif
+constexpr int kBlocksPerCU = DPS_BLOCKS_PER_CU;
+constexpr int kCUs = 256;
+
+#ifndef DPS_RS_NT_STORE
+#define DPS_RS_NT_STORE 1
+#endif
+
+__device__ __forceinline__ u32x4 load_stream(const char *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ void store_rs(char *p, u32x4 v)
+{
+#if DPS_RS_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+#else
+    *reinterpret_cast<u32x4 *>(p) = v;
+#endif
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned h) { return __uint_as_float(h << 16); }
 
@@ -153,14 +184,79 @@ __device__ __forceinline__ void rs_scalar_range(const RsParams &p, int K, int c,
     }
 }
 
+// The 128-bit body of a tile: nv vectors (nv == kBlock*U when FULL). The FULL
+// variant has no per-lane conditions, so all loads are issued back to back and
+// the stores are not separated by waits on earlier memory operations.
+template <int DT, int EP, int KT, int U, bool FULL>
+__device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const int c,
+                                           const long long off, char *dst, const long long nv)
+{
+    using A = typename Tr<DT>::Acc;
+    constexpr int V = Tr<DT>::V;
+    const int tid = threadIdx.x;
+    A acc[U][V];
+    if constexpr (KT != 0) {
+        // issue all U*K loads, then fold in ring order
+        u32x4 v[U][KT];
+#pragma unroll
+        for (int m = 0; m < KT; ++m) {
+            const char *ps = p.src[fold_rank(c, m, KT)] + off;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const long long q = FULL ? (long long)tid + u * kBlock
+                                         : min((long long)tid + u * kBlock, nv - 1);
+                v[u][m] = load_stream(ps + q * 16);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < KT; ++m) {
+            const float w = p.w[fold_rank(c, m, KT)];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                A x[V];
+                unpack<DT>(v[u][m], x);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
+            }
+        }
+    } else {
+        for (int m = 0; m < K; ++m) {
+            const int r = fold_rank(c, m, K);
+            const char *ps = p.src[r] + off;
+            const float w = p.w[r];
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const long long q = FULL ? (long long)tid + u * kBlock
+                                         : min((long long)tid + u * kBlock, nv - 1);
+                v[u] = load_stream(ps + q * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                A x[V];
+                unpack<DT>(v[u], x);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const long long q = (long long)tid + u * kBlock;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[u][e] = finish<EP>(acc[u][e], p.scale);
+        if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]));
+    }
+}
+
 template <int DT, int EP, int KT, int U>
-__global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
+__device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const long long bid)
 {
     using A = typename Tr<DT>::Acc;
     constexpr int ES = Tr<DT>::ES, V = Tr<DT>::V;
     constexpr long long TE = (long long)kBlock * U * V;
-    const int K = KT ? KT : p.k;
-    const long long bid = blockIdx.x;
     const long long seg = bid / p.tiles_per_seg;
     const long long t = bid - seg * p.tiles_per_seg;
     const int s = (int)(seg / K);
@@ -170,8 +266,9 @@ __global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
     if (j0 >= j1) return;
     const long long base = (long long)c * p.L;
     const long long nc = max(0LL, min(p.L, p.n - base));
-    const bool fast = p.fast[c] != 0;
-    const long long head = fast ? (long long)(((16 - ((p.ph0[c] + j0 * ES) & 15)) & 15) / ES) : 0;
+    const int meta = p.meta[c];
+    const bool fast = (meta & 16) != 0;
+    const long long head = fast ? (long long)(((16 - (((meta & 15) + j0 * ES) & 15)) & 15) / ES) : 0;
     const long long body = min(j0 + head, j1);
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
@@ -184,65 +281,21 @@ __global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
     }
     const long long ve = min(e1, nc);
     const long long nv = ve > e0 ? (ve - e0) / V : 0;
-    if (nv > 0) {
-        const int tid = threadIdx.x;
-        char *dst = p.dst[c] + e0 * ES;
-        const long long off = (base + e0) * ES;
-        A acc[U][V];
-        if constexpr (KT != 0) {
-            // issue all U*K loads, then fold in ring order
-            u32x4 v[U][KT];
-#pragma unroll
-            for (int m = 0; m < KT; ++m) {
-                const char *ps = p.src[fold_rank(c, m, KT)] + off;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const long long q = min((long long)tid + u * kBlock, nv - 1);
-                    v[u][m] = *reinterpret_cast<const u32x4 *>(ps + q * 16);
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < KT; ++m) {
-                const float w = p.w[fold_rank(c, m, KT)];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    A x[V];
-                    unpack<DT>(v[u][m], x);
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
-                }
-            }
-        } else {
-            for (int m = 0; m < K; ++m) {
-                const int r = fold_rank(c, m, K);
-                const char *ps = p.src[r] + off;
-                const float w = p.w[r];
-                u32x4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const long long q = min((long long)tid + u * kBlock, nv - 1);
-                    v[u] = *reinterpret_cast<const u32x4 *>(ps + q * 16);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    A x[V];
-                    unpack<DT>(v[u], x);
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        acc[u][e] = m == 0 ? term<EP>(x[e], w) : acc[u][e] + term<EP>(x[e], w);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const long long q = (long long)tid + u * kBlock;
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[u][e] = finish<EP>(acc[u][e], p.scale);
-            if (q < nv) *reinterpret_cast<u32x4 *>(dst + q * 16) = pack<DT>(acc[u]);
-        }
-    }
+    char *dst = p.dst[c] + e0 * ES;
+    const long long off = (base + e0) * ES;
+    if (nv == (long long)kBlock * U)
+        rs_vectors<DT, EP, KT, U, true>(p, K, c, off, dst, nv);
+    else if (nv > 0)
+        rs_vectors<DT, EP, KT, U, false>(p, K, c, off, dst, nv);
     rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, e0 + nv * V, e1);
+}
+
+template <int DT, int EP, int KT, int U>
+__global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
+{
+    const int K = KT ? KT : p.k;
+    for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
+        rs_tile<DT, EP, KT, U>(p, K, bid);
 }
 
 // ------------------------------------------------------------------ AllGather
@@ -275,13 +328,40 @@ __device__ __forceinline__ void ag_scalar_range(const AgParams &p, int K, int c,
     }
 }
 
+// The 128-bit body of an AllGather tile. Destinations are visited as ranks
+// c+1, c+2, ... (mod K), with rank c itself last and left out when SKIP_OWN, so
+// the store sequence has no per-rank branch.
+template <int ES, int KT, int U, bool FULL, bool SKIP_OWN>
+__device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const int c,
+                                           const char *src, const long long off, const long long nv)
+{
+    const int tid = threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const long long q = FULL ? (long long)tid + u * kBlock : min((long long)tid + u * kBlock, nv - 1);
+        v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
+    }
+    const int nr = SKIP_OWN ? K - 1 : K;
+#pragma unroll
+    for (int i = 0; i < (KT ? (SKIP_OWN ? KT - 1 : KT) : kMaxK); ++i) {
+        if (!KT && i >= nr) break;
+        int r = c + 1 + i;
+        r = r >= K ? r - K : r;
+        char *d = p.dst[r] + off;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long q = (long long)tid + u * kBlock;
+            if (FULL || q < nv) *reinterpret_cast<u32x4 *>(d + q * 16) = v[u];
+        }
+    }
+}
+
 template <int ES, int KT, int U>
-__global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
+__device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const long long bid)
 {
     constexpr int V = 16 / ES;
     constexpr long long TE = (long long)kBlock * U * V;
-    const int K = KT ? KT : p.k;
-    const long long bid = blockIdx.x;
     const long long seg = bid / p.tiles_per_seg;
     const long long t = bid - seg * p.tiles_per_seg;
     const int s = (int)(seg / K);
@@ -291,8 +371,9 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
     const long long j0 = (long long)s * p.sub;
     const long long j1 = min(min(j0 + p.sub, p.L), nc);   // valid elements only
     if (j0 >= j1) return;
-    const bool fast = p.fast[c] != 0;
-    const long long head = fast ? (long long)(((16 - ((p.ph0[c] + j0 * ES) & 15)) & 15) / ES) : 0;
+    const int meta = p.meta[c];
+    const bool fast = (meta & 16) != 0;
+    const long long head = fast ? (long long)(((16 - (((meta & 15) + j0 * ES) & 15)) & 15) / ES) : 0;
     const long long body = min(j0 + head, j1);
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
@@ -304,29 +385,24 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
         return;
     }
     const long long nv = (e1 - e0) / V;
-    if (nv > 0) {
-        const int tid = threadIdx.x;
-        const char *src = p.src[c] + e0 * ES;
-        const long long off = (base + e0) * ES;
-        u32x4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const long long q = min((long long)tid + u * kBlock, nv - 1);
-            v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
-        }
-#pragma unroll
-        for (int r = 0; r < (KT ? KT : kMaxK); ++r) {
-            if (!KT && r >= K) break;
-            if (p.skip_own && r == c) continue;
-            char *d = p.dst[r] + off;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const long long q = (long long)tid + u * kBlock;
-                if (q < nv) *reinterpret_cast<u32x4 *>(d + q * 16) = v[u];
-            }
-        }
+    const char *src = p.src[c] + e0 * ES;
+    const long long off = (base + e0) * ES;
+    if (nv == (long long)kBlock * U) {
+        if (p.skip_own) ag_vectors<ES, KT, U, true, true>(p, K, c, src, off, nv);
+        else ag_vectors<ES, KT, U, true, false>(p, K, c, src, off, nv);
+    } else if (nv > 0) {
+        if (p.skip_own) ag_vectors<ES, KT, U, false, true>(p, K, c, src, off, nv);
+        else ag_vectors<ES, KT, U, false, false>(p, K, c, src, off, nv);
     }
     ag_scalar_range<ES, KT>(p, K, c, base, e0 + nv * V, e1);
+}
+
+template <int ES, int KT, int U>
+__global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
+{
+    const int K = KT ? KT : p.k;
+    for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
+        ag_tile<ES, KT, U>(p, K, bid);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -376,38 +452,54 @@ int rs_vectors_per_thread(int dt)
 
 }  // namespace
 
+namespace {
+
+// bit 4: every input of shard c (at element c*L) and the shard's output share
+// one 16-byte phase; bits 0-3: that phase
+int phase_meta(const char *const *ins, long long in_off_bytes, int k, const char *out)
+{
+    const unsigned ph = (unsigned)((uintptr_t)out & 15);
+    bool same = true;
+    for (int r = 0; r < k; ++r)
+        same = same && (unsigned)(((uintptr_t)ins[r] + (uintptr_t)in_off_bytes) & 15) == ph;
+    return (same ? 16 : 0) | (int)ph;
+}
+
+long long grid_for(long long total_tiles, int max_blocks)
+{
+    long long cap = max_blocks > 0 ? max_blocks
+                    : kBlocksPerCU > 0 ? (long long)kBlocksPerCU * kCUs : 0x7fffffffLL;
+    return total_tiles < cap ? total_tiles : cap;
+}
+
+}  // namespace
+
 long long plan_rs(RsParams &p, int dt)
 {
     const int es = elem_size(dt);
-    for (int c = 0; c < p.k; ++c) {
-        const unsigned ph = (unsigned)((uintptr_t)p.dst[c] & 15);
-        bool same = true;
-        for (int r = 0; r < p.k; ++r)
-            same = same && (unsigned)(((uintptr_t)p.src[r] + (uintptr_t)(c * p.L * es)) & 15) == ph;
-        p.fast[c] = same ? 1 : 0;
-        p.ph0[c] = (unsigned char)ph;
-    }
+    for (int c = 0; c < p.k; ++c)
+        p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c]);
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
-    return (long long)p.S * p.k * p.tiles_per_seg;
+    p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
+    return grid_for(p.total_tiles, p.max_blocks);
 }
 
 long long plan_ag(AgParams &p, int dt)
 {
     const int es = elem_size(dt);
     for (int c = 0; c < p.k; ++c) {
-        const unsigned ph = (unsigned)((uintptr_t)p.src[c] & 15);
-        bool same = true;
-        for (int r = 0; r < p.k; ++r)
-            same = same && (unsigned)(((uintptr_t)p.dst[r] + (uintptr_t)(c * p.L * es)) & 15) == ph;
-        p.fast[c] = same ? 1 : 0;
-        p.ph0[c] = (unsigned char)ph;
+        // the K outputs at element c*L against the shard (the "input" here)
+        const char *outs[kMaxK];
+        for (int r = 0; r < p.k; ++r) outs[r] = p.dst[r];
+        p.meta[c] = phase_meta(outs, (long long)c * p.L * es, p.k, p.src[c]);
     }
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kBlock * kAgU * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
-    return (long long)p.S * p.k * p.tiles_per_seg;
+    p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
+    return grid_for(p.total_tiles, p.max_blocks);
 }
 
 hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t st)
