@@ -17,6 +17,7 @@ Other measurements (each prints its own JSON line):
   --config weighted  token-weighted AllReduce, K=8, 10,000,019 fp32
   --config c3        RS+AG of 1 GiB/rank fp32 (K=8) concurrent with a bf16
                      8192^3 GEMM on another stream
+  --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
 from __future__ import annotations
@@ -324,7 +325,31 @@ def bench_c3(args):
                                    "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}
 
 
-CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3}
+def bench_copy(args):
+    """A plain elementwise device copy of known size (1 GiB read + 1 GiB
+    written): the practical HBM ceiling on this GPU, and the reference against
+    which the HBM byte counters are scaled."""
+    import torch
+    n = 1 << 28
+    xs = [torch.ones(n, device="cuda") for _ in range(2)]
+    ys = [torch.empty(n, device="cuda") for _ in range(2)]
+    flip = [0]
+
+    def go():
+        i = flip[0]
+        flip[0] ^= 1
+        torch.neg(xs[i], out=ys[i])
+    ms = _time_ms(go, warm=6, reps=9)
+    med = statistics.median(ms)
+    b = 2 * n * 4
+    return {"metric": "plain elementwise copy (torch.neg), 1 GiB fp32 in, 1 GiB out",
+            "unit": "GB/s", "value": round(b / (med * 1e-3) / 1e9, 1),
+            "median_us": round(1e3 * med, 2), "bytes_per_launch": b,
+            "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
+           "copy": bench_copy}
 
 
 def main():

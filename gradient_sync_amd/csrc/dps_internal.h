@@ -23,9 +23,10 @@ struct RsParams {
     const char *src[kMaxK];     // rank r input, element 0
     char *dst[kMaxK];           // shard c output, element 0 of the shard
     float w[kMaxK];             // per-rank weights f32(t_r) (kWeighted)
-    // shard c: bit 4 set when all inputs and the output share one address phase
-    // modulo 16 bytes; bits 0-3 hold that phase at shard element 0. 32-bit
-    // words so the kernel reads them with scalar loads.
+    // shard c: bit 8 set when all inputs and the output share one address phase
+    // modulo 16 bytes; bits 0-7 hold the alignment anchor's address modulo 256
+    // at shard element 0. 32-bit words so the kernel reads them with scalar
+    // loads.
     int meta[kMaxK];
     float scale;                // 1/K (kMul), K (kDiv), sum of tokens (kWeighted)
     int write_pads;             // write zero into elements n_c..L-1 of every shard

@@ -41,7 +41,13 @@ template <> struct Tr<kI32>  { using Acc = unsigned; static constexpr int ES = 4
 
 // vectors per thread per tile
 template <int DT> struct RsU { static constexpr int U = 2; };
-constexpr int kAgU = 2;
+#ifndef DPS_AG_U
+#define DPS_AG_U 2
+#endif
+constexpr int kAgU = DPS_AG_U;
+#ifndef DPS_AG_NT_LOAD
+#define DPS_AG_NT_LOAD 0
+#endif
 // persistent grid: workgroups per CU and the CU count the default assumes
 // Default grid: one workgroup per tile (a wave that finishes its tile exits
 // instead of waiting for its stores before loading the next tile). A positive
@@ -55,6 +61,19 @@ constexpr int kCUs = 256;
 #ifndef DPS_RS_NT_STORE
 #define DPS_RS_NT_STORE 1
 #endif
+
+// Tile bodies start on a kAlign-byte boundary of the dominant stream: the K
+// inputs for ReduceScatter (unless DPS_RS_ALIGN_OUT), the K outputs for
+// AllGather.
+#ifndef DPS_ALIGN
+#define DPS_ALIGN 128
+#endif
+#ifndef DPS_RS_ALIGN_OUT
+#define DPS_RS_ALIGN_OUT 0
+#endif
+constexpr int kAlign = DPS_ALIGN;
+constexpr int kFastBit = 256;
+static_assert(kAlign >= 16 && kAlign <= 256 && (kAlign & (kAlign - 1)) == 0, "alignment");
 
 __device__ __forceinline__ u32x4 load_stream(const char *p)
 {
@@ -267,8 +286,9 @@ __device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const lo
     const long long base = (long long)c * p.L;
     const long long nc = max(0LL, min(p.L, p.n - base));
     const int meta = p.meta[c];
-    const bool fast = (meta & 16) != 0;
-    const long long head = fast ? (long long)(((16 - (((meta & 15) + j0 * ES) & 15)) & 15) / ES) : 0;
+    const bool fast = (meta & kFastBit) != 0;
+    const long long head = fast ? (long long)(((kAlign - (((meta & 255) + j0 * ES) & (kAlign - 1))) &
+                                               (kAlign - 1)) / ES) : 0;
     const long long body = min(j0 + head, j1);
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
@@ -340,7 +360,11 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const long long q = FULL ? (long long)tid + u * kBlock : min((long long)tid + u * kBlock, nv - 1);
+#if DPS_AG_NT_LOAD
+        v[u] = load_stream(src + q * 16);
+#else
         v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
+#endif
     }
     const int nr = SKIP_OWN ? K - 1 : K;
 #pragma unroll
@@ -372,8 +396,9 @@ __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const lo
     const long long j1 = min(min(j0 + p.sub, p.L), nc);   // valid elements only
     if (j0 >= j1) return;
     const int meta = p.meta[c];
-    const bool fast = (meta & 16) != 0;
-    const long long head = fast ? (long long)(((16 - (((meta & 15) + j0 * ES) & 15)) & 15) / ES) : 0;
+    const bool fast = (meta & kFastBit) != 0;
+    const long long head = fast ? (long long)(((kAlign - (((meta & 255) + j0 * ES) & (kAlign - 1))) &
+                                               (kAlign - 1)) / ES) : 0;
     const long long body = min(j0 + head, j1);
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
@@ -456,13 +481,20 @@ namespace {
 
 // bit 4: every input of shard c (at element c*L) and the shard's output share
 // one 16-byte phase; bits 0-3: that phase
-int phase_meta(const char *const *ins, long long in_off_bytes, int k, const char *out)
+// kFastBit: every stream ins[r] + in_off and `out` share one 16-byte phase.
+// Bits 0-7: the address phase modulo 256 of the anchor stream (ins[0] + in_off
+// when anchor_ins, else out) at shard element 0; tile bodies start where the
+// anchor is kAlign-byte aligned, so its wave-wide 1 KiB accesses cover whole
+// cache lines.
+int phase_meta(const char *const *ins, long long in_off_bytes, int k, const char *out,
+               bool anchor_ins)
 {
     const unsigned ph = (unsigned)((uintptr_t)out & 15);
     bool same = true;
     for (int r = 0; r < k; ++r)
         same = same && (unsigned)(((uintptr_t)ins[r] + (uintptr_t)in_off_bytes) & 15) == ph;
-    return (same ? 16 : 0) | (int)ph;
+    const uintptr_t anchor = anchor_ins ? (uintptr_t)ins[0] + (uintptr_t)in_off_bytes : (uintptr_t)out;
+    return (same ? kFastBit : 0) | (int)(anchor & 255);
 }
 
 long long grid_for(long long total_tiles, int max_blocks)
@@ -478,7 +510,7 @@ long long plan_rs(RsParams &p, int dt)
 {
     const int es = elem_size(dt);
     for (int c = 0; c < p.k; ++c)
-        p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c]);
+        p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c], !DPS_RS_ALIGN_OUT);
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
@@ -493,7 +525,7 @@ long long plan_ag(AgParams &p, int dt)
         // the K outputs at element c*L against the shard (the "input" here)
         const char *outs[kMaxK];
         for (int r = 0; r < p.k; ++r) outs[r] = p.dst[r];
-        p.meta[c] = phase_meta(outs, (long long)c * p.L * es, p.k, p.src[c]);
+        p.meta[c] = phase_meta(outs, (long long)c * p.L * es, p.k, p.src[c], true);
     }
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kBlock * kAgU * (16 / es);
