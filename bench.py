@@ -34,8 +34,29 @@ MFMA_F32_TFLOPS = 157.3        # dense fp32 matrix
 MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 
 
+# HBM bytes per full-bucket launch from two rocprofv3 PMC passes (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
+# sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
+MEASURED_TRAFFIC = {
+    "sources_sha256": "5d1e6c7fa8eeb56503474c0148f257710a4a0907e905af703ce58ed6532cfc7c"
+                      "4654b4c820abfecd7711b119a967e292af0956bcc797d798fb436ea42601cb63",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195400.7 + 49744.5) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24937.5 + 390626.0) * 1024,
+}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = ""
+    for f in ("sync_kernels.hip", "dps_internal.h"):
+        with open(os.path.join(here, "gradient_sync_amd", "csrc", f), "rb") as fh:
+            out += hashlib.sha256(fh.read()).hexdigest()
+    return out
 
 
 def host_cores() -> int:
@@ -106,6 +127,8 @@ def bench_layer(args):
     dom = max(tot, key=tot.get)
     achieved = kern[dom]["gbs"]
     names = {"rs": "rs_kernel<bf16, avg, K=8>", "ag": "ag_kernel<2-byte, K=8>"}
+    traffic = (round(MEASURED_TRAFFIC[names[dom]])
+               if kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"] else None)
     line = {
         "metric": "reduce-scatter+all-gather HBM GB/s (% of peak), K=8 bf16 25M-elem buckets",
         "value": round(value, 2),
@@ -132,7 +155,8 @@ def bench_layer(args):
                                 for kk, v in d.items()} for k_, d in kern.items()},
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "bytes_per_launch": launch_bytes,
                      "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements"},
     }
