@@ -7,10 +7,20 @@
 //
 // Both operands are k-contiguous (the linear-layer weight layout), so each
 // lane's MFMA operand is one 16-byte run of 8 bf16 values in LDS.
-// Workgroup: 256 threads = 2x2 waves, 128x128 tile of C, depth-32 k steps
-// staged through LDS with the next step's global loads issued before the
-// current step's MFMAs. Each wave owns 64x64 = 2x2 blocks of
-// v_mfma_f32_32x32x16_bf16.
+//
+// Workgroup: 512 threads = 8 waves arranged 2 (rows) x 4 (columns) over a
+// 256x256 tile of C; each wave owns 128x64 = 4x2 blocks of
+// v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane). k is walked in
+// stages of 32 through double-buffered LDS (2 x 32 KiB); the next stage's global
+// loads (4 x 16 bytes per thread) are issued before the current stage's MFMAs.
+// A 256x256 tile does 128 flop per byte loaded, which keeps the kernel off the
+// L2 bandwidth limit a 128x128 tile (64 flop/byte) runs into.
+// Tiles are ordered so that the workgroups running together on one XCD (ids
+// round-robin over 8 XCDs) cover a compact block of C and share A and B rows
+// in that XCD's L2.
+//
+// Edge tiles (M or N not multiples of 256, Kd not a multiple of 32) take a
+// guarded path: out-of-range rows and k-chunks load zeros, stores are masked.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l):
 //   A operand: A[i = l % 32][k = 8*(l/32) + 0..7]
@@ -25,7 +35,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 128, TK = 32, LDK = TK + 8;
+constexpr int TM = 256, TN = 256, TK = 32, LDK = TK + 8;   // LDS row: 40 bf16 = 80 bytes
+constexpr int NT = 512;                                     // threads per workgroup
+constexpr int WM = 128, WN = 64;                            // per-wave tile
+constexpr int BI = WM / 32, BJ = WN / 32;                   // MFMA blocks per wave
 
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f)
 {
@@ -35,79 +48,112 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f)
     return (unsigned short)(u >> 16);
 }
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const unsigned short *__restrict__ A,
-                                                        const unsigned short *__restrict__ B,
-                                                        unsigned short *__restrict__ C, long long M,
-                                                        long long N, long long Kd)
+// Workgroup id -> (tile row, tile col). Ids go round-robin to the 8 XCDs; the
+// ids of one XCD are handed a compact group of tiles (GROUP tile rows at a
+// time, column-major inside the group) so that concurrently running
+// workgroups of one XCD reuse A and B rows from its L2.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int &tm, int &tn)
 {
-    __shared__ __attribute__((aligned(16))) unsigned short As[TM][LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short Bs[TN][LDK];
+    const int total = tiles_m * tiles_n;
+    constexpr int XCDS = 8, GROUP = 4;
+    if (total % XCDS == 0) {
+        const int per = total / XCDS;
+        id = (id % XCDS) * per + id / XCDS;      // contiguous range per XCD
+    }
+    const int group_tiles = GROUP * tiles_n;
+    const int g = id / group_tiles;
+    const int first_m = g * GROUP;
+    const int rows = min(GROUP, tiles_m - first_m);
+    const int in = id - g * group_tiles;
+    tm = first_m + in % rows;
+    tn = in / rows;
+}
+
+template <bool EDGE>
+__global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__restrict__ A,
+                                                       const unsigned short *__restrict__ B,
+                                                       unsigned short *__restrict__ C, int M, int N,
+                                                       int Kd, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) unsigned short As[2][TM][LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][TN][LDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wi = wave >> 1, wj = wave & 1;
-    const long long m0 = (long long)blockIdx.y * TM, n0 = (long long)blockIdx.x * TN;
+    const int wi = wave >> 2, wj = wave & 3;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
 
-    // global -> register staging: two 16-byte chunks of A and of B per thread
+    // global -> register staging: rows lr, lr+128 of A and of B, 8 bf16 at k lk
     const int lr = tid >> 2, lk = (tid & 3) * 8;
     u32x4 ra[2], rb[2];
-    auto gload = [&](long long k0) {
+    auto gload = [&](int k0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const long long gi = m0 + lr + 64 * h, gj = n0 + lr + 64 * h, gk = k0 + lk;
-            const bool kin = gk + 8 <= Kd;
-            ra[h] = (gi < M && kin) ? *reinterpret_cast<const u32x4 *>(A + gi * Kd + gk) : u32x4{0, 0, 0, 0};
-            rb[h] = (gj < N && kin) ? *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk) : u32x4{0, 0, 0, 0};
+            const long long gi = m0 + lr + 128 * h, gj = n0 + lr + 128 * h;
+            const int gk = k0 + lk;
+            if (EDGE) {
+                const bool kin = gk + 8 <= Kd;
+                ra[h] = (gi < M && kin) ? *reinterpret_cast<const u32x4 *>(A + gi * Kd + gk) : u32x4{0, 0, 0, 0};
+                rb[h] = (gj < N && kin) ? *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk) : u32x4{0, 0, 0, 0};
+            } else {
+                ra[h] = *reinterpret_cast<const u32x4 *>(A + gi * Kd + gk);
+                rb[h] = *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk);
+            }
         }
     };
-    auto sstore = [&]() {
+    auto sstore = [&](int buf) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<u32x4 *>(&As[lr + 64 * h][lk]) = ra[h];
-            *reinterpret_cast<u32x4 *>(&Bs[lr + 64 * h][lk]) = rb[h];
+            *reinterpret_cast<u32x4 *>(&As[buf][lr + 128 * h][lk]) = ra[h];
+            *reinterpret_cast<u32x4 *>(&Bs[buf][lr + 128 * h][lk]) = rb[h];
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[BI][BJ];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < BI; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+        for (int b = 0; b < BJ; ++b) acc[a][b] = f32x16{};
 
+    const int stages = (Kd + TK - 1) / TK;
     gload(0);
-    sstore();
+    sstore(0);
     __syncthreads();
-    for (long long k0 = 0; k0 < Kd; k0 += TK) {
-        const bool more = k0 + TK < Kd;
-        if (more) gload(k0 + TK);
+    int buf = 0;
+    for (int s = 0; s < stages; ++s) {
+        const bool more = s + 1 < stages;
+        if (more) gload((s + 1) * TK);
 #pragma unroll
         for (int ks = 0; ks < TK / 16; ++ks) {
-            bf16x8 av[2], bv[2];
+            bf16x8 av[BI], bv[BJ];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                av[t] = *reinterpret_cast<const bf16x8 *>(&As[wi * 64 + t * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
-                bv[t] = *reinterpret_cast<const bf16x8 *>(&Bs[wj * 64 + t * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
-            }
+            for (int a = 0; a < BI; ++a)
+                av[a] = *reinterpret_cast<const bf16x8 *>(&As[buf][wi * WM + a * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int b = 0; b < BJ; ++b)
+                bv[b] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * WN + b * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+            for (int a = 0; a < BI; ++a)
+#pragma unroll
+                for (int b = 0; b < BJ; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
         }
-        __syncthreads();
         if (more) {
-            sstore();
+            sstore(buf ^ 1);
             __syncthreads();
+            buf ^= 1;
         }
     }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < BI; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < BJ; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const long long gi = m0 + wi * 64 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const long long gj = n0 + wj * 64 + b * 32 + (lane & 31);
-                if (gi < M && gj < N) C[gi * N + gj] = f32_to_bf16_rne(acc[a][b][r]);
+                const long long gi = m0 + wi * WM + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const long long gj = n0 + wj * WN + b * 32 + (lane & 31);
+                if (!EDGE || (gi < M && gj < N)) C[gi * N + gj] = f32_to_bf16_rne(acc[a][b][r]);
             }
 }
 
@@ -116,11 +162,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const unsigned short *__
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
                             long long Kd, hipStream_t st)
 {
-    const long long gx = (N + TN - 1) / TN, gy = (M + TM - 1) / TM;
-    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
-                       (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
-                       M, N, Kd);
+    if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
+    if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const bool edge = (M % TM) || (N % TN) || (Kd % TK);
+    const unsigned grid = (unsigned)(tm * tn);
+    if (edge)
+        hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(NT), 0, st, (const unsigned short *)a,
+                           (const unsigned short *)b, (unsigned short *)c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+    else
+        hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid), dim3(NT), 0, st, (const unsigned short *)a,
+                           (const unsigned short *)b, (unsigned short *)c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
     return hipGetLastError();
 }
 

@@ -5,10 +5,14 @@
 // weight gradient that is then reduce-scattered).
 //
 // One workgroup (4 waves) computes a 64x64 tile of C for one batch entry
-// (blockIdx.z = rank). Each wave owns a 32x32 quadrant and accumulates it with
-// v_mfma_f32_32x32x2f32 over k in steps of 2; A and B tiles of depth 16 are
-// staged through LDS, A stored k-major so each MFMA operand read is one
-// contiguous 32-float row segment per half-wave.
+// (rank = workgroup id mod K). Each wave owns a 32x32 quadrant and accumulates
+// it with v_mfma_f32_32x32x2f32. The k dimension is walked in stages of 32: the
+// next two stages' A and B tiles are in flight from global memory into
+// registers (16-byte loads where the tile is whole and aligned) while the
+// current stage's MFMAs run from LDS; LDS is double-buffered so one barrier per
+// stage suffices. A is
+// kept k-major in LDS so each MFMA operand read is one contiguous 32-float row
+// segment per half-wave.
 //
 // MFMA 32x32x2 f32 operand layout (lane l of the wave):
 //   A operand: A[i = l % 32][k = l / 32]      B operand: B[k = l / 32][j = l % 32]
@@ -19,62 +23,128 @@ namespace dps {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64, BN = 64, BK = 16;
+constexpr int BM = 64, BN = 64, BK = 32, LDP = 64 + 4;
+
+// Stage loader: 2 float4 of A and 2 float4 of B per thread.
+template <int TA>
+struct Stage {
+    f32x4 a[2], b[2];
+
+    __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ B,
+                                         long long M, long long N, long long Kd, long long m0,
+                                         long long n0, long long k0, bool vec_a, bool vec_b)
+    {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (TA == 0) {
+                // A stored [M][Kd]: row m0 + t/8 + 32h, k k0 + (t%8)*4 .. +3
+                const long long i = m0 + (t >> 3) + 32 * h, k = k0 + (t & 7) * 4;
+                if (vec_a) {
+                    a[h] = *reinterpret_cast<const f32x4 *>(A + i * Kd + k);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[h][e] = (i < M && k + e < Kd) ? A[i * Kd + k + e] : 0.0f;
+                }
+            } else {
+                // A stored [Kd][M]: k row k0 + t/16 + 16h, i m0 + (t%16)*4 .. +3
+                const long long k = k0 + (t >> 4) + 16 * h, i = m0 + (t & 15) * 4;
+                if (vec_a) {
+                    a[h] = *reinterpret_cast<const f32x4 *>(A + k * M + i);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[h][e] = (k < Kd && i + e < M) ? A[k * M + i + e] : 0.0f;
+                }
+            }
+            // B stored [Kd][N]: k row k0 + t/16 + 16h, j n0 + (t%16)*4 .. +3
+            const long long k = k0 + (t >> 4) + 16 * h, j = n0 + (t & 15) * 4;
+            if (vec_b) {
+                b[h] = *reinterpret_cast<const f32x4 *>(B + k * N + j);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) b[h][e] = (k < Kd && j + e < N) ? B[k * N + j + e] : 0.0f;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float (*As)[LDP], float (*Bs)[LDP]) const
+    {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (TA == 0) {
+                const int i = (t >> 3) + 32 * h, k = (t & 7) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) As[k + e][i] = a[h][e];
+            } else {
+                *reinterpret_cast<f32x4 *>(&As[(t >> 4) + 16 * h][(t & 15) * 4]) = a[h];
+            }
+            *reinterpret_cast<f32x4 *>(&Bs[(t >> 4) + 16 * h][(t & 15) * 4]) = b[h];
+        }
+    }
+};
 
 template <int TA>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g)
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g, const int tiles_x)
 {
-    const int bz = blockIdx.z;
+    // 1-D grid, batch entry = id mod nb: with 8 ranks, workgroup ids round-robin
+    // over the 8 XCDs put every tile of rank r on XCD r, so a rank's A and B
+    // stay in one XCD's L2
+    const int id = blockIdx.x;
+    const int bz = id % g.nb;
+    const int tile = id / g.nb;
     const float *__restrict__ A = g.a[bz];
     const float *__restrict__ B = g.b[bz];
     float *__restrict__ C = g.c[bz];
     const long long M = g.M, N = g.N, Kd = g.Kd;
-    const long long m0 = (long long)blockIdx.y * BM, n0 = (long long)blockIdx.x * BN;
+    const long long m0 = (long long)(tile / tiles_x) * BM, n0 = (long long)(tile % tiles_x) * BN;
 
-    __shared__ float As[BK][BM + 4];   // As[k][i]
-    __shared__ float Bs[BK][BN + 4];   // Bs[k][j]
+    __shared__ __attribute__((aligned(16))) float As[2][BK][LDP];   // As[buf][k][i]
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDP];   // Bs[buf][k][j]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wi = wave >> 1, wj = wave & 1;
-    f32x16 acc = {};
+    // whole-tile 16-byte loads need the tile inside the matrix, 16-byte aligned
+    // base pointers and row lengths that keep every row 16-byte aligned
+    const bool rows_a = ((uintptr_t)A & 15) == 0 && m0 + BM <= M &&
+                        (TA == 0 ? (Kd & 3) == 0 : (M & 3) == 0);
+    const bool rows_b = ((uintptr_t)B & 15) == 0 && n0 + BN <= N && (N & 3) == 0;
+    const long long stages = (Kd + BK - 1) / BK;
 
-    for (long long k0 = 0; k0 < Kd; k0 += BK) {
-        if (TA == 0) {
-            // A stored [M][Kd]: thread -> row tid/4, 4 consecutive k
-            const int i = tid >> 2, kq = (tid & 3) * 4;
-            const long long gi = m0 + i;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const long long gk = k0 + kq + e;
-                As[kq + e][i] = (gi < M && gk < Kd) ? A[gi * Kd + gk] : 0.0f;
-            }
-        } else {
-            // A stored [Kd][M]: thread -> k row tid/16, 4 consecutive i
-            const int kr = tid >> 4, iq = (tid & 15) * 4;
-            const long long gk = k0 + kr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const long long gi = m0 + iq + e;
-                As[kr][iq + e] = (gk < Kd && gi < M) ? A[gk * M + gi] : 0.0f;
-            }
-        }
-        {
-            const int kr = tid >> 4, jq = (tid & 15) * 4;
-            const long long gk = k0 + kr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const long long gj = n0 + jq + e;
-                Bs[kr][jq + e] = (gk < Kd && gj < N) ? B[gk * N + gj] : 0.0f;
-            }
-        }
-        __syncthreads();
+    f32x16 acc = {};
+    // stages s+1 and s+2 are in flight in registers while stage s is multiplied
+    Stage<TA> r0, r1;
+    auto load = [&](Stage<TA> &r, long long s) {
+        const long long k0 = s * BK;
+        r.load(A, B, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd, rows_b && k0 + BK <= Kd);
+    };
+    auto mma = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 2) {
-            const float a = As[kk + (lane >> 5)][wi * 32 + (lane & 31)];
-            const float b = Bs[kk + (lane >> 5)][wj * 32 + (lane & 31)];
+            const float a = As[buf][kk + (lane >> 5)][wi * 32 + (lane & 31)];
+            const float b = Bs[buf][kk + (lane >> 5)][wj * 32 + (lane & 31)];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
+    };
+    load(r0, 0);
+    if (stages > 1) load(r1, 1);
+    r0.store(As[0], Bs[0]);
+    __syncthreads();
+    // unrolled by two so that each register set has a fixed role
+    for (long long s = 0; s < stages; s += 2) {
+        // stage s from LDS buffer 0; r0 is free, r1 holds stage s+1
+        if (s + 2 < stages) load(r0, s + 2);
+        mma(0);
+        if (s + 1 >= stages) break;
+        r1.store(As[1], Bs[1]);
+        __syncthreads();
+        // stage s+1 from LDS buffer 1; r1 is free, r0 holds stage s+2
+        if (s + 3 < stages) load(r1, s + 3);
+        mma(1);
+        if (s + 2 >= stages) break;
+        r0.store(As[0], Bs[0]);
         __syncthreads();
     }
 #pragma unroll
@@ -91,12 +161,12 @@ hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
 {
     if (g.nb <= 0 || g.M <= 0 || g.N <= 0) return hipSuccess;
     const long long gx = (g.N + BN - 1) / BN, gy = (g.M + BM - 1) / BM;
-    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)g.nb);
+    const long long blocks = gx * gy * g.nb;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (g.trans_a)
-        hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
     else
-        hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
     return hipGetLastError();
 }
 
