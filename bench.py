@@ -311,18 +311,21 @@ def bench_c3(args):
     a, b = gen.gemm_bf16_inputs(5, 8192, 8192, 8192, device="cuda")
     c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    comm_bytes = 2 * (k + 1) * n * 4
+    flops = 2 * 8192 ** 3
 
-    def comm(stream=None):
-        dps.dp_reduce_scatter(xs, sh, op="sum", stream=stream)
-        dps.dp_all_gather(sh, out, stream=stream)
+    def make_comm(cap):
+        def comm(stream=None):
+            dps.dp_reduce_scatter_ex(xs, sh, op="sum", max_workgroups=cap, stream=stream)
+            dps.dp_all_gather_ex(sh, out, max_workgroups=cap, stream=stream)
+        return comm
 
-    def gemm(stream=None):
-        dps.dp_gemm_bf16(a, b, c, stream=stream)
+    def make_gemm(share):
+        def gemm(stream=None):
+            dps.dp_gemm_bf16_ex(a, b, c, share_cu=share, stream=stream)
+        return gemm
 
-    t_comm = statistics.median(_time_ms(comm))
-    t_gemm = statistics.median(_time_ms(gemm))
-
-    def concurrent(first):
+    def concurrent(comm, gemm, first):
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         ea = torch.cuda.Event(enable_timing=True)
@@ -338,25 +341,48 @@ def bench_c3(args):
         torch.cuda.synchronize()
         return max(start.elapsed_time(ea), start.elapsed_time(eb))
 
+    # Schedules: c3_base = default grids, GEMM launched first; sp = the
+    # collective launched first (schedule prioritisation) with its resident
+    # workgroups capped so the GEMM still gets CUs; share = one persistent sync
+    # workgroup per CU beside one GEMM workgroup of the smaller-register variant.
+    schedules = [("base", 0, False, "gemm"), ("base_comm_first", 0, False, "comm"),
+                 ("sp_cap256", 256, False, "comm"), ("sp_cap128", 128, False, "comm"),
+                 ("share_cu", 256, True, "comm"), ("share_cu_gemm_first", 256, True, "gemm")]
+    iso = {}
     res = {}
-    for first in ("gemm", "comm"):
+    for name, cap, share, first in schedules:
+        comm, gemm = make_comm(cap), make_gemm(share)
+        if (cap, "comm") not in iso:
+            iso[(cap, "comm")] = statistics.median(_time_ms(comm))
+        if (share, "gemm") not in iso:
+            iso[(share, "gemm")] = statistics.median(_time_ms(gemm))
+        t_comm, t_gemm = iso[(cap, "comm")], iso[(share, "gemm")]
         for _ in range(6):
-            concurrent(first)
-        tc = statistics.median([concurrent(first) for _ in range(9)])
+            concurrent(comm, gemm, first)
+        tc = statistics.median([concurrent(comm, gemm, first) for _ in range(9)])
         s = (t_comm + t_gemm) / tc
         s_ideal = (t_comm + t_gemm) / max(t_comm, t_gemm)
-        res[f"{first}_first"] = {"t_concurrent_ms": round(tc, 4), "S": round(s, 4),
-                                 "S_ideal": round(s_ideal, 4),
-                                 "S_over_S_ideal": round(s / s_ideal, 4),
-                                 "pct_of_ideal_gain": round(100 * (s - 1) / (s_ideal - 1), 1)
-                                 if s_ideal > 1 else None}
-    comm_bytes = 2 * (k + 1) * n * 4
-    flops = 2 * 8192 ** 3
+        log(f"[c3] {name}: T_comm {t_comm:.3f} T_gemm {t_gemm:.3f} T_conc {tc:.3f} S {s:.3f}")
+        res[name] = {"comm_max_workgroups": cap, "gemm_share_cu": share, "first": first,
+                     "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
+                     "t_concurrent_ms": round(tc, 4), "S": round(s, 4),
+                     "S_ideal": round(s_ideal, 4), "S_over_S_ideal": round(s / s_ideal, 4),
+                     "pct_of_ideal_gain": round(100 * (s - 1) / (s_ideal - 1), 1)
+                     if s_ideal > 1 else None}
+    best_serial = min(v for (_, kind), v in iso.items() if kind == "comm") + \
+        min(v for (_, kind), v in iso.items() if kind == "gemm")
+    for v in res.values():
+        v["S_vs_best_serial"] = round(best_serial / v["t_concurrent_ms"], 4)
+    t_comm0, t_gemm0 = iso[(0, "comm")], iso[(False, "gemm")]
     return {"metric": "C3: RS+AG (K=8, 1 GiB/rank fp32) concurrent with bf16 GEMM 8192^3",
-            "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
-            "comm_gbs": round(comm_bytes / (t_comm * 1e-3) / 1e9, 1),
-            "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
-            "gemm_frac_of_bf16_peak": round(flops / (t_gemm * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
+            "t_comm_ms": round(t_comm0, 4), "t_gemm_ms": round(t_gemm0, 4),
+            "comm_gbs": round(comm_bytes / (t_comm0 * 1e-3) / 1e9, 1),
+            "gemm_tflops": round(flops / (t_gemm0 * 1e-3) / 1e12, 1),
+            "gemm_frac_of_bf16_peak": round(flops / (t_gemm0 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
+            "best_serial_ms": round(best_serial, 4),
+            "S_definition": "S = (T_comm + T_gemm) / T_concurrent with T_comm, T_gemm of the "
+                            "same kernels run alone; S_ideal = (T_comm + T_gemm) / max; "
+                            "pct_of_ideal_gain = (S-1)/(S_ideal-1)",
             "results": res,
             "config": {"workload": "K=8 x 268,435,456 fp32 RS(sum)+AG on stream A, "
                                    "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}

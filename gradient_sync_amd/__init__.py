@@ -26,7 +26,8 @@ import torch  # loads the HIP runtime the library binds to
 __all__ = [
     "DpsyncError", "lib", "dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
     "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
-    "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS",
+    "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
+    "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,16 +41,28 @@ DP_MAX_K = 64
 # every symbol include/dpsync.h declares
 EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
            "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
-           "dp_fsdp_layer", "dp_gemm_bf16")
+           "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
+           "dp_all_reduce_ex", "dp_gemm_bf16_ex")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
+DP_LAUNCH_SHARE_CU = 1
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _sz = ctypes.c_size_t
 _lib = None
+
+
+class LaunchOpts(ctypes.Structure):
+    """dp_launch_opts_t: max_workgroups (0 = one workgroup per tile), flags."""
+    _fields_ = [("max_workgroups", ctypes.c_int), ("flags", ctypes.c_int),
+                ("reserved", ctypes.c_int * 2)]
+
+    @classmethod
+    def make(cls, max_workgroups: int = 0, share_cu: bool = False):
+        return cls(max_workgroups, DP_LAUNCH_SHARE_CU if share_cu else 0, (ctypes.c_int * 2)(0, 0))
 
 
 class DpsyncError(RuntimeError):
@@ -89,6 +102,15 @@ def lib():
         L.dp_fsdp_layer.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dp_gemm_bf16.restype = _int
         L.dp_gemm_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
+        P = ctypes.POINTER(LaunchOpts)
+        L.dp_reduce_scatter_ex.restype = _int
+        L.dp_reduce_scatter_ex.argtypes = [_vp, _vp, _sz, _int, _int, _int, _int, P, _vp]
+        L.dp_all_gather_ex.restype = _int
+        L.dp_all_gather_ex.argtypes = [_vp, _vp, _sz, _int, _int, _int, P, _vp]
+        L.dp_all_reduce_ex.restype = _int
+        L.dp_all_reduce_ex.argtypes = [_vp, _vp, _sz, _int, _int, _int, _int, P, _vp]
+        L.dp_gemm_bf16_ex.restype = _int
+        L.dp_gemm_bf16_ex.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, P, _vp]
         _lib = L
     return _lib
 
@@ -163,8 +185,7 @@ def _numel_check(ts, n, what):
 
 # ----------------------------------------------------------------- the calls
 
-def dp_reduce_scatter(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
-    """recv[c] (ceil(n/K) elements) <- shard c of the ring-order sum of send[r]."""
+def _rs(send, recv, op, s_chunks, stream, n, opts):
     send = _tensors(send, "send")
     recv = _tensors(recv, "recv", send[0].dtype)
     k = len(send)
@@ -173,13 +194,26 @@ def dp_reduce_scatter(send, recv, op: str = "sum", s_chunks: int = 1, stream=Non
     _numel_check(recv, dp_shard_len(n, k), "recv")
     if len(recv) != k:
         raise ValueError("send and recv need one buffer per rank")
-    _check(lib().dp_reduce_scatter(ptr_array([t.data_ptr() for t in send]),
-                                   ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
-                                   _OPS[op], s_chunks, _stream(stream)), "dp_reduce_scatter")
+    args = (ptr_array([t.data_ptr() for t in send]), ptr_array([t.data_ptr() for t in recv]), n, k,
+            _dt(send[0]), _OPS[op], s_chunks)
+    if opts is None:
+        _check(lib().dp_reduce_scatter(*args, _stream(stream)), "dp_reduce_scatter")
+    else:
+        _check(lib().dp_reduce_scatter_ex(*args, opts, _stream(stream)), "dp_reduce_scatter_ex")
 
 
-def dp_all_gather(send, recv, n=None, s_chunks: int = 1, stream=None):
-    """recv[r][c*L + j] <- send[c][j] for the valid elements of every shard."""
+def dp_reduce_scatter(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
+    """recv[c] (ceil(n/K) elements) <- shard c of the ring-order sum of send[r]."""
+    _rs(send, recv, op, s_chunks, stream, n, None)
+
+
+def dp_reduce_scatter_ex(send, recv, op: str = "sum", s_chunks: int = 1, max_workgroups: int = 0,
+                         stream=None, n=None):
+    """dp_reduce_scatter with a cap on resident workgroups (0 = default grid)."""
+    _rs(send, recv, op, s_chunks, stream, n, ctypes.byref(LaunchOpts.make(max_workgroups)))
+
+
+def _ag(send, recv, n, s_chunks, stream, opts):
     send = _tensors(send, "send")
     recv = _tensors(recv, "recv", send[0].dtype)
     k = len(send)
@@ -190,12 +224,24 @@ def dp_all_gather(send, recv, n=None, s_chunks: int = 1, stream=None):
         _numel_check([t], max(0, min(L, n - c * L)), f"send[{c}]")
     if len(recv) != k:
         raise ValueError("send and recv need one buffer per rank")
-    _check(lib().dp_all_gather(ptr_array([t.data_ptr() for t in send]),
-                               ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
-                               s_chunks, _stream(stream)), "dp_all_gather")
+    args = (ptr_array([t.data_ptr() for t in send]), ptr_array([t.data_ptr() for t in recv]), n, k,
+            _dt(send[0]), s_chunks)
+    if opts is None:
+        _check(lib().dp_all_gather(*args, _stream(stream)), "dp_all_gather")
+    else:
+        _check(lib().dp_all_gather_ex(*args, opts, _stream(stream)), "dp_all_gather_ex")
 
 
-def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
+def dp_all_gather(send, recv, n=None, s_chunks: int = 1, stream=None):
+    """recv[r][c*L + j] <- send[c][j] for the valid elements of every shard."""
+    _ag(send, recv, n, s_chunks, stream, None)
+
+
+def dp_all_gather_ex(send, recv, n=None, s_chunks: int = 1, max_workgroups: int = 0, stream=None):
+    _ag(send, recv, n, s_chunks, stream, ctypes.byref(LaunchOpts.make(max_workgroups)))
+
+
+def _ar(send, recv, op, s_chunks, stream, n, opts):
     send = _tensors(send, "send")
     recv = _tensors(recv, "recv", send[0].dtype)
     k = len(send)
@@ -204,9 +250,21 @@ def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n
     _numel_check(recv, n, "recv")
     if len(recv) != k:
         raise ValueError("send and recv need one buffer per rank")
-    _check(lib().dp_all_reduce(ptr_array([t.data_ptr() for t in send]),
-                               ptr_array([t.data_ptr() for t in recv]), n, k, _dt(send[0]),
-                               _OPS[op], s_chunks, _stream(stream)), "dp_all_reduce")
+    args = (ptr_array([t.data_ptr() for t in send]), ptr_array([t.data_ptr() for t in recv]), n, k,
+            _dt(send[0]), _OPS[op], s_chunks)
+    if opts is None:
+        _check(lib().dp_all_reduce(*args, _stream(stream)), "dp_all_reduce")
+    else:
+        _check(lib().dp_all_reduce_ex(*args, opts, _stream(stream)), "dp_all_reduce_ex")
+
+
+def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n=None):
+    _ar(send, recv, op, s_chunks, stream, n, None)
+
+
+def dp_all_reduce_ex(send, recv, op: str = "sum", s_chunks: int = 1, max_workgroups: int = 0,
+                     stream=None, n=None):
+    _ar(send, recv, op, s_chunks, stream, n, ctypes.byref(LaunchOpts.make(max_workgroups)))
 
 
 def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=None):
@@ -255,13 +313,27 @@ def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_
                                _stream(stream)), "dp_fsdp_layer")
 
 
-def dp_gemm_bf16(a, b, c, stream=None):
-    """c[m,n] = a[m,kk] @ b[n,kk]^T in bf16 with fp32 accumulation."""
+def _gemm(a, b, c, stream, opts):
     for name, t in (("a", a), ("b", b), ("c", c)):
         _tensors([t], name, torch.bfloat16)
     m, kk = a.shape
     n = b.shape[0]
     if b.shape[1] != kk or tuple(c.shape) != (m, n):
         raise ValueError("dp_gemm_bf16: shapes must be a[m,k], b[n,k], c[m,n]")
-    _check(lib().dp_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), m, n, kk,
-                              _stream(stream)), "dp_gemm_bf16")
+    if opts is None:
+        _check(lib().dp_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), m, n, kk,
+                                  _stream(stream)), "dp_gemm_bf16")
+    else:
+        _check(lib().dp_gemm_bf16_ex(a.data_ptr(), b.data_ptr(), c.data_ptr(), m, n, kk, opts,
+                                     _stream(stream)), "dp_gemm_bf16_ex")
+
+
+def dp_gemm_bf16(a, b, c, stream=None):
+    """c[m,n] = a[m,kk] @ b[n,kk]^T in bf16 with fp32 accumulation."""
+    _gemm(a, b, c, stream, None)
+
+
+def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None):
+    """dp_gemm_bf16; share_cu selects the variant that leaves room for a sync
+    workgroup on every CU."""
+    _gemm(a, b, c, stream, ctypes.byref(LaunchOpts.make(0, share_cu)))

@@ -30,6 +30,20 @@ bool overlap(Range a, Range b) { return a.hi > a.lo && b.hi > b.lo && a.lo < b.h
 
 bool valid_k(int k) { return k >= 1 && k <= DP_MAX_K; }
 
+// launch options: NULL = defaults; a negative cap, unknown flags or non-zero
+// reserved words are invalid
+bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr)
+{
+    max_wg = 0;
+    if (share_cu) *share_cu = false;
+    if (!o) return true;
+    if (o->max_workgroups < 0 || (o->flags & ~DP_LAUNCH_SHARE_CU) || o->reserved[0] || o->reserved[1])
+        return false;
+    max_wg = o->max_workgroups;
+    if (share_cu) *share_cu = (o->flags & DP_LAUNCH_SHARE_CU) != 0;
+    return true;
+}
+
 bool valid_dtype(int dt) { return dt == DP_F32 || dt == DP_BF16 || dt == DP_I32; }
 
 // every element non-null and element-aligned
@@ -91,7 +105,7 @@ dp_status_t validate_rs_ag_common(const void *const *send, void *const *recv, si
 // out[c] = element 0 of shard c's output region.
 dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t L, int k, int dt,
                    int ep, float scale, const float *w, int write_pads, int s_chunks,
-                   hipStream_t st)
+                   hipStream_t st, int max_wg = 0)
 {
     dps::RsParams p;
     memset(&p, 0, sizeof(p));
@@ -106,11 +120,12 @@ dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t
     p.L = L;
     p.k = k;
     p.S = s_chunks;
+    p.max_blocks = max_wg;
     return hip_status(dps::launch_rs(p, dt, ep, st));
 }
 
 dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_t L, int k, int dt,
-                   int skip_own, int s_chunks, hipStream_t st)
+                   int skip_own, int s_chunks, hipStream_t st, int max_wg = 0)
 {
     dps::AgParams p;
     memset(&p, 0, sizeof(p));
@@ -123,6 +138,7 @@ dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_
     p.L = L;
     p.k = k;
     p.S = s_chunks;
+    p.max_blocks = max_wg;
     return hip_status(dps::launch_ag(p, dt, st));
 }
 
@@ -140,16 +156,16 @@ dp_status_t check_ar_alias(const void *const *send, void *const *recv, size_t n,
 }
 
 dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, int dt, int ep,
-                   float scale, const float *w, int s_chunks, hipStream_t st)
+                   float scale, const float *w, int s_chunks, hipStream_t st, int max_wg = 0)
 {
     const int es = dps::elem_size(dt);
     const int64_t L = (int64_t)dp_shard_len(n, k);
     char *rs_out[DP_MAX_K];
     for (int c = 0; c < k; ++c) rs_out[c] = (char *)recv[c] + (size_t)c * (size_t)L * (size_t)es;
-    dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st);
+    dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st, max_wg);
     if (s != DP_OK) return s;
     return run_ag((const void *const *)rs_out, (char *const *)recv, (int64_t)n, L, k, dt, 1,
-                  s_chunks, st);
+                  s_chunks, st, max_wg);
 }
 
 }  // namespace
@@ -178,9 +194,11 @@ int dp_last_hip_error(void) { return g_last_hip_error; }
 
 int dp_version(void) { return 100; }
 
-dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t n, int k, int dt,
-                              int op, int s_chunks, void *stream)
+dp_status_t dp_reduce_scatter_ex(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                                 int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
+    int max_wg;
+    if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
@@ -200,12 +218,20 @@ dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t
     float scale;
     pick_epilogue(op, k, ep, scale);
     return run_rs(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, ep, scale, nullptr, 1,
-                  s_chunks, (hipStream_t)stream);
+                  s_chunks, (hipStream_t)stream, max_wg);
 }
 
-dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, int k, int dt,
-                          int s_chunks, void *stream)
+dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                              int op, int s_chunks, void *stream)
 {
+    return dp_reduce_scatter_ex(send, recv, n, k, dt, op, s_chunks, nullptr, stream);
+}
+
+dp_status_t dp_all_gather_ex(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                             int s_chunks, const dp_launch_opts_t *opts, void *stream)
+{
+    int max_wg;
+    if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     const int es = dps::elem_size(dt);
@@ -222,12 +248,20 @@ dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, 
         }
     }
     return run_ag(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, in_place ? 1 : 0,
-                  s_chunks, (hipStream_t)stream);
+                  s_chunks, (hipStream_t)stream, max_wg);
 }
 
-dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k, int dt,
-                          int op, int s_chunks, void *stream)
+dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                          int s_chunks, void *stream)
 {
+    return dp_all_gather_ex(send, recv, n, k, dt, s_chunks, nullptr, stream);
+}
+
+dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                             int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
+{
+    int max_wg;
+    if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
@@ -237,7 +271,13 @@ dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, 
     int ep;
     float scale;
     pick_epilogue(op, k, ep, scale);
-    return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream);
+    return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream, max_wg);
+}
+
+dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                          int op, int s_chunks, void *stream)
+{
+    return dp_all_reduce_ex(send, recv, n, k, dt, op, s_chunks, nullptr, stream);
 }
 
 dp_status_t dp_weighted_reduce(const void *const *send, void *const *recv, const int64_t *tokens,
@@ -338,9 +378,12 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
                   dps::kSum, 1.0f, nullptr, 1, 1, st);
 }
 
-dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n, int64_t kk,
-                         void *stream)
+dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, int64_t n,
+                            int64_t kk, const dp_launch_opts_t *opts, void *stream)
 {
+    int max_wg;
+    bool share_cu;
+    if (!opts_ok(opts, max_wg, &share_cu)) return DP_ERR_INVALID_ARG;
     if (!a || !b || !c || m < 1 || n < 1 || kk < 1) return DP_ERR_INVALID_ARG;
     if (m > (1 << 24) || n > (1 << 24) || kk > (1 << 24)) return DP_ERR_INVALID_ARG;
     if (kk % 8 != 0 || ((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)c & 1))
@@ -348,7 +391,13 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
     const Range rc = span(c, (size_t)(m * n) * 2);
     if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
         return DP_ERR_ALIAS;
-    return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, (hipStream_t)stream));
+    return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, share_cu, (hipStream_t)stream));
+}
+
+dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n, int64_t kk,
+                         void *stream)
+{
+    return dp_gemm_bf16_ex(a, b, c, m, n, kk, nullptr, stream);
 }
 
 }  // extern "C"

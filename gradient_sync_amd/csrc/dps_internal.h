@@ -72,8 +72,10 @@ struct GemmF32Batch {
 };
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t stream);
 
-// bf16 GEMM, C[M,N] = A[M,Kd] * B[Kd,N], row-major, fp32 accumulation.
+// bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
+// share_cu selects the variant with depth-32 k stages (fewer registers, so a
+// sync workgroup fits on the same CU).
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, hipStream_t stream);
+                            long long Kd, bool share_cu, hipStream_t stream);
 
 }  // namespace dps

@@ -11,15 +11,15 @@
 // Workgroup: 512 threads = 8 waves arranged 2 (rows) x 4 (columns) over a
 // 256x256 tile of C; each wave owns 128x64 = 4x2 blocks of
 // v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane). k is walked in
-// stages of 32 through double-buffered LDS (2 x 32 KiB); the next stage's global
-// loads (4 x 16 bytes per thread) are issued before the current stage's MFMAs.
+// stages of TK (32 or 64) through double-buffered LDS; the next stage's global
+// loads (16-byte chunks) are issued before the current stage's MFMAs.
 // A 256x256 tile does 128 flop per byte loaded, which keeps the kernel off the
 // L2 bandwidth limit a 128x128 tile (64 flop/byte) runs into.
 // Tiles are ordered so that the workgroups running together on one XCD (ids
 // round-robin over 8 XCDs) cover a compact block of C and share A and B rows
 // in that XCD's L2.
 //
-// Edge tiles (M or N not multiples of 256, Kd not a multiple of 32) take a
+// Edge tiles (M or N not multiples of 256, Kd not a multiple of TK) take a
 // guarded path: out-of-range rows and k-chunks load zeros, stores are masked.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l):
@@ -35,7 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 256, TN = 256, TK = 32, LDK = TK + 8;   // LDS row: 40 bf16 = 80 bytes
+constexpr int TM = 256, TN = 256;                           // workgroup tile of C
 constexpr int NT = 512;                                     // threads per workgroup
 constexpr int WM = 128, WN = 64;                            // per-wave tile
 constexpr int BI = WM / 32, BJ = WN / 32;                   // MFMA blocks per wave
@@ -69,12 +69,19 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int &t
     tn = in / rows;
 }
 
-template <bool EDGE>
+// TK: k depth of one LDS stage (64: full 128-byte rows per load, 228 VGPRs,
+// 144 KiB LDS; 32: 198 VGPRs and 80 KiB, which leaves room on the CU for a
+// sync workgroup beside the GEMM workgroup).
+template <bool EDGE, int TK>
 __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__restrict__ A,
                                                        const unsigned short *__restrict__ B,
                                                        unsigned short *__restrict__ C, int M, int N,
                                                        int Kd, int tiles_m, int tiles_n)
 {
+    constexpr int LDK = TK + 8;      // LDS row padded by 16 bytes
+    constexpr int CH = TK / 8;       // 16-byte chunks per tile row
+    constexpr int RPP = NT / CH;     // rows loaded per pass
+    constexpr int HP = TM / RPP;     // passes per tile
     __shared__ __attribute__((aligned(16))) unsigned short As[2][TM][LDK];
     __shared__ __attribute__((aligned(16))) unsigned short Bs[2][TN][LDK];
 
@@ -84,13 +91,13 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
 
-    // global -> register staging: rows lr, lr+128 of A and of B, 8 bf16 at k lk
-    const int lr = tid >> 2, lk = (tid & 3) * 8;
-    u32x4 ra[2], rb[2];
+    // global -> register staging: rows lr + RPP*h of A and of B, 8 bf16 at k lk
+    const int lr = tid / CH, lk = (tid % CH) * 8;
+    u32x4 ra[HP], rb[HP];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const long long gi = m0 + lr + 128 * h, gj = n0 + lr + 128 * h;
+        for (int h = 0; h < HP; ++h) {
+            const long long gi = m0 + lr + RPP * h, gj = n0 + lr + RPP * h;
             const int gk = k0 + lk;
             if (EDGE) {
                 const bool kin = gk + 8 <= Kd;
@@ -104,9 +111,9 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<u32x4 *>(&As[buf][lr + 128 * h][lk]) = ra[h];
-            *reinterpret_cast<u32x4 *>(&Bs[buf][lr + 128 * h][lk]) = rb[h];
+        for (int h = 0; h < HP; ++h) {
+            *reinterpret_cast<u32x4 *>(&As[buf][lr + RPP * h][lk]) = ra[h];
+            *reinterpret_cast<u32x4 *>(&Bs[buf][lr + RPP * h][lk]) = rb[h];
         }
     };
 
@@ -157,22 +164,33 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
             }
 }
 
+template <int TK>
+void launch_tk(const void *a, const void *b, void *c, int M, int N, int Kd, int tm, int tn,
+               hipStream_t st)
+{
+    const bool edge = (M % TM) || (N % TN) || (Kd % TK);
+    const unsigned grid = (unsigned)tm * (unsigned)tn;
+    const auto *A = (const unsigned short *)a;
+    const auto *B = (const unsigned short *)b;
+    auto *C = (unsigned short *)c;
+    if (edge)
+        hipLaunchKernelGGL((gemm_bf16_kernel<true, TK>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, TK>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, hipStream_t st)
+                            long long Kd, bool share_cu, hipStream_t st)
 {
     if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
     const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
     if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const bool edge = (M % TM) || (N % TN) || (Kd % TK);
-    const unsigned grid = (unsigned)(tm * tn);
-    if (edge)
-        hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(NT), 0, st, (const unsigned short *)a,
-                           (const unsigned short *)b, (unsigned short *)c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+    if (share_cu)
+        launch_tk<32>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
     else
-        hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid), dim3(NT), 0, st, (const unsigned short *)a,
-                           (const unsigned short *)b, (unsigned short *)c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+        launch_tk<64>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
     return hipGetLastError();
 }
 

@@ -45,6 +45,13 @@ template <int DT> struct RsU { static constexpr int U = 2; };
 #define DPS_AG_U 2
 #endif
 constexpr int kAgU = DPS_AG_U;
+#ifndef DPS_AG_BLOCK
+#define DPS_AG_BLOCK 256
+#endif
+constexpr int kAgBlock = DPS_AG_BLOCK;   // threads per AllGather workgroup
+#ifndef DPS_AG_NT_STORE
+#define DPS_AG_NT_STORE 1
+#endif
 #ifndef DPS_AG_NT_LOAD
 #define DPS_AG_NT_LOAD 0
 #endif
@@ -56,7 +63,10 @@ constexpr int kAgU = DPS_AG_U;
 #define DPS_BLOCKS_PER_CU 0
 #endif
 constexpr int kBlocksPerCU = DPS_BLOCKS_PER_CU;
-constexpr int kCUs = 256;
+#ifndef DPS_CUS
+#define DPS_CUS 256
+#endif
+constexpr int kCUs = DPS_CUS;
 
 #ifndef DPS_RS_NT_STORE
 #define DPS_RS_NT_STORE 1
@@ -83,6 +93,15 @@ __device__ __forceinline__ u32x4 load_stream(const char *p)
 __device__ __forceinline__ void store_rs(char *p, u32x4 v)
 {
 #if DPS_RS_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+#else
+    *reinterpret_cast<u32x4 *>(p) = v;
+#endif
+}
+
+__device__ __forceinline__ void store_ag(char *p, u32x4 v)
+{
+#if DPS_AG_NT_STORE
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 #else
     *reinterpret_cast<u32x4 *>(p) = v;
@@ -332,7 +351,7 @@ __device__ __forceinline__ void ag_scalar_range(const AgParams &p, int K, int c,
                                                 long long lo, long long hi)
 {
     const char *src = p.src[c];
-    for (long long j = lo + threadIdx.x; j < hi; j += kBlock) {
+    for (long long j = lo + threadIdx.x; j < hi; j += kAgBlock) {
         unsigned short h = 0;
         unsigned w = 0;
         if constexpr (ES == 2) h = *reinterpret_cast<const unsigned short *>(src + j * ES);
@@ -359,7 +378,7 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const long long q = FULL ? (long long)tid + u * kBlock : min((long long)tid + u * kBlock, nv - 1);
+        const long long q = FULL ? (long long)tid + u * kAgBlock : min((long long)tid + u * kAgBlock, nv - 1);
 #if DPS_AG_NT_LOAD
         v[u] = load_stream(src + q * 16);
 #else
@@ -375,8 +394,8 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
         char *d = p.dst[r] + off;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long long q = (long long)tid + u * kBlock;
-            if (FULL || q < nv) *reinterpret_cast<u32x4 *>(d + q * 16) = v[u];
+            const long long q = (long long)tid + u * kAgBlock;
+            if (FULL || q < nv) store_ag(d + q * 16, v[u]);
         }
     }
 }
@@ -385,7 +404,7 @@ template <int ES, int KT, int U>
 __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const long long bid)
 {
     constexpr int V = 16 / ES;
-    constexpr long long TE = (long long)kBlock * U * V;
+    constexpr long long TE = (long long)kAgBlock * U * V;
     const long long seg = bid / p.tiles_per_seg;
     const long long t = bid - seg * p.tiles_per_seg;
     const int s = (int)(seg / K);
@@ -412,7 +431,7 @@ __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const lo
     const long long nv = (e1 - e0) / V;
     const char *src = p.src[c] + e0 * ES;
     const long long off = (base + e0) * ES;
-    if (nv == (long long)kBlock * U) {
+    if (nv == (long long)kAgBlock * U) {
         if (p.skip_own) ag_vectors<ES, KT, U, true, true>(p, K, c, src, off, nv);
         else ag_vectors<ES, KT, U, true, false>(p, K, c, src, off, nv);
     } else if (nv > 0) {
@@ -423,7 +442,7 @@ __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const lo
 }
 
 template <int ES, int KT, int U>
-__global__ __launch_bounds__(kBlock) void ag_kernel(const AgParams p)
+__global__ __launch_bounds__(kAgBlock) void ag_kernel(const AgParams p)
 {
     const int K = KT ? KT : p.k;
     for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
@@ -453,7 +472,7 @@ hipError_t rs_k(const RsParams &p, long long grid, hipStream_t st)
 template <int ES, int KT>
 hipError_t ag_go(const AgParams &p, long long grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
     return hipGetLastError();
 }
 
@@ -528,7 +547,7 @@ long long plan_ag(AgParams &p, int dt)
         p.meta[c] = phase_meta(outs, (long long)c * p.L * es, p.k, p.src[c], true);
     }
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kBlock * kAgU * (16 / es);
+    const long long te = (long long)kAgBlock * kAgU * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);

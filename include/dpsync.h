@@ -182,6 +182,44 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
 dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n,
                          int64_t kk, void *stream);
 
+/*
+ * Launch options for running a collective beside other GPU work (concurrent
+ * computation and communication, "Optimizing ML Concurrent Computation and
+ * Communication with GPU DMA Engines", section Q2: schedule prioritisation and
+ * resource partitioning decide how the collective and the GEMM share CUs).
+ *   max_workgroups : 0 = the default grid (one workgroup per tile). > 0 caps
+ *                    the sync kernels at that many resident workgroups
+ *                    (256 threads each), which then walk the tiles
+ *                    persistently; results are bit-identical either way.
+ *   flags          : DP_LAUNCH_SHARE_CU selects, for dp_gemm_bf16_ex, the GEMM
+ *                    variant with a smaller register footprint (depth-32 k
+ *                    stages) so that a sync workgroup can be resident on the
+ *                    same CU as a GEMM workgroup. Ignored by the sync calls.
+ *   reserved       : must be zero.
+ * A NULL opts pointer means all defaults. Invalid fields return
+ * DP_ERR_INVALID_ARG.
+ */
+#define DP_LAUNCH_SHARE_CU 1
+
+typedef struct {
+    int max_workgroups;
+    int flags;
+    int reserved[2];
+} dp_launch_opts_t;
+
+/* The same operations as dp_reduce_scatter, dp_all_gather, dp_all_reduce and
+ * dp_gemm_bf16, with launch options. */
+dp_status_t dp_reduce_scatter_ex(const void *const *send, void *const *recv, size_t n, int k,
+                                 int dt, int op, int s_chunks, const dp_launch_opts_t *opts,
+                                 void *stream);
+dp_status_t dp_all_gather_ex(const void *const *send, void *const *recv, size_t n, int k,
+                             int dt, int s_chunks, const dp_launch_opts_t *opts, void *stream);
+dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t n, int k,
+                             int dt, int op, int s_chunks, const dp_launch_opts_t *opts,
+                             void *stream);
+dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, int64_t n,
+                            int64_t kk, const dp_launch_opts_t *opts, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

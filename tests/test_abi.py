@@ -174,3 +174,23 @@ def test_binding_rejects_host_tensors():
     t = [torch.zeros(10) for _ in range(2)]
     with pytest.raises(ValueError):
         dps.dp_all_reduce(t, t)
+
+
+def test_launch_options_validation():
+    L = dps.lib()
+    a, b = fake(4), fake(4, base=1 << 41)
+    bad = [dps.LaunchOpts(-1, 0, (ctypes.c_int * 2)(0, 0)),
+           dps.LaunchOpts(0, 4, (ctypes.c_int * 2)(0, 0)),
+           dps.LaunchOpts(0, 0, (ctypes.c_int * 2)(1, 0))]
+    for o in bad:
+        r = ctypes.byref(o)
+        assert L.dp_reduce_scatter_ex(P(a), P(b), 100, 4, F32, SUM, 1, r, None) == INVALID
+        assert L.dp_all_gather_ex(P(a), P(b), 100, 4, F32, 1, r, None) == INVALID
+        assert L.dp_all_reduce_ex(P(a), P(b), 100, 4, F32, SUM, 1, r, None) == INVALID
+        assert L.dp_gemm_bf16_ex(1 << 40, 1 << 41, 1 << 42, 8, 8, 8, r, None) == INVALID
+    ok = ctypes.byref(dps.LaunchOpts.make(16, True))
+    # valid options, still rejected for the usual reasons (nothing is launched)
+    assert L.dp_reduce_scatter_ex(P(a), P(b), 100, 0, F32, SUM, 1, ok, None) == INVALID
+    assert L.dp_all_reduce_ex(P(a), P(b), 0, 4, F32, SUM, 1, ok, None) == OK
+    assert L.dp_gemm_bf16_ex(1 << 40, 1 << 41, 1 << 42, 8, 8, 12, ok, None) == UNSUPPORTED
+    assert L.dp_reduce_scatter_ex(P(a), P(b), 0, 4, F32, SUM, 1, None, None) == OK

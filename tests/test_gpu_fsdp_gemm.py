@@ -187,3 +187,22 @@ def test_gemm_bf16_8192_sampled():
     rows = np.concatenate([rng.integers(0, m, 3000), [0, 0, m - 1, m - 1, 127, 128]])
     cols = np.concatenate([rng.integers(0, n, 3000), [0, n - 1, 0, n - 1, 128, 127]])
     check_gemm(a, b, rows.astype(np.int64), cols.astype(np.int64))
+
+
+@pytest.mark.parametrize("m,n,kk", [(256, 256, 32), (200, 136, 40), (512, 768, 1024), (8192, 8192, 8192)])
+def test_gemm_bf16_share_cu_variant(m, n, kk):
+    """The depth-32 variant (DP_LAUNCH_SHARE_CU) against the oracle; it sums in
+    a different order than the default, so both are checked against fp64."""
+    say(f"gemm bf16 share-cu {m}x{n}x{kk}")
+    a, b = gen.gemm_bf16_inputs(9, m, n, kk, device=DEV)
+    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dps.dp_gemm_bf16_ex(a, b, c, share_cu=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(m + kk)
+    rows = np.concatenate([rng.integers(0, m, 2000), [0, m - 1]]).astype(np.int64)
+    cols = np.concatenate([rng.integers(0, n, 2000), [n - 1, 0]]).astype(np.int64)
+    ref, absr = oracle.gemm_bf16_at(_bits(a), np.ascontiguousarray(_bits(b).T), rows, cols,
+                                    nthreads=16)
+    got = oracle.bf16_to_f32(_bits(c)[rows, cols]).astype(np.float64)
+    g = gamma(kk + 1)
+    assert np.all(np.abs(got - ref) <= U_BF16 * (np.abs(ref) + g * absr) + g * absr)

@@ -380,3 +380,31 @@ def test_one_gib_per_rank_k8_fp32_sampled():
         assert bits_equal(to_np(out[r][ti]), want)
     for r in range(1, k):
         assert torch.equal(out[0], out[r])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_capped_grid_is_bit_identical(dtype):
+    """With a cap on resident workgroups the kernels walk their tiles
+    persistently; the results must not change."""
+    for k, n, off in ((8, 8 * 4096 * 5 + 37, 0), (3, 100_003, 1), (8, 10_000_019 // 16, 3)):
+        xs, hx = make_inputs(dtype, k, n, seed=40 + k, off=off)
+        op = "sum" if dtype == torch.int32 else "avg"
+        want_sh = oracle.reduce_scatter(hx, op=op)
+        want = oracle.all_gather(want_sh, n)
+        L = dps.dp_shard_len(n, k)
+        for cap in (1, 3, 64, 256):
+            say(f"capped k={k} n={n} {dtype} cap={cap}")
+            sh = [Guarded(L, dtype) for _ in range(k)]
+            out = [Guarded(n, dtype, 1) for _ in range(k)]
+            out2 = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+            dps.dp_reduce_scatter_ex([g.t for g in xs], [s.t for s in sh], op=op, s_chunks=2,
+                                     max_workgroups=cap)
+            dps.dp_all_gather_ex([s.t for s in sh], [o.t for o in out], n=n, max_workgroups=cap)
+            dps.dp_all_reduce_ex([g.t for g in xs], out2, op=op, max_workgroups=cap)
+            torch.cuda.synchronize()
+            for c in range(k):
+                assert bits_equal(to_np(sh[c].t), want_sh[c]), (cap, c)
+                assert sh[c].intact() and out[c].intact()
+            for r in (0, k - 1):
+                assert bits_equal(to_np(out[r].t), want[r]), (cap, r)
+                assert bits_equal(to_np(out2[r]), want[r]), (cap, r)
