@@ -17,6 +17,7 @@ Other measurements (each prints its own JSON line):
   --config weighted  token-weighted AllReduce, K=8, 10,000,019 fp32
   --config c3        RS+AG of 1 GiB/rank fp32 (K=8) concurrent with a bf16
                      8192^3 GEMM on another stream
+  --config fused_ar  the layer buckets as one-pass AllReduce, against RS+AG
   --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
@@ -282,19 +283,52 @@ def bench_weighted(args):
     xs2 = gen.ring_uniform_inputs(6, k, n, device="cuda")
     out2 = [torch.empty(n, device="cuda") for _ in range(k)]
     flip = [0]
-
-    def go():
-        a, o = (xs, out) if flip[0] == 0 else (xs2, out2)
-        flip[0] ^= 1
-        dps.dp_weighted_reduce(a, o, toks)
-    ms = _time_ms(go)
-    med = statistics.median(ms)
-    b = 2 * (k + 1) * n * 4
+    res = {}
+    for name, two_phase, b in (("one_pass", False, 2 * k * n * 4),
+                               ("two_phase", True, 2 * (k + 1) * n * 4)):
+        def go():
+            a, o = (xs, out) if flip[0] == 0 else (xs2, out2)
+            flip[0] ^= 1
+            dps.dp_weighted_reduce_ex(a, o, toks, two_phase=two_phase)
+        med = statistics.median(_time_ms(go))
+        res[name] = {"median_us": round(1e3 * med, 2), "bytes": b,
+                     "gbs": round(b / (med * 1e-3) / 1e9, 1),
+                     "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
     return {"metric": "token-weighted AllReduce K=8 N=10,000,019 fp32", "unit": "GB/s",
-            "value": round(b / (med * 1e-3) / 1e9, 1), "median_us": round(1e3 * med, 2),
-            "tokens": toks, "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "value": res["one_pass"]["gbs"], "results": res, "tokens": toks,
             "config": {"workload": "K=8, 10,000,019 fp32 uniform[-1,1), log-normal(7,1) "
                                    "token counts, 2 docs/rank"}}
+
+
+def bench_fused_ar(args):
+    """The layer buckets as one one-pass AllReduce per bucket, against the
+    ReduceScatter + AllGather step over the same buckets."""
+    import torch
+
+    import gen
+    from gradient_sync_amd.buckets import BucketedSync
+    k = 8
+    grads = gen.layer_grads_bf16(3, k, device="cuda")
+    out = [torch.empty(gen.LAYER_PARAMS, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
+    res = {}
+    for name, fn, b in (("one_pass_all_reduce", sync.step_all_reduce, sync.all_reduce_bytes()),
+                        ("reduce_scatter_all_gather", sync.step, sync.algorithmic_bytes())):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / args.steps
+        res[name] = {"ms_per_step": round(1e3 * t, 4), "bytes_per_step": b,
+                     "gbs": round(b / t / 1e9, 1), "pct_of_peak": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
+    res["speedup"] = round(res["reduce_scatter_all_gather"]["ms_per_step"] /
+                           res["one_pass_all_reduce"]["ms_per_step"], 4)
+    return {"metric": "averaged AllReduce of the K=8 bf16 layer buckets: one pass vs RS+AG",
+            "unit": "ms", "results": res,
+            "config": {"workload": "K=8, 218,103,808 bf16 per rank, 9 buckets of <=25,000,000"}}
 
 
 def bench_c3(args):
@@ -412,7 +446,7 @@ def bench_copy(args):
 
 
 CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
-           "copy": bench_copy}
+           "fused_ar": bench_fused_ar, "copy": bench_copy}
 
 
 def main():

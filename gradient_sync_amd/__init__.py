@@ -28,6 +28,7 @@ __all__ = [
     "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
     "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
     "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
+    "dp_weighted_reduce_ex",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,11 +43,12 @@ DP_MAX_K = 64
 EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
            "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
-           "dp_all_reduce_ex", "dp_gemm_bf16_ex")
+           "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
 DP_LAUNCH_SHARE_CU = 1
+DP_LAUNCH_TWO_PHASE = 2
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -61,8 +63,9 @@ class LaunchOpts(ctypes.Structure):
                 ("reserved", ctypes.c_int * 2)]
 
     @classmethod
-    def make(cls, max_workgroups: int = 0, share_cu: bool = False):
-        return cls(max_workgroups, DP_LAUNCH_SHARE_CU if share_cu else 0, (ctypes.c_int * 2)(0, 0))
+    def make(cls, max_workgroups: int = 0, share_cu: bool = False, two_phase: bool = False):
+        flags = (DP_LAUNCH_SHARE_CU if share_cu else 0) | (DP_LAUNCH_TWO_PHASE if two_phase else 0)
+        return cls(max_workgroups, flags, (ctypes.c_int * 2)(0, 0))
 
 
 class DpsyncError(RuntimeError):
@@ -111,6 +114,8 @@ def lib():
         L.dp_all_reduce_ex.argtypes = [_vp, _vp, _sz, _int, _int, _int, _int, P, _vp]
         L.dp_gemm_bf16_ex.restype = _int
         L.dp_gemm_bf16_ex.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, P, _vp]
+        L.dp_weighted_reduce_ex.restype = _int
+        L.dp_weighted_reduce_ex.argtypes = [_vp, _vp, _vp, _sz, _int, _int, _int, P, _vp]
         _lib = L
     return _lib
 
@@ -263,11 +268,14 @@ def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n
 
 
 def dp_all_reduce_ex(send, recv, op: str = "sum", s_chunks: int = 1, max_workgroups: int = 0,
-                     stream=None, n=None):
-    _ar(send, recv, op, s_chunks, stream, n, ctypes.byref(LaunchOpts.make(max_workgroups)))
+                     two_phase: bool = False, stream=None, n=None):
+    """dp_all_reduce with launch options; two_phase runs ReduceScatter then
+    AllGather instead of the one-pass kernel (same results)."""
+    _ar(send, recv, op, s_chunks, stream, n,
+        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase)))
 
 
-def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=None):
+def _wr(send, recv, tokens, s_chunks, stream, n, opts):
     send = _tensors(send, "send")
     recv = _tensors(recv, "recv", send[0].dtype)
     k = len(send)
@@ -277,10 +285,23 @@ def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=Non
     if len(recv) != k or len(tokens) != k:
         raise ValueError("send, recv and tokens need one entry per rank")
     toks = (ctypes.c_int64 * k)(*[int(t) for t in tokens])
-    _check(lib().dp_weighted_reduce(ptr_array([t.data_ptr() for t in send]),
-                                    ptr_array([t.data_ptr() for t in recv]), toks, n, k,
-                                    _dt(send[0]), s_chunks, _stream(stream)),
-           "dp_weighted_reduce")
+    args = (ptr_array([t.data_ptr() for t in send]), ptr_array([t.data_ptr() for t in recv]), toks,
+            n, k, _dt(send[0]), s_chunks)
+    if opts is None:
+        _check(lib().dp_weighted_reduce(*args, _stream(stream)), "dp_weighted_reduce")
+    else:
+        _check(lib().dp_weighted_reduce_ex(*args, opts, _stream(stream)), "dp_weighted_reduce_ex")
+
+
+def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=None):
+    """recv[r] <- sum_r f32(t_r) send[r] / f32(sum_r t_r), on every rank."""
+    _wr(send, recv, tokens, s_chunks, stream, n, None)
+
+
+def dp_weighted_reduce_ex(send, recv, tokens, s_chunks: int = 1, max_workgroups: int = 0,
+                          two_phase: bool = False, stream=None, n=None):
+    _wr(send, recv, tokens, s_chunks, stream, n,
+        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase)))
 
 
 def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_shard=None,

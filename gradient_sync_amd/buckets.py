@@ -104,6 +104,20 @@ class BucketedSync:
                     e1.record(torch_stream)
                     events.append((kind, b, e0, e1))
 
+    def step_all_reduce(self, stream=None):
+        """Each bucket as one AllReduce call (the one-pass kernel: every shard
+        folded once and written to all K outputs; no shard buffer)."""
+        st = _stream(stream)
+        L = lib()
+        for b, (send, _, dst, n) in enumerate(self.calls):
+            rc = L.dp_all_reduce(send, dst, n, self.k, self.dtype, self.op, self.s_chunks, st)
+            if rc:
+                _check(rc, f"bucket {b} all_reduce")
+
+    def all_reduce_bytes(self) -> int:
+        """Bytes one one-pass AllReduce step must move: K*n read, K*n written."""
+        return sum(2 * self.k * n * self.es for _, n in self.plan)
+
     def algorithmic_bytes(self) -> int:
         """Bytes one step must move: per bucket, ReduceScatter reads K*n and
         writes n elements, AllGather reads n and writes K*n."""

@@ -32,15 +32,19 @@ bool valid_k(int k) { return k >= 1 && k <= DP_MAX_K; }
 
 // launch options: NULL = defaults; a negative cap, unknown flags or non-zero
 // reserved words are invalid
-bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr)
+bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr,
+             bool *two_phase = nullptr)
 {
     max_wg = 0;
     if (share_cu) *share_cu = false;
+    if (two_phase) *two_phase = false;
     if (!o) return true;
-    if (o->max_workgroups < 0 || (o->flags & ~DP_LAUNCH_SHARE_CU) || o->reserved[0] || o->reserved[1])
+    if (o->max_workgroups < 0 || (o->flags & ~(DP_LAUNCH_SHARE_CU | DP_LAUNCH_TWO_PHASE)) ||
+        o->reserved[0] || o->reserved[1])
         return false;
     max_wg = o->max_workgroups;
     if (share_cu) *share_cu = (o->flags & DP_LAUNCH_SHARE_CU) != 0;
+    if (two_phase) *two_phase = (o->flags & DP_LAUNCH_TWO_PHASE) != 0;
     return true;
 }
 
@@ -156,10 +160,28 @@ dp_status_t check_ar_alias(const void *const *send, void *const *recv, size_t n,
 }
 
 dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, int dt, int ep,
-                   float scale, const float *w, int s_chunks, hipStream_t st, int max_wg = 0)
+                   float scale, const float *w, int s_chunks, hipStream_t st, int max_wg = 0,
+                   bool two_phase = false)
 {
     const int es = dps::elem_size(dt);
     const int64_t L = (int64_t)dp_shard_len(n, k);
+    if (!two_phase) {
+        // one pass: fold each shard and write it to every rank's output
+        dps::RsParams p;
+        memset(&p, 0, sizeof(p));
+        for (int r = 0; r < k; ++r) {
+            p.src[r] = (const char *)send[r];
+            p.dst[r] = (char *)recv[r];
+            p.w[r] = w ? w[r] : 1.0f;
+        }
+        p.scale = scale;
+        p.n = (long long)n;
+        p.L = L;
+        p.k = k;
+        p.S = s_chunks;
+        p.max_blocks = max_wg;
+        return hip_status(dps::launch_ar(p, dt, ep, st));
+    }
     char *rs_out[DP_MAX_K];
     for (int c = 0; c < k; ++c) rs_out[c] = (char *)recv[c] + (size_t)c * (size_t)L * (size_t)es;
     dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st, max_wg);
@@ -261,7 +283,8 @@ dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t 
                              int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
+    bool two_phase;
+    if (!opts_ok(opts, max_wg, nullptr, &two_phase)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
@@ -271,7 +294,8 @@ dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t 
     int ep;
     float scale;
     pick_epilogue(op, k, ep, scale);
-    return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream, max_wg);
+    return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream, max_wg,
+                  two_phase);
 }
 
 dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k, int dt,
@@ -283,6 +307,16 @@ dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, 
 dp_status_t dp_weighted_reduce(const void *const *send, void *const *recv, const int64_t *tokens,
                                size_t n, int k, int dt, int s_chunks, void *stream)
 {
+    return dp_weighted_reduce_ex(send, recv, tokens, n, k, dt, s_chunks, nullptr, stream);
+}
+
+dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
+                                  const int64_t *tokens, size_t n, int k, int dt, int s_chunks,
+                                  const dp_launch_opts_t *opts, void *stream)
+{
+    int max_wg;
+    bool two_phase;
+    if (!opts_ok(opts, max_wg, nullptr, &two_phase)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK) return s;
     if (dt == DP_I32) return DP_ERR_UNSUPPORTED;
@@ -299,7 +333,7 @@ dp_status_t dp_weighted_reduce(const void *const *send, void *const *recv, const
     s = check_ar_alias(send, recv, n, k, dps::elem_size(dt));
     if (s != DP_OK) return s;
     return run_ar(send, recv, n, k, dt, dps::kWeighted, (float)total, w, s_chunks,
-                  (hipStream_t)stream);
+                  (hipStream_t)stream, max_wg, two_phase);
 }
 
 dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,

@@ -57,6 +57,10 @@ long long plan_rs(RsParams &p, int dt);
 long long plan_ag(AgParams &p, int dt);
 
 hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t stream);
+// Fused AllReduce: RsParams with dst[r] = rank r's n-element output; every
+// shard's fold goes straight to all K outputs (no shard buffer, no pads).
+long long plan_ar(RsParams &p, int dt);
+hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t stream);
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t stream);
 
 // Batched fp32 GEMM on MFMA: for each batch b < nb,

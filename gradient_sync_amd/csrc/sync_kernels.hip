@@ -193,8 +193,10 @@ __device__ __forceinline__ A finish(A acc, float scale)
     else return acc;
 }
 
-// One element of shard c, shard-local index j (< n_c).
-template <int DT, int EP, int KT>
+// One element of shard c at global index g: the ring-order fold and the
+// epilogue. Stored to `out`, or with AR (fused AllReduce) to element g of every
+// rank's output dst[r].
+template <int DT, int EP, int KT, bool AR>
 __device__ __forceinline__ void rs_elem(const RsParams &p, int K, int c, long long g, char *out)
 {
     using A = typename Tr<DT>::Acc;
@@ -207,25 +209,36 @@ __device__ __forceinline__ void rs_elem(const RsParams &p, int K, int c, long lo
         const int r = fold_rank(c, m, K);
         acc = acc + term<EP>(load1<DT>(p.src[r] + g * ES), p.w[r]);
     }
-    store1<DT>(out, finish<EP>(acc, p.scale));
+    acc = finish<EP>(acc, p.scale);
+    if constexpr (AR) {
+#pragma unroll
+        for (int i = 0; i < (KT ? KT : kMaxK); ++i) {
+            if (!KT && i >= K) break;
+            store1<DT>(p.dst[fold_rank(c, i, K)] + g * ES, acc);
+        }
+    } else {
+        store1<DT>(out, acc);
+    }
 }
 
-template <int DT, int EP, int KT>
+template <int DT, int EP, int KT, bool AR>
 __device__ __forceinline__ void rs_scalar_range(const RsParams &p, int K, int c, long long base,
                                                 long long nc, long long lo, long long hi)
 {
     constexpr int ES = Tr<DT>::ES;
-    char *dst = p.dst[c];
+    char *dst = AR ? nullptr : p.dst[c];
     for (long long j = lo + threadIdx.x; j < hi; j += kBlock) {
-        if (j < nc) rs_elem<DT, EP, KT>(p, K, c, base + j, dst + j * ES);
-        else if (p.write_pads) store1<DT>(dst + j * ES, typename Tr<DT>::Acc(0));
+        if (j < nc) rs_elem<DT, EP, KT, AR>(p, K, c, base + j, AR ? nullptr : dst + j * ES);
+        else if (!AR && p.write_pads) store1<DT>(dst + j * ES, typename Tr<DT>::Acc(0));
     }
 }
 
 // The 128-bit body of a tile: nv vectors (nv == kBlock*U when FULL). The FULL
 // variant has no per-lane conditions, so all loads are issued back to back and
-// the stores are not separated by waits on earlier memory operations.
-template <int DT, int EP, int KT, int U, bool FULL>
+// the stores are not separated by waits on earlier memory operations. With AR
+// the packed result goes to offset `off` of all K outputs (ranks c+1, c+2, ...,
+// c, no per-rank branch) instead of to `dst`.
+template <int DT, int EP, int KT, int U, bool FULL, bool AR>
 __device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const int c,
                                            const long long off, char *dst, const long long nv)
 {
@@ -285,11 +298,20 @@ __device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const
         const long long q = (long long)tid + u * kBlock;
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[u][e] = finish<EP>(acc[u][e], p.scale);
-        if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]));
+        if constexpr (AR) {
+            const u32x4 o = pack<DT>(acc[u]);
+#pragma unroll
+            for (int i = 0; i < (KT ? KT : kMaxK); ++i) {
+                if (!KT && i >= K) break;
+                if (FULL || q < nv) store_ag(p.dst[fold_rank(c, i, K)] + off + q * 16, o);
+            }
+        } else {
+            if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]));
+        }
     }
 }
 
-template <int DT, int EP, int KT, int U>
+template <int DT, int EP, int KT, int U, bool AR>
 __device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const long long bid)
 {
     using A = typename Tr<DT>::Acc;
@@ -312,39 +334,32 @@ __device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const lo
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
 
-    if (t == 0 && body > j0) rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, j0, body);
+    if (t == 0 && body > j0) rs_scalar_range<DT, EP, KT, AR>(p, K, c, base, nc, j0, body);
     if (e0 >= e1) return;
     if (!fast) {
-        rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, e0, e1);
+        rs_scalar_range<DT, EP, KT, AR>(p, K, c, base, nc, e0, e1);
         return;
     }
     const long long ve = min(e1, nc);
     const long long nv = ve > e0 ? (ve - e0) / V : 0;
-    char *dst = p.dst[c] + e0 * ES;
+    char *dst = AR ? nullptr : p.dst[c] + e0 * ES;
     const long long off = (base + e0) * ES;
     if (nv == (long long)kBlock * U)
-        rs_vectors<DT, EP, KT, U, true>(p, K, c, off, dst, nv);
+        rs_vectors<DT, EP, KT, U, true, AR>(p, K, c, off, dst, nv);
     else if (nv > 0)
-        rs_vectors<DT, EP, KT, U, false>(p, K, c, off, dst, nv);
-    rs_scalar_range<DT, EP, KT>(p, K, c, base, nc, e0 + nv * V, e1);
+        rs_vectors<DT, EP, KT, U, false, AR>(p, K, c, off, dst, nv);
+    rs_scalar_range<DT, EP, KT, AR>(p, K, c, base, nc, e0 + nv * V, e1);
 }
 
-template <int DT, int EP, int KT, int U>
+template <int DT, int EP, int KT, int U, bool AR>
 __global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
 {
     const int K = KT ? KT : p.k;
     for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
-        rs_tile<DT, EP, KT, U>(p, K, bid);
+        rs_tile<DT, EP, KT, U, AR>(p, K, bid);
 }
 
 // ------------------------------------------------------------------ AllGather
-
-template <int ES>
-__device__ __forceinline__ void copy1(char *d, const char *s)
-{
-    if constexpr (ES == 2) *reinterpret_cast<unsigned short *>(d) = *reinterpret_cast<const unsigned short *>(s);
-    else *reinterpret_cast<unsigned *>(d) = *reinterpret_cast<const unsigned *>(s);
-}
 
 template <int ES, int KT>
 __device__ __forceinline__ void ag_scalar_range(const AgParams &p, int K, int c, long long base,
@@ -451,22 +466,44 @@ __global__ __launch_bounds__(kAgBlock) void ag_kernel(const AgParams p)
 
 // ------------------------------------------------------------------ launchers
 
-template <int DT, int EP, int KT>
+template <int DT, int EP, int KT, bool AR>
 hipError_t rs_go(const RsParams &p, long long grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 
-template <int DT, int EP>
+template <int DT, int EP, bool AR>
 hipError_t rs_k(const RsParams &p, long long grid, hipStream_t st)
 {
     switch (p.k) {
-    case 2: return rs_go<DT, EP, 2>(p, grid, st);
-    case 4: return rs_go<DT, EP, 4>(p, grid, st);
-    case 8: return rs_go<DT, EP, 8>(p, grid, st);
-    default: return rs_go<DT, EP, 0>(p, grid, st);
+    case 2: return rs_go<DT, EP, 2, AR>(p, grid, st);
+    case 4: return rs_go<DT, EP, 4, AR>(p, grid, st);
+    case 8: return rs_go<DT, EP, 8, AR>(p, grid, st);
+    default: return rs_go<DT, EP, 0, AR>(p, grid, st);
     }
+}
+
+template <bool AR>
+hipError_t rs_dispatch(const RsParams &q, int dt, int ep, long long grid, hipStream_t st)
+{
+    if (dt == kF32) {
+        switch (ep) {
+        case kSum: return rs_k<kF32, kSum, AR>(q, grid, st);
+        case kMul: return rs_k<kF32, kMul, AR>(q, grid, st);
+        case kDiv: return rs_k<kF32, kDiv, AR>(q, grid, st);
+        default: return rs_k<kF32, kWeighted, AR>(q, grid, st);
+        }
+    }
+    if (dt == kBF16) {
+        switch (ep) {
+        case kSum: return rs_k<kBF16, kSum, AR>(q, grid, st);
+        case kMul: return rs_k<kBF16, kMul, AR>(q, grid, st);
+        case kDiv: return rs_k<kBF16, kDiv, AR>(q, grid, st);
+        default: return rs_k<kBF16, kWeighted, AR>(q, grid, st);
+        }
+    }
+    return rs_k<kI32, kSum, AR>(q, grid, st);
 }
 
 template <int ES, int KT>
@@ -498,8 +535,6 @@ int rs_vectors_per_thread(int dt)
 
 namespace {
 
-// bit 4: every input of shard c (at element c*L) and the shard's output share
-// one 16-byte phase; bits 0-3: that phase
 // kFastBit: every stream ins[r] + in_off and `out` share one 16-byte phase.
 // Bits 0-7: the address phase modulo 256 of the anchor stream (ins[0] + in_off
 // when anchor_ins, else out) at shard element 0; tile bodies start where the
@@ -559,23 +594,34 @@ hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t st)
     const long long grid = plan_rs(q, dt);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (dt == kF32) {
-        switch (ep) {
-        case kSum: return rs_k<kF32, kSum>(q, grid, st);
-        case kMul: return rs_k<kF32, kMul>(q, grid, st);
-        case kDiv: return rs_k<kF32, kDiv>(q, grid, st);
-        default: return rs_k<kF32, kWeighted>(q, grid, st);
-        }
+    return rs_dispatch<false>(q, dt, ep, grid, st);
+}
+
+long long plan_ar(RsParams &p, int dt)
+{
+    const int es = elem_size(dt);
+    for (int c = 0; c < p.k; ++c) {
+        // the K inputs and the K outputs at element c*L; anchor: output 0
+        const long long off = (long long)c * p.L * es;
+        const int m_in = phase_meta(p.src, off, p.k, p.dst[0] + off, false);
+        const int m_out = phase_meta(p.dst, off, p.k, p.dst[0] + off, false);
+        p.meta[c] = (m_in & m_out & kFastBit) | (m_out & 255);
     }
-    if (dt == kBF16) {
-        switch (ep) {
-        case kSum: return rs_k<kBF16, kSum>(q, grid, st);
-        case kMul: return rs_k<kBF16, kMul>(q, grid, st);
-        case kDiv: return rs_k<kBF16, kDiv>(q, grid, st);
-        default: return rs_k<kBF16, kWeighted>(q, grid, st);
-        }
-    }
-    return rs_k<kI32, kSum>(q, grid, st);
+    p.write_pads = 0;
+    p.sub = ceil_div(p.L, p.S);
+    const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
+    p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
+    p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
+    return grid_for(p.total_tiles, p.max_blocks);
+}
+
+hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t st)
+{
+    RsParams q = p;
+    const long long grid = plan_ar(q, dt);
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return rs_dispatch<true>(q, dt, ep, grid, st);
 }
 
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t st)

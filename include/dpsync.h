@@ -119,9 +119,13 @@ dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, 
  * five building blocks"; T_AR,ring equation in "Sharding and Parallelism").
  *   send[r], recv[r] : n elements. Every recv[r] receives the full reduced
  *   vector, bit-identical to dp_all_gather(dp_reduce_scatter(send)).
- *   Shard c is first reduced into recv[c] at offset c*L, then copied from
- *   there to the other ranks; no workspace is used.
- *   In place: recv[r] == send[r] for every r is allowed.
+ *   By default one pass folds each shard in ring order and writes the result
+ *   to all K outputs (K*n*s bytes read and K*n*s written, against (K+1)*n*s
+ *   each way for the two collectives); with DP_LAUNCH_TWO_PHASE
+ *   (dp_all_reduce_ex) shard c is first reduced into recv[c] at offset c*L,
+ *   then copied from there to the other ranks. No workspace either way.
+ *   In place: for every r, recv[r] either equals send[r] or overlaps no send
+ *   buffer; receive buffers are pairwise disjoint.
  */
 dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k,
                           int dt, int op, int s_chunks, void *stream);
@@ -194,12 +198,16 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
  *   flags          : DP_LAUNCH_SHARE_CU selects, for dp_gemm_bf16_ex, the GEMM
  *                    variant with a smaller register footprint (depth-32 k
  *                    stages) so that a sync workgroup can be resident on the
- *                    same CU as a GEMM workgroup. Ignored by the sync calls.
+ *                    same CU as a GEMM workgroup. DP_LAUNCH_TWO_PHASE makes
+ *                    dp_all_reduce_ex / dp_weighted_reduce_ex run a
+ *                    ReduceScatter then an AllGather instead of the one-pass
+ *                    kernel (same results). Other calls ignore the flags.
  *   reserved       : must be zero.
  * A NULL opts pointer means all defaults. Invalid fields return
  * DP_ERR_INVALID_ARG.
  */
 #define DP_LAUNCH_SHARE_CU 1
+#define DP_LAUNCH_TWO_PHASE 2
 
 typedef struct {
     int max_workgroups;
@@ -219,6 +227,9 @@ dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t 
                              void *stream);
 dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, int64_t n,
                             int64_t kk, const dp_launch_opts_t *opts, void *stream);
+dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
+                                  const int64_t *tokens, size_t n, int k, int dt, int s_chunks,
+                                  const dp_launch_opts_t *opts, void *stream);
 
 #ifdef __cplusplus
 }

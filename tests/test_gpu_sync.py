@@ -408,3 +408,45 @@ def test_capped_grid_is_bit_identical(dtype):
             for r in (0, k - 1):
                 assert bits_equal(to_np(out[r].t), want[r]), (cap, r)
                 assert bits_equal(to_np(out2[r]), want[r]), (cap, r)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+@pytest.mark.parametrize("k,n,in_off,out_off", [(8, 8 * 4096 * 3 + 11, 0, 0), (8, 100_003, 1, 3),
+                                                (5, 7777, 0, 2), (1, 64, 0, 0), (16, 50_001, 2, 2),
+                                                (8, 3, 0, 0)])
+def test_one_pass_all_reduce_equals_two_phase(dtype, k, n, in_off, out_off):
+    """The one-pass AllReduce (default) and the ReduceScatter + AllGather pair
+    give the oracle's bits, out of place (any alignment) and in place."""
+    xs, hx = make_inputs(dtype, k, n, seed=60 + n % 97, off=in_off)
+    op = "sum" if dtype == torch.int32 else "avg"
+    want = oracle.all_reduce(hx, op=op)
+    for two_phase in (False, True):
+        for cap in (0, 5):
+            say(f"ar k={k} n={n} {dtype} two_phase={two_phase} cap={cap}")
+            outs = [Guarded(n, dtype, out_off) for _ in range(k)]
+            dps.dp_all_reduce_ex([g.t for g in xs], [o.t for o in outs], op=op, s_chunks=3,
+                                 max_workgroups=cap, two_phase=two_phase)
+            torch.cuda.synchronize()
+            for r in range(k):
+                assert bits_equal(to_np(outs[r].t), want[r]), (two_phase, cap, r)
+                assert outs[r].intact()
+    # in place, one pass
+    dps.dp_all_reduce([g.t for g in xs], [g.t for g in xs], op=op)
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(xs[r].t), want[r])
+        assert xs[r].intact()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_weighted_one_pass_equals_two_phase(dtype):
+    k, n = 8, 1_000_003
+    xs, hx = make_inputs(dtype, k, n, seed=61)
+    toks = gen.token_counts(7, k)
+    want = oracle.weighted_all_reduce(hx, toks, nthreads=8)
+    for two_phase in (False, True):
+        out = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+        dps.dp_weighted_reduce_ex([g.t for g in xs], out, toks, two_phase=two_phase)
+        torch.cuda.synchronize()
+        for r in (0, 3, k - 1):
+            assert bits_equal(to_np(out[r]), want[r]), two_phase
