@@ -39,10 +39,10 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "5d1e6c7fa8eeb56503474c0148f257710a4a0907e905af703ce58ed6532cfc7c"
-                      "4654b4c820abfecd7711b119a967e292af0956bcc797d798fb436ea42601cb63",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195400.7 + 49744.5) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24937.5 + 390626.0) * 1024,
+    "sources_sha256": "42c9464ce4dcbe9aa452f09ead63a78d4b219294ab6c220d9daa8eb4ac5f0524"
+                      "9cbbc1ae223ff22b77248ea989eb14366c635a20aa08e93c02234093617dccd8",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195407.1 + 49747.1) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24800.5 + 390847.7) * 1024,
 }
 
 
