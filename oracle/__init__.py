@@ -67,6 +67,10 @@ def lib():
         for name in ("orc_fold_f32_at", "orc_fold_bf16_at"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [_vp, _vp, _i64, _int, _int, _int, _vp]
+        L.orc_scatter_accumulate.restype = None
+        L.orc_scatter_accumulate.argtypes = [_int, _vp, _vp, _i64, _i64, _int]
+        L.orc_settle.restype = None
+        L.orc_settle.argtypes = [_int, _vp, _vp, _i64, _i64, _int, ctypes.c_float]
         L.orc_ag.restype = None
         L.orc_ag.argtypes = [_int, _vp, _vp, _i64, _i64, _int, _int]
         L.orc_ar.restype = _int
@@ -186,6 +190,27 @@ def fold_at(xs_compact, shard_ids, op: str = "sum", order: str = "ring"):
     fn(_ptrs(xs_compact), sid.ctypes.data, sid.size, k, {"sum": SUM, "avg": AVG}[op],
        ORDERS[order], out.ctypes.data)
     return out
+
+
+def scatter_accumulate(g, acc, k: int, L: int | None = None):
+    """Push gradient g (n elements) into the K owners' fp32 accumulators acc
+    (list of K float32 arrays of length L, updated in place)."""
+    n = int(g.size)
+    L = shard_len(n, k) if L is None else L
+    dt = _dtype_code([g])
+    assert dt in (0, 1) and all(a.dtype == np.float32 and a.size >= L for a in acc)
+    if n:
+        lib().orc_scatter_accumulate(dt, g.ctypes.data, _ptrs(acc), n, L, k)
+    return acc
+
+
+def settle(acc, n: int, k: int, dtype=np.float32, divisor: float = 1.0, L: int | None = None):
+    """Final shards from the accumulators: cast(acc / divisor), pads zero."""
+    L = shard_len(n, k) if L is None else L
+    outs = [np.zeros(L, dtype=dtype) for _ in range(k)]
+    if L:
+        lib().orc_settle(_DT[np.dtype(dtype)], _ptrs(acc), _ptrs(outs), n, L, k, divisor)
+    return outs
 
 
 def all_gather(shards, n: int, L: int | None = None, nthreads: int = 1):

@@ -330,6 +330,47 @@ void orc_fold_bf16_at(const uint16_t *const *x, const int32_t *shard_id, int64_t
     }
 }
 
+/* ------------------------------------------------- scatter-accumulate, settle
+ * On-demand communication ("Using ODC to Accelerate AMD SFT Training", section
+ * "From Collective Primitives to Two One-sided P2P Primitives", Figure 2): a
+ * rank that has computed a gradient pushes each shard of it to the shard's
+ * owner, which adds it into its gradient accumulator Acc; after the minibatch
+ * one settle makes the accumulated shards final (section "From Per-iteration
+ * to Per-minibatch Synchronization").
+ *
+ * Push of one gradient g (n elements, shard length L, k owners):
+ *   acc[c][j] = acc[c][j] + f32(g[c*L + j])   for every c and j < n_c,
+ * one fp32 addition per element, in the order the pushes are made.
+ * Settle: out[c][j] = cast(acc[c][j] / divisor) for j < n_c, pads zero. */
+
+/* dtype of g: 0 = f32, 1 = bf16 */
+void orc_scatter_accumulate(int dtype, const void *g, float *const *acc, int64_t n, int64_t L,
+                            int k)
+{
+    for (int c = 0; c < k; ++c) {
+        int64_t nc = orc_shard_valid(n, L, c);
+        for (int64_t j = 0; j < nc; ++j) {
+            int64_t i = (int64_t)c * L + j;
+            float v = dtype == 1 ? orc_bf16_to_f32(((const uint16_t *)g)[i]) : ((const float *)g)[i];
+            acc[c][j] = acc[c][j] + v;
+        }
+    }
+}
+
+/* dtype of out: 0 = f32, 1 = bf16 */
+void orc_settle(int dtype, const float *const *acc, void *const *out, int64_t n, int64_t L, int k,
+                float divisor)
+{
+    for (int c = 0; c < k; ++c) {
+        int64_t nc = orc_shard_valid(n, L, c);
+        for (int64_t j = 0; j < L; ++j) {
+            float v = j < nc ? acc[c][j] / divisor : 0.0f;
+            if (dtype == 1) ((uint16_t *)out[c])[j] = j < nc ? orc_bf16_from_f32(v) : 0;
+            else ((float *)out[c])[j] = v;
+        }
+    }
+}
+
 /* -------------------------------------------------------------- AllGather
  * out[r][i] = shard[i / L][i mod L] for every rank r and 0 <= i < n. */
 

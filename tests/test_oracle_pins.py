@@ -451,3 +451,100 @@ def test_mutant_divide_by_wrong_count_is_caught():
     s = oracle.reduce_scatter(xs, op="sum")
     wrong = [x / np.float32(k - 1) for x in s]
     assert any(w.tobytes() != (x * np.float32(1 / k)).tobytes() for w, x in zip(wrong, s))
+
+
+# --------------------------------------- scatter-accumulate and one settle
+
+def _microbatches(k, counts, n, seed, integer=False):
+    """g[r][m]: rank r's m-th microbatch gradient, fp32."""
+    out = []
+    for r in range(k):
+        gs = []
+        for m in range(counts[r]):
+            x = gen.uniform_pm1(seed, 40 + m, r, n)
+            gs.append((gen.int_copy(x).to(torch.float32) if integer else x).numpy())
+        out.append(gs)
+    return out
+
+
+def test_scatter_accumulate_settle_is_the_exact_sum_on_integers():
+    """Pushes of uneven microbatch counts in any order, then one settle, give
+    sum over ranks and microbatches (exact for integer values)."""
+    k, n, counts = 4, 1001, [1, 3, 0, 2]
+    g = _microbatches(k, counts, n, 50, integer=True)
+    exact = sum(gm.astype(np.int64) for gr in g for gm in gr)
+    L = oracle.shard_len(n, k)
+    rng = np.random.default_rng(0)
+    pushes = [(r, m) for r in range(k) for m in range(counts[r])]
+    for order in (pushes, list(reversed(pushes)), [pushes[i] for i in rng.permutation(len(pushes))]):
+        acc = [np.zeros(L, np.float32) for _ in range(k)]
+        for r, m in order:
+            oracle.scatter_accumulate(g[r][m], acc, k)
+        out = oracle.settle(acc, n, k)
+        full = np.concatenate([out[c][:oracle.shard_valid(n, L, c)] for c in range(k)])
+        assert np.array_equal(full.astype(np.int64), exact)
+
+
+def test_padded_reduce_scatter_steps_match_on_integers():
+    """The collective baseline pads every rank to the largest microbatch count
+    with empty (zero) gradients and reduce-scatters step by step; on integer
+    values it reaches the same sums as the pushes."""
+    k, n, counts = 4, 777, [2, 1, 3, 1]
+    g = _microbatches(k, counts, n, 51, integer=True)
+    L = oracle.shard_len(n, k)
+    acc_push = [np.zeros(L, np.float32) for _ in range(k)]
+    for r in range(k):
+        for gm in g[r]:
+            oracle.scatter_accumulate(gm, acc_push, k)
+    acc_pad = [np.zeros(L, np.float32) for _ in range(k)]
+    zero = np.zeros(n, np.float32)
+    for m in range(max(counts)):
+        step = [g[r][m] if m < counts[r] else zero for r in range(k)]
+        shards = oracle.reduce_scatter(step, op="sum")
+        oracle.scatter_accumulate(np.concatenate(shards), acc_pad, k, L=L)
+    for c in range(k):
+        assert np.array_equal(acc_push[c], acc_pad[c])
+
+
+def test_scatter_accumulate_within_summation_bound():
+    k, n, counts = 8, 2003, [3, 1, 1, 4, 2, 1, 1, 2]
+    g = _microbatches(k, counts, n, 52)
+    L = oracle.shard_len(n, k)
+    acc = [np.zeros(L, np.float32) for _ in range(k)]
+    for r in range(k):
+        for gm in g[r]:
+            oracle.scatter_accumulate(gm, acc, k)
+    got = np.concatenate([acc[c][:oracle.shard_valid(n, L, c)] for c in range(k)])
+    ex = sum(gm.astype(np.float64) for gr in g for gm in gr)
+    ab = sum(np.abs(gm.astype(np.float64)) for gr in g for gm in gr)
+    assert np.all(np.abs(got - ex) <= _gamma(sum(counts)) * ab)
+
+
+def test_settle_scaling_and_rounding():
+    k, n = 3, 100
+    acc = [gen.uniform_pm1(53, 0, c, 34).numpy() * np.float32(64) for c in range(k)]
+    out = oracle.settle(acc, n, k, divisor=4.0)
+    for c in range(k):
+        nc = oracle.shard_valid(n, 34, c)
+        assert out[c][:nc].tobytes() == (acc[c][:nc] * np.float32(0.25)).tobytes()
+        assert not out[c][nc:].any()
+    ob = oracle.settle(acc, n, k, dtype=np.uint16, divisor=4.0)
+    want = torch.from_numpy(np.concatenate([(acc[c] * np.float32(0.25))[:oracle.shard_valid(n, 34, c)]
+                                            for c in range(k)])).to(torch.bfloat16)
+    got = np.concatenate([ob[c][:oracle.shard_valid(n, 34, c)] for c in range(k)])
+    assert np.array_equal(got, want.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_mutant_lost_push_is_caught():
+    """Dropping one push (a gradient that never lands before the settle) is
+    caught by the exact-sum pin."""
+    k, n, counts = 4, 301, [1, 2, 1, 1]
+    g = _microbatches(k, counts, n, 54, integer=True)
+    exact = sum(gm.astype(np.int64) for gr in g for gm in gr)
+    L = oracle.shard_len(n, k)
+    acc = [np.zeros(L, np.float32) for _ in range(k)]
+    for r in range(k):
+        for gm in g[r][:1]:                      # rank r's later microbatches are lost
+            oracle.scatter_accumulate(gm, acc, k)
+    full = np.concatenate([acc[c][:oracle.shard_valid(n, L, c)] for c in range(k)])
+    assert not np.array_equal(full.astype(np.int64), exact)
