@@ -18,6 +18,8 @@ Other measurements (each prints its own JSON line):
   --config c3        RS+AG of 1 GiB/rank fp32 (K=8) concurrent with a bf16
                      8192^3 GEMM on another stream
   --config fused_ar  the layer buckets as one-pass AllReduce, against RS+AG
+  --config odc       one minibatch with uneven microbatch counts: ODC pushes
+                     and one settle vs padded per-microbatch ReduceScatter
   --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
@@ -422,6 +424,106 @@ def bench_c3(args):
                                    "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}
 
 
+def bench_odc(args):
+    """One minibatch of gradient synchronisation with uneven microbatch counts:
+    on-demand scatter-accumulate pushes with one settle, against the padded
+    per-microbatch ReduceScatter baseline. A push carries one microbatch's
+    gradients of a whole transformer layer; every microbatch slot, padded ones
+    included, has its own gradient buffer, so the working set (about 23 GB) is
+    far larger than the on-chip caches."""
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, n, s = 8, gen.LAYER_PARAMS, 2
+    counts = gen.microbatch_counts(1, k)
+    mmax, total = max(counts), sum(counts)
+    L = dps.dp_shard_len(n, k)
+    grads = [[gen.microbatch_grad(1, r, m, n, device="cuda") for m in range(counts[r])]
+             for r in range(k)]
+    # an empty (padding) bucket contributes a zero gradient of its own
+    padded = [[grads[r][m] if counts[r] > m else torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+               for r in range(k)] for m in range(mmax)]
+    rounds = [[padded[m][r] for r in range(k) if counts[r] > m] for m in range(mmax)]
+    acc = [torch.zeros(L, dtype=torch.float32, device="cuda") for _ in range(k)]
+    out = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    shard_buf = torch.empty(k * L, dtype=torch.bfloat16, device="cuda")
+    shard_views = [shard_buf[c * L:(c + 1) * L] for c in range(k)]
+    div = float(total)
+
+    def settle():
+        dps.dp_settle(acc, out, n, divisor=div, reset=True)
+
+    def odc_nopad_drain():
+        for rnd in rounds:
+            dps.dp_scatter_accumulate(rnd, acc)
+        settle()
+
+    def odc_nopad_per_push():
+        for rnd in rounds:
+            for g in rnd:
+                dps.dp_scatter_accumulate(g, acc)
+        settle()
+
+    def odc_pad_drain():
+        for rnd in padded:
+            dps.dp_scatter_accumulate(rnd, acc)
+        settle()
+
+    def nccl_pad():
+        for rnd in padded:
+            dps.dp_reduce_scatter(rnd, shard_views, op="sum")
+            dps.dp_scatter_accumulate(shard_buf, acc)
+        settle()
+
+    settle_b = 8 * n + k * L * s
+    push_b = lambda p: p * n * s + 8 * n
+    sched = {
+        "odc_nopad_drain": (odc_nopad_drain, mmax * 8 * n + total * n * s + settle_b, mmax + 1),
+        "odc_nopad_per_push": (odc_nopad_per_push, total * push_b(1) + settle_b, total + 1),
+        "odc_pad_drain": (odc_pad_drain, mmax * push_b(k) + settle_b, mmax + 1),
+        "nccl_pad": (nccl_pad, mmax * (k * n * s + k * L * s + k * L * s + 8 * k * L) + settle_b,
+                     2 * mmax + 1),
+    }
+    res = {}
+    for name, (fn, b, launches) in sched.items():
+        log(f"[bench] odc schedule {name}")
+        ms = _time_ms(fn, warm=2, reps=7)
+        med = statistics.median(ms)
+        res[name] = {"median_ms": round(med, 4), "min_ms": round(min(ms), 4), "launches": launches,
+                     "bytes": b, "gbs": round(b / (med * 1e-3) / 1e9, 1),
+                     "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    for name in ("odc_nopad_drain", "odc_pad_drain", "odc_nopad_per_push"):
+        res[name]["speedup_vs_nccl_pad"] = round(res["nccl_pad"]["median_ms"] /
+                                                 res[name]["median_ms"], 4)
+    # kernel rooflines: one push of all K ranks' gradients, one single push, the settle
+    kern = {}
+    flip = [0]
+
+    def push8():
+        flip[0] = (flip[0] + 1) % mmax
+        dps.dp_scatter_accumulate(padded[flip[0]], acc)
+
+    flat = [g for rnd in rounds for g in rnd]
+
+    def push1():
+        flip[0] = (flip[0] + 1) % total
+        dps.dp_scatter_accumulate(flat[flip[0]], acc)
+    for name, fn, b in (("scatter_accumulate_np8", push8, push_b(k)),
+                        ("scatter_accumulate_np1", push1, push_b(1)),
+                        ("settle_bf16_reset", settle, settle_b)):
+        med = statistics.median(_time_ms(fn, warm=3, reps=15))
+        kern[name] = {"median_us": round(1e3 * med, 2), "bytes": b,
+                      "gbs": round(b / (med * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"metric": "one minibatch of ODC gradient sync vs padded ReduceScatter, K=8, "
+                      "one layer (218,103,808 bf16) per microbatch gradient",
+            "unit": "ms", "counts": counts, "results": res, "kernels": kern,
+            "config": {"workload": "K=8, 218,103,808 bf16 N(0,1e-3^2) per microbatch, microbatch "
+                                   "counts ceil(tokens/2048) from log-normal(7,1) token counts "
+                                   "(2 docs/rank, seed 1), fp32 owner accumulators, bf16 settle"}}
+
+
 def bench_copy(args):
     """A plain elementwise device copy of known size (1 GiB read + 1 GiB
     written): the practical HBM ceiling on this GPU, and the reference against
@@ -446,7 +548,7 @@ def bench_copy(args):
 
 
 CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
-           "fused_ar": bench_fused_ar, "copy": bench_copy}
+           "fused_ar": bench_fused_ar, "odc": bench_odc, "copy": bench_copy}
 
 
 def main():

@@ -171,3 +171,24 @@ def gemm_bf16_inputs(seed: int, m: int, n: int, kk: int, device="cpu"):
     a = bf16_normal(seed, 30, 0, m * kk, 1.0, device=device).view(m, kk)
     b = bf16_normal(seed, 31, 0, n * kk, 1.0, device=device).view(n, kk)
     return a, b
+
+
+# Variable-length minibatch of an SFT step: each rank's documents are packed
+# into microbatches of at most MICROBATCH_TOKENS tokens, so ranks run uneven
+# microbatch counts.
+MICROBATCH_TOKENS = 2048
+
+
+def microbatch_counts(seed: int, k: int, tokens_per_microbatch: int = MICROBATCH_TOKENS,
+                      docs_per_rank: int = 2) -> list[int]:
+    """Per-rank microbatch counts max(1, ceil(t_r / tokens_per_microbatch)) for
+    the token counts of token_counts(seed, k, docs_per_rank)."""
+    t = token_counts(seed, k, docs_per_rank)
+    return [max(1, -(-x // tokens_per_microbatch)) for x in t]
+
+
+def microbatch_grad(seed: int, rank: int, m: int, n: int, dtype=torch.bfloat16,
+                    std: float = 1e-3, device="cpu") -> torch.Tensor:
+    """Rank `rank`'s gradient from its m-th microbatch: N(0, std^2) in fp32,
+    rounded to nearest-even `dtype` (tensor id 40 + m)."""
+    return normal(seed, 40 + m, rank, n, std=std, device=device).to(dtype)

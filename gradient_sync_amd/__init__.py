@@ -28,7 +28,7 @@ __all__ = [
     "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
     "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
     "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
-    "dp_weighted_reduce_ex",
+    "dp_weighted_reduce_ex", "dp_scatter_accumulate", "dp_settle",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +43,8 @@ DP_MAX_K = 64
 EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version",
            "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
-           "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex")
+           "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex",
+           "dp_scatter_accumulate", "dp_settle")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
@@ -116,6 +117,10 @@ def lib():
         L.dp_gemm_bf16_ex.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, P, _vp]
         L.dp_weighted_reduce_ex.restype = _int
         L.dp_weighted_reduce_ex.argtypes = [_vp, _vp, _vp, _sz, _int, _int, _int, P, _vp]
+        L.dp_scatter_accumulate.restype = _int
+        L.dp_scatter_accumulate.argtypes = [_vp, _int, _int, _vp, _sz, _int, _vp]
+        L.dp_settle.restype = _int
+        L.dp_settle.argtypes = [_vp, _vp, _sz, _int, _int, ctypes.c_float, _int, _vp]
         _lib = L
     return _lib
 
@@ -358,3 +363,40 @@ def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None):
     """dp_gemm_bf16; share_cu selects the variant that leaves room for a sync
     workgroup on every CU."""
     _gemm(a, b, c, stream, ctypes.byref(LaunchOpts.make(0, share_cu)))
+
+
+def dp_scatter_accumulate(grads, acc, stream=None, n=None):
+    """Apply the pushes `grads` (one tensor or a list, in push order) to the K
+    owners' fp32 accumulators: acc[c][j] += f32(g[c*L + j]) for each g in turn
+    (ODC scatter-accumulate)."""
+    if isinstance(grads, torch.Tensor):
+        grads = [grads]
+    grads = _tensors(grads, "grads")
+    acc = _tensors(acc, "acc", torch.float32)
+    k = len(acc)
+    n = grads[0].numel() if n is None else n
+    _numel_check(grads, n, "grads")
+    _numel_check(acc, dp_shard_len(n, k), "acc")
+    if grads[0].dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("grads must be float32 or bfloat16")
+    _check(lib().dp_scatter_accumulate(ptr_array([t.data_ptr() for t in grads]), len(grads),
+                                       _dt(grads[0]), ptr_array([t.data_ptr() for t in acc]), n, k,
+                                       _stream(stream)), "dp_scatter_accumulate")
+
+
+def dp_settle(acc, out, n, divisor: float = 1.0, reset: bool = False, stream=None):
+    """out[c][j] = cast(acc[c][j] / divisor), pads zero; optionally zero the
+    accumulators afterwards (ODC per-minibatch settle)."""
+    acc = _tensors(acc, "acc", torch.float32)
+    out = _tensors(out, "out")
+    k = len(acc)
+    if len(out) != k:
+        raise ValueError("acc and out need one buffer per owner")
+    L = dp_shard_len(n, k)
+    _numel_check(acc, L, "acc")
+    _numel_check(out, L, "out")
+    if out[0].dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check(lib().dp_settle(ptr_array([t.data_ptr() for t in acc]),
+                           ptr_array([t.data_ptr() for t in out]), n, k, _dt(out[0]),
+                           float(divisor), 1 if reset else 0, _stream(stream)), "dp_settle")

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "dps_internal.h"
+#include "odc_internal.h"
 #include "dpsync.h"
 
 static_assert(dps::kMaxK == DP_MAX_K, "kernel and ABI rank limits differ");
@@ -426,6 +427,72 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
     if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
         return DP_ERR_ALIAS;
     return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, share_cu, (hipStream_t)stream));
+}
+
+dp_status_t dp_scatter_accumulate(const void *const *grads, int np, int dt, float *const *acc,
+                                  size_t n, int k, void *stream)
+{
+    if (!valid_k(k) || np < 1 || np > DP_MAX_K) return DP_ERR_INVALID_ARG;
+    if (dt != DP_F32 && dt != DP_BF16) return DP_ERR_UNSUPPORTED;
+    const int es = dps::elem_size(dt);
+    if (!size_ok(n, es)) return DP_ERR_INVALID_ARG;
+    if (n == 0) return (grads && acc) ? DP_OK : DP_ERR_INVALID_ARG;
+    if (!ptrs_ok(grads, np, es) || !ptrs_ok((const void *const *)acc, k, 4))
+        return DP_ERR_INVALID_ARG;
+    const size_t L = dp_shard_len(n, k);
+    for (int c = 0; c < k; ++c)
+        for (int i = 0; i < np; ++i)
+            if (overlap(span(acc[c], L * 4), span(grads[i], n * es))) return DP_ERR_ALIAS;
+    if (!pairwise_disjoint((void *const *)acc, k, L * 4)) return DP_ERR_ALIAS;
+    dps::SaParams p;
+    memset(&p, 0, sizeof(p));
+    for (int i = 0; i < np; ++i) p.g[i] = (const char *)grads[i];
+    for (int c = 0; c < k; ++c) p.acc[c] = acc[c];
+    p.n = (long long)n;
+    p.L = (long long)L;
+    p.np = np;
+    p.k = k;
+    return hip_status(dps::launch_scatter_accumulate(p, dt, (hipStream_t)stream));
+}
+
+dp_status_t dp_settle(float *const *acc, void *const *out, size_t n, int k, int dt, float divisor,
+                      int reset, void *stream)
+{
+    if (!valid_k(k)) return DP_ERR_INVALID_ARG;
+    if (dt != DP_F32 && dt != DP_BF16) return DP_ERR_UNSUPPORTED;
+    const int es = dps::elem_size(dt);
+    if (!size_ok(n, 4)) return DP_ERR_INVALID_ARG;
+    uint32_t bits;
+    memcpy(&bits, &divisor, 4);
+    const uint32_t ex = (bits >> 23) & 0xffu;
+    if (ex == 0xffu || (bits & 0x7fffffffu) == 0) return DP_ERR_INVALID_ARG;
+    if (n == 0) return (acc && out) ? DP_OK : DP_ERR_INVALID_ARG;
+    if (!ptrs_ok((const void *const *)acc, k, 4) || !ptrs_ok((const void *const *)out, k, es))
+        return DP_ERR_INVALID_ARG;
+    const size_t L = dp_shard_len(n, k);
+    const bool in_place_ok = dt == DP_F32 && !reset;
+    for (int c = 0; c < k; ++c)
+        for (int q = 0; q < k; ++q) {
+            if (in_place_ok && c == q && out[c] == (void *)acc[c]) continue;
+            if (overlap(span(out[c], L * es), span(acc[q], L * 4))) return DP_ERR_ALIAS;
+        }
+    if (!pairwise_disjoint((void *const *)acc, k, L * 4) || !pairwise_disjoint(out, k, L * es))
+        return DP_ERR_ALIAS;
+    dps::SettleParams p;
+    memset(&p, 0, sizeof(p));
+    for (int c = 0; c < k; ++c) {
+        p.acc[c] = acc[c];
+        p.out[c] = (char *)out[c];
+    }
+    // a normal power of two (zero fraction bits) has an exact reciprocal, and
+    // multiplying by it rounds the same real number as dividing
+    const bool mul = (bits & 0x7fffffu) == 0 && ex != 0;
+    p.scale = mul ? 1.0f / divisor : divisor;
+    p.reset = reset ? 1 : 0;
+    p.n = (long long)n;
+    p.L = (long long)L;
+    p.k = k;
+    return hip_status(dps::launch_settle(p, dt, mul, (hipStream_t)stream));
 }
 
 dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n, int64_t kk,

@@ -231,6 +231,51 @@ dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
                                   const int64_t *tokens, size_t n, int k, int dt, int s_chunks,
                                   const dp_launch_opts_t *opts, void *stream);
 
+/*
+ * On-demand communication: scatter-accumulate push ("Using ODC to Accelerate
+ * AMD SFT Training", section "From Collective Primitives to Two One-sided P2P
+ * Primitives", Figure 2: after computing a gradient, a rank pushes each shard
+ * of it to the rank that owns the shard, which adds it into its gradient
+ * accumulator Acc).
+ *   grads[i] : push i's gradient (one rank's microbatch gradient), n elements
+ *              of dt (DP_F32 or DP_BF16), i < np, 1 <= np <= DP_MAX_K
+ *   acc[c]   : owner c's fp32 accumulator, L = dp_shard_len(n, k) elements
+ *   Effect   : for i = 0, 1, ..., np-1 in that order,
+ *              acc[c][j] = acc[c][j] + f32(grads[i][c*L + j]) for j < n_c
+ *              (one fp32 addition each, no FMA); pads j >= n_c untouched.
+ * One call with np pushes gives the same bits as np calls with one push each,
+ * in the same order: an owner applying, in arrival order, all pushes that have
+ * landed. Calls on one stream apply in issue order, so any push sequence has a
+ * deterministic result, the left fold of the pushed values. The accumulators
+ * must be pairwise disjoint and overlap no gradient (DP_ERR_ALIAS); gradients
+ * may overlap one another. dt = DP_I32 returns DP_ERR_UNSUPPORTED. The fast
+ * path needs 16-byte alignment of acc[c] and of every grads[i] + c*L; any
+ * element alignment works.
+ */
+dp_status_t dp_scatter_accumulate(const void *const *grads, int np, int dt, float *const *acc,
+                                  size_t n, int k, void *stream);
+
+/*
+ * On-demand communication: the per-minibatch settle ("Using ODC to Accelerate
+ * AMD SFT Training", section "From Per-iteration to Per-minibatch
+ * Synchronization": gradients accumulate over the minibatch and one settle at
+ * its end makes them final before the optimizer reads them).
+ *   acc[c] : owner c's fp32 accumulator (L elements)
+ *   out[c] : owner c's settled shard, L elements of dt (DP_F32 or DP_BF16)
+ *   Effect : out[c][j] = cast(acc[c][j] / divisor) for j < n_c (one IEEE fp32
+ *            division, bf16 rounded to nearest even once), out[c][j] = 0 for
+ *            n_c <= j < L. divisor = 1 gives the sum; the number of
+ *            contributions gives the mean. With reset != 0 the accumulator's
+ *            valid elements are set to zero afterwards, ready for the next
+ *            minibatch.
+ * divisor must be finite and non-zero (DP_ERR_INVALID_ARG). The outputs must
+ * be pairwise disjoint and must not overlap any accumulator, except that with
+ * dt = DP_F32 and reset = 0 out[c] may equal acc[c] (settle in place); other
+ * overlaps return DP_ERR_ALIAS.
+ */
+dp_status_t dp_settle(float *const *acc, void *const *out, size_t n, int k, int dt, float divisor,
+                      int reset, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -194,3 +194,34 @@ def test_launch_options_validation():
     assert L.dp_all_reduce_ex(P(a), P(b), 0, 4, F32, SUM, 1, ok, None) == OK
     assert L.dp_gemm_bf16_ex(1 << 40, 1 << 41, 1 << 42, 8, 8, 12, ok, None) == UNSUPPORTED
     assert L.dp_reduce_scatter_ex(P(a), P(b), 0, 4, F32, SUM, 1, None, None) == OK
+
+
+def test_odc_validation():
+    L = dps.lib()
+    g, acc, out = 1 << 40, fake(4, base=1 << 41), fake(4, base=1 << 42)
+    sa = L.dp_scatter_accumulate
+    gs = [g, g + 4096]
+    assert sa(P(gs), 2, F32, P(acc), 1000, 0, None) == INVALID           # k out of range
+    assert sa(P(gs), 0, F32, P(acc), 1000, 4, None) == INVALID           # no push
+    assert sa(P(gs), 65, F32, P(acc), 1000, 4, None) == INVALID
+    assert sa(P(gs), 2, I32, P(acc), 1000, 4, None) == UNSUPPORTED
+    assert sa(P([g, 0]), 2, F32, P(acc), 1000, 4, None) == INVALID
+    assert sa(None, 1, F32, P(acc), 1000, 4, None) == INVALID
+    assert sa(P([g + 1]), 1, BF16, P(acc), 1000, 4, None) == INVALID    # misaligned gradient
+    assert sa(P(gs), 2, F32, P([acc[0] + 2] + acc[1:]), 1000, 4, None) == INVALID
+    assert sa(P(gs), 2, F32, P([g + 6000] + acc[1:]), 1000, 4, None) == ALIAS   # inside grad 1
+    assert sa(P(gs), 2, F32, P([acc[0], acc[0] + 16] + acc[2:]), 1000, 4, None) == ALIAS
+    assert sa(P(gs), 2, BF16, P(acc), 0, 4, None) == OK                 # n == 0 is a no-op
+    st = L.dp_settle
+    assert st(P(acc), P(out), 1000, 4, F32, 0.0, 0, None) == INVALID  # zero divisor
+    assert st(P(acc), P(out), 1000, 4, F32, float("inf"), 0, None) == INVALID
+    assert st(P(acc), P(out), 1000, 4, F32, float("nan"), 0, None) == INVALID
+    assert st(P(acc), P(out), 1000, 4, I32, 1.0, 0, None) == UNSUPPORTED
+    assert st(P(acc), P([out[0] + 1] + out[1:]), 1000, 4, BF16, 1.0, 0, None) == INVALID
+    assert st(P(acc), P([acc[1]] + out[1:]), 1000, 4, F32, 1.0, 0, None) == ALIAS
+    # in place is allowed only for fp32 output without reset
+    assert st(P(acc), P(acc), 0, 4, F32, 1.0, 0, None) == OK
+    assert st(P(acc), P(acc), 1000, 4, F32, 1.0, 1, None) == ALIAS
+    assert st(P(acc), P(acc), 1000, 4, BF16, 1.0, 0, None) == ALIAS
+    assert st(P(acc), P([out[0], out[0] + 8] + out[2:]), 1000, 4, F32, 1.0, 0, None) == ALIAS
+    assert st(P(acc), P(out), 0, 4, BF16, 3.0, 1, None) == OK
