@@ -20,6 +20,8 @@ Other measurements (each prints its own JSON line):
   --config fused_ar  the layer buckets as one-pass AllReduce, against RS+AG
   --config odc       one minibatch with uneven microbatch counts: ODC pushes
                      and one settle vs padded per-microbatch ReduceScatter
+  --config odc_push  the ODC push (8 gradients per launch) and settle kernels
+                     alone, for profiling
   --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
@@ -424,6 +426,63 @@ def bench_c3(args):
                                    "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}
 
 
+def _odc_kernel_rooflines(rounds8, singles, acc, out, n, div, with_np1):
+    """Average launch time of the push kernel with np = 8 (rotating over
+    rounds8, each a list of 8 gradients) and np = 1 (rotating over singles),
+    and of the bf16 settle with reset, against HBM peak."""
+    import gradient_sync_amd as dps
+    k = len(acc)
+    L = dps.dp_shard_len(n, k)
+    flip = [0, 0]
+
+    def push8():
+        flip[0] = (flip[0] + 1) % len(rounds8)
+        dps.dp_scatter_accumulate(rounds8[flip[0]], acc)
+
+    def push1():
+        flip[1] = (flip[1] + 1) % len(singles)
+        dps.dp_scatter_accumulate(singles[flip[1]], acc)
+
+    def settle():
+        dps.dp_settle(acc, out, n, divisor=div, reset=True)
+    cases = [("scatter_accumulate_np8", push8, 8 * n * 2 + 8 * n)]
+    if with_np1:
+        cases.append(("scatter_accumulate_np1", push1, n * 2 + 8 * n))
+    cases.append(("settle_bf16_reset", settle, 8 * n + k * L * 2))
+    kern = {}
+    batch = 10
+
+    def many(fn):
+        return lambda: [fn() for _ in range(batch)]
+    for name, fn, b in cases:
+        # back-to-back launches between two events, so that host-side argument
+        # marshalling overlaps the previous launch
+        med = statistics.median(_time_ms(many(fn), warm=1, reps=5)) / batch
+        kern[name] = {"median_us": round(1e3 * med, 2), "bytes": b,
+                      "gbs": round(b / (med * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return kern
+
+
+def bench_odc_push(args):
+    """The ODC kernels alone at layer size (for profiling): 60 pushes of 8
+    gradients each, then 60 bf16 settles with reset."""
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    k, n = 8, gen.LAYER_PARAMS
+    L = dps.dp_shard_len(n, k)
+    grads = [gen.microbatch_grad(1, r, m, n, device="cuda") for m in range(2) for r in range(k)]
+    acc = [torch.zeros(L, dtype=torch.float32, device="cuda") for _ in range(k)]
+    out = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    kern = _odc_kernel_rooflines([grads[:k], grads[k:]], grads, acc, out, n, 16.0, with_np1=False)
+    return {"metric": "ODC push (8 gradients per launch) and settle kernels, K=8, one layer",
+            "unit": "us", "kernels": kern,
+            "config": {"workload": "K=8, 218,103,808 bf16 N(0,1e-3^2) gradients, two sets of 8 "
+                                   "alternating, fp32 accumulators, bf16 settle with reset"}}
+
+
 def bench_odc(args):
     """One minibatch of gradient synchronisation with uneven microbatch counts:
     on-demand scatter-accumulate pushes with one settle, against the padded
@@ -497,25 +556,8 @@ def bench_odc(args):
         res[name]["speedup_vs_nccl_pad"] = round(res["nccl_pad"]["median_ms"] /
                                                  res[name]["median_ms"], 4)
     # kernel rooflines: one push of all K ranks' gradients, one single push, the settle
-    kern = {}
-    flip = [0]
-
-    def push8():
-        flip[0] = (flip[0] + 1) % mmax
-        dps.dp_scatter_accumulate(padded[flip[0]], acc)
-
     flat = [g for rnd in rounds for g in rnd]
-
-    def push1():
-        flip[0] = (flip[0] + 1) % total
-        dps.dp_scatter_accumulate(flat[flip[0]], acc)
-    for name, fn, b in (("scatter_accumulate_np8", push8, push_b(k)),
-                        ("scatter_accumulate_np1", push1, push_b(1)),
-                        ("settle_bf16_reset", settle, settle_b)):
-        med = statistics.median(_time_ms(fn, warm=3, reps=15))
-        kern[name] = {"median_us": round(1e3 * med, 2), "bytes": b,
-                      "gbs": round(b / (med * 1e-3) / 1e9, 1),
-                      "frac_of_peak": round(b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    kern = _odc_kernel_rooflines(padded, flat, acc, out, n, div, with_np1=True)
     return {"metric": "one minibatch of ODC gradient sync vs padded ReduceScatter, K=8, "
                       "one layer (218,103,808 bf16) per microbatch gradient",
             "unit": "ms", "counts": counts, "results": res, "kernels": kern,
@@ -548,7 +590,8 @@ def bench_copy(args):
 
 
 CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
-           "fused_ar": bench_fused_ar, "odc": bench_odc, "copy": bench_copy}
+           "fused_ar": bench_fused_ar, "odc": bench_odc, "odc_push": bench_odc_push,
+           "copy": bench_copy}
 
 
 def main():

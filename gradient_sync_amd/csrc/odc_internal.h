@@ -12,7 +12,7 @@ namespace dps {
 struct SaParams {
     const char *g[kMaxK];       // push i's gradient, element 0
     float *acc[kMaxK];          // owner c's accumulator, element 0 of its shard
-    int aligned[kMaxK];         // set by the launcher: shard c takes the 16-byte path
+    int aligned[kMaxK];         // set by the launcher: shard c takes the vector path
     long long n, L, tiles_per_shard;
     int np, k;
 };

@@ -29,15 +29,70 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kOdcBlock = 256;
-constexpr long long kOdcTile = 4096;        // elements of one shard per workgroup tile
-constexpr int kPushUnroll = 4;              // gradients whose loads are in flight together
+// Tuning knobs (measured at layer size on MI355X; defaults are the best found)
+#ifndef DPS_ODC_TILE
+#define DPS_ODC_TILE 4096          // elements of one shard per workgroup tile
+#endif
+#ifndef DPS_ODC_PUSH_UNROLL
+#define DPS_ODC_PUSH_UNROLL 4      // gradients whose loads are in flight together
+#endif
+#ifndef DPS_ODC_NT_ACC
+#define DPS_ODC_NT_ACC 1           // 1: nontemporal accumulator stores, 2: loads and stores
+#endif
+#ifndef DPS_ODC_NT_OUT
+#define DPS_ODC_NT_OUT 1           // nontemporal stores of the settled shards
+#endif
 
-// elements per 16-byte gradient group and groups per thread per tile
+constexpr int kOdcBlock = 256;
+constexpr long long kOdcTile = DPS_ODC_TILE;
+constexpr int kPushUnroll = DPS_ODC_PUSH_UNROLL;
+
+__device__ __forceinline__ f32x4 ld_acc(const float *p)
+{
+#if DPS_ODC_NT_ACC >= 2
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+#else
+    return *reinterpret_cast<const f32x4 *>(p);
+#endif
+}
+
+__device__ __forceinline__ void st_acc(float *p, f32x4 v)
+{
+#if DPS_ODC_NT_ACC >= 1
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+#else
+    *reinterpret_cast<f32x4 *>(p) = v;
+#endif
+}
+
+template <typename V>
+__device__ __forceinline__ void st_out(V *p, V v)
+{
+#if DPS_ODC_NT_OUT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+#ifndef DPS_ODC_BF16_GROUP
+#define DPS_ODC_BF16_GROUP 8       // bf16 elements per thread group: 8 (16-byte loads) or 4 (8-byte)
+#endif
+
+// G elements per thread group (the gradient load is G*s bytes, the
+// accumulator G*4 bytes); U groups per thread per tile. With G = 4 every
+// accumulator store instruction covers one contiguous 1 KiB per wave and the
+// written bytes equal the accumulator bytes; bf16 with G = 8 (16-byte gradient
+// loads, two 16-byte accumulator stores per group) writes about 12% more
+// partial lines but runs faster on MI355X.
 template <int DT> struct Grp {
-    static constexpr int G = DT == kBF16 ? 8 : 4;
+    static constexpr int G = DT == kBF16 ? DPS_ODC_BF16_GROUP : 4;
     static constexpr int U = (int)(kOdcTile / (kOdcBlock * G));
+    static constexpr int W = G * (DT == kBF16 ? 2 : 4) / 4;     // 32-bit words per gradient load
 };
+template <int W> struct GradVec;
+template <> struct GradVec<2> { typedef u32x2 T; };
+template <> struct GradVec<4> { typedef u32x4 T; };
 
 __device__ __forceinline__ float ld_elem(const char *g, long long i, int dt)
 {
@@ -55,19 +110,19 @@ __device__ __forceinline__ unsigned to_bf16_bits(float f)
     return u >> 16;
 }
 
-// add one 16-byte gradient group (G elements) into G accumulator values
-template <int DT>
-__device__ __forceinline__ void add_group(float *a, const u32x4 v)
+// add one gradient group (W words = G elements) into G accumulator values
+template <int DT, int W, typename V>
+__device__ __forceinline__ void add_group(float *a, const V v)
 {
     if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < W; ++w) {
             a[2 * w] = a[2 * w] + __uint_as_float(v[w] << 16);
             a[2 * w + 1] = a[2 * w + 1] + __uint_as_float(v[w] & 0xffff0000u);
         }
     } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) a[w] = a[w] + __uint_as_float(v[w]);
+        for (int w = 0; w < W; ++w) a[w] = a[w] + __uint_as_float(v[w]);
     }
 }
 
@@ -75,7 +130,8 @@ template <int DT>
 __global__ __launch_bounds__(kOdcBlock) void scatter_accumulate_kernel(const SaParams p)
 {
     constexpr int ES = DT == kBF16 ? 2 : 4;
-    constexpr int G = Grp<DT>::G, U = Grp<DT>::U;
+    constexpr int G = Grp<DT>::G, U = Grp<DT>::U, W = Grp<DT>::W;
+    typedef typename GradVec<W>::T V;
     const long long bid = blockIdx.x;
     const int c = (int)(bid / p.tiles_per_shard);
     const long long t = bid - (long long)c * p.tiles_per_shard;
@@ -94,17 +150,17 @@ __global__ __launch_bounds__(kOdcBlock) void scatter_accumulate_kernel(const SaP
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             q[u] = min((long long)threadIdx.x + u * kOdcBlock, ng - 1);
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(acc + e0 + q[u] * G);
+            const float *ap = acc + e0 + q[u] * G;
 #pragma unroll
             for (int h = 0; h < G / 4; ++h) {
-                const f32x4 v = ap[h];
+                const f32x4 v = ld_acc(ap + 4 * h);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[u][4 * h + e] = v[e];
             }
         }
         const long long goff = (base + e0) * ES;
         for (int i0 = 0; i0 < p.np; i0 += kPushUnroll) {
-            u32x4 v[kPushUnroll][U];
+            V v[kPushUnroll][U];
 #pragma unroll
             for (int i = 0; i < kPushUnroll; ++i) {
                 if (i0 + i < p.np) {
@@ -112,24 +168,24 @@ __global__ __launch_bounds__(kOdcBlock) void scatter_accumulate_kernel(const SaP
 #pragma unroll
                     for (int u = 0; u < U; ++u)
                         v[i][u] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4 *>(g + q[u] * 16));
+                            reinterpret_cast<const V *>(g + q[u] * (G * ES)));
                 }
             }
 #pragma unroll
             for (int i = 0; i < kPushUnroll; ++i) {
                 if (i0 + i < p.np) {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) add_group<DT>(a[u], v[i][u]);
+                    for (int u = 0; u < U; ++u) add_group<DT, W>(a[u], v[i][u]);
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if ((long long)threadIdx.x + u * kOdcBlock < ng) {
-                f32x4 *ap = reinterpret_cast<f32x4 *>(acc + e0 + q[u] * G);
+                float *ap = acc + e0 + q[u] * G;
 #pragma unroll
                 for (int h = 0; h < G / 4; ++h)
-                    ap[h] = f32x4{a[u][4 * h], a[u][4 * h + 1], a[u][4 * h + 2], a[u][4 * h + 3]};
+                    st_acc(ap + 4 * h, f32x4{a[u][4 * h], a[u][4 * h + 1], a[u][4 * h + 2], a[u][4 * h + 3]});
             }
         }
     }
@@ -185,11 +241,11 @@ __global__ __launch_bounds__(kOdcBlock) void settle_kernel(const SettleParams p)
                 if constexpr (DT == kBF16) {
                     const unsigned lo = to_bf16_bits(r[0]) | (to_bf16_bits(r[1]) << 16);
                     const unsigned hi = to_bf16_bits(r[2]) | (to_bf16_bits(r[3]) << 16);
-                    *reinterpret_cast<u32x2 *>(out + 2 * j) = u32x2{lo, hi};
+                    st_out(reinterpret_cast<u32x2 *>(out + 2 * j), u32x2{lo, hi});
                 } else {
-                    *reinterpret_cast<f32x4 *>(out + 4 * j) = f32x4{r[0], r[1], r[2], r[3]};
+                    st_out(reinterpret_cast<f32x4 *>(out + 4 * j), f32x4{r[0], r[1], r[2], r[3]});
                 }
-                if (p.reset) *reinterpret_cast<f32x4 *>(acc + j) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (p.reset) st_acc(acc + j, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
             }
         }
     }
@@ -211,10 +267,11 @@ hipError_t launch_scatter_accumulate(const SaParams &p0, int dt, hipStream_t st)
 {
     SaParams p = p0;
     const long long es = elem_size(dt);
+    const int gbytes = dt == kBF16 ? Grp<kBF16>::G * 2 : Grp<kF32>::G * 4;
     for (int c = 0; c < p.k; ++c) {
         bool ok = (uintptr_t)p.acc[c] % 16 == 0;
         for (int i = 0; i < p.np && ok; ++i)
-            ok = ((uintptr_t)p.g[i] + (uintptr_t)((long long)c * p.L * es)) % 16 == 0;
+            ok = ((uintptr_t)p.g[i] + (uintptr_t)((long long)c * p.L * es)) % (uintptr_t)gbytes == 0;
         p.aligned[c] = ok ? 1 : 0;
     }
     p.tiles_per_shard = ceil_div_ll(p.L, kOdcTile);
