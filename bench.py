@@ -165,9 +165,24 @@ def bench_layer(args):
                      "bytes_per_launch": launch_bytes,
                      "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements"},
     }
+    line["sharded_model"] = sharded_model(sync.plan, k, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_layer(grads, k, args.cpu_seconds)
     return line
+
+
+def sharded_model(plan, k, s):
+    """Best-case transport time of the same step on K GPUs of one board, from
+    the ring and direct-link bounds (no launch or protocol cost)."""
+    from gradient_sync_amd import costmodel as cm
+    ring = sum(cm.t_reduce_scatter_ring(n * s, k, cm.XGMI_LINK_BPS) +
+               cm.t_all_gather_ring(n * s, k, cm.XGMI_LINK_BPS) for _, n in plan)
+    direct = sum(2 * cm.t_direct_pull(n * s, k) for _, n in plan)
+    return {"ring_xgmi_ms_per_step": round(1e3 * ring, 4),
+            "direct_7link_ms_per_step": round(1e3 * direct, 4),
+            "model": "ReduceScatter + AllGather per bucket over K GPUs, xGMI 76.8 GB/s per "
+                     "directional link: one ring B(K-1)/(K W) per phase, or all K-1 peer "
+                     "links at once B/(K W)"}
 
 
 def cpu_baseline_layer(grads, k, seconds):
@@ -185,14 +200,25 @@ def cpu_baseline_layer(grads, k, seconds):
     while reps == 0 or t < seconds:
         t0 = time.perf_counter()
         sh = oracle.reduce_scatter(xs, op="avg", nthreads=cores)
-        oracle.all_gather(sh, n, nthreads=cores)
+        out = oracle.all_gather(sh, n, nthreads=cores)
         t += time.perf_counter() - t0
         reps += 1
     b = 2 * (k + 1) * n * 2
+    # once more on one thread: the per-element order does not depend on the
+    # thread count, so the bits must be the same
+    t0 = time.perf_counter()
+    sh1 = oracle.reduce_scatter(xs, op="avg", nthreads=1)
+    out1 = oracle.all_gather(sh1, n, nthreads=1)
+    t1 = time.perf_counter() - t0
+    same = all(a.tobytes() == c.tobytes() for a, c in zip(out, out1))
+    if not same:
+        raise RuntimeError("oracle results differ between 1 and many threads")
     return {"value": round(reps * b / t / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{reps} x (ReduceScatter avg + AllGather) of bucket 0 "
-                      f"(K=8 x 25,000,000 bf16), {t:.1f} s"}
+                      f"(K=8 x 25,000,000 bf16), {t:.1f} s",
+            "single_thread_value": round(b / t1 / 1e9, 3),
+            "single_thread_bits_equal": same}
 
 
 # ------------------------------------------------------------ other configs
