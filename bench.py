@@ -22,6 +22,8 @@ Other measurements (each prints its own JSON line):
                      and one settle vs padded per-microbatch ReduceScatter
   --config odc_push  the ODC push (8 gradients per launch) and settle kernels
                      alone, for profiling
+  --config overlap   backward weight GEMMs of one layer (K=8) with the bucketed
+                     AllReduce overlapped on a second stream, vs one stream
   --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
@@ -43,10 +45,10 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "42c9464ce4dcbe9aa452f09ead63a78d4b219294ab6c220d9daa8eb4ac5f0524"
-                      "9cbbc1ae223ff22b77248ea989eb14366c635a20aa08e93c02234093617dccd8",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195407.1 + 49747.1) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24800.5 + 390847.7) * 1024,
+    "sources_sha256": "c423ea65f932a4b9c24a35f1d1745a40ce6017632e2e09b1de932837716f7dea"
+                      "1b105bcbcb59989569f478a8dc7f97b3ed5a21ecb01159ef74eeadfaf776232a",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195406.7 + 49748.4) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24802.7 + 390822.3) * 1024,
 }
 
 
@@ -592,6 +594,74 @@ def bench_odc(args):
                                    "(2 docs/rank, seed 1), fp32 owner accumulators, bf16 settle"}}
 
 
+def bench_overlap(args):
+    """Backward weight-gradient GEMMs of one layer for K=8 ranks with the
+    bucketed averaged AllReduce overlapped on a second stream (a bucket goes as
+    soon as all its gradients exist), against the same work on one stream.
+    Variants: default kernels; the lean AllReduce (64 VGPRs, fits beside a GEMM
+    workgroup) capped at 256 workgroups; the GEMM variant that leaves room for a
+    default AllReduce workgroup."""
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    from gradient_sync_amd.buckets import BucketedSync
+    k, total, cap = 8, gen.LAYER_PARAMS, gen.BUCKET_ELEMS
+    pieces = gen.layer_backward_pieces()
+    grad = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    out = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    nb = -(-total // cap)
+    ev = dps.HipEvents(nb)
+    comm = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    sync = BucketedSync(grad, out, cap, op="avg")
+    res = {}
+    for t in (256, 1024):
+        log(f"[bench] overlap t={t}")
+        dy, x = gen.backward_operands(6, k, pieces, t, device="cuda")
+        flops = 2 * total * t * k
+
+        def gemms(share_cu=False):
+            for g, (off, m, n) in enumerate(pieces):
+                for r in range(k):
+                    dps.dp_gemm_bf16_ex(dy[g * k + r], x[g * k + r],
+                                        grad[r][off:off + m * n].view(m, n), share_cu=share_cu)
+
+        def serial(**o):
+            dps.dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, cap, op="avg", **o)
+
+        def overlapped(**o):
+            comm.wait_stream(cur)
+            dps.dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, cap, op="avg",
+                                              compute_stream=cur, comm_stream=comm, events=ev, **o)
+            cur.wait_stream(comm)
+        med = lambda fn: statistics.median(_time_ms(fn, warm=3, reps=9))
+        r = {"gemm_flops": flops}
+        r["t_gemm_ms"] = med(gemms)
+        r["t_gemm_share_cu_ms"] = med(lambda: gemms(True))
+        r["t_comm_ms"] = med(sync.step_all_reduce)
+        variants = (("overlap", {}), ("overlap_lean_cap256", {"lean": True, "max_workgroups": 256}),
+                    ("overlap_share_cu_cap256", {"share_cu": True, "max_workgroups": 256}))
+        r["t_serial_ms"] = med(lambda: serial())
+        for name, o in variants:
+            r[f"t_{name}_ms"] = med(lambda: overlapped(**o))
+        for name, _ in variants:
+            r[f"hidden_comm_frac_{name}"] = round(
+                (r["t_serial_ms"] - r[f"t_{name}_ms"]) / r["t_comm_ms"], 4)
+            r[f"speedup_{name}"] = round(r["t_serial_ms"] / r[f"t_{name}_ms"], 4)
+        r["gemm_tflops"] = round(flops / (r["t_gemm_ms"] * 1e-3) / 1e12, 1)
+        res[f"t{t}"] = {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in r.items()}
+        del dy, x
+        torch.cuda.empty_cache()
+    ev.close()
+    return {"metric": "backward weight GEMMs with bucketed averaged AllReduce overlapped, K=8, "
+                      "one layer", "unit": "ms", "results": res,
+            "config": {"workload": "K=8 ranks, the layer's 7 weight gradients (218,103,808 per "
+                                   "rank) as bf16 GEMMs dW = dY^T X over t tokens per rank "
+                                   "(t = 256 and 1024), 25,000,000-element buckets, one-pass "
+                                   "averaged AllReduce per bucket"}}
+
+
 def bench_copy(args):
     """A plain elementwise device copy of known size (1 GiB read + 1 GiB
     written): the practical HBM ceiling on this GPU, and the reference against
@@ -617,7 +687,7 @@ def bench_copy(args):
 
 CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
            "fused_ar": bench_fused_ar, "odc": bench_odc, "odc_push": bench_odc_push,
-           "copy": bench_copy}
+           "overlap": bench_overlap, "copy": bench_copy}
 
 
 def main():

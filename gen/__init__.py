@@ -192,3 +192,25 @@ def microbatch_grad(seed: int, rank: int, m: int, n: int, dtype=torch.bfloat16,
     """Rank `rank`'s gradient from its m-th microbatch: N(0, std^2) in fp32,
     rounded to nearest-even `dtype` (tensor id 40 + m)."""
     return normal(seed, 40 + m, rank, n, std=std, device=device).to(dtype)
+
+
+def layer_backward_pieces() -> list[tuple[int, int, int]]:
+    """(offset, m, n) of the layer's weight gradients in the flat per-rank
+    vector, in backward order (down, up, gate, o, v, k, q: the reverse of
+    registration order, as DDP assigns buckets)."""
+    out, off = [], 0
+    for _, a, b in reversed(LAYER_MATRICES):
+        out.append((off, a, b))
+        off += a * b
+    return out
+
+
+def backward_operands(seed: int, k: int, pieces, t: int, device="cpu", dy_std: float = 1e-3):
+    """Per (piece g, rank r), index g*k + r: dy [m, t] ~ N(0, dy_std^2) and
+    x [n, t] ~ N(0, 1), bf16, token-contiguous (tensor ids 70 + g and 90 + g)."""
+    dy, x = [], []
+    for g, (_, m, n) in enumerate(pieces):
+        for r in range(k):
+            dy.append(bf16_normal(seed, 70 + g, r, m * t, dy_std, device=device).view(m, t))
+            x.append(bf16_normal(seed, 90 + g, r, n * t, 1.0, device=device).view(n, t))
+    return dy, x

@@ -28,7 +28,8 @@ __all__ = [
     "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
     "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
     "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
-    "dp_weighted_reduce_ex", "dp_scatter_accumulate", "dp_settle",
+    "dp_weighted_reduce_ex", "dp_scatter_accumulate", "dp_settle", "GradPiece", "HipEvents",
+    "dp_backward_allreduce_overlap",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,12 +45,13 @@ EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version"
            "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
            "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex",
-           "dp_scatter_accumulate", "dp_settle")
+           "dp_scatter_accumulate", "dp_settle", "dp_backward_allreduce_overlap")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
 DP_LAUNCH_SHARE_CU = 1
 DP_LAUNCH_TWO_PHASE = 2
+DP_LAUNCH_LEAN = 4
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -64,9 +66,57 @@ class LaunchOpts(ctypes.Structure):
                 ("reserved", ctypes.c_int * 2)]
 
     @classmethod
-    def make(cls, max_workgroups: int = 0, share_cu: bool = False, two_phase: bool = False):
-        flags = (DP_LAUNCH_SHARE_CU if share_cu else 0) | (DP_LAUNCH_TWO_PHASE if two_phase else 0)
+    def make(cls, max_workgroups: int = 0, share_cu: bool = False, two_phase: bool = False,
+             lean: bool = False):
+        flags = ((DP_LAUNCH_SHARE_CU if share_cu else 0) | (DP_LAUNCH_TWO_PHASE if two_phase else 0)
+                 | (DP_LAUNCH_LEAN if lean else 0))
         return cls(max_workgroups, flags, (ctypes.c_int * 2)(0, 0))
+
+
+class GradPiece(ctypes.Structure):
+    """dp_grad_piece_t: an [m, n] weight gradient at element `offset` of the
+    flat per-rank gradient vector."""
+    _fields_ = [("offset", ctypes.c_int64), ("m", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class HipEvents:
+    """n hipEvent_t handles (timing disabled) from the HIP runtime the process
+    already uses, for the calls that order two streams with caller-owned
+    events. Destroyed with the object."""
+
+    _hip = None
+
+    def __init__(self, n: int):
+        if HipEvents._hip is None:
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_vp), ctypes.c_uint]
+            h.hipEventCreateWithFlags.restype = _int
+            h.hipEventDestroy.argtypes = [_vp]
+            h.hipEventDestroy.restype = _int
+            HipEvents._hip = h
+        self.handles = []
+        for _ in range(n):
+            ev = _vp()
+            rc = HipEvents._hip.hipEventCreateWithFlags(ctypes.byref(ev), 0x2)   # hipEventDisableTiming
+            if rc != 0:
+                self.close()
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.handles.append(ev.value)
+        self.array = (_vp * max(1, n))(*self.handles)
+
+    def close(self):
+        for h in self.handles:
+            HipEvents._hip.hipEventDestroy(_vp(h))
+        self.handles = []
+
+    def __len__(self):
+        return len(self.handles)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class DpsyncError(RuntimeError):
@@ -120,6 +170,9 @@ def lib():
         L.dp_scatter_accumulate.restype = _int
         L.dp_scatter_accumulate.argtypes = [_vp, _int, _int, _vp, _sz, _int, _vp]
         L.dp_settle.restype = _int
+        L.dp_backward_allreduce_overlap.restype = _int
+        L.dp_backward_allreduce_overlap.argtypes = [
+            _int, _int, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _int, P, _vp, _vp, _vp, _int]
         L.dp_settle.argtypes = [_vp, _vp, _sz, _int, _int, ctypes.c_float, _int, _vp]
         _lib = L
     return _lib
@@ -218,9 +271,11 @@ def dp_reduce_scatter(send, recv, op: str = "sum", s_chunks: int = 1, stream=Non
 
 
 def dp_reduce_scatter_ex(send, recv, op: str = "sum", s_chunks: int = 1, max_workgroups: int = 0,
-                         stream=None, n=None):
-    """dp_reduce_scatter with a cap on resident workgroups (0 = default grid)."""
-    _rs(send, recv, op, s_chunks, stream, n, ctypes.byref(LaunchOpts.make(max_workgroups)))
+                         stream=None, n=None, lean: bool = False):
+    """dp_reduce_scatter with a cap on resident workgroups (0 = default grid)
+    and the lean (64-VGPR) kernel variant."""
+    _rs(send, recv, op, s_chunks, stream, n,
+        ctypes.byref(LaunchOpts.make(max_workgroups, lean=lean)))
 
 
 def _ag(send, recv, n, s_chunks, stream, opts):
@@ -273,11 +328,12 @@ def dp_all_reduce(send, recv, op: str = "sum", s_chunks: int = 1, stream=None, n
 
 
 def dp_all_reduce_ex(send, recv, op: str = "sum", s_chunks: int = 1, max_workgroups: int = 0,
-                     two_phase: bool = False, stream=None, n=None):
+                     two_phase: bool = False, stream=None, n=None, lean: bool = False):
     """dp_all_reduce with launch options; two_phase runs ReduceScatter then
-    AllGather instead of the one-pass kernel (same results)."""
+    AllGather instead of the one-pass kernel, lean the 64-VGPR kernel variant
+    (same results either way)."""
     _ar(send, recv, op, s_chunks, stream, n,
-        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase)))
+        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase, lean=lean)))
 
 
 def _wr(send, recv, tokens, s_chunks, stream, n, opts):
@@ -304,9 +360,9 @@ def dp_weighted_reduce(send, recv, tokens, s_chunks: int = 1, stream=None, n=Non
 
 
 def dp_weighted_reduce_ex(send, recv, tokens, s_chunks: int = 1, max_workgroups: int = 0,
-                          two_phase: bool = False, stream=None, n=None):
+                          two_phase: bool = False, stream=None, n=None, lean: bool = False):
     _wr(send, recv, tokens, s_chunks, stream, n,
-        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase)))
+        ctypes.byref(LaunchOpts.make(max_workgroups, two_phase=two_phase, lean=lean)))
 
 
 def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_shard=None,
@@ -400,3 +456,39 @@ def dp_settle(acc, out, n, divisor: float = 1.0, reset: bool = False, stream=Non
     _check(lib().dp_settle(ptr_array([t.data_ptr() for t in acc]),
                            ptr_array([t.data_ptr() for t in out]), n, k, _dt(out[0]),
                            float(divisor), 1 if reset else 0, _stream(stream)), "dp_settle")
+
+
+def dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, bucket_elems, op="avg",
+                                  compute_stream=None, comm_stream=None, events=None,
+                                  max_workgroups=0, share_cu=False, two_phase=False, lean=False):
+    """Backward weight gradients (bf16 GEMMs, piece by piece for every rank) on
+    compute_stream, with each bucket AllReduced on comm_stream as soon as it is
+    complete. pieces: list of (offset, m, n); dy, x: lists indexed [g*k + r] of
+    [m, t] / [n, t] bf16 tensors; grad, out: K flat bf16 vectors. With
+    comm_stream equal to compute_stream (the default: both the current
+    stream) the whole pass runs on one stream."""
+    grad = _tensors(grad, "grad", torch.bfloat16)
+    out = _tensors(out, "out", torch.bfloat16)
+    k = len(grad)
+    total = grad[0].numel()
+    _numel_check(out, total, "out")
+    n_pieces = len(pieces)
+    dy = _tensors(dy, "dy", torch.bfloat16)
+    x = _tensors(x, "x", torch.bfloat16)
+    if len(dy) != n_pieces * k or len(x) != n_pieces * k or len(out) != k:
+        raise ValueError("need one dy and one x per (piece, rank) and one out per rank")
+    for g, (_, m, n) in enumerate(pieces):
+        for r in range(k):
+            _numel_check([dy[g * k + r]], m * t, "dy")
+            _numel_check([x[g * k + r]], n * t, "x")
+    arr = (GradPiece * n_pieces)(*[GradPiece(o, m, n) for o, m, n in pieces])
+    cs = _stream(compute_stream)
+    ms = _stream(comm_stream) if comm_stream is not None else cs
+    ev = events.array if events is not None else None
+    nev = len(events) if events is not None else 0
+    opts = LaunchOpts.make(max_workgroups, share_cu=share_cu, two_phase=two_phase, lean=lean)
+    _check(lib().dp_backward_allreduce_overlap(
+        k, n_pieces, arr, t, ptr_array([a.data_ptr() for a in dy]),
+        ptr_array([b.data_ptr() for b in x]), ptr_array([g.data_ptr() for g in grad]),
+        ptr_array([o.data_ptr() for o in out]), total, bucket_elems, _OPS[op],
+        ctypes.byref(opts), cs, ms, ev, nev), "dp_backward_allreduce_overlap")

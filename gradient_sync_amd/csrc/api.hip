@@ -34,18 +34,21 @@ bool valid_k(int k) { return k >= 1 && k <= DP_MAX_K; }
 // launch options: NULL = defaults; a negative cap, unknown flags or non-zero
 // reserved words are invalid
 bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr,
-             bool *two_phase = nullptr)
+             bool *two_phase = nullptr, bool *lean = nullptr)
 {
     max_wg = 0;
     if (share_cu) *share_cu = false;
     if (two_phase) *two_phase = false;
+    if (lean) *lean = false;
     if (!o) return true;
-    if (o->max_workgroups < 0 || (o->flags & ~(DP_LAUNCH_SHARE_CU | DP_LAUNCH_TWO_PHASE)) ||
+    if (o->max_workgroups < 0 ||
+        (o->flags & ~(DP_LAUNCH_SHARE_CU | DP_LAUNCH_TWO_PHASE | DP_LAUNCH_LEAN)) ||
         o->reserved[0] || o->reserved[1])
         return false;
     max_wg = o->max_workgroups;
     if (share_cu) *share_cu = (o->flags & DP_LAUNCH_SHARE_CU) != 0;
     if (two_phase) *two_phase = (o->flags & DP_LAUNCH_TWO_PHASE) != 0;
+    if (lean) *lean = (o->flags & DP_LAUNCH_LEAN) != 0;
     return true;
 }
 
@@ -110,7 +113,7 @@ dp_status_t validate_rs_ag_common(const void *const *send, void *const *recv, si
 // out[c] = element 0 of shard c's output region.
 dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t L, int k, int dt,
                    int ep, float scale, const float *w, int write_pads, int s_chunks,
-                   hipStream_t st, int max_wg = 0)
+                   hipStream_t st, int max_wg = 0, bool lean = false)
 {
     dps::RsParams p;
     memset(&p, 0, sizeof(p));
@@ -126,7 +129,7 @@ dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t
     p.k = k;
     p.S = s_chunks;
     p.max_blocks = max_wg;
-    return hip_status(dps::launch_rs(p, dt, ep, st));
+    return hip_status(dps::launch_rs(p, dt, ep, st, lean));
 }
 
 dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_t L, int k, int dt,
@@ -162,7 +165,7 @@ dp_status_t check_ar_alias(const void *const *send, void *const *recv, size_t n,
 
 dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, int dt, int ep,
                    float scale, const float *w, int s_chunks, hipStream_t st, int max_wg = 0,
-                   bool two_phase = false)
+                   bool two_phase = false, bool lean = false)
 {
     const int es = dps::elem_size(dt);
     const int64_t L = (int64_t)dp_shard_len(n, k);
@@ -181,11 +184,12 @@ dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, 
         p.k = k;
         p.S = s_chunks;
         p.max_blocks = max_wg;
-        return hip_status(dps::launch_ar(p, dt, ep, st));
+        return hip_status(dps::launch_ar(p, dt, ep, st, lean));
     }
     char *rs_out[DP_MAX_K];
     for (int c = 0; c < k; ++c) rs_out[c] = (char *)recv[c] + (size_t)c * (size_t)L * (size_t)es;
-    dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st, max_wg);
+    dp_status_t s =
+        run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st, max_wg, lean);
     if (s != DP_OK) return s;
     return run_ag((const void *const *)rs_out, (char *const *)recv, (int64_t)n, L, k, dt, 1,
                   s_chunks, st, max_wg);
@@ -221,7 +225,8 @@ dp_status_t dp_reduce_scatter_ex(const void *const *send, void *const *recv, siz
                                  int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
+    bool lean;
+    if (!opts_ok(opts, max_wg, nullptr, nullptr, &lean)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
@@ -241,7 +246,7 @@ dp_status_t dp_reduce_scatter_ex(const void *const *send, void *const *recv, siz
     float scale;
     pick_epilogue(op, k, ep, scale);
     return run_rs(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, ep, scale, nullptr, 1,
-                  s_chunks, (hipStream_t)stream, max_wg);
+                  s_chunks, (hipStream_t)stream, max_wg, lean);
 }
 
 dp_status_t dp_reduce_scatter(const void *const *send, void *const *recv, size_t n, int k, int dt,
@@ -284,8 +289,8 @@ dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t 
                              int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    bool two_phase;
-    if (!opts_ok(opts, max_wg, nullptr, &two_phase)) return DP_ERR_INVALID_ARG;
+    bool two_phase, lean;
+    if (!opts_ok(opts, max_wg, nullptr, &two_phase, &lean)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK || n == 0) return s;
     if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
@@ -296,7 +301,7 @@ dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t 
     float scale;
     pick_epilogue(op, k, ep, scale);
     return run_ar(send, recv, n, k, dt, ep, scale, nullptr, s_chunks, (hipStream_t)stream, max_wg,
-                  two_phase);
+                  two_phase, lean);
 }
 
 dp_status_t dp_all_reduce(const void *const *send, void *const *recv, size_t n, int k, int dt,
@@ -316,8 +321,8 @@ dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
                                   const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    bool two_phase;
-    if (!opts_ok(opts, max_wg, nullptr, &two_phase)) return DP_ERR_INVALID_ARG;
+    bool two_phase, lean;
+    if (!opts_ok(opts, max_wg, nullptr, &two_phase, &lean)) return DP_ERR_INVALID_ARG;
     dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
     if (s != DP_OK) return s;
     if (dt == DP_I32) return DP_ERR_UNSUPPORTED;
@@ -334,7 +339,7 @@ dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
     s = check_ar_alias(send, recv, n, k, dps::elem_size(dt));
     if (s != DP_OK) return s;
     return run_ar(send, recv, n, k, dt, dps::kWeighted, (float)total, w, s_chunks,
-                  (hipStream_t)stream, max_wg, two_phase);
+                  (hipStream_t)stream, max_wg, two_phase, lean);
 }
 
 dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
@@ -427,6 +432,102 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
     if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
         return DP_ERR_ALIAS;
     return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, share_cu, (hipStream_t)stream));
+}
+
+dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_piece_t *pieces,
+                                          int64_t t, const void *const *dy, const void *const *x,
+                                          void *const *grad, void *const *out, int64_t total,
+                                          int64_t bucket_elems, int op,
+                                          const dp_launch_opts_t *opts, void *compute_stream,
+                                          void *comm_stream, void *const *events, int n_events)
+{
+    int max_wg;
+    bool share_cu, two_phase, lean;
+    if (!opts_ok(opts, max_wg, &share_cu, &two_phase, &lean)) return DP_ERR_INVALID_ARG;
+    if (!valid_k(k) || n_pieces < 1 || !pieces || t < 1 || t > (1 << 24) || total < 1 ||
+        bucket_elems < 1 || !size_ok((size_t)total, 2))
+        return DP_ERR_INVALID_ARG;
+    if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
+    if (t % 8 != 0) return DP_ERR_UNSUPPORTED;
+    // the pieces tile [0, total) in order
+    int64_t off = 0;
+    for (int g = 0; g < n_pieces; ++g) {
+        const dp_grad_piece_t &p = pieces[g];
+        if (p.offset != off || p.m < 1 || p.n < 1 || p.m > (1 << 24) || p.n > (1 << 24))
+            return DP_ERR_INVALID_ARG;
+        off += p.m * p.n;
+        if (off > total) return DP_ERR_INVALID_ARG;
+    }
+    if (off != total) return DP_ERR_INVALID_ARG;
+    if (!dy || !x || !ptrs_ok((const void *const *)grad, k, 2) ||
+        !ptrs_ok((const void *const *)out, k, 2))
+        return DP_ERR_INVALID_ARG;
+    for (int i = 0; i < n_pieces * k; ++i) {
+        if (!dy[i] || !x[i]) return DP_ERR_INVALID_ARG;
+        if (((uintptr_t)dy[i] & 15) || ((uintptr_t)x[i] & 15)) return DP_ERR_UNSUPPORTED;
+    }
+    const size_t bytes = (size_t)total * 2;
+    if (!pairwise_disjoint(grad, k, bytes)) return DP_ERR_ALIAS;
+    dp_status_t s = check_ar_alias((const void *const *)grad, out, (size_t)total, k, 2);
+    if (s != DP_OK) return s;
+    for (int g = 0; g < n_pieces; ++g)
+        for (int r = 0; r < k; ++r) {
+            const int i = g * k + r;
+            const Range ra = span(dy[i], (size_t)(pieces[g].m * t) * 2);
+            const Range rb = span(x[i], (size_t)(pieces[g].n * t) * 2);
+            for (int q = 0; q < k; ++q) {
+                const Range rg = span(grad[q], bytes), ro = span(out[q], bytes);
+                if (overlap(ra, rg) || overlap(rb, rg) || overlap(ra, ro) || overlap(rb, ro))
+                    return DP_ERR_ALIAS;
+            }
+        }
+    const int64_t nb = (total + bucket_elems - 1) / bucket_elems;
+    hipStream_t cs = (hipStream_t)compute_stream, ms = (hipStream_t)comm_stream;
+    const bool two_streams = cs != ms;
+    if (two_streams) {
+        if (!events || n_events < nb) return DP_ERR_INVALID_ARG;
+        for (int64_t b = 0; b < nb; ++b)
+            if (!events[b]) return DP_ERR_INVALID_ARG;
+    }
+    int ep;
+    float scale;
+    pick_epilogue(op, k, ep, scale);
+
+    // Backward order: piece g's gradient for every rank, then every bucket that
+    // is now complete for all ranks goes to the comm stream, in bucket order.
+    int64_t next = 0;
+    for (int g = 0; g < n_pieces; ++g) {
+        const dp_grad_piece_t &p = pieces[g];
+        for (int r = 0; r < k; ++r) {
+            char *c = (char *)grad[r] + (size_t)p.offset * 2;
+            hipError_t e = dps::launch_gemm_bf16(dy[g * k + r], x[g * k + r], c, p.m, p.n, t,
+                                                 share_cu, cs);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        const int64_t done = p.offset + p.m * p.n;
+        for (; next < nb; ++next) {
+            const int64_t b0 = next * bucket_elems;
+            const int64_t bn = (total - b0 < bucket_elems) ? total - b0 : bucket_elems;
+            if (b0 + bn > done) break;
+            const void *src[DP_MAX_K];
+            void *dst[DP_MAX_K];
+            for (int r = 0; r < k; ++r) {
+                src[r] = (const char *)grad[r] + (size_t)b0 * 2;
+                dst[r] = (char *)out[r] + (size_t)b0 * 2;
+            }
+            hipStream_t st = cs;
+            if (two_streams) {
+                hipError_t e = hipEventRecord((hipEvent_t)events[next], cs);
+                if (e == hipSuccess) e = hipStreamWaitEvent(ms, (hipEvent_t)events[next], 0);
+                if (e != hipSuccess) return hip_status(e);
+                st = ms;
+            }
+            s = run_ar(src, dst, (size_t)bn, k, DP_BF16, ep, scale, nullptr, 1, st, max_wg, two_phase,
+                       lean);
+            if (s != DP_OK) return s;
+        }
+    }
+    return DP_OK;
 }
 
 dp_status_t dp_scatter_accumulate(const void *const *grads, int np, int dt, float *const *acc,

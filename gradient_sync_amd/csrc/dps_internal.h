@@ -53,14 +53,16 @@ struct AgParams {
 // Fill the phase table and tiling of the parameter blocks; returns the grid size.
 // The kernels are persistent: each workgroup walks tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ... of the flat (sub-chunk, shard, tile) space.
-long long plan_rs(RsParams &p, int dt);
+// lean: the variant with one vector per lane per rank and at most 64 VGPRs
+// (same results), which fits beside a register-heavy kernel on one CU.
+long long plan_rs(RsParams &p, int dt, bool lean = false);
 long long plan_ag(AgParams &p, int dt);
 
-hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t stream);
+hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t stream, bool lean = false);
 // Fused AllReduce: RsParams with dst[r] = rank r's n-element output; every
 // shard's fold goes straight to all K outputs (no shard buffer, no pads).
-long long plan_ar(RsParams &p, int dt);
-hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t stream);
+long long plan_ar(RsParams &p, int dt, bool lean = false);
+hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t stream, bool lean = false);
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t stream);
 
 // Batched fp32 GEMM on MFMA: for each batch b < nb,

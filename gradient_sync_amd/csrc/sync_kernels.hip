@@ -359,6 +359,17 @@ __global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
         rs_tile<DT, EP, KT, U, AR>(p, K, bid);
 }
 
+// Lean variant: one vector per lane per rank and at most 64 VGPRs (8 waves per
+// SIMD), so one of its workgroups fits in the registers a 224-VGPR GEMM
+// workgroup (two waves per SIMD) leaves free on a CU.
+template <int DT, int EP, int KT, bool AR>
+__global__ __launch_bounds__(kBlock, 8) void rs_kernel_lean(const RsParams p)
+{
+    const int K = KT ? KT : p.k;
+    for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
+        rs_tile<DT, EP, KT, 1, AR>(p, K, bid);
+}
+
 // ------------------------------------------------------------------ AllGather
 
 template <int ES, int KT>
@@ -467,43 +478,46 @@ __global__ __launch_bounds__(kAgBlock) void ag_kernel(const AgParams p)
 // ------------------------------------------------------------------ launchers
 
 template <int DT, int EP, int KT, bool AR>
-hipError_t rs_go(const RsParams &p, long long grid, hipStream_t st)
+hipError_t rs_go(const RsParams &p, long long grid, bool lean, hipStream_t st)
 {
-    hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    if (lean)
+        hipLaunchKernelGGL((rs_kernel_lean<DT, EP, KT, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    else
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 
 template <int DT, int EP, bool AR>
-hipError_t rs_k(const RsParams &p, long long grid, hipStream_t st)
+hipError_t rs_k(const RsParams &p, long long grid, bool lean, hipStream_t st)
 {
     switch (p.k) {
-    case 2: return rs_go<DT, EP, 2, AR>(p, grid, st);
-    case 4: return rs_go<DT, EP, 4, AR>(p, grid, st);
-    case 8: return rs_go<DT, EP, 8, AR>(p, grid, st);
-    default: return rs_go<DT, EP, 0, AR>(p, grid, st);
+    case 2: return rs_go<DT, EP, 2, AR>(p, grid, lean, st);
+    case 4: return rs_go<DT, EP, 4, AR>(p, grid, lean, st);
+    case 8: return rs_go<DT, EP, 8, AR>(p, grid, lean, st);
+    default: return rs_go<DT, EP, 0, AR>(p, grid, lean, st);
     }
 }
 
 template <bool AR>
-hipError_t rs_dispatch(const RsParams &q, int dt, int ep, long long grid, hipStream_t st)
+hipError_t rs_dispatch(const RsParams &q, int dt, int ep, long long grid, bool lean, hipStream_t st)
 {
     if (dt == kF32) {
         switch (ep) {
-        case kSum: return rs_k<kF32, kSum, AR>(q, grid, st);
-        case kMul: return rs_k<kF32, kMul, AR>(q, grid, st);
-        case kDiv: return rs_k<kF32, kDiv, AR>(q, grid, st);
-        default: return rs_k<kF32, kWeighted, AR>(q, grid, st);
+        case kSum: return rs_k<kF32, kSum, AR>(q, grid, lean, st);
+        case kMul: return rs_k<kF32, kMul, AR>(q, grid, lean, st);
+        case kDiv: return rs_k<kF32, kDiv, AR>(q, grid, lean, st);
+        default: return rs_k<kF32, kWeighted, AR>(q, grid, lean, st);
         }
     }
     if (dt == kBF16) {
         switch (ep) {
-        case kSum: return rs_k<kBF16, kSum, AR>(q, grid, st);
-        case kMul: return rs_k<kBF16, kMul, AR>(q, grid, st);
-        case kDiv: return rs_k<kBF16, kDiv, AR>(q, grid, st);
-        default: return rs_k<kBF16, kWeighted, AR>(q, grid, st);
+        case kSum: return rs_k<kBF16, kSum, AR>(q, grid, lean, st);
+        case kMul: return rs_k<kBF16, kMul, AR>(q, grid, lean, st);
+        case kDiv: return rs_k<kBF16, kDiv, AR>(q, grid, lean, st);
+        default: return rs_k<kBF16, kWeighted, AR>(q, grid, lean, st);
         }
     }
-    return rs_k<kI32, kSum, AR>(q, grid, st);
+    return rs_k<kI32, kSum, AR>(q, grid, lean, st);
 }
 
 template <int ES, int KT>
@@ -526,8 +540,9 @@ hipError_t ag_k(const AgParams &p, long long grid, hipStream_t st)
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-int rs_vectors_per_thread(int dt)
+int rs_vectors_per_thread(int dt, bool lean)
 {
+    if (lean) return 1;
     return dt == kF32 ? RsU<kF32>::U : dt == kBF16 ? RsU<kBF16>::U : RsU<kI32>::U;
 }
 
@@ -560,13 +575,13 @@ long long grid_for(long long total_tiles, int max_blocks)
 
 }  // namespace
 
-long long plan_rs(RsParams &p, int dt)
+long long plan_rs(RsParams &p, int dt, bool lean)
 {
     const int es = elem_size(dt);
     for (int c = 0; c < p.k; ++c)
         p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c], !DPS_RS_ALIGN_OUT);
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
+    const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);
@@ -588,16 +603,16 @@ long long plan_ag(AgParams &p, int dt)
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
-hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t st)
+hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t st, bool lean)
 {
     RsParams q = p;
-    const long long grid = plan_rs(q, dt);
+    const long long grid = plan_rs(q, dt, lean);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return rs_dispatch<false>(q, dt, ep, grid, st);
+    return rs_dispatch<false>(q, dt, ep, grid, lean, st);
 }
 
-long long plan_ar(RsParams &p, int dt)
+long long plan_ar(RsParams &p, int dt, bool lean)
 {
     const int es = elem_size(dt);
     for (int c = 0; c < p.k; ++c) {
@@ -609,19 +624,19 @@ long long plan_ar(RsParams &p, int dt)
     }
     p.write_pads = 0;
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kBlock * rs_vectors_per_thread(dt) * (16 / es);
+    const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
-hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t st)
+hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t st, bool lean)
 {
     RsParams q = p;
-    const long long grid = plan_ar(q, dt);
+    const long long grid = plan_ar(q, dt, lean);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return rs_dispatch<true>(q, dt, ep, grid, st);
+    return rs_dispatch<true>(q, dt, ep, grid, lean, st);
 }
 
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t st)

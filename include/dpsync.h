@@ -201,13 +201,20 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
  *                    same CU as a GEMM workgroup. DP_LAUNCH_TWO_PHASE makes
  *                    dp_all_reduce_ex / dp_weighted_reduce_ex run a
  *                    ReduceScatter then an AllGather instead of the one-pass
- *                    kernel (same results). Other calls ignore the flags.
+ *                    kernel (same results). DP_LAUNCH_LEAN selects, for the
+ *                    ReduceScatter and AllReduce kernels, the variant with one
+ *                    16-byte vector per lane per rank and at most 64 VGPRs
+ *                    (same results): one of its workgroups fits in the
+ *                    registers that a workgroup of dp_gemm_bf16's default
+ *                    variant leaves free on a CU, so the two kernels can be
+ *                    resident together. Other calls ignore the flags.
  *   reserved       : must be zero.
  * A NULL opts pointer means all defaults. Invalid fields return
  * DP_ERR_INVALID_ARG.
  */
 #define DP_LAUNCH_SHARE_CU 1
 #define DP_LAUNCH_TWO_PHASE 2
+#define DP_LAUNCH_LEAN 4
 
 typedef struct {
     int max_workgroups;
@@ -230,6 +237,56 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
 dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
                                   const int64_t *tokens, size_t n, int k, int dt, int s_chunks,
                                   const dp_launch_opts_t *opts, void *stream);
+
+/*
+ * Backward pass with the gradient AllReduce overlapped, bucket by bucket
+ * ("CMU 11-868 L14-L15 ...", section "When to sync: gradient bucketing":
+ * gradients appear layer by layer from the back, parameters sit in buckets in
+ * that order, and a bucket is AllReduced as soon as every gradient in it is
+ * ready while backward goes on computing earlier layers).
+ *
+ * Each rank's gradient is one flat bf16 vector of `total` elements made of
+ * n_pieces weight gradients in backward order. Piece g is an [m, n] row-major
+ * matrix at element `offset` (the pieces must tile [0, total) in order):
+ *   grad[r][offset + i*n + j] = sum_s dy[g*k + r][i, s] * x[g*k + r][j, s]
+ * i.e. dW = dY^T X for a linear layer, with dy [m, t] and x [n, t] stored
+ * token-contiguous (t tokens per rank, t a multiple of 8, 16-byte aligned), bf16
+ * in, fp32 accumulation on MFMA, bf16 out (the dp_gemm_bf16 kernel).
+ * Bucket b covers [b*bucket_elems, min((b+1)*bucket_elems, total)).
+ *
+ * Schedule: on compute_stream, for each piece in order, the k GEMMs of that
+ * piece; after them, every bucket whose elements are now all computed is
+ * AllReduced (op DP_SUM or DP_AVG, bf16, fp32 accumulation in ring order, the
+ * dp_all_reduce kernel) from grad into out on comm_stream, in bucket order.
+ * The comm stream waits for the bucket with events[b] (recorded on
+ * compute_stream after the bucket's last GEMM); events is a HOST array of at
+ * least ceil(total / bucket_elems) hipEvent_t created by the caller.
+ * When comm_stream == compute_stream everything runs in that one stream in the
+ * same order (no overlap, events unused and may be NULL).
+ * opts: DP_LAUNCH_SHARE_CU selects the GEMM variant that leaves room for a
+ * sync workgroup on each CU; DP_LAUNCH_LEAN the AllReduce variant that fits
+ * beside the default GEMM; max_workgroups caps the AllReduce grid;
+ * DP_LAUNCH_TWO_PHASE runs each AllReduce as ReduceScatter then AllGather.
+ *
+ * The results do not depend on the schedule: out equals dp_all_reduce of the
+ * computed grad, bit for bit. out[r] may equal grad[r] (in place); other
+ * overlaps between grad, out, dy and x return DP_ERR_ALIAS. Completion: the
+ * gradients are final when compute_stream completes and the outputs when
+ * comm_stream completes. All arguments are validated before anything is
+ * enqueued; a launch failure part way returns DP_ERR_HIP with the earlier
+ * work already enqueued.
+ */
+typedef struct {
+    int64_t offset;  /* element offset of the piece in every rank's gradient vector */
+    int64_t m, n;    /* the piece is an [m, n] row-major matrix */
+} dp_grad_piece_t;
+
+dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_piece_t *pieces,
+                                          int64_t t, const void *const *dy, const void *const *x,
+                                          void *const *grad, void *const *out, int64_t total,
+                                          int64_t bucket_elems, int op,
+                                          const dp_launch_opts_t *opts, void *compute_stream,
+                                          void *comm_stream, void *const *events, int n_events);
 
 /*
  * On-demand communication: scatter-accumulate push ("Using ODC to Accelerate

@@ -180,7 +180,7 @@ def test_launch_options_validation():
     L = dps.lib()
     a, b = fake(4), fake(4, base=1 << 41)
     bad = [dps.LaunchOpts(-1, 0, (ctypes.c_int * 2)(0, 0)),
-           dps.LaunchOpts(0, 4, (ctypes.c_int * 2)(0, 0)),
+           dps.LaunchOpts(0, 8, (ctypes.c_int * 2)(0, 0)),
            dps.LaunchOpts(0, 0, (ctypes.c_int * 2)(1, 0))]
     for o in bad:
         r = ctypes.byref(o)
@@ -225,3 +225,38 @@ def test_odc_validation():
     assert st(P(acc), P(acc), 1000, 4, BF16, 1.0, 0, None) == ALIAS
     assert st(P(acc), P([out[0], out[0] + 8] + out[2:]), 1000, 4, F32, 1.0, 0, None) == ALIAS
     assert st(P(acc), P(out), 0, 4, BF16, 3.0, 1, None) == OK
+
+
+def test_overlap_validation():
+    L = dps.lib()
+    k, t = 2, 16
+    pieces = [(0, 32, 32), (1024, 16, 8)]
+    total = 1024 + 128
+    arr = (dps.GradPiece * 2)(*[dps.GradPiece(*p) for p in pieces])
+    dy, x = fake(4, base=1 << 40), fake(4, base=1 << 41)
+    grad, out = fake(k, base=1 << 42), fake(k, base=1 << 43)
+    ev = P(fake(2, base=1 << 44))
+    o = ctypes.byref(dps.LaunchOpts.make())
+    s1, s2 = 1 << 20, 2 << 20            # two distinct (fake) streams
+
+    def call(k_=k, n_p=2, arr_=arr, t_=t, dy_=dy, x_=x, grad_=grad, out_=out, total_=total,
+             bucket=500, op=AVG, opts=o, cs=s1, ms=s2, ev_=ev, nev=3):
+        return L.dp_backward_allreduce_overlap(k_, n_p, arr_, t_, P(dy_), P(x_), P(grad_),
+                                               P(out_), total_, bucket, op, opts, cs, ms, ev_, nev)
+    assert call(k_=0) == INVALID
+    assert call(n_p=0) == INVALID
+    assert call(t_=12) == UNSUPPORTED                       # tokens not a multiple of 8
+    assert call(op=7) == UNSUPPORTED
+    assert call(total_=total + 1) == INVALID                # pieces do not tile the vector
+    bad = (dps.GradPiece * 2)(dps.GradPiece(0, 32, 32), dps.GradPiece(1000, 16, 8))
+    assert call(arr_=bad) == INVALID                        # gap / overlap between pieces
+    assert call(dy_=[dy[0] + 8] + dy[1:]) == UNSUPPORTED     # operand not 16-byte aligned
+    assert call(dy_=[0] + dy[1:]) == INVALID
+    assert call(grad_=[grad[0], grad[0] + 64]) == ALIAS     # gradient vectors overlap
+    assert call(out_=[grad[1], out[1]]) == ALIAS            # output on another rank's gradient
+    assert call(x_=[grad[0]] + x[1:]) == ALIAS              # operand inside a gradient
+    assert call(nev=2) == INVALID                           # 3 buckets need 3 events
+    assert call(ev_=None, nev=0) == INVALID
+    assert call(bucket=0) == INVALID
+    bad_opts = dps.LaunchOpts(0, 8, (ctypes.c_int * 2)(0, 0))
+    assert call(opts=ctypes.byref(bad_opts)) == INVALID

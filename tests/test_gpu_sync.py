@@ -450,3 +450,45 @@ def test_weighted_one_pass_equals_two_phase(dtype):
         torch.cuda.synchronize()
         for r in (0, 3, k - 1):
             assert bits_equal(to_np(out[r]), want[r]), two_phase
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_lean_variant_is_bit_identical(dtype):
+    """The 64-VGPR kernel variant (one vector per lane per rank) against the
+    oracle: ReduceScatter, one-pass and two-phase AllReduce, weighted, with and
+    without a grid cap, over aligned, misaligned, multi-tile and ragged sizes."""
+    for k, n, off in ((8, 8 * 2048 * 5 + 37, 0), (3, 100_003, 1), (8, 1_250_003, 3), (5, 17, 0),
+                      (16, 4096 * 16 + 5, 2)):
+        xs, hx = make_inputs(dtype, k, n, seed=70 + k, off=off)
+        op = "sum" if dtype == torch.int32 else "avg"
+        want_sh = oracle.reduce_scatter(hx, op=op)
+        want = oracle.all_gather(want_sh, n)
+        L = dps.dp_shard_len(n, k)
+        for cap in (0, 7, 256):
+            say(f"lean k={k} n={n} {dtype} cap={cap}")
+            sh = [Guarded(L, dtype) for _ in range(k)]
+            out = [Guarded(n, dtype, 1) for _ in range(k)]
+            out2 = [Guarded(n, dtype) for _ in range(k)]
+            dps.dp_reduce_scatter_ex([g.t for g in xs], [s.t for s in sh], op=op, s_chunks=2,
+                                     max_workgroups=cap, lean=True)
+            dps.dp_all_reduce_ex([g.t for g in xs], [o.t for o in out], op=op,
+                                 max_workgroups=cap, lean=True)
+            dps.dp_all_reduce_ex([g.t for g in xs], [o.t for o in out2], op=op,
+                                 max_workgroups=cap, lean=True, two_phase=True)
+            torch.cuda.synchronize()
+            for c in range(k):
+                assert bits_equal(to_np(sh[c].t), want_sh[c]), (cap, c)
+                assert sh[c].intact()
+            for r in range(k):
+                assert bits_equal(to_np(out[r].t), want[r]), (cap, r)
+                assert bits_equal(to_np(out2[r].t), want[r]), (cap, r)
+                assert out[r].intact() and out2[r].intact()
+            if dtype != torch.int32:
+                toks = gen.token_counts(70 + k, k)
+                wo = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+                dps.dp_weighted_reduce_ex([g.t for g in xs], wo, toks, max_workgroups=cap,
+                                          lean=True)
+                torch.cuda.synchronize()
+                ww = oracle.weighted_all_reduce(hx, toks)
+                for r in (0, k - 1):
+                    assert bits_equal(to_np(wo[r]), ww[r]), (cap, r)
