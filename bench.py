@@ -24,6 +24,7 @@ Other measurements (each prints its own JSON line):
                      alone, for profiling
   --config overlap   backward weight GEMMs of one layer (K=8) with the bucketed
                      AllReduce overlapped on a second stream, vs one stream
+  --config gemm      the bf16 8192^3 GEMM alone (and the library GEMM for context)
   --config copy      plain 1 GiB elementwise copy (HBM ceiling, counter scale)
   --config all       the default line, then all of the above
 """
@@ -662,6 +663,35 @@ def bench_overlap(args):
                                    "averaged AllReduce per bucket"}}
 
 
+def bench_gemm(args):
+    """The bf16 GEMM of the concurrency measurement alone (C = A B^T, 8192^3),
+    default and CU-sharing variants, against the MFMA roofline; the vendor
+    library GEMM (torch.matmul, hipBLASLt) on the same operands for context."""
+    import torch
+
+    import gen
+    import gradient_sync_amd as dps
+    m = n = kk = 8192
+    a, b = gen.gemm_bf16_inputs(5, m, n, kk, device="cuda")
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    flops = 2 * m * n * kk
+    res = {}
+    bt = b.t()
+    for name, fn in (("dp_gemm_bf16", lambda: dps.dp_gemm_bf16(a, b, c)),
+                     ("dp_gemm_bf16_share_cu", lambda: dps.dp_gemm_bf16_ex(a, b, c, share_cu=True)),
+                     ("library_torch_matmul", lambda: torch.matmul(a, bt, out=c))):
+        med = statistics.median(_time_ms(fn, warm=6, reps=9))
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"median_ms": round(med, 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / MFMA_BF16_TFLOPS, 4)}
+    return {"metric": "bf16 GEMM C = A B^T, 8192^3, fp32 accumulation", "unit": "TFLOP/s",
+            "value": res["dp_gemm_bf16"]["tflops"], "results": res,
+            "roofline": {"bound": "mfma", "achieved": res["dp_gemm_bf16"]["tflops"],
+                         "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": res["dp_gemm_bf16"]["frac_of_peak"]},
+            "config": {"workload": "A, B bf16 [8192, 8192] ~ N(0,1), k-contiguous"}}
+
+
 def bench_copy(args):
     """A plain elementwise device copy of known size (1 GiB read + 1 GiB
     written): the practical HBM ceiling on this GPU, and the reference against
@@ -687,7 +717,7 @@ def bench_copy(args):
 
 CONFIGS = {"ring1m": bench_ring1m, "fsdp": bench_fsdp, "weighted": bench_weighted, "c3": bench_c3,
            "fused_ar": bench_fused_ar, "odc": bench_odc, "odc_push": bench_odc_push,
-           "overlap": bench_overlap, "copy": bench_copy}
+           "overlap": bench_overlap, "gemm": bench_gemm, "copy": bench_copy}
 
 
 def main():
