@@ -6,10 +6,12 @@ buffers, each holding the bf16 gradients of one transformer layer (GQA q/o
 4096x4096, k/v 4096x1024, SwiGLU 3 x 4096x14336: 218,103,808 values,
 N(0, 1e-3)), cut into 9 buckets of at most 25,000,000 elements. A step is, for
 every bucket in order, an averaged ReduceScatter (fp32 accumulation in ring
-order) into per-rank shards followed by an AllGather back to every rank.
-`value` is algorithmic HBM bytes per step (ReduceScatter reads K*n and writes
-n, AllGather reads n and writes K*n, per bucket of n elements) times steps,
-over the wall time of the timed steps, in GB/s.
+order) into per-rank shards followed by an AllGather back to every rank, with
+consecutive buckets pipelined: the ReduceScatter of bucket b+1 and the
+AllGather of bucket b run in one launch. `value` is algorithmic HBM bytes per
+step (ReduceScatter reads K*n and writes n, AllGather reads n and writes K*n,
+per bucket of n elements) times steps, over the wall time of the timed steps,
+in GB/s. The same step without the pipelining is reported beside it.
 
 Other measurements (each prints its own JSON line):
   --config ring1m    K=4, 1,048,576 fp32 and int32, S=4, AllReduce
@@ -42,14 +44,15 @@ MFMA_F32_TFLOPS = 157.3        # dense fp32 matrix
 MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 
 
-# HBM bytes per full-bucket launch from two rocprofv3 PMC passes (FETCH_SIZE x 2.0,
+# HBM bytes per full-size launch from two rocprofv3 PMC passes (FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "c423ea65f932a4b9c24a35f1d1745a40ce6017632e2e09b1de932837716f7dea"
-                      "1b105bcbcb59989569f478a8dc7f97b3ed5a21ecb01159ef74eeadfaf776232a",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195406.7 + 49748.4) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24802.7 + 390822.3) * 1024,
+    "sources_sha256": "3672ae1a2db5d984683d6f9afc853ec13bdcc0f562dcf5837ddf03c4e13ddf8e"
+                      "97bb01548be6ad91cf58f0ee07b2e06de3efba446e85aa33d38aa8702d7b0932",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49736.9) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24799.9 + 390808.7) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220206.0 + 440386.3) * 1024,
 }
 
 
@@ -93,50 +96,56 @@ def bench_layer(args):
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
     step_bytes = sync.algorithmic_bytes()
 
-    for _ in range(args.warmup):
-        sync.step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        sync.step()
-    ev1.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+    log(f"[bench] warmup {args.warmup}; timing {args.steps} pipelined steps, then plain steps")
+    wall, gpu_ms = timed(sync.step_pipelined)
     value = step_bytes * args.steps / wall / 1e9
+    wall_plain, _ = timed(sync.step)
+    value_plain = step_bytes * args.steps / wall_plain / 1e9
     # Per-kernel durations: the same steps again, with a pair of HIP events
     # recorded on the launch stream around every launch. Kept out of the
-    # throughput loop above because 36 event records per step cost ~0.1 ms.
+    # throughput loops above because an event pair per launch costs ~0.1 ms.
     events = []
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        sync.step(events=events)
+        sync.step_pipelined(events=events)
     torch.cuda.synchronize()
 
-    # per-launch durations of full-size buckets, per kernel
+    # per-launch durations of launches on full-size buckets only, per kernel
     full = gen.BUCKET_ELEMS
-    per = {"rs": [], "ag": []}
-    tot = {"rs": 0.0, "ag": 0.0}
+    per = {"rs": [], "rsag": [], "ag": []}
+    tot = {"rs": 0.0, "rsag": 0.0, "ag": 0.0}
     for kind, b, e0, e1 in events:
         ms = e0.elapsed_time(e1)
         tot[kind] += ms
-        if sync.plan[b][1] == full:
+        sizes = [sync.plan[b][1]] + ([sync.plan[b - 1][1]] if kind == "rsag" else [])
+        if all(n == full for n in sizes):
             per[kind].append(ms)
-    launch_bytes = (k + 1) * full * 2
+    bytes_of = {"rs": (k + 1) * full * 2, "ag": (k + 1) * full * 2, "rsag": 2 * (k + 1) * full * 2}
     kern = {kind: {"avg_us": 1e3 * statistics.mean(v), "median_us": 1e3 * statistics.median(v),
-                   "gbs": launch_bytes / (statistics.mean(v) * 1e-3) / 1e9, "launches": len(v)}
-            for kind, v in per.items()}
+                   "gbs": bytes_of[kind] / (statistics.mean(v) * 1e-3) / 1e9, "launches": len(v)}
+            for kind, v in per.items() if v}
     dom = max(tot, key=tot.get)
     achieved = kern[dom]["gbs"]
-    names = {"rs": "rs_kernel<bf16, avg, K=8>", "ag": "ag_kernel<2-byte, K=8>"}
+    launch_bytes = bytes_of[dom]
+    names = {"rs": "rs_kernel<bf16, avg, K=8>", "ag": "ag_kernel<2-byte, K=8>",
+             "rsag": "rsag_kernel<bf16, avg, K=8>"}
     traffic = (round(MEASURED_TRAFFIC[names[dom]])
-               if kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"] else None)
+               if kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"]
+               and names[dom] in MEASURED_TRAFFIC else None)
     line = {
         "metric": "reduce-scatter+all-gather HBM GB/s (% of peak), K=8 bf16 25M-elem buckets",
         "value": round(value, 2),
@@ -152,11 +161,17 @@ def bench_layer(args):
         "data": "synthetic",
         "config": {"workload": "K=8 emulated ranks, one GQA+SwiGLU layer (hidden 4096) of bf16 "
                                "grads = 218,103,808 per rank, 9 buckets of <=25,000,000, "
-                               "averaged ReduceScatter then AllGather per bucket",
+                               "averaged ReduceScatter then AllGather per bucket, the "
+                               "ReduceScatter of bucket b+1 fused with the AllGather of b",
                    "ranks": k, "params_per_rank": total, "bucket_elems": gen.BUCKET_ELEMS,
                    "buckets": len(sync.plan), "op": "avg", "accumulate": "fp32, ring order"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "plain_step": {"value": round(value_plain, 2),
+                       "pct_of_peak": round(100 * value_plain / HBM_PEAK_GBS, 2),
+                       "ms_per_step": round(1e3 * wall_plain / args.steps, 4),
+                       "schedule": "ReduceScatter then AllGather, one launch each, bucket by "
+                                   "bucket"},
         "kernel_timing": "HIP events around every launch in a second pass of the same steps",
         "bytes_per_step": step_bytes,
         "kernels": {names[k_]: {kk: (round(v, 2) if isinstance(v, float) else v)
@@ -166,7 +181,8 @@ def bench_layer(args):
                      "traffic": traffic,
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "bytes_per_launch": launch_bytes,
-                     "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements"},
+                     "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements and phase; the "
+                                   "fused launch carries one ReduceScatter and one AllGather"},
     }
     line["sharded_model"] = sharded_model(sync.plan, k, 2)
     if not args.no_cpu_baseline:

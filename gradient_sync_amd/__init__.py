@@ -29,7 +29,7 @@ __all__ = [
     "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
     "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
     "dp_weighted_reduce_ex", "dp_scatter_accumulate", "dp_settle", "GradPiece", "HipEvents",
-    "dp_backward_allreduce_overlap",
+    "dp_backward_allreduce_overlap", "dp_reduce_scatter_all_gather",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +45,8 @@ EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version"
            "dp_reduce_scatter", "dp_all_gather", "dp_all_reduce", "dp_weighted_reduce",
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
            "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex",
-           "dp_scatter_accumulate", "dp_settle", "dp_backward_allreduce_overlap")
+           "dp_scatter_accumulate", "dp_settle", "dp_backward_allreduce_overlap",
+           "dp_reduce_scatter_all_gather")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
@@ -170,6 +171,9 @@ def lib():
         L.dp_scatter_accumulate.restype = _int
         L.dp_scatter_accumulate.argtypes = [_vp, _int, _int, _vp, _sz, _int, _vp]
         L.dp_settle.restype = _int
+        L.dp_reduce_scatter_all_gather.restype = _int
+        L.dp_reduce_scatter_all_gather.argtypes = [_vp, _vp, _sz, _vp, _vp, _sz, _int, _int, _int,
+                                                   _int, _vp]
         L.dp_backward_allreduce_overlap.restype = _int
         L.dp_backward_allreduce_overlap.argtypes = [
             _int, _int, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _int, P, _vp, _vp, _vp, _int]
@@ -492,3 +496,28 @@ def dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, bucket_elems, op=
         ptr_array([b.data_ptr() for b in x]), ptr_array([g.data_ptr() for g in grad]),
         ptr_array([o.data_ptr() for o in out]), total, bucket_elems, _OPS[op],
         ctypes.byref(opts), cs, ms, ev, nev), "dp_backward_allreduce_overlap")
+
+
+def dp_reduce_scatter_all_gather(rs_send, rs_recv, ag_send, ag_recv, op: str = "sum",
+                                 rs_n=None, ag_n=None, s_chunks: int = 1, stream=None):
+    """ReduceScatter of (rs_send -> rs_recv) and AllGather of (ag_send ->
+    ag_recv) in one launch; the two buffer sets must be disjoint."""
+    rs_send = _tensors(rs_send, "rs_send")
+    dt = rs_send[0].dtype
+    rs_recv = _tensors(rs_recv, "rs_recv", dt)
+    ag_send = _tensors(ag_send, "ag_send", dt)
+    ag_recv = _tensors(ag_recv, "ag_recv", dt)
+    k = len(rs_send)
+    if not (len(rs_recv) == len(ag_send) == len(ag_recv) == k):
+        raise ValueError("every buffer set needs one tensor per rank")
+    rs_n = rs_send[0].numel() if rs_n is None else rs_n
+    ag_n = ag_recv[0].numel() if ag_n is None else ag_n
+    _numel_check(rs_send, rs_n, "rs_send")
+    _numel_check(rs_recv, dp_shard_len(rs_n, k), "rs_recv")
+    _numel_check(ag_send, dp_shard_len(ag_n, k), "ag_send")
+    _numel_check(ag_recv, ag_n, "ag_recv")
+    P = lambda ts: ptr_array([t.data_ptr() for t in ts])
+    _check(lib().dp_reduce_scatter_all_gather(P(rs_send), P(rs_recv), rs_n, P(ag_send),
+                                              P(ag_recv), ag_n, k, _dt(rs_send[0]), _OPS[op],
+                                              s_chunks, _stream(stream)),
+           "dp_reduce_scatter_all_gather")

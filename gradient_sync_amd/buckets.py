@@ -122,3 +122,36 @@ class BucketedSync:
         """Bytes one step must move: per bucket, ReduceScatter reads K*n and
         writes n elements, AllGather reads n and writes K*n."""
         return sum(2 * (self.k + 1) * n * self.es for _, n in self.plan)
+
+    def step_pipelined(self, stream=None, events=None):
+        """The same step with consecutive buckets overlapped: ReduceScatter of
+        bucket 0, then for b = 1.. one launch that reduces bucket b while
+        gathering bucket b-1, then the AllGather of the last bucket. Same bits as
+        step(). `events` as in step(), kinds "rs", "rsag", "ag"."""
+        st = _stream(stream)
+        L = lib()
+        torch_stream = stream if isinstance(stream, torch.cuda.Stream) else None
+        nb = len(self.calls)
+
+        def launch(kind, b, fn):
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(torch_stream)
+            rc = fn()
+            if rc:
+                _check(rc, f"bucket {b} {kind}")
+            if events is not None:
+                e1.record(torch_stream)
+                events.append((kind, b, e0, e1))
+        send, sh, _, n = self.calls[0]
+        launch("rs", 0, lambda: L.dp_reduce_scatter(send, sh, n, self.k, self.dtype, self.op,
+                                                    self.s_chunks, st))
+        for b in range(1, nb):
+            send, sh, _, n = self.calls[b]
+            _, psh, pdst, pn = self.calls[b - 1]
+            launch("rsag", b, lambda: L.dp_reduce_scatter_all_gather(
+                send, sh, n, psh, pdst, pn, self.k, self.dtype, self.op, self.s_chunks, st))
+        _, sh, dst, n = self.calls[nb - 1]
+        launch("ag", nb - 1, lambda: L.dp_all_gather(sh, dst, n, self.k, self.dtype,
+                                                     self.s_chunks, st))

@@ -195,6 +195,53 @@ dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, 
                   s_chunks, st, max_wg);
 }
 
+// ReduceScatter argument checks (shared by the single and the fused call);
+// in_place reports the documented in-place form.
+dp_status_t check_rs(const void *const *send, void *const *recv, size_t n, int k, int dt, int op,
+                     int s_chunks, bool &in_place)
+{
+    in_place = false;
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK || n == 0) return s;
+    if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
+    if (dt == DP_I32 && op != DP_SUM) return DP_ERR_UNSUPPORTED;
+    const int es = dps::elem_size(dt);
+    const size_t L = dp_shard_len(n, k);
+    in_place = n == L * (size_t)k;
+    for (int c = 0; c < k && in_place; ++c)
+        in_place = (const char *)recv[c] == (const char *)send[c] + (size_t)c * L * (size_t)es;
+    if (!in_place) {
+        for (int c = 0; c < k; ++c)
+            for (int r = 0; r < k; ++r)
+                if (overlap(span(recv[c], L * es), span(send[r], n * es))) return DP_ERR_ALIAS;
+        if (!pairwise_disjoint(recv, k, L * es)) return DP_ERR_ALIAS;
+    }
+    return DP_OK;
+}
+
+// AllGather argument checks; in_place: shard c already sits in recv[c].
+dp_status_t check_ag(const void *const *send, void *const *recv, size_t n, int k, int dt,
+                     int s_chunks, bool &in_place)
+{
+    in_place = false;
+    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    if (s != DP_OK || n == 0) return s;
+    const int es = dps::elem_size(dt);
+    const size_t L = dp_shard_len(n, k);
+    if (!pairwise_disjoint(recv, k, n * es)) return DP_ERR_ALIAS;
+    in_place = true;
+    for (int c = 0; c < k && in_place; ++c)
+        in_place = (const char *)send[c] == (const char *)recv[c] + (size_t)c * L * (size_t)es;
+    if (!in_place) {
+        for (int c = 0; c < k; ++c) {
+            const size_t nc = (size_t)shard_valid((int64_t)n, (int64_t)L, c);
+            for (int r = 0; r < k; ++r)
+                if (overlap(span(send[c], nc * es), span(recv[r], n * es))) return DP_ERR_ALIAS;
+        }
+    }
+    return DP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,23 +272,11 @@ dp_status_t dp_reduce_scatter_ex(const void *const *send, void *const *recv, siz
                                  int op, int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    bool lean;
+    bool lean, in_place;
     if (!opts_ok(opts, max_wg, nullptr, nullptr, &lean)) return DP_ERR_INVALID_ARG;
-    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    dp_status_t s = check_rs(send, recv, n, k, dt, op, s_chunks, in_place);
     if (s != DP_OK || n == 0) return s;
-    if (op != DP_SUM && op != DP_AVG) return DP_ERR_UNSUPPORTED;
-    if (dt == DP_I32 && op != DP_SUM) return DP_ERR_UNSUPPORTED;
-    const int es = dps::elem_size(dt);
     const size_t L = dp_shard_len(n, k);
-    bool in_place = n == L * (size_t)k;
-    for (int c = 0; c < k && in_place; ++c)
-        in_place = (const char *)recv[c] == (const char *)send[c] + (size_t)c * L * (size_t)es;
-    if (!in_place) {
-        for (int c = 0; c < k; ++c)
-            for (int r = 0; r < k; ++r)
-                if (overlap(span(recv[c], L * es), span(send[r], n * es))) return DP_ERR_ALIAS;
-        if (!pairwise_disjoint(recv, k, L * es)) return DP_ERR_ALIAS;
-    }
     int ep;
     float scale;
     pick_epilogue(op, k, ep, scale);
@@ -259,22 +294,11 @@ dp_status_t dp_all_gather_ex(const void *const *send, void *const *recv, size_t 
                              int s_chunks, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
+    bool in_place;
     if (!opts_ok(opts, max_wg)) return DP_ERR_INVALID_ARG;
-    dp_status_t s = validate_rs_ag_common(send, recv, n, k, dt, s_chunks);
+    dp_status_t s = check_ag(send, recv, n, k, dt, s_chunks, in_place);
     if (s != DP_OK || n == 0) return s;
-    const int es = dps::elem_size(dt);
     const size_t L = dp_shard_len(n, k);
-    if (!pairwise_disjoint(recv, k, n * es)) return DP_ERR_ALIAS;
-    bool in_place = true;
-    for (int c = 0; c < k && in_place; ++c)
-        in_place = (const char *)send[c] == (const char *)recv[c] + (size_t)c * L * (size_t)es;
-    if (!in_place) {
-        for (int c = 0; c < k; ++c) {
-            const size_t nc = (size_t)shard_valid((int64_t)n, (int64_t)L, c);
-            for (int r = 0; r < k; ++r)
-                if (overlap(span(send[c], nc * es), span(recv[r], n * es))) return DP_ERR_ALIAS;
-        }
-    }
     return run_ag(send, (char *const *)recv, (int64_t)n, (int64_t)L, k, dt, in_place ? 1 : 0,
                   s_chunks, (hipStream_t)stream, max_wg);
 }
@@ -283,6 +307,66 @@ dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, 
                           int s_chunks, void *stream)
 {
     return dp_all_gather_ex(send, recv, n, k, dt, s_chunks, nullptr, stream);
+}
+
+dp_status_t dp_reduce_scatter_all_gather(const void *const *rs_send, void *const *rs_recv,
+                                         size_t rs_n, const void *const *ag_send,
+                                         void *const *ag_recv, size_t ag_n, int k, int dt, int op,
+                                         int s_chunks, void *stream)
+{
+    bool rs_in_place, ag_in_place;
+    dp_status_t s = check_rs(rs_send, rs_recv, rs_n, k, dt, op, s_chunks, rs_in_place);
+    if (s != DP_OK) return s;
+    s = check_ag(ag_send, ag_recv, ag_n, k, dt, s_chunks, ag_in_place);
+    if (s != DP_OK) return s;
+    if (rs_n == 0 && ag_n == 0) return DP_OK;
+    const int es = dps::elem_size(dt);
+    const size_t Lr = dp_shard_len(rs_n, k), La = dp_shard_len(ag_n, k);
+    if (rs_n && ag_n) {
+        // the two operations must not touch each other's buffers
+        for (int i = 0; i < k; ++i) {
+            const Range r_in = span(rs_send[i], rs_n * es), r_out = span(rs_recv[i], Lr * es);
+            for (int j = 0; j < k; ++j) {
+                const Range a_in = span(ag_send[j], La * es), a_out = span(ag_recv[j], ag_n * es);
+                if (overlap(r_in, a_in) || overlap(r_in, a_out) || overlap(r_out, a_in) ||
+                    overlap(r_out, a_out))
+                    return DP_ERR_ALIAS;
+            }
+        }
+    }
+    int ep;
+    float scale;
+    pick_epilogue(op, k, ep, scale);
+    hipStream_t st = (hipStream_t)stream;
+    if (ag_n == 0)
+        return run_rs(rs_send, (char *const *)rs_recv, (int64_t)rs_n, (int64_t)Lr, k, dt, ep, scale,
+                      nullptr, 1, s_chunks, st);
+    if (rs_n == 0)
+        return run_ag(ag_send, (char *const *)ag_recv, (int64_t)ag_n, (int64_t)La, k, dt,
+                      ag_in_place ? 1 : 0, s_chunks, st);
+    dps::RsParams rp;
+    dps::AgParams ap;
+    memset(&rp, 0, sizeof(rp));
+    memset(&ap, 0, sizeof(ap));
+    for (int r = 0; r < k; ++r) {
+        rp.src[r] = (const char *)rs_send[r];
+        rp.dst[r] = (char *)rs_recv[r];
+        rp.w[r] = 1.0f;
+        ap.src[r] = (const char *)ag_send[r];
+        ap.dst[r] = (char *)ag_recv[r];
+    }
+    rp.scale = scale;
+    rp.write_pads = 1;
+    rp.n = (long long)rs_n;
+    rp.L = (long long)Lr;
+    rp.k = k;
+    rp.S = s_chunks;
+    ap.skip_own = ag_in_place ? 1 : 0;
+    ap.n = (long long)ag_n;
+    ap.L = (long long)La;
+    ap.k = k;
+    ap.S = s_chunks;
+    return hip_status(dps::launch_rsag(rp, ap, dt, ep, st));
 }
 
 dp_status_t dp_all_reduce_ex(const void *const *send, void *const *recv, size_t n, int k, int dt,

@@ -64,6 +64,9 @@ hipError_t launch_rs(const RsParams &p, int dt, int ep, hipStream_t stream, bool
 long long plan_ar(RsParams &p, int dt, bool lean = false);
 hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t stream, bool lean = false);
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t stream);
+// A ReduceScatter (rp, epilogue ep) and an AllGather (ap) of disjoint buffer
+// sets in one launch, one tile per workgroup, the two kinds interleaved.
+hipError_t launch_rsag(const RsParams &rp, const AgParams &ap, int dt, int ep, hipStream_t stream);
 
 // Batched fp32 GEMM on MFMA: for each batch b < nb,
 // C_b[M,N] = op(A_b)[M,Kd] * B_b[Kd,N], row-major; op(A) = A ([M,Kd]) or, with

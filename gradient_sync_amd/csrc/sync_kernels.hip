@@ -475,6 +475,40 @@ __global__ __launch_bounds__(kAgBlock) void ag_kernel(const AgParams p)
         ag_tile<ES, KT, U>(p, K, bid);
 }
 
+// ------------------------------------------- ReduceScatter + AllGather fused
+
+static_assert(kAgBlock == kBlock, "the fused kernel runs both tile kinds with one block size");
+
+// A ReduceScatter of one buffer set and an AllGather of another in one launch
+// (bucket b+1 reduced while bucket b is gathered): the ReduceScatter reads K
+// bytes per byte written and the AllGather the reverse, so running their tiles
+// side by side gives HBM a copy-like read/write mix. In each run of 16
+// workgroup ids the first 8 (one per XCD, ids go round-robin over the 8 XCDs)
+// take ReduceScatter tiles and the next 8 AllGather tiles; the tiles left over
+// when one kind runs out go to the other.
+#ifndef DPS_RSAG_GROUP
+#define DPS_RSAG_GROUP 8
+#endif
+template <int DT, int EP, int KT>
+__global__ __launch_bounds__(kBlock) void rsag_kernel(const RsParams rp, const AgParams ap)
+{
+    constexpr int ES = Tr<DT>::ES;
+    constexpr long long G = DPS_RSAG_GROUP;
+    const int K = KT ? KT : rp.k;
+    const long long nr = rp.total_tiles, na = ap.total_tiles;
+    const long long paired = ((nr < na ? nr : na) / G) * G;
+    const long long bid = blockIdx.x;
+    if (bid < 2 * paired) {
+        const long long idx = (bid / (2 * G)) * G + bid % G;
+        if ((bid / G) & 1) ag_tile<ES, KT, kAgU>(ap, K, idx);
+        else rs_tile<DT, EP, KT, RsU<DT>::U, false>(rp, K, idx);
+        return;
+    }
+    const long long rem = bid - 2 * paired;
+    if (rem < nr - paired) rs_tile<DT, EP, KT, RsU<DT>::U, false>(rp, K, paired + rem);
+    else ag_tile<ES, KT, kAgU>(ap, K, paired + rem - (nr - paired));
+}
+
 // ------------------------------------------------------------------ launchers
 
 template <int DT, int EP, int KT, bool AR>
@@ -637,6 +671,46 @@ hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t st, bool lea
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     return rs_dispatch<true>(q, dt, ep, grid, lean, st);
+}
+
+template <int DT, int EP>
+hipError_t rsag_k(const RsParams &rp, const AgParams &ap, long long grid, hipStream_t st)
+{
+    switch (rp.k) {
+    case 2: hipLaunchKernelGGL((rsag_kernel<DT, EP, 2>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
+    case 4: hipLaunchKernelGGL((rsag_kernel<DT, EP, 4>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
+    case 8: hipLaunchKernelGGL((rsag_kernel<DT, EP, 8>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
+    default: hipLaunchKernelGGL((rsag_kernel<DT, EP, 0>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rsag(const RsParams &rp0, const AgParams &ap0, int dt, int ep, hipStream_t st)
+{
+    RsParams rp = rp0;
+    AgParams ap = ap0;
+    rp.max_blocks = 0;
+    ap.max_blocks = 0;
+    plan_rs(rp, dt);
+    plan_ag(ap, dt);
+    const long long grid = rp.total_tiles + ap.total_tiles;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (dt == kF32) {
+        switch (ep) {
+        case kSum: return rsag_k<kF32, kSum>(rp, ap, grid, st);
+        case kMul: return rsag_k<kF32, kMul>(rp, ap, grid, st);
+        default: return rsag_k<kF32, kDiv>(rp, ap, grid, st);
+        }
+    }
+    if (dt == kBF16) {
+        switch (ep) {
+        case kSum: return rsag_k<kBF16, kSum>(rp, ap, grid, st);
+        case kMul: return rsag_k<kBF16, kMul>(rp, ap, grid, st);
+        default: return rsag_k<kBF16, kDiv>(rp, ap, grid, st);
+        }
+    }
+    return rsag_k<kI32, kSum>(rp, ap, grid, st);
 }
 
 hipError_t launch_ag(const AgParams &p, int dt, hipStream_t st)

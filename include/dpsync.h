@@ -115,6 +115,26 @@ dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, 
                           int dt, int s_chunks, void *stream);
 
 /*
+ * A ReduceScatter of one buffer set and an AllGather of another, in one launch:
+ * the step of a bucketed sync in which bucket b+1 is reduced while bucket b is
+ * gathered, so that the two phases of consecutive buckets pipeline the way the
+ * chunks of a ring do (CMU notes, "Why a ring: chop the data so transfers
+ * pipeline"). On one GPU it also balances HBM traffic: the ReduceScatter reads
+ * k bytes for every byte it writes and the AllGather writes k for every byte
+ * it reads.
+ *   Same results as dp_reduce_scatter(rs_send, rs_recv, rs_n, k, dt, op,
+ *   s_chunks) followed by dp_all_gather(ag_send, ag_recv, ag_n, k, dt,
+ *   s_chunks), bit for bit; each operation follows that call's buffer and
+ *   in-place rules, and no buffer of one operation may overlap a buffer of
+ *   the other (DP_ERR_ALIAS). rs_n or ag_n may be 0 (then only the other
+ *   operation runs).
+ */
+dp_status_t dp_reduce_scatter_all_gather(const void *const *rs_send, void *const *rs_recv,
+                                         size_t rs_n, const void *const *ag_send,
+                                         void *const *ag_recv, size_t ag_n, int k, int dt, int op,
+                                         int s_chunks, void *stream);
+
+/*
  * AllReduce = ReduceScatter followed by AllGather (CMU notes, section "NCCL's
  * five building blocks"; T_AR,ring equation in "Sharding and Parallelism").
  *   send[r], recv[r] : n elements. Every recv[r] receives the full reduced

@@ -260,3 +260,24 @@ def test_overlap_validation():
     assert call(bucket=0) == INVALID
     bad_opts = dps.LaunchOpts(0, 8, (ctypes.c_int * 2)(0, 0))
     assert call(opts=ctypes.byref(bad_opts)) == INVALID
+
+
+def test_fused_rs_ag_validation():
+    L = dps.lib()
+    k, n = 4, 1000
+    Lk = dps.dp_shard_len(n, k)
+    rs_s, rs_r = fake(k, base=1 << 40), fake(k, base=1 << 41)
+    ag_s, ag_r = fake(k, base=1 << 42), fake(k, base=1 << 43)
+
+    def call(a=rs_s, b=rs_r, na=n, c=ag_s, d=ag_r, nb=n, k_=k, dt=F32, op=SUM, s=1):
+        return L.dp_reduce_scatter_all_gather(P(a), P(b), na, P(c), P(d), nb, k_, dt, op, s, None)
+    assert call(k_=0) == INVALID
+    assert call(s=0) == INVALID
+    assert call(dt=7) == UNSUPPORTED
+    assert call(dt=I32, op=AVG) == UNSUPPORTED
+    assert call(b=[rs_s[1] + 64] + rs_r[1:]) == ALIAS          # RS output inside an RS input
+    assert call(d=[ag_r[0], ag_r[0] + 400] + ag_r[2:]) == ALIAS  # AG outputs overlap
+    assert call(c=[rs_s[0]] + ag_s[1:]) == ALIAS               # AG input inside an RS input
+    assert call(d=[rs_r[2]] + ag_r[1:]) == ALIAS               # AG output on an RS shard
+    assert call(na=0, nb=0) == OK
+    assert Lk == 250

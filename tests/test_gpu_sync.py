@@ -12,7 +12,7 @@ import gen
 import gradient_sync_amd as dps
 import oracle
 from gradient_sync_amd.buckets import BucketedSync
-from tests.helpers import bits_equal, say, to_np
+from tests.helpers import bits_equal, from_np, say, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -492,3 +492,80 @@ def test_lean_variant_is_bit_identical(dtype):
                 ww = oracle.weighted_all_reduce(hx, toks)
                 for r in (0, k - 1):
                     assert bits_equal(to_np(wo[r]), ww[r]), (cap, r)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_fused_rs_ag_equals_separate(dtype):
+    """One launch doing a ReduceScatter of one set and an AllGather of another:
+    both results bit-exact against the oracle, for equal and unequal sizes
+    (so one kind of tile runs out first), misaligned buffers, in-place forms and
+    an empty side."""
+    op = "sum" if dtype == torch.int32 else "avg"
+    for k, n_rs, n_ag, off, in_place in ((8, 25_000 * 8 + 3, 25_000 * 8 + 3, 0, False),
+                                         (8, 8 * 2048 * 3 + 5, 8 * 2048 * 9 + 1, 1, False),
+                                         (3, 100_003, 7, 2, False), (5, 17, 40_000, 0, False),
+                                         (8, 8 * 4096 * 4, 8 * 4096 * 4, 0, True),
+                                         (4, 0, 9_999, 0, False), (4, 9_999, 0, 3, False)):
+        say(f"fused rs+ag k={k} n_rs={n_rs} n_ag={n_ag} off={off} in_place={in_place} {dtype}")
+        xs, hx = make_inputs(dtype, k, n_rs, seed=300 + k, off=off)
+        L_rs, L_ag = dps.dp_shard_len(n_rs, k), dps.dp_shard_len(n_ag, k)
+        gs, hg = make_inputs(dtype, k, n_ag, seed=400 + k)      # gather sources: values per rank
+        shards = [Guarded(max(L_ag, 1), dtype, off) for _ in range(k)]
+        want_ag_sh = [h[c * L_ag:(c + 1) * L_ag] for c, h in enumerate(hg)] if n_ag else []
+        for c in range(k):
+            if n_ag:
+                v = np.zeros(L_ag, dtype=hg[0].dtype)
+                v[:len(want_ag_sh[c])] = want_ag_sh[c]
+                shards[c].t[:L_ag].copy_(from_np(v)[:L_ag])
+        ag_out = [Guarded(max(n_ag, 1), dtype) for _ in range(k)]
+        if in_place:
+            rs_out = [xs[c].t[c * L_rs:(c + 1) * L_rs] for c in range(k)]
+            ag_out = [Guarded(n_ag, dtype) for _ in range(k)]
+            for c in range(k):
+                ag_out[c].t[c * L_ag:(c + 1) * L_ag].copy_(shards[c].t[:L_ag])
+            ag_src = [ag_out[c].t[c * L_ag:(c + 1) * L_ag] for c in range(k)]
+        else:
+            rs_out = [Guarded(max(L_rs, 1), dtype).t[:L_rs] for _ in range(k)]
+            ag_src = [s.t[:L_ag] for s in shards]
+        want_rs = oracle.reduce_scatter(hx, op=op) if n_rs else []
+        want_ag = oracle.all_gather([np.ascontiguousarray(to_np(s)) for s in ag_src], n_ag) if n_ag else []
+        dps.dp_reduce_scatter_all_gather([g.t for g in xs], rs_out, ag_src,
+                                         [o.t[:n_ag] for o in ag_out], op=op, rs_n=n_rs, ag_n=n_ag)
+        torch.cuda.synchronize()
+        for c in range(k):
+            if n_rs:
+                assert bits_equal(to_np(rs_out[c]), want_rs[c]), (k, n_rs, c)
+            if n_ag:
+                assert bits_equal(to_np(ag_out[c].t[:n_ag]), want_ag[c]), (k, n_ag, c)
+            assert ag_out[c].intact()
+            if not in_place:
+                assert xs[c].intact()
+
+
+def test_pipelined_layer_step_k8_bf16_full_size():
+    """The bucket pipeline (ReduceScatter of bucket b+1 fused with the
+    AllGather of bucket b) over the full layer equals the oracle bucket by
+    bucket, every element, and equals the plain step."""
+    k = 8
+    say("pipelined layer step k=8 bf16")
+    grads = gen.layer_grads_bf16(3, k, device=DEV)
+    out = [torch.full((gen.LAYER_PARAMS,), float("nan"), dtype=torch.bfloat16, device=DEV)
+           for _ in range(k)]
+    sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
+    sync.step_pipelined()
+    torch.cuda.synchronize()
+    got = [to_np(o) for o in out]
+    hg = [to_np(g) for g in grads]
+    for b, (off, n) in enumerate(sync.plan):
+        want_sh = oracle.reduce_scatter([h[off:off + n] for h in hg], op="avg", nthreads=16)
+        for c in range(k):
+            assert bits_equal(to_np(sync.shard_view(b, c)), want_sh[c]), (b, c)
+        want = oracle.all_gather(want_sh, n, nthreads=16)
+        for r in (0, 3, k - 1):
+            assert bits_equal(got[r][off:off + n], want[r]), (b, r)
+    out2 = [torch.empty_like(o) for o in out]
+    sync2 = BucketedSync(grads, out2, gen.BUCKET_ELEMS, op="avg")
+    sync2.step()
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(out2[r]), got[r])
