@@ -83,6 +83,7 @@ constexpr int kCUs = DPS_CUS;
 #endif
 constexpr int kAlign = DPS_ALIGN;
 constexpr int kFastBit = 256;
+constexpr int kOutAlignBit = 512;   // AllGather: the K outputs share one 16-byte phase
 static_assert(kAlign >= 16 && kAlign <= 256 && (kAlign & (kAlign - 1)) == 0, "alignment");
 
 __device__ __forceinline__ u32x4 load_stream(const char *p)
@@ -426,6 +427,50 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
     }
 }
 
+// The AllGather body when the K outputs share a 16-byte phase but the shard
+// does not: stores stay 16-byte aligned, and each lane assembles its 16 source
+// bytes from dword-aligned loads (for 2-byte elements at an odd element
+// address, five dwords joined with a byte shift). src is the shard address of
+// chunk 0; the caller keeps every dword read inside the shard's valid range.
+template <int ES, int KT, int U, bool FULL, bool SKIP_OWN>
+__device__ __forceinline__ void ag_vectors_shifted(const AgParams &p, const int K, const int c,
+                                                   const char *src, const long long off,
+                                                   const long long nv)
+{
+    const int tid = threadIdx.x;
+    const unsigned shift = (unsigned)((uintptr_t)src & 3);      // 0, or 2 for 2-byte elements
+    const unsigned *w0 = reinterpret_cast<const unsigned *>(src - shift);
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const long long q = FULL ? (long long)tid + u * kAgBlock : min((long long)tid + u * kAgBlock, nv - 1);
+        const unsigned *w = w0 + q * 4;
+        if (ES == 2 && shift) {
+            unsigned a[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) a[i] = w[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[u][i] = __builtin_amdgcn_alignbyte(a[i + 1], a[i], 2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[u][i] = w[i];
+        }
+    }
+    const int nr = SKIP_OWN ? K - 1 : K;
+#pragma unroll
+    for (int i = 0; i < (KT ? (SKIP_OWN ? KT - 1 : KT) : kMaxK); ++i) {
+        if (!KT && i >= nr) break;
+        int r = c + 1 + i;
+        r = r >= K ? r - K : r;
+        char *d = p.dst[r] + off;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long q = (long long)tid + u * kAgBlock;
+            if (FULL || q < nv) store_ag(d + q * 16, v[u]);
+        }
+    }
+}
+
 template <int ES, int KT, int U>
 __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const long long bid)
 {
@@ -442,16 +487,43 @@ __device__ __forceinline__ void ag_tile(const AgParams &p, const int K, const lo
     if (j0 >= j1) return;
     const int meta = p.meta[c];
     const bool fast = (meta & kFastBit) != 0;
-    const long long head = fast ? (long long)(((kAlign - (((meta & 255) + j0 * ES) & (kAlign - 1))) &
-                                               (kAlign - 1)) / ES) : 0;
+    const bool out_aligned = (meta & kOutAlignBit) != 0;
+    const long long head = (fast || out_aligned)
+                               ? (long long)(((kAlign - (((meta & 255) + j0 * ES) & (kAlign - 1))) &
+                                              (kAlign - 1)) / ES)
+                               : 0;
     const long long body = min(j0 + head, j1);
     const long long e0 = body + t * TE;
     const long long e1 = min(e0 + TE, j1);
 
     if (t == 0 && body > j0) ag_scalar_range<ES, KT>(p, K, c, base, j0, body);
     if (e0 >= e1) return;
-    if (!fast) {
+    if (!fast && !out_aligned) {
         ag_scalar_range<ES, KT>(p, K, c, base, e0, e1);
+        return;
+    }
+    if (!fast) {
+        // outputs aligned, shard not: shifted loads. A 2-byte shift reads the
+        // dword before a chunk and the one after it, so the first chunk of the
+        // shard and a chunk ending at the last valid element go element-wise.
+        const bool shifted = ES == 2 && (((uintptr_t)p.src[c] + (uintptr_t)(e0 * ES)) & 3) != 0;
+        long long v0 = e0;
+        if (shifted && v0 == 0) v0 += V;
+        long long nv = v0 < e1 ? (e1 - v0) / V : 0;
+        if (shifted && nv > 0 && v0 + nv * V >= nc) --nv;
+        if (v0 > e0) ag_scalar_range<ES, KT>(p, K, c, base, e0, min(v0, e1));
+        if (nv > 0) {
+            const char *src = p.src[c] + v0 * ES;
+            const long long off = (base + v0) * ES;
+            if (nv == (long long)kAgBlock * U) {
+                if (p.skip_own) ag_vectors_shifted<ES, KT, U, true, true>(p, K, c, src, off, nv);
+                else ag_vectors_shifted<ES, KT, U, true, false>(p, K, c, src, off, nv);
+            } else {
+                if (p.skip_own) ag_vectors_shifted<ES, KT, U, false, true>(p, K, c, src, off, nv);
+                else ag_vectors_shifted<ES, KT, U, false, false>(p, K, c, src, off, nv);
+            }
+        }
+        ag_scalar_range<ES, KT>(p, K, c, base, max(v0, e0) + max(nv, 0LL) * V, e1);
         return;
     }
     const long long nv = (e1 - e0) / V;
@@ -628,7 +700,13 @@ long long plan_ag(AgParams &p, int dt)
         // the K outputs at element c*L against the shard (the "input" here)
         const char *outs[kMaxK];
         for (int r = 0; r < p.k; ++r) outs[r] = p.dst[r];
-        p.meta[c] = phase_meta(outs, (long long)c * p.L * es, p.k, p.src[c], true);
+        const long long off = (long long)c * p.L * es;
+        p.meta[c] = phase_meta(outs, off, p.k, p.src[c], true);
+        bool same = true;
+        for (int r = 1; r < p.k; ++r)
+            same = same && (((uintptr_t)outs[r] + (uintptr_t)off) & 15) ==
+                               (((uintptr_t)outs[0] + (uintptr_t)off) & 15);
+        if (same) p.meta[c] |= kOutAlignBit;
     }
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kAgBlock * kAgU * (16 / es);

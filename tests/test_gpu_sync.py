@@ -569,3 +569,32 @@ def test_pipelined_layer_step_k8_bf16_full_size():
     torch.cuda.synchronize()
     for r in range(k):
         assert bits_equal(to_np(out2[r]), got[r])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_ag_misaligned_shards_multi_tile(dtype):
+    """Shards whose 16-byte phase differs from the outputs' (the shifted-load
+    path: dword loads, for 2-byte elements joined with a 2-byte shift), over
+    several tiles per shard, a ragged last shard, shards starting at the
+    buffer's first element and ending at its last valid one; and outputs whose
+    phases differ from each other (element-wise path)."""
+    for k, n in ((8, 8 * 4096 * 3 + 5), (3, 100_003), (8, 10_000_019 // 64)):
+        L = dps.dp_shard_len(n, k)
+        for sh_off, out_offs in ((1, [0] * k), (3, [0] * k), (2, [0] * k), (0, [1] * k),
+                                 (5, [3] * k), (1, [r % 3 for r in range(k)])):
+            say(f"ag-misaligned k={k} n={n} {dtype} sh_off={sh_off} out_offs={out_offs[:3]}")
+            shards = []
+            for c in range(k):
+                nc = max(0, min(L, n - c * L))
+                g = Guarded(nc, dtype, sh_off)          # exactly the valid elements
+                v = gen.raw_u64(12, 2, c, 0, nc).to(torch.int32)
+                g.t.copy_((v if dtype == torch.int32 else
+                           (v.to(torch.float32) * 2.0 ** -31).to(dtype)).to(DEV))
+                shards.append(g)
+            outs = [Guarded(n, dtype, out_offs[r]) for r in range(k)]
+            want = oracle.all_gather([to_np(g.t) for g in shards], n, L=L)
+            dps.dp_all_gather([g.t for g in shards], [o.t for o in outs], n=n)
+            torch.cuda.synchronize()
+            for r in range(k):
+                assert bits_equal(to_np(outs[r].t), want[r]), (k, n, sh_off, r)
+                assert outs[r].intact()
