@@ -48,11 +48,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "3672ae1a2db5d984683d6f9afc853ec13bdcc0f562dcf5837ddf03c4e13ddf8e"
+    "sources_sha256": "508daab374bccf8e04a0a84ce7d0c28e87d2c085e9471d058cb32e5d9d5e1b70"
                       "97bb01548be6ad91cf58f0ee07b2e06de3efba446e85aa33d38aa8702d7b0932",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49736.9) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24799.9 + 390808.7) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220206.0 + 440386.3) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49738.8) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24809.4 + 390824.6) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220219.3 + 440376.9) * 1024,
 }
 
 
