@@ -27,67 +27,81 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64, BN = 64, BK = 32, LDP = 64 + 4;
 
-// Stage loader: 2 float4 of A and 2 float4 of B per thread.
-template <int TA>
+#ifndef DPS_GEMM_F32_SPLIT_MAX
+#define DPS_GEMM_F32_SPLIT_MAX 256      // largest grid that gets eight waves per tile
+#endif
+
+// Stage loader: the 64x32 A and 32x64 B tiles of one stage as 2 x 256 float4
+// each; with NT threads every thread takes 512/NT of them (h = 0, 1 for 256
+// threads; h = threadIdx.x / 256 for 512).
+template <int TA, int NT>
 struct Stage {
-    f32x4 a[2], b[2];
+    static constexpr int NH = 512 / NT;
+    f32x4 a[NH], b[NH];
 
     __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ B,
                                          long long M, long long N, long long Kd, long long m0,
                                          long long n0, long long k0, bool vec_a, bool vec_b)
     {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x & 255;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int hh = 0; hh < NH; ++hh) {
+            const int h = NH == 2 ? hh : (int)(threadIdx.x >> 8);
             if (TA == 0) {
                 // A stored [M][Kd]: row m0 + t/8 + 32h, k k0 + (t%8)*4 .. +3
                 const long long i = m0 + (t >> 3) + 32 * h, k = k0 + (t & 7) * 4;
                 if (vec_a) {
-                    a[h] = *reinterpret_cast<const f32x4 *>(A + i * Kd + k);
+                    a[hh] = *reinterpret_cast<const f32x4 *>(A + i * Kd + k);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a[h][e] = (i < M && k + e < Kd) ? A[i * Kd + k + e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) a[hh][e] = (i < M && k + e < Kd) ? A[i * Kd + k + e] : 0.0f;
                 }
             } else {
                 // A stored [Kd][M]: k row k0 + t/16 + 16h, i m0 + (t%16)*4 .. +3
                 const long long k = k0 + (t >> 4) + 16 * h, i = m0 + (t & 15) * 4;
                 if (vec_a) {
-                    a[h] = *reinterpret_cast<const f32x4 *>(A + k * M + i);
+                    a[hh] = *reinterpret_cast<const f32x4 *>(A + k * M + i);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a[h][e] = (k < Kd && i + e < M) ? A[k * M + i + e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) a[hh][e] = (k < Kd && i + e < M) ? A[k * M + i + e] : 0.0f;
                 }
             }
             // B stored [Kd][N]: k row k0 + t/16 + 16h, j n0 + (t%16)*4 .. +3
             const long long k = k0 + (t >> 4) + 16 * h, j = n0 + (t & 15) * 4;
             if (vec_b) {
-                b[h] = *reinterpret_cast<const f32x4 *>(B + k * N + j);
+                b[hh] = *reinterpret_cast<const f32x4 *>(B + k * N + j);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b[h][e] = (k < Kd && j + e < N) ? B[k * N + j + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) b[hh][e] = (k < Kd && j + e < N) ? B[k * N + j + e] : 0.0f;
             }
         }
     }
 
     __device__ __forceinline__ void store(float (*As)[LDP], float (*Bs)[LDP]) const
     {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x & 255;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int hh = 0; hh < NH; ++hh) {
+            const int h = NH == 2 ? hh : (int)(threadIdx.x >> 8);
             if (TA == 0) {
                 const int i = (t >> 3) + 32 * h, k = (t & 7) * 4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) As[k + e][i] = a[h][e];
+                for (int e = 0; e < 4; ++e) As[k + e][i] = a[hh][e];
             } else {
-                *reinterpret_cast<f32x4 *>(&As[(t >> 4) + 16 * h][(t & 15) * 4]) = a[h];
+                *reinterpret_cast<f32x4 *>(&As[(t >> 4) + 16 * h][(t & 15) * 4]) = a[hh];
             }
-            *reinterpret_cast<f32x4 *>(&Bs[(t >> 4) + 16 * h][(t & 15) * 4]) = b[h];
+            *reinterpret_cast<f32x4 *>(&Bs[(t >> 4) + 16 * h][(t & 15) * 4]) = b[hh];
         }
     }
 };
 
-template <int TA>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g, const int tiles_x)
+// NT = 256: four waves, one 32x32 quadrant each over the whole k range.
+// NT = 512 (grids too small to fill the CUs): eight waves; waves 4-7 take the
+// upper half of every 32-deep stage for the same quadrants, and their partial
+// tiles are added to those of waves 0-3 through LDS at the end (a fixed order:
+// lower half + upper half), so twice as many SIMDs run half-length MFMA chains.
+template <int TA, int NT>
+__global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, const int tiles_x)
 {
     // 1-D grid, batch entry = id mod nb: with 8 ranks, workgroup ids round-robin
     // over the 8 XCDs put every tile of rank r on XCD r, so a rank's A and B
@@ -105,7 +119,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g, con
     __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDP];   // Bs[buf][k][j]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wi = wave >> 1, wj = wave & 1;
+    const int wi = (wave & 3) >> 1, wj = wave & 1;
+    constexpr int KSPAN = NT == 512 ? BK / 2 : BK;     // k values of a stage per wave
+    const int kbase = NT == 512 ? (wave >> 2) * KSPAN : 0;
     // whole-tile 16-byte loads need the tile inside the matrix, 16-byte aligned
     // base pointers and row lengths that keep every row 16-byte aligned
     const bool rows_a = ((uintptr_t)A & 15) == 0 && m0 + BM <= M &&
@@ -115,14 +131,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g, con
 
     f32x16 acc = {};
     // stages s+1 and s+2 are in flight in registers while stage s is multiplied
-    Stage<TA> r0, r1;
-    auto load = [&](Stage<TA> &r, long long s) {
+    Stage<TA, NT> r0, r1;
+    auto load = [&](Stage<TA, NT> &r, long long s) {
         const long long k0 = s * BK;
         r.load(A, B, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd, rows_b && k0 + BK <= Kd);
     };
     auto mma = [&](int buf) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 2) {
+        for (int kk = kbase; kk < kbase + KSPAN; kk += 2) {
             const float a = As[buf][kk + (lane >> 5)][wi * 32 + (lane & 31)];
             const float b = Bs[buf][kk + (lane >> 5)][wj * 32 + (lane & 31)];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
@@ -147,6 +163,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Batch g, con
         r0.store(As[0], Bs[0]);
         __syncthreads();
     }
+    if (NT == 512) {
+        // upper-half partial tiles through LDS (reusing the stage buffers)
+        float *red = &As[0][0][0];          // 4 quadrants x 16 x 64 floats = 16 KiB
+        __syncthreads();
+        if (wave >= 4) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[((wave & 3) * 16 + r) * 64 + lane] = acc[r];
+        }
+        __syncthreads();
+        if (wave >= 4) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = acc[r] + red[(wave * 16 + r) * 64 + lane];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const long long gi = m0 + wi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -163,10 +192,15 @@ hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
     const long long gx = (g.N + BN - 1) / BN, gy = (g.M + BM - 1) / BM;
     const long long blocks = gx * gy * g.nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (g.trans_a)
-        hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
-    else
-        hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
+    // grids that leave CUs idle get eight waves per tile (k split in two)
+    const bool split = blocks <= DPS_GEMM_F32_SPLIT_MAX;
+    if (g.trans_a) {
+        if (split) hipLaunchKernelGGL((gemm_f32_kernel<1, 512>), dim3((unsigned)blocks), dim3(512), 0, st, g, (int)gx);
+        else hipLaunchKernelGGL((gemm_f32_kernel<1, 256>), dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
+    } else {
+        if (split) hipLaunchKernelGGL((gemm_f32_kernel<0, 512>), dim3((unsigned)blocks), dim3(512), 0, st, g, (int)gx);
+        else hipLaunchKernelGGL((gemm_f32_kernel<0, 256>), dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
+    }
     return hipGetLastError();
 }
 
