@@ -74,6 +74,17 @@ def host_cores() -> int:
     return min(len(os.sched_getaffinity(0)), 16)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def bf16_bits(t):
     import numpy as np
     import torch
@@ -237,7 +248,8 @@ def cpu_baseline_layer(grads, k, seconds):
             "sample": f"{reps} x (ReduceScatter avg + AllGather) of bucket 0 "
                       f"(K=8 x 25,000,000 bf16), {t:.1f} s",
             "single_thread_value": round(b / t1 / 1e9, 3),
-            "single_thread_bits_equal": same}
+            "single_thread_bits_equal": same,
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 # ------------------------------------------------------------ other configs

@@ -1,0 +1,90 @@
+"""Properties of the gfx950 code the library's kernels compile to (CPU only:
+hipcc cross-compiles the device code; nothing runs).
+
+- no kernel spills to scratch;
+- the sync kernels move data with 16-byte vector loads and stores;
+- the lean ReduceScatter/AllReduce variant stays within 64 VGPRs, and the GEMM
+  variants within the budgets that let a sync workgroup share a CU with them;
+- no packed-fp32 instructions (the build disables them) and no scalar-cache
+  stores anywhere.
+"""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from gradient_sync_amd import _build as B
+
+SOURCES = ["sync_kernels.hip", "odc_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    """{kernel symbol: (descriptor text, body text)} over all sources."""
+    out = {}
+    with tempfile.TemporaryDirectory() as tmp:
+        procs = []
+        for src in SOURCES:
+            asm = os.path.join(tmp, src + ".s")
+            cmd = [B.HIPCC, *B.FLAGS, "-I", B.CSRC, "-I", os.path.join(B.ROOT, "include"),
+                   "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm]
+            procs.append((asm, subprocess.Popen(cmd, stdout=subprocess.DEVNULL,
+                                                stderr=subprocess.DEVNULL)))
+        for asm, p in procs:
+            assert p.wait() == 0, f"hipcc failed for {asm}"
+            text = open(asm).read()
+            for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+                name = m.group(1)
+                start = re.search(r"^" + re.escape(name) + r":", text, re.M).start()
+                end = text.index(".Lfunc_end", start)
+                out[name] = (m.group(2), text[start:end])
+    assert len(out) > 50
+    return out
+
+
+def field(desc, key):
+    return int(re.search(r"\." + key + r" (\d+)", desc).group(1))
+
+
+def pick(kernels, *parts):
+    found = {n: v for n, v in kernels.items() if all(p in n for p in parts)}
+    assert found, parts
+    return found
+
+
+def test_no_scratch(kernels):
+    for name, (desc, _) in kernels.items():
+        assert field(desc, "amdhsa_private_segment_fixed_size") == 0, name
+
+
+def test_sync_kernels_use_16_byte_accesses(kernels):
+    for parts in (("rs_kernelILi1ELi1ELi8ELi2ELb0",), ("rs_kernelILi1ELi1ELi8ELi2ELb1",),
+                  ("ag_kernelILi2ELi8ELi2",), ("rsag_kernelILi1ELi1ELi8",),
+                  ("scatter_accumulate_kernelILi1",)):
+        for name, (_, body) in pick(kernels, *parts).items():
+            assert "global_load_dwordx4" in body, name
+            assert "global_store_dwordx4" in body, name
+
+
+def test_register_budgets(kernels):
+    for name, (desc, _) in pick(kernels, "rs_kernel_lean").items():
+        assert field(desc, "amdhsa_next_free_vgpr") <= 64, name
+    # two waves per SIMD of the default GEMM leave 512 - 2*224 = 64 registers:
+    # room for one lean sync wave
+    for name, (desc, _) in pick(kernels, "gemm_bf16_kernelILb0ELi64").items():
+        assert field(desc, "amdhsa_next_free_vgpr") <= 224, name
+    # the CU-sharing GEMM leaves room for one default sync wave (<= 96)
+    sync = max(field(d, "amdhsa_next_free_vgpr")
+               for d, _ in pick(kernels, "rs_kernelILi1ELi1ELi8ELi2").values())
+    for name, (desc, _) in pick(kernels, "gemm_bf16_kernelILb0ELi32").items():
+        assert 2 * field(desc, "amdhsa_next_free_vgpr") + sync <= 512, name
+
+
+def test_no_packed_fp32_and_no_scalar_stores(kernels):
+    banned = re.compile(r"\b(v_pk_(add|mul|fma)_f32|s_store_|s_buffer_store|s_atomic_|"
+                        r"s_buffer_atomic|s_dcache_wb|s_dcache_discard)")
+    for name, (_, body) in kernels.items():
+        m = banned.search(body)
+        assert m is None, (name, m.group(0) if m else None)
