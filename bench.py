@@ -671,11 +671,12 @@ def bench_overlap(args):
         dy, x = gen.backward_operands(6, k, pieces, t, device="cuda")
         flops = 2 * total * t * k
 
-        def gemms(share_cu=False):
+        def gemms(share_cu=False, lean=False):
             for g, (off, m, n) in enumerate(pieces):
                 for r in range(k):
                     dps.dp_gemm_bf16_ex(dy[g * k + r], x[g * k + r],
-                                        grad[r][off:off + m * n].view(m, n), share_cu=share_cu)
+                                        grad[r][off:off + m * n].view(m, n), share_cu=share_cu,
+                                        lean=lean)
 
         def serial(**o):
             dps.dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, cap, op="avg", **o)
@@ -688,11 +689,14 @@ def bench_overlap(args):
         med = lambda fn: statistics.median(_time_ms(fn, warm=3, reps=9))
         r = {"gemm_flops": flops}
         r["t_gemm_ms"] = med(gemms)
-        r["t_gemm_share_cu_ms"] = med(lambda: gemms(True))
+        r["t_gemm_lean_ms"] = med(lambda: gemms(lean=True))
+        r["t_gemm_share_cu_ms"] = med(lambda: gemms(share_cu=True))
         r["t_comm_ms"] = med(sync.step_all_reduce)
         variants = (("overlap", {}), ("overlap_lean_cap256", {"lean": True, "max_workgroups": 256}),
                     ("overlap_share_cu_cap256", {"share_cu": True, "max_workgroups": 256}))
+        # serial reference: the default (fastest) kernels on one stream
         r["t_serial_ms"] = med(lambda: serial())
+        r["t_serial_lean_ms"] = med(lambda: serial(lean=True))
         for name, o in variants:
             r[f"t_{name}_ms"] = med(lambda: overlapped(**o))
         for name, _ in variants:
@@ -713,9 +717,12 @@ def bench_overlap(args):
 
 
 def bench_gemm(args):
-    """The bf16 GEMM of the concurrency measurement alone (C = A B^T, 8192^3),
-    default and CU-sharing variants, against the MFMA roofline; the vendor
-    library GEMM (torch.matmul, hipBLASLt) on the same operands for context."""
+    """The bf16 GEMM of the concurrency measurement alone (C = A B^T, 8192^3):
+    the default (4-wave) kernel and the two 8-wave variants that leave room for
+    a sync workgroup on each CU, against the MFMA roofline; the vendor library
+    GEMM (torch.matmul, hipBLASLt) on the same operands for context. The
+    variants are timed in interleaved rounds of 8 back-to-back calls after ~1 s
+    of warm-up, so that they see the same clock and power state."""
     import torch
 
     import gen
@@ -724,17 +731,30 @@ def bench_gemm(args):
     a, b = gen.gemm_bf16_inputs(5, m, n, kk, device="cuda")
     c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
     flops = 2 * m * n * kk
-    res = {}
     bt = b.t()
-    for name, fn in (("dp_gemm_bf16", lambda: dps.dp_gemm_bf16(a, b, c)),
-                     ("dp_gemm_bf16_share_cu", lambda: dps.dp_gemm_bf16_ex(a, b, c, share_cu=True)),
-                     ("library_torch_matmul", lambda: torch.matmul(a, bt, out=c))):
-        med = statistics.median(_time_ms(fn, warm=6, reps=9))
+    fns = {"dp_gemm_bf16": lambda: dps.dp_gemm_bf16(a, b, c),
+           "dp_gemm_bf16_lean": lambda: dps.dp_gemm_bf16_ex(a, b, c, lean=True),
+           "dp_gemm_bf16_share_cu": lambda: dps.dp_gemm_bf16_ex(a, b, c, share_cu=True),
+           "library_torch_matmul": lambda: torch.matmul(a, bt, out=c)}
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        for fn in fns.values():
+            fn()
+        torch.cuda.synchronize()
+    times = {name: [] for name in fns}
+    for _ in range(8):
+        for name, fn in fns.items():
+            times[name].extend(_time_batch_ms(fn, batch=8, warm=0, reps=1))
+    res = {}
+    for name, v in times.items():
+        med = statistics.median(v)
         tf = flops / (med * 1e-3) / 1e12
         res[name] = {"median_ms": round(med, 4), "tflops": round(tf, 1),
                      "frac_of_peak": round(tf / MFMA_BF16_TFLOPS, 4)}
     return {"metric": "bf16 GEMM C = A B^T, 8192^3, fp32 accumulation", "unit": "TFLOP/s",
             "value": res["dp_gemm_bf16"]["tflops"], "results": res,
+            "timing": "interleaved rounds of 8 back-to-back calls between two events, "
+                      "after ~1 s of warm-up; median per call",
             "roofline": {"bound": "mfma", "achieved": res["dp_gemm_bf16"]["tflops"],
                          "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": res["dp_gemm_bf16"]["frac_of_peak"]},

@@ -419,10 +419,11 @@ def dp_gemm_bf16(a, b, c, stream=None):
     _gemm(a, b, c, stream, None)
 
 
-def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None):
-    """dp_gemm_bf16; share_cu selects the variant that leaves room for a sync
-    workgroup on every CU."""
-    _gemm(a, b, c, stream, ctypes.byref(LaunchOpts.make(0, share_cu)))
+def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None, lean: bool = False):
+    """dp_gemm_bf16 with a variant choice: share_cu selects the variant that
+    leaves room for a default sync workgroup on every CU, lean the one beside
+    which a lean sync workgroup fits; neither, the fastest (same bits)."""
+    _gemm(a, b, c, stream, ctypes.byref(LaunchOpts.make(0, share_cu, lean=lean)))
 
 
 def dp_scatter_accumulate(grads, acc, stream=None, n=None):

@@ -33,6 +33,13 @@ bool valid_k(int k) { return k >= 1 && k <= DP_MAX_K; }
 
 // launch options: NULL = defaults; a negative cap, unknown flags or non-zero
 // reserved words are invalid
+// DP_LAUNCH_SHARE_CU and DP_LAUNCH_LEAN pick the GEMM variants that leave room
+// for a sync workgroup on each CU; neither: the fastest variant.
+int gemm_variant(bool share_cu, bool lean)
+{
+    return share_cu ? dps::kGemmShareCU : lean ? dps::kGemmCoresident : dps::kGemmFast;
+}
+
 bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr,
              bool *two_phase = nullptr, bool *lean = nullptr)
 {
@@ -506,8 +513,8 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
                             int64_t kk, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    bool share_cu;
-    if (!opts_ok(opts, max_wg, &share_cu)) return DP_ERR_INVALID_ARG;
+    bool share_cu, lean;
+    if (!opts_ok(opts, max_wg, &share_cu, nullptr, &lean)) return DP_ERR_INVALID_ARG;
     if (!a || !b || !c || m < 1 || n < 1 || kk < 1) return DP_ERR_INVALID_ARG;
     if (m > (1 << 24) || n > (1 << 24) || kk > (1 << 24)) return DP_ERR_INVALID_ARG;
     if (kk % 8 != 0 || ((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)c & 1))
@@ -515,7 +522,8 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
     const Range rc = span(c, (size_t)(m * n) * 2);
     if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
         return DP_ERR_ALIAS;
-    return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, share_cu, (hipStream_t)stream));
+    return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, gemm_variant(share_cu, lean),
+                                            (hipStream_t)stream));
 }
 
 dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_piece_t *pieces,
@@ -585,7 +593,7 @@ dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_pie
         for (int r = 0; r < k; ++r) {
             char *c = (char *)grad[r] + (size_t)p.offset * 2;
             hipError_t e = dps::launch_gemm_bf16(dy[g * k + r], x[g * k + r], c, p.m, p.n, t,
-                                                 share_cu, cs);
+                                                 gemm_variant(share_cu, lean), cs);
             if (e != hipSuccess) return hip_status(e);
         }
         const int64_t done = p.offset + p.m * p.n;

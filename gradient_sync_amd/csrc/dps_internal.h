@@ -82,9 +82,13 @@ struct GemmF32Batch {
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t stream);
 
 // bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
-// share_cu selects the variant with depth-32 k stages (fewer registers, so a
-// sync workgroup fits on the same CU).
+// GEMM variants: kGemmFast = the 4-wave kernel (every register of each SIMD)
+// where the shape allows, else the 8-wave one; kGemmCoresident = the 8-wave
+// kernel with depth-64 stages (224 VGPRs: a lean sync workgroup fits beside it
+// on a CU); kGemmShareCU = the 8-wave kernel with depth-32 stages (198 VGPRs: a
+// default sync workgroup fits beside it).
+enum GemmVariant { kGemmFast = 0, kGemmCoresident = 1, kGemmShareCU = 2 };
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, bool share_cu, hipStream_t stream);
+                            long long Kd, int variant, hipStream_t stream);
 
 }  // namespace dps

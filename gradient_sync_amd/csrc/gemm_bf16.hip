@@ -6,26 +6,39 @@
 // dependence between them).
 //
 // Both operands are k-contiguous (the linear-layer weight layout), so each
-// lane's MFMA operand is one 16-byte run of 8 bf16 values in LDS.
+// lane's MFMA operand is one 16-byte run of 8 bf16 values in LDS. Every variant
+// walks k in ascending 16-element steps with one v_mfma_f32_32x32x16_bf16 per
+// step and output block, so all variants produce the same bits.
 //
-// Workgroup: 512 threads = 8 waves arranged 2 (rows) x 4 (columns) over a
-// 256x256 tile of C; each wave owns 128x64 = 4x2 blocks of
-// v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane). k is walked in
-// stages of TK (32 or 64) through double-buffered LDS. With EARLY, a stage's
-// operands are loaded into registers two stages ahead and written to the idle
-// LDS buffer at the start of the next stage, so the LDS writes overlap that
-// stage's MFMAs instead of standing between the MFMAs and the barrier (+6-8%
-// at 8192^3); otherwise the next stage's global loads are issued before the
-// current stage's MFMAs and written after them. Both launched variants use
-// EARLY (same register count).
-// A 256x256 tile does 128 flop per byte loaded, which keeps the kernel off the
-// L2 bandwidth limit a 128x128 tile (64 flop/byte) runs into.
-// Tiles are ordered so that the workgroups running together on one XCD (ids
-// round-robin over 8 XCDs) cover a compact block of C and share A and B rows
-// in that XCD's L2.
+// Two designs over a 256x256 tile of C:
 //
-// Edge tiles (M or N not multiples of 256, Kd not a multiple of TK) take a
-// guarded path: out-of-range rows and k-chunks load zeros, stores are masked.
+// * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
+//   multiple of 64 and at least 2048): 4 waves, one per SIMD, each owning a 128x128 quarter (4x4 MFMA
+//   blocks, 256 fp32 accumulators per lane held in the accumulation registers).
+//   A 128x128 wave tile reads 8 fragments from LDS per 16 MFMAs, against 6
+//   per 8 for a 128x64 wave tile, so the LDS read traffic per flop drops by a
+//   third, which is what bounds the 8-wave design below. With one wave per SIMD
+//   nothing hides an LDS wait, so the stage is software-pipelined by hand: the
+//   fragments of the next k step are read while the current step's MFMAs run
+//   (two fragment register sets), and each of the 16 groups of 4 MFMAs also
+//   carries one 16-byte LDS store of the next stage and one global load of the
+//   stage after it (scheduling fences keep that interleave). Global loads use a
+//   buffer descriptor on the tile's first row, so their addresses are one
+//   per-lane offset register plus a scalar offset.
+//
+// * gemm_bf16_kernel: 8 waves arranged 2 (rows) x 4 (columns), each wave
+//   128x64 = 4x2 MFMA blocks (128 fp32 accumulators per lane), k stages of TK
+//   (32 or 64) through double-buffered LDS. It fits in 224 (TK=64) or 198
+//   (TK=32) VGPRs, which leaves room for a sync workgroup on the same CU; it also
+//   takes any shape (edge tiles on a guarded path). With EARLY, a stage's
+//   operands are loaded into registers two stages ahead and written to the
+//   idle LDS buffer at the start of the next stage, so the LDS writes overlap
+//   that stage's MFMAs instead of standing between the MFMAs and the barrier.
+//
+// A 256x256 tile does 128 flop per byte loaded, which keeps the kernels off the
+// L2 bandwidth limit a 128x128 tile (64 flop/byte) runs into. Tiles are ordered
+// so that the workgroups running together on one XCD (ids round-robin over 8
+// XCDs) cover a compact block of C and share A and B rows in that XCD's L2.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l):
 //   A operand: A[i = l % 32][k = 8*(l/32) + 0..7]
@@ -180,6 +193,128 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
             }
 }
 
+
+// ----------------------------------------------------------- 4-wave kernel
+
+constexpr int W4_NT = 256;                  // 4 waves
+constexpr int W4_TK = 64;                   // k per stage
+constexpr int W4_LDK = W4_TK + 8;           // LDS row padded by 16 bytes (no bank conflicts)
+constexpr int W4_CH = W4_TK / 8;            // 16-byte chunks per tile row
+constexpr int W4_RPP = W4_NT / W4_CH;       // rows loaded per pass (32)
+constexpr int W4_HP = TM / W4_RPP;          // passes per operand tile (8)
+constexpr int W4_KS = W4_TK / 16;           // MFMA k steps per stage (4)
+constexpr int W4_B = 4;                     // 32x32 MFMA blocks per wave side (128 = 4 x 32)
+constexpr long long kW4MinK = 2048;         // shortest k range given to the 4-wave kernel
+static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of MFMAs");
+
+// keeps the compiler's scheduler from moving instructions across it, so the
+// interleave of LDS reads, LDS stores, global loads and MFMAs stays as written
+#define W4_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+__global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned short *__restrict__ A,
+                                                             const unsigned short *__restrict__ B,
+                                                             unsigned short *__restrict__ C, int M,
+                                                             int N, int Kd, int tiles_m,
+                                                             int tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) unsigned short As[2][TM][W4_LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][TN][W4_LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wi = wave >> 1, wj = wave & 1;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
+
+    // Staging: 16 registers of 16 bytes per lane; st[h] holds A row lr + 32h and
+    // st[8 + h] B row lr + 32h, at k chunk lk, of one stage. Byte offsets inside
+    // the tile's rows fit 31 bits (checked by the launcher).
+    const int lr = tid / W4_CH, lk = (tid % W4_CH) * 8;
+    const unsigned voff = (unsigned)((lr * Kd + lk) * 2);
+    const __amdgpu_buffer_rsrc_t rA =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * Kd), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * Kd), (short)0, 0x7fffffff, 0x00020000);
+    u32x4 st[2 * W4_HP];
+    auto gload1 = [&](int j, int k0) {
+        const int so = (W4_RPP * (j % W4_HP) * Kd + k0) * 2;
+        st[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              j < W4_HP ? rA : rB, voff, so, 0));
+    };
+    auto sstore1 = [&](int buf, int j) {
+        unsigned short *row = j < W4_HP ? &As[buf][lr + W4_RPP * (j % W4_HP)][lk]
+                                        : &Bs[buf][lr + W4_RPP * (j % W4_HP)][lk];
+        *reinterpret_cast<u32x4 *>(row) = st[j];
+    };
+
+    f32x16 acc[W4_B][W4_B];
+#pragma unroll
+    for (int a = 0; a < W4_B; ++a)
+#pragma unroll
+        for (int b = 0; b < W4_B; ++b) acc[a][b] = f32x16{};
+
+    // two fragment sets: k step ks computes from set ks & 1 while the next
+    // step's fragments arrive in the other
+    bf16x8 av[2][W4_B], bv[2][W4_B];
+    auto rd = [&](int set, int buf, int ks, int x) {
+        const int r = lane & 31, kc = ks * 16 + 8 * (lane >> 5);
+        av[set][x] = *reinterpret_cast<const bf16x8 *>(&As[buf][wi * 128 + x * 32 + r][kc]);
+        bv[set][x] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * 128 + x * 32 + r][kc]);
+    };
+
+    // One stage from LDS buffer buf: 16 groups of 4 MFMAs (k step ks, A block a);
+    // group j also reads fragment pair a of step ks+1, stores staging register j
+    // (the next stage) into the idle buffer and reloads it from k offset kload.
+    auto stage = [&](int buf, int kload) {
+#pragma unroll
+        for (int x = 0; x < W4_B; ++x) rd(0, buf, 0, x);
+        W4_FENCE();
+#pragma unroll
+        for (int ks = 0; ks < W4_KS; ++ks) {
+#pragma unroll
+            for (int a = 0; a < W4_B; ++a) {
+                const int j = ks * W4_B + a;
+                if (ks + 1 < W4_KS) rd((ks + 1) & 1, buf, ks + 1, a);
+                sstore1(buf ^ 1, j);
+                gload1(j, kload);
+#pragma unroll
+                for (int b = 0; b < W4_B; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][a], bv[ks & 1][b],
+                                                                        acc[a][b], 0, 0, 0);
+                W4_FENCE();
+            }
+        }
+    };
+
+    const int stages = Kd / W4_TK;
+#pragma unroll
+    for (int j = 0; j < 2 * W4_HP; ++j) gload1(j, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * W4_HP; ++j) sstore1(0, j);
+#pragma unroll
+    for (int j = 0; j < 2 * W4_HP; ++j) gload1(j, min(1, stages - 1) * W4_TK);
+    __syncthreads();
+    int buf = 0;
+    for (int s = 0; s < stages; ++s) {
+        // Stage s+1 (staged during stage s-1) goes to the idle buffer, which
+        // every wave finished reading before the last barrier; stage s+2 is
+        // loaded. Past the end the loads repeat the last stage and the stores
+        // land in a buffer that is never read again, so the loop has no branch.
+        stage(buf, min(s + 2, stages - 1) * W4_TK);
+        __syncthreads();
+        buf ^= 1;
+    }
+#pragma unroll
+    for (int a = 0; a < W4_B; ++a)
+#pragma unroll
+        for (int b = 0; b < W4_B; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const long long gi = m0 + wi * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const long long gj = n0 + wj * 128 + b * 32 + (lane & 31);
+                C[gi * N + gj] = f32_to_bf16_rne(acc[a][b][r]);
+            }
+}
+
 template <int TK, bool EARLY>
 void launch_tk(const void *a, const void *b, void *c, int M, int N, int Kd, int tm, int tn,
                hipStream_t st)
@@ -198,15 +333,28 @@ void launch_tk(const void *a, const void *b, void *c, int M, int N, int Kd, int 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, bool share_cu, hipStream_t st)
+                            long long Kd, int variant, hipStream_t st)
 {
     if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
     const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
     if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (share_cu)
+    // the 4-wave kernel: whole tiles only, byte offsets inside a tile's 256 rows
+    // (512 * Kd) within its buffer descriptor's 31-bit range, and a k range long
+    // enough that the main loop outweighs the per-tile prologue and epilogue,
+    // which one wave per SIMD cannot overlap with another workgroup's MFMAs
+    // (measured: 1.19x the 8-wave kernel at 8192^3, 1.00x at kk = 1024, 0.8x at
+    // kk = 256)
+    const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
+                    Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL;
+    if (w4) {
+        hipLaunchKernelGGL(gemm_bf16_w4_kernel, dim3((unsigned)(tm * tn)), dim3(W4_NT), 0, st,
+                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
+                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+    } else if (variant == kGemmShareCU) {
         launch_tk<32, true>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
-    else
+    } else {
         launch_tk<64, true>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
+    }
     return hipGetLastError();
 }
 

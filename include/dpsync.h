@@ -202,6 +202,10 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
  *   m, n, kk >= 1 (else DP_ERR_INVALID_ARG); kk must be a multiple of 8 and a,
  *   b 16-byte aligned (else DP_ERR_UNSUPPORTED); c must not overlap a or b
  *   (DP_ERR_ALIAS).
+ *   The products are summed over k in ascending steps of 16 into fp32, the
+ *   same order for every shape path and variant; m and n multiples of 256 and
+ *   kk a multiple of 64 and >= 2048 run the 4-wave kernel (one wave per SIMD),
+ *   other shapes the 8-wave kernel (guarded edge tiles where needed).
  */
 dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n,
                          int64_t kk, void *stream);
@@ -216,18 +220,22 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
  *                    (256 threads each), which then walk the tiles
  *                    persistently; results are bit-identical either way.
  *   flags          : DP_LAUNCH_SHARE_CU selects, for dp_gemm_bf16_ex, the GEMM
- *                    variant with a smaller register footprint (depth-32 k
- *                    stages) so that a sync workgroup can be resident on the
- *                    same CU as a GEMM workgroup. DP_LAUNCH_TWO_PHASE makes
+ *                    variant with a smaller register footprint (8 waves,
+ *                    depth-32 k stages, 198 VGPRs) so that a default sync
+ *                    workgroup can be resident on the same CU as a GEMM
+ *                    workgroup. DP_LAUNCH_TWO_PHASE makes
  *                    dp_all_reduce_ex / dp_weighted_reduce_ex run a
  *                    ReduceScatter then an AllGather instead of the one-pass
  *                    kernel (same results). DP_LAUNCH_LEAN selects, for the
  *                    ReduceScatter and AllReduce kernels, the variant with one
  *                    16-byte vector per lane per rank and at most 64 VGPRs
- *                    (same results): one of its workgroups fits in the
- *                    registers that a workgroup of dp_gemm_bf16's default
- *                    variant leaves free on a CU, so the two kernels can be
- *                    resident together. Other calls ignore the flags.
+ *                    (same results), and for the GEMM the 8-wave variant with
+ *                    depth-64 stages (224 VGPRs): one lean sync workgroup fits
+ *                    in the registers that GEMM workgroup leaves free on a CU,
+ *                    so the two kernels can be resident together. (The default
+ *                    GEMM runs one wave per SIMD and uses all of its registers
+ *                    where the shape allows; every GEMM variant gives the same
+ *                    bits.) Other calls ignore the flags.
  *   reserved       : must be zero.
  * A NULL opts pointer means all defaults. Invalid fields return
  * DP_ERR_INVALID_ARG.
@@ -284,8 +292,8 @@ dp_status_t dp_weighted_reduce_ex(const void *const *send, void *const *recv,
  * When comm_stream == compute_stream everything runs in that one stream in the
  * same order (no overlap, events unused and may be NULL).
  * opts: DP_LAUNCH_SHARE_CU selects the GEMM variant that leaves room for a
- * sync workgroup on each CU; DP_LAUNCH_LEAN the AllReduce variant that fits
- * beside the default GEMM; max_workgroups caps the AllReduce grid;
+ * sync workgroup on each CU; DP_LAUNCH_LEAN the AllReduce variant and the GEMM
+ * variant that fit together on a CU; max_workgroups caps the AllReduce grid;
  * DP_LAUNCH_TWO_PHASE runs each AllReduce as ReduceScatter then AllGather.
  *
  * The results do not depend on the schedule: out equals dp_all_reduce of the

@@ -75,6 +75,11 @@ def test_register_budgets(kernels):
     # room for one lean sync wave
     for name, (desc, _) in pick(kernels, "gemm_bf16_kernelILb0ELi64").items():
         assert field(desc, "amdhsa_next_free_vgpr") <= 224, name
+    # the 4-wave GEMM: 256 accumulators in the accumulation registers, the
+    # rest within the 256 architectural VGPRs (one wave per SIMD)
+    for name, (desc, _) in pick(kernels, "gemm_bf16_w4_kernel").items():
+        assert field(desc, "amdhsa_accum_offset") == 256, name
+        assert field(desc, "amdhsa_next_free_vgpr") <= 512, name
     # the CU-sharing GEMM leaves room for one default sync wave (<= 96)
     sync = max(field(d, "amdhsa_next_free_vgpr")
                for d, _ in pick(kernels, "rs_kernelILi1ELi1ELi8ELi2").values())

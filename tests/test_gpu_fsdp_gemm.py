@@ -189,10 +189,48 @@ def test_gemm_bf16_8192_sampled():
     check_gemm(a, b, rows.astype(np.int64), cols.astype(np.int64))
 
 
+@pytest.mark.parametrize("m,n,kk", [(256, 256, 2048), (512, 768, 2112), (1024, 256, 4096),
+                                    (768, 512, 320), (2048, 2048, 64)])
+def test_gemm_bf16_variants_bit_identical(m, n, kk):
+    """Whole 256x256 tiles with kk a multiple of 64 and >= 2048 run the 4-wave
+    kernel; the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
+    DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, so
+    all agree bit for bit (shorter k ranges take the 8-wave kernel on every
+    path: the last two cases). The default result is also checked against the
+    oracle (exactly on small-integer inputs, within the fp32 summation bound on
+    N(0,1) inputs); an odd number of k stages (2112 = 33 x 64) and grids that
+    are not a multiple of 8 tiles are among the cases."""
+    say(f"gemm bf16 variants {m}x{n}x{kk}")
+    a, b = gen.gemm_bf16_inputs(11, m, n, kk, device=DEV)
+    outs = []
+    for opts in ({}, {"lean": True}, {"share_cu": True}):
+        c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+        dps.dp_gemm_bf16_ex(a, b, c, **opts)
+        torch.cuda.synchronize()
+        outs.append(_bits(c))
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[2])
+    rng = np.random.default_rng(kk)
+    rows = np.concatenate([rng.integers(0, m, 1500), [0, m - 1, 255, 256 % m]]).astype(np.int64)
+    cols = np.concatenate([rng.integers(0, n, 1500), [n - 1, 0, 256 % n, 255]]).astype(np.int64)
+    check_gemm(a, b, rows, cols)
+    # small integers: every fp32 partial sum is exact (|sum| <= 4 kk < 2^24), so
+    # the result is the exact sum rounded once to bf16
+    g = torch.Generator().manual_seed(m + kk)
+    ai = torch.randint(-2, 3, (m, kk), generator=g).to(torch.bfloat16).to(DEV)
+    bi = torch.randint(-2, 3, (n, kk), generator=g).to(torch.bfloat16).to(DEV)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    dps.dp_gemm_bf16(ai, bi, c)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_bf16_at(_bits(ai), np.ascontiguousarray(_bits(bi).T), rows, cols,
+                                 nthreads=16)
+    assert np.array_equal(_bits(c)[rows, cols], oracle.bf16_from_f32(ref.astype(np.float32)))
+
+
 @pytest.mark.parametrize("m,n,kk", [(256, 256, 32), (200, 136, 40), (512, 768, 1024), (8192, 8192, 8192)])
 def test_gemm_bf16_share_cu_variant(m, n, kk):
-    """The depth-32 variant (DP_LAUNCH_SHARE_CU) against the oracle; it sums in
-    a different order than the default, so both are checked against fp64."""
+    """The depth-32 variant (DP_LAUNCH_SHARE_CU) against the oracle, including
+    shapes with edge tiles."""
     say(f"gemm bf16 share-cu {m}x{n}x{kk}")
     a, b = gen.gemm_bf16_inputs(9, m, n, kk, device=DEV)
     c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
