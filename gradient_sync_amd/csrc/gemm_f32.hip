@@ -27,6 +27,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64, BN = 64, BK = 32, LDP = 64 + 4;
 
+#ifndef DPS_GEMM_F32_DEPTH
+#define DPS_GEMM_F32_DEPTH 2            // k stages in flight from global memory (even)
+#endif
+constexpr int kDepth = DPS_GEMM_F32_DEPTH;
+static_assert(kDepth >= 2 && kDepth % 2 == 0, "an even number of register stages");
+
 #ifndef DPS_GEMM_F32_SPLIT_MAX
 #define DPS_GEMM_F32_SPLIT_MAX 256      // largest grid that gets eight waves per tile
 #endif
@@ -39,10 +45,15 @@ struct Stage {
     static constexpr int NH = 512 / NT;
     f32x4 a[NH], b[NH];
 
+    // WHOLE: every tile is inside the matrices and 16-byte aligned, so all
+    // loads are unconditional 16-byte loads (the guarded form, if-converted by
+    // the compiler, would issue both forms and wait on all of them)
+    template <bool WHOLE>
     __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ B,
                                          long long M, long long N, long long Kd, long long m0,
                                          long long n0, long long k0, bool vec_a, bool vec_b)
     {
+        if (WHOLE) vec_a = vec_b = true;
         const int t = threadIdx.x & 255;
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -100,7 +111,7 @@ struct Stage {
 // upper half of every 32-deep stage for the same quadrants, and their partial
 // tiles are added to those of waves 0-3 through LDS at the end (a fixed order:
 // lower half + upper half), so twice as many SIMDs run half-length MFMA chains.
-template <int TA, int NT>
+template <int TA, int NT, bool WHOLE>
 __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, const int tiles_x)
 {
     // 1-D grid, batch entry = id mod nb: with 8 ranks, workgroup ids round-robin
@@ -130,11 +141,15 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
     const long long stages = (Kd + BK - 1) / BK;
 
     f32x16 acc = {};
-    // stages s+1 and s+2 are in flight in registers while stage s is multiplied
-    Stage<TA, NT> r0, r1;
-    auto load = [&](Stage<TA, NT> &r, long long s) {
+    // DEPTH register sets: while stage s is multiplied from LDS, stages
+    // s+1 .. s+DEPTH-1 are in flight from global memory and the set that held
+    // stage s (already in LDS) takes stage s+DEPTH, so every load has DEPTH-1
+    // stages of compute to arrive in
+    Stage<TA, NT> r[kDepth];
+    auto load = [&](Stage<TA, NT> &st, long long s) {
         const long long k0 = s * BK;
-        r.load(A, B, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd, rows_b && k0 + BK <= Kd);
+        st.template load<WHOLE>(A, B, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd,
+                                rows_b && k0 + BK <= Kd);
     };
     auto mma = [&](int buf) {
 #pragma unroll
@@ -144,24 +159,45 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
     };
-    load(r0, 0);
-    if (stages > 1) load(r1, 1);
-    r0.store(As[0], Bs[0]);
-    __syncthreads();
-    // unrolled by two so that each register set has a fixed role
-    for (long long s = 0; s < stages; s += 2) {
-        // stage s from LDS buffer 0; r0 is free, r1 holds stage s+1
-        if (s + 2 < stages) load(r0, s + 2);
-        mma(0);
-        if (s + 1 >= stages) break;
-        r1.store(As[1], Bs[1]);
+    if (WHOLE) {
+        // stages is a multiple of kDepth (checked by the launcher); the body has
+        // no branch, so no load can be moved down to its use: past the end the
+        // loads repeat the last stage and the last store lands in a buffer that
+        // is never read
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) load(r[i], i);
+        r[0].store(As[0], Bs[0]);
         __syncthreads();
-        // stage s+1 from LDS buffer 1; r1 is free, r0 holds stage s+2
-        if (s + 3 < stages) load(r1, s + 3);
-        mma(1);
-        if (s + 2 >= stages) break;
-        r0.store(As[0], Bs[0]);
+        for (long long s = 0; s < stages; s += kDepth) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                const long long st = s + i;
+                load(r[i], min(st + kDepth, stages - 1));
+                mma(i & 1);
+                r[(i + 1) % kDepth].store(As[(i + 1) & 1], Bs[(i + 1) & 1]);
+                __syncthreads();
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i)
+            if (i < stages) load(r[i], i);
+        r[0].store(As[0], Bs[0]);
         __syncthreads();
+        // unrolled by kDepth (even) so that each register set and LDS buffer has
+        // a fixed role: stage s + i uses set i and LDS buffer i & 1
+        for (long long s = 0; s < stages; s += kDepth) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                const long long st = s + i;
+                if (st >= stages) break;
+                if (st + kDepth < stages) load(r[i], st + kDepth);
+                mma(i & 1);
+                if (st + 1 >= stages) break;
+                r[(i + 1) % kDepth].store(As[(i + 1) & 1], Bs[(i + 1) & 1]);
+                __syncthreads();
+            }
+        }
     }
     if (NT == 512) {
         // upper-half partial tiles through LDS (reusing the stage buffers)
@@ -184,6 +220,15 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
     }
 }
 
+template <int TA, int NT>
+void launch_f32(const GemmF32Batch &g, long long blocks, long long gx, bool whole, hipStream_t st)
+{
+    if (whole)
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, true>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, false>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
@@ -192,14 +237,20 @@ hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
     const long long gx = (g.N + BN - 1) / BN, gy = (g.M + BM - 1) / BM;
     const long long blocks = gx * gy * g.nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // whole tiles, whole k stages and 16-byte aligned rows everywhere: the
+    // unguarded kernel
+    bool whole = g.M % BM == 0 && g.N % BN == 0 && g.Kd % (BK * kDepth) == 0 && g.N % 4 == 0 &&
+                 (g.trans_a ? g.M % 4 == 0 : g.Kd % 4 == 0);
+    for (int i = 0; i < g.nb && whole; ++i)
+        whole = ((uintptr_t)g.a[i] & 15) == 0 && ((uintptr_t)g.b[i] & 15) == 0;
     // grids that leave CUs idle get eight waves per tile (k split in two)
     const bool split = blocks <= DPS_GEMM_F32_SPLIT_MAX;
     if (g.trans_a) {
-        if (split) hipLaunchKernelGGL((gemm_f32_kernel<1, 512>), dim3((unsigned)blocks), dim3(512), 0, st, g, (int)gx);
-        else hipLaunchKernelGGL((gemm_f32_kernel<1, 256>), dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
+        if (split) launch_f32<1, 512>(g, blocks, gx, whole, st);
+        else launch_f32<1, 256>(g, blocks, gx, whole, st);
     } else {
-        if (split) hipLaunchKernelGGL((gemm_f32_kernel<0, 512>), dim3((unsigned)blocks), dim3(512), 0, st, g, (int)gx);
-        else hipLaunchKernelGGL((gemm_f32_kernel<0, 256>), dim3((unsigned)blocks), dim3(256), 0, st, g, (int)gx);
+        if (split) launch_f32<0, 512>(g, blocks, gx, whole, st);
+        else launch_f32<0, 256>(g, blocks, gx, whole, st);
     }
     return hipGetLastError();
 }
