@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdpsync.so")
-SOURCES = ["api.hip", "sync_kernels.hip", "gemm_f32.hip", "gemm_bf16.hip", "odc_kernels.hip"]
+SOURCES = ["api.hip", "sync_kernels.hip", "gemm_f32.hip", "gemm_bf16.hip", "odc_kernels.hip",
+           "fsdp_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -473,25 +473,54 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
             if (overlap(outs[a], outs[b])) return DP_ERR_ALIAS;
     }
     hipStream_t st = (hipStream_t)stream;
-    // 1. forward: all-gather the weight row shards into every rank's W
-    dp_status_t s = run_ag((const void *const *)w_shard, (char *const *)w_full, d * f, R * f, k,
-                           DP_F32, 0, 1, st);
-    if (s != DP_OK) return s;
-    // 2. local dot y_r = x_r . W
     dps::GemmF32Batch g;
     memset(&g, 0, sizeof(g));
     for (int r = 0; r < k; ++r) {
         g.a[r] = x_local[r];
         g.b[r] = w_full[r];
         g.c[r] = y_local[r];
+        g.b_shard[r] = w_shard[r];
+        g.b_copy[r] = w_full[r];
     }
     g.nb = k;
     g.M = m_local;
     g.N = f;
     g.Kd = d;
     g.trans_a = 0;
-    s = hip_status(dps::launch_gemm_f32(g, st));
+    g.b_rows = R;
+    dp_status_t s;
+    if (dps::gemm_f32_fusable_gather(g, k)) {
+        // 1+2 in one launch: the dot reads W's rows from the shards, and the
+        // tiles of the first tile row write the gathered W into every w_full
+        s = hip_status(dps::launch_gemm_f32(g, st));
+    } else {
+        // 1. forward: all-gather the weight row shards into every rank's W
+        s = run_ag((const void *const *)w_shard, (char *const *)w_full, d * f, R * f, k, DP_F32, 0,
+                   1, st);
+        if (s != DP_OK) return s;
+        // 2. local dot y_r = x_r . W
+        g.b_rows = 0;
+        s = hip_status(dps::launch_gemm_f32(g, st));
+    }
     if (s != DP_OK || !bwd) return s;
+    // 3+4 in one launch where the shapes allow: dW_r = x_r^T . dy_r for every
+    // rank and the ReduceScatter of dW from the K blocks in LDS
+    if (dps::fsdp_bwd_fusable(k, m_local, d, f)) {
+        dps::FsdpBwdParams p;
+        memset(&p, 0, sizeof(p));
+        for (int r = 0; r < k; ++r) {
+            p.x[r] = x_local[r];
+            p.dy[r] = dy_local[r];
+            p.dw_full[r] = dw_full[r];
+            p.dw_shard[r] = dw_shard[r];
+        }
+        p.k = k;
+        p.m = m_local;
+        p.d = d;
+        p.f = f;
+        p.R = R;
+        return hip_status(dps::launch_fsdp_bwd_fused(p, st));
+    }
     // 3. backward: dW_r = x_r^T . dy_r
     for (int r = 0; r < k; ++r) {
         g.a[r] = x_local[r];
@@ -502,6 +531,7 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
     g.N = f;
     g.Kd = m_local;
     g.trans_a = 1;
+    g.b_rows = 0;
     s = hip_status(dps::launch_gemm_f32(g, st));
     if (s != DP_OK) return s;
     // 4. reduce-scatter dW back to the row shards (sum, pad rows zero)

@@ -78,8 +78,31 @@ struct GemmF32Batch {
     int nb;
     long long M, N, Kd;
     int trans_a;
+    // b_rows > 0 (trans_a == 0): B is the same for every entry and given as row
+    // shards, row k in b_shard[k / b_rows] (b ignored); entries with b_copy[i]
+    // set also receive a copy of B there (the gathered matrix). Shapes:
+    // gemm_f32_fusable_gather().
+    const float *b_shard[kMaxK];
+    long long b_rows;
+    float *b_copy[kMaxK];
 };
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t stream);
+bool gemm_f32_fusable_gather(const GemmF32Batch &g, int n_shards);
+
+// FSDP backward in one launch: dw_full[r] = x[r]^T . dy[r] ([d, f], fp32 MFMA,
+// the same bits as launch_gemm_f32 with trans_a) and dw_shard[c] = the ring-order
+// fp32 sum of rows c*R .. (c+1)*R - 1 of every dw_full (the same bits as the
+// ReduceScatter kernel). Shapes: fsdp_bwd_fusable().
+struct FsdpBwdParams {
+    const float *x[kMaxK];      // [m, d]
+    const float *dy[kMaxK];     // [m, f]
+    float *dw_full[kMaxK];      // [d, f]
+    float *dw_shard[kMaxK];     // [R, f]
+    int k;
+    long long m, d, f, R;
+};
+bool fsdp_bwd_fusable(int k, long long m, long long d, long long f);
+hipError_t launch_fsdp_bwd_fused(const FsdpBwdParams &p, hipStream_t stream);
 
 // bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
 // GEMM variants: kGemmFast = the 4-wave kernel (every register of each SIMD)

@@ -1,0 +1,123 @@
+// Backward half of the FSDP layer step in one launch: every rank's weight
+// gradient dW_r = x_r^T . dy_r and its ReduceScatter back to the row shards
+// ("Sharding and Parallelism", section "FSDP and ZeRO": the backward pass
+// produces the gradient of the gathered weight and reduce-scatters it so each
+// rank keeps the rows it owns; section "The cost of the inserted collectives":
+// the collective that follows the dot).
+//
+// A workgroup owns one 32x32 block (rows i0.., columns j0..) of the [d, f]
+// gradient for all K ranks: wave r computes rank r's block with
+// v_mfma_f32_32x32x2f32 over the m tokens in ascending order (the same chain as
+// the stand-alone GEMM, so dW_r has the same bits), writes it to dw_full[r] and
+// to LDS, and after one barrier the workgroup folds the K blocks in the ring
+// order of the block's shard into dw_shard (the same fold as the ReduceScatter
+// kernel, so the shard has the same bits as ReduceScatter(dw_full)). One launch
+// replaces a GEMM launch and a ReduceScatter launch, and the K blocks are
+// folded from LDS instead of being read back from HBM.
+//
+// The MFMA operands come straight from global memory into registers: for a k
+// pair, lanes 0-31 read x_r[k][i0 .. i0+31] and lanes 32-63 x_r[k+1][...] (two
+// 128-byte rows), and the same for dy_r, which is already the operand layout
+// of the 32x32x2 instruction (A[i][k] = x[k][i], B[k][j] = dy[k][j]):
+//   A operand: A[i = l % 32][k = l / 32]      B operand: B[k = l / 32][j = l % 32]
+//   D register q: D[i = 8*(q/4) + 4*(l/32) + q%4][j = l % 32]
+#include "dps_internal.h"
+
+namespace dps {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int FB = 32;       // block edge
+constexpr int FQ = 16;       // k pairs per chunk of operands
+
+template <int K>
+__global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
+{
+    __shared__ float T[K][FB * FB];          // rank r's block, element i*32 + j
+    const int lane = threadIdx.x & 63;
+    const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long nbj = p.f / FB;
+    const long long i0 = (blockIdx.x / nbj) * FB, j0 = (blockIdx.x % nbj) * FB;
+    const long long kh = lane >> 5, col = lane & 31;
+    const float *__restrict__ x = p.x[r] + kh * p.d + i0 + col;
+    const float *__restrict__ dy = p.dy[r] + kh * p.f + j0 + col;
+
+    // chunks of FQ k pairs: a chunk's 2*FQ operand loads are issued together,
+    // then its FQ MFMAs run (two waves per SIMD overlap one wave's loads with
+    // the other's MFMAs; keeping 2 or 4 chunks in flight per wave measured
+    // slower, chunks of 4 to 32 pairs the same)
+    const long long chunks = p.m / (2 * FQ);
+    f32x16 acc = {};
+    for (long long c = 0; c < chunks; ++c) {
+        float a[FQ], b[FQ];
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) {
+            const long long k = (c * FQ + q) * 2;
+            a[q] = x[k * p.d];
+            b[q] = dy[k * p.f];
+        }
+        // keep the scheduler from moving the loads down next to their MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+    }
+
+    float *__restrict__ dwf = p.dw_full[r];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int i = 8 * (q >> 2) + 4 * (int)kh + (q & 3);
+        dwf[(i0 + i) * p.f + j0 + col] = acc[q];
+        T[r][i * FB + col] = acc[q];
+    }
+    __syncthreads();
+
+    // shard c holds rows c*R ..; its fold visits ranks c+1, c+2, ..., c (mod K)
+    const int c = (int)(i0 / p.R);
+    float *__restrict__ out = p.dw_shard[c] + (i0 - (long long)c * p.R) * p.f + j0;
+    for (int e = threadIdx.x; e < FB * FB; e += 64 * K) {
+        int rr = c + 1 >= K ? c + 1 - K : c + 1;
+        float s = T[rr][e];
+#pragma unroll
+        for (int m = 1; m < K; ++m) {
+            rr = rr + 1 >= K ? 0 : rr + 1;
+            s = s + T[rr][e];
+        }
+        out[(e / FB) * p.f + (e % FB)] = s;
+    }
+}
+
+template <int K>
+hipError_t go(const FsdpBwdParams &p, hipStream_t st)
+{
+    const long long blocks = (p.d / FB) * (p.f / FB);
+    hipLaunchKernelGGL((fsdp_bwd_kernel<K>), dim3((unsigned)blocks), dim3(64 * K), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fsdp_bwd_fusable(int k, long long m, long long d, long long f)
+{
+    // whole 32x32 blocks, no shard pad rows, each block inside one shard, whole
+    // operand chunks, and at most 8 ranks (one wave per rank)
+    return k >= 1 && k <= 8 && d % k == 0 && (d / k) % FB == 0 && f % FB == 0 &&
+           m % (2 * FQ) == 0 && (d / FB) * (f / FB) <= 0x7fffffffLL;
+}
+
+hipError_t launch_fsdp_bwd_fused(const FsdpBwdParams &p, hipStream_t st)
+{
+    if (!fsdp_bwd_fusable(p.k, p.m, p.d, p.f)) return hipErrorInvalidValue;
+    switch (p.k) {
+    case 1: return go<1>(p, st);
+    case 2: return go<2>(p, st);
+    case 3: return go<3>(p, st);
+    case 4: return go<4>(p, st);
+    case 5: return go<5>(p, st);
+    case 6: return go<6>(p, st);
+    case 7: return go<7>(p, st);
+    default: return go<8>(p, st);
+    }
+}
+
+}  // namespace dps

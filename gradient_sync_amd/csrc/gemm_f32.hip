@@ -44,16 +44,31 @@ template <int TA, int NT>
 struct Stage {
     static constexpr int NH = 512 / NT;
     f32x4 a[NH], b[NH];
+    long long kb;                       // k0 of the stage held
+
+    // the B tile held, written to rows kb.. of the [Kd][N] matrix W (whole tiles)
+    __device__ __forceinline__ void copy_b(float *__restrict__ W, long long N, long long n0) const
+    {
+        const int t = threadIdx.x & 255;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            const int h = NH == 2 ? hh : (int)(threadIdx.x >> 8);
+            const long long k = kb + (t >> 4) + 16 * h, j = n0 + (t & 15) * 4;
+            *reinterpret_cast<f32x4 *>(W + k * N + j) = b[hh];
+        }
+    }
 
     // WHOLE: every tile is inside the matrices and 16-byte aligned, so all
     // loads are unconditional 16-byte loads (the guarded form, if-converted by
     // the compiler, would issue both forms and wait on all of them)
+    // Bk0: address of row k0 of B (B may be split into row shards).
     template <bool WHOLE>
-    __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ B,
+    __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ Bk0,
                                          long long M, long long N, long long Kd, long long m0,
                                          long long n0, long long k0, bool vec_a, bool vec_b)
     {
         if (WHOLE) vec_a = vec_b = true;
+        kb = k0;
         const int t = threadIdx.x & 255;
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -78,12 +93,12 @@ struct Stage {
                 }
             }
             // B stored [Kd][N]: k row k0 + t/16 + 16h, j n0 + (t%16)*4 .. +3
-            const long long k = k0 + (t >> 4) + 16 * h, j = n0 + (t & 15) * 4;
+            const long long kr = (t >> 4) + 16 * h, k = k0 + kr, j = n0 + (t & 15) * 4;
             if (vec_b) {
-                b[hh] = *reinterpret_cast<const f32x4 *>(B + k * N + j);
+                b[hh] = *reinterpret_cast<const f32x4 *>(Bk0 + kr * N + j);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b[hh][e] = (k < Kd && j + e < N) ? B[k * N + j + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) b[hh][e] = (k < Kd && j + e < N) ? Bk0[kr * N + j + e] : 0.0f;
             }
         }
     }
@@ -111,7 +126,12 @@ struct Stage {
 // upper half of every 32-deep stage for the same quadrants, and their partial
 // tiles are added to those of waves 0-3 through LDS at the end (a fixed order:
 // lower half + upper half), so twice as many SIMDs run half-length MFMA chains.
-template <int TA, int NT, bool WHOLE>
+// FUSE (whole tiles, A not transposed): B's rows come from row shards
+// (row k in b_shard[k / b_rows], each k stage inside one shard) and every B
+// tile loaded is also written to b_copy[entry] by one of the tiles that load
+// it, so one launch does the AllGather of the shards and the dot that
+// consumes it.
+template <int TA, int NT, bool WHOLE, bool FUSE>
 __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, const int tiles_x)
 {
     // 1-D grid, batch entry = id mod nb: with 8 ranks, workgroup ids round-robin
@@ -148,8 +168,22 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
     Stage<TA, NT> r[kDepth];
     auto load = [&](Stage<TA, NT> &st, long long s) {
         const long long k0 = s * BK;
-        st.template load<WHOLE>(A, B, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd,
+        const float *Bk0 = B + k0 * N;
+        if (FUSE) {
+            const long long c = k0 / g.b_rows;
+            Bk0 = g.b_shard[c] + (k0 - c * g.b_rows) * N;
+        }
+        st.template load<WHOLE>(A, Bk0, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd,
                                 rows_b && k0 + BK <= Kd);
+    };
+    // the copy of a B tile is written by one of the tiles_y tiles that load
+    // it: stage s by the tile in tile row s mod tiles_y, so the extra writes
+    // are spread evenly over the tile rows
+    float *__restrict__ Wc = FUSE ? g.b_copy[bz] : nullptr;
+    const long long tiles_y = (M + BM - 1) / BM, ty = m0 / BM;
+    auto put = [&](const Stage<TA, NT> &st, int buf) {
+        st.store(As[buf], Bs[buf]);
+        if (FUSE && Wc && (st.kb / BK) % tiles_y == ty) st.copy_b(Wc, N, n0);
     };
     auto mma = [&](int buf) {
 #pragma unroll
@@ -166,7 +200,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
         // is never read
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) load(r[i], i);
-        r[0].store(As[0], Bs[0]);
+        put(r[0], 0);
         __syncthreads();
         for (long long s = 0; s < stages; s += kDepth) {
 #pragma unroll
@@ -174,7 +208,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
                 const long long st = s + i;
                 load(r[i], min(st + kDepth, stages - 1));
                 mma(i & 1);
-                r[(i + 1) % kDepth].store(As[(i + 1) & 1], Bs[(i + 1) & 1]);
+                put(r[(i + 1) % kDepth], (i + 1) & 1);
                 __syncthreads();
             }
         }
@@ -223,13 +257,40 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmF32Batch g, cons
 template <int TA, int NT>
 void launch_f32(const GemmF32Batch &g, long long blocks, long long gx, bool whole, hipStream_t st)
 {
+    if constexpr (TA == 0) {
+        if (g.b_rows > 0) {
+            hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, true, true>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+            return;
+        }
+    }
     if (whole)
-        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, true>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, true, false>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
     else
-        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, false>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, NT, false, false>), dim3((unsigned)blocks), dim3(NT), 0, st, g, (int)gx);
+}
+
+// whole tiles, whole stage groups and 16-byte aligned rows everywhere
+bool f32_whole(const GemmF32Batch &g)
+{
+    bool whole = g.M % BM == 0 && g.N % BN == 0 && g.Kd % (BK * kDepth) == 0 && g.N % 4 == 0 &&
+                 (g.trans_a ? g.M % 4 == 0 : g.Kd % 4 == 0);
+    for (int i = 0; i < g.nb && whole; ++i)
+        whole = ((uintptr_t)g.a[i] & 15) == 0 && (g.b_rows > 0 || ((uintptr_t)g.b[i] & 15) == 0);
+    return whole;
 }
 
 }  // namespace
+
+bool gemm_f32_fusable_gather(const GemmF32Batch &g, int n_shards)
+{
+    if (g.trans_a || g.b_rows <= 0 || g.b_rows % BK != 0 || !f32_whole(g)) return false;
+    if (g.b_rows * n_shards < g.Kd) return false;
+    for (int c = 0; c < n_shards; ++c)
+        if (((uintptr_t)g.b_shard[c] & 15) != 0) return false;
+    for (int i = 0; i < g.nb; ++i)
+        if (g.b_copy[i] && ((uintptr_t)g.b_copy[i] & 15) != 0) return false;
+    return true;
+}
 
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
 {
@@ -237,12 +298,8 @@ hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
     const long long gx = (g.N + BN - 1) / BN, gy = (g.M + BM - 1) / BM;
     const long long blocks = gx * gy * g.nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // whole tiles, whole k stages and 16-byte aligned rows everywhere: the
-    // unguarded kernel
-    bool whole = g.M % BM == 0 && g.N % BN == 0 && g.Kd % (BK * kDepth) == 0 && g.N % 4 == 0 &&
-                 (g.trans_a ? g.M % 4 == 0 : g.Kd % 4 == 0);
-    for (int i = 0; i < g.nb && whole; ++i)
-        whole = ((uintptr_t)g.a[i] & 15) == 0 && ((uintptr_t)g.b[i] & 15) == 0;
+    const bool whole = f32_whole(g);
+    if (g.b_rows > 0 && (g.trans_a || !whole || g.b_rows % BK != 0)) return hipErrorInvalidValue;
     // grids that leave CUs idle get eight waves per tile (k split in two)
     const bool split = blocks <= DPS_GEMM_F32_SPLIT_MAX;
     if (g.trans_a) {

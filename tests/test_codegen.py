@@ -17,7 +17,7 @@ import pytest
 
 from gradient_sync_amd import _build as B
 
-SOURCES = ["sync_kernels.hip", "odc_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["sync_kernels.hip", "odc_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip", "fsdp_kernels.hip"]
 
 
 @pytest.fixture(scope="module")

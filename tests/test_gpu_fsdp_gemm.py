@@ -88,6 +88,20 @@ def check_fsdp(x, w, dy, k, exact=False):
             ab = ab_dw[c * R:c * R + rows]
             err = np.abs(g[:rows].astype(np.float64) - ws_[:rows])
             assert np.all(err <= gamma(ml + k + 2) * ab)
+    # dw_full: each rank's x_r^T dy_r within the summation bound, and dw_shard is
+    # exactly the ring-order ReduceScatter of the dw_full the GPU wrote (the
+    # fused backward kernel folds its blocks from LDS; the other path runs the
+    # ReduceScatter kernel on dw_full)
+    for r in range(k):
+        ref, ab = oracle.gemm_f64(host["xl"][r], host["dyl"][r], trans_a=True)
+        if exact:
+            assert bits_equal(got["dwf"][r], ref.astype(np.float32))
+        else:
+            err = np.abs(got["dwf"][r].astype(np.float64) - ref)
+            assert np.all(err <= gamma(ml + 2) * ab)
+    rs = oracle.reduce_scatter([g.ravel() for g in got["dwf"]], op="sum", L=R * f)
+    for c in range(k):
+        assert bits_equal(got["dws"][c].ravel(), rs[c])
     # global view: concatenated y is x @ w (normwise)
     ycat = np.concatenate(got["y"]).astype(np.float64)
     ref = xn.astype(np.float64) @ wn.astype(np.float64)
@@ -114,8 +128,17 @@ def test_fsdp_integer_values_exact():
 
 
 @pytest.mark.parametrize("k,m,d,f", [(3, 111, 45, 29), (8, 64, 100, 70), (1, 5, 3, 2),
-                                     (5, 5 * 33, 64, 130), (2, 256, 96, 64)])
+                                     (5, 5 * 33, 64, 130), (2, 256, 96, 64),
+                                     (4, 4 * 64, 256, 96), (7, 7 * 32, 7 * 32, 64),
+                                     (8, 8 * 32, 512, 32), (2, 256, 128, 128),
+                                     (4, 4 * 64, 256, 64), (8, 8 * 64, 256, 128)])
 def test_fsdp_ragged_shapes(k, m, d, f):
+    """The first five shapes take the separate launches (AllGather, GEMM, GEMM,
+    ReduceScatter). The next three take the fused backward kernel (whole 32x32
+    blocks, shards of a multiple of 32 rows, m_local a multiple of 32) with
+    K = 4, 7 and 8; the last three also the fused forward (whole 64x64 tiles,
+    d a multiple of 64, shards of a multiple of 32 rows: the AllGather folded
+    into the GEMM's operand loads)."""
     say(f"fsdp ragged k={k} m={m} d={d} f={f}")
     g = torch.Generator().manual_seed(k * m + d)
     x = torch.randn(m, d, generator=g)
