@@ -489,7 +489,40 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
     g.trans_a = 0;
     g.b_rows = R;
     dp_status_t s;
-    if (dps::gemm_f32_fusable_gather(g, k)) {
+    const bool fwd_fused = dps::gemm_f32_fusable_gather(g, k);
+    const int64_t n_fwd = (m_local / 64) * (f / 64) * k;
+    if (fwd_fused && bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
+        n_fwd + (d / 32) * (f / 32) <= 0x7fffffffLL) {
+        // the whole step in one launch: forward tiles (AllGather folded into
+        // the dot) beside backward blocks (ReduceScatter folded into the dW
+        // kernel); the two halves share no data
+        dps::FsdpStepParams p;
+        memset(&p, 0, sizeof(p));
+        for (int r = 0; r < k; ++r) {
+            p.fwd.a[r] = x_local[r];
+            p.fwd.c[r] = y_local[r];
+            p.fwd.b_shard[r] = w_shard[r];
+            p.fwd.b_copy[r] = w_full[r];
+            p.bwd.x[r] = x_local[r];
+            p.bwd.dy[r] = dy_local[r];
+            p.bwd.dw_full[r] = dw_full[r];
+            p.bwd.dw_shard[r] = dw_shard[r];
+        }
+        p.fwd.nb = k;
+        p.fwd.M = m_local;
+        p.fwd.N = f;
+        p.fwd.Kd = d;
+        p.fwd.b_rows = R;
+        p.bwd.k = k;
+        p.bwd.m = m_local;
+        p.bwd.d = d;
+        p.bwd.f = f;
+        p.bwd.R = R;
+        p.tiles_x = (int)(f / 64);
+        p.n_fwd = (int)n_fwd;
+        return hip_status(dps::launch_fsdp_step(p, st));
+    }
+    if (fwd_fused) {
         // 1+2 in one launch: the dot reads W's rows from the shards, and the
         // tiles of the first tile row write the gathered W into every w_full
         s = hip_status(dps::launch_gemm_f32(g, st));

@@ -104,6 +104,36 @@ struct FsdpBwdParams {
 bool fsdp_bwd_fusable(int k, long long m, long long d, long long f);
 hipError_t launch_fsdp_bwd_fused(const FsdpBwdParams &p, hipStream_t stream);
 
+// The whole FSDP step in one launch for K <= 8: the forward dot with the
+// AllGather folded in (a GemmF32Batch in shard mode, cut to 8 entries) beside
+// the fused backward. n_fwd = the forward's tile count, tiles_x = its tiles per
+// row. Shapes: gemm_f32_fusable_gather() and fsdp_bwd_fusable().
+struct FsdpFwd8 {
+    const float *a[8];
+    const float *b[8];
+    float *c[8];
+    int nb;
+    long long M, N, Kd;
+    int trans_a;
+    const float *b_shard[8];
+    long long b_rows;
+    float *b_copy[8];
+};
+struct FsdpBwd8 {
+    const float *x[8];
+    const float *dy[8];
+    float *dw_full[8];
+    float *dw_shard[8];
+    int k;
+    long long m, d, f, R;
+};
+struct FsdpStepParams {
+    FsdpFwd8 fwd;
+    FsdpBwd8 bwd;
+    int n_fwd, tiles_x;
+};
+hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t stream);
+
 // bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
 // GEMM variants: kGemmFast = the 4-wave kernel (every register of each SIMD)
 // where the shape allows, else the 8-wave one; kGemmCoresident = the 8-wave

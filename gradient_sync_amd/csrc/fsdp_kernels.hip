@@ -21,61 +21,64 @@
 // of the 32x32x2 instruction (A[i][k] = x[k][i], B[k][j] = dy[k][j]):
 //   A operand: A[i = l % 32][k = l / 32]      B operand: B[k = l / 32][j = l % 32]
 //   D register q: D[i = 8*(q/4) + 4*(l/32) + q%4][j = l % 32]
-#include "dps_internal.h"
+#include "gemm_f32_tile.h"
 
 namespace dps {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using f32tile::f32x16;
 
 constexpr int FB = 32;       // block edge
 constexpr int FQ = 16;       // k pairs per chunk of operands
 
-template <int K>
-__global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
+// Block id of the backward half for NTH threads (NTH >= 64 K; waves K.. only
+// join the fold). P is FsdpBwdParams or a struct with the same fields.
+template <int K, int NTH, class P>
+__device__ __forceinline__ void fsdp_bwd_block(const P &p, const long long id)
 {
     __shared__ float T[K][FB * FB];          // rank r's block, element i*32 + j
     const int lane = threadIdx.x & 63;
     const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long long nbj = p.f / FB;
-    const long long i0 = (blockIdx.x / nbj) * FB, j0 = (blockIdx.x % nbj) * FB;
+    const long long i0 = (id / nbj) * FB, j0 = (id % nbj) * FB;
     const long long kh = lane >> 5, col = lane & 31;
-    const float *__restrict__ x = p.x[r] + kh * p.d + i0 + col;
-    const float *__restrict__ dy = p.dy[r] + kh * p.f + j0 + col;
 
-    // chunks of FQ k pairs: a chunk's 2*FQ operand loads are issued together,
-    // then its FQ MFMAs run (two waves per SIMD overlap one wave's loads with
-    // the other's MFMAs; keeping 2 or 4 chunks in flight per wave measured
-    // slower, chunks of 4 to 32 pairs the same)
-    const long long chunks = p.m / (2 * FQ);
-    f32x16 acc = {};
-    for (long long c = 0; c < chunks; ++c) {
-        float a[FQ], b[FQ];
+    if (r < K) {
+        const float *__restrict__ x = p.x[r] + kh * p.d + i0 + col;
+        const float *__restrict__ dy = p.dy[r] + kh * p.f + j0 + col;
+        // chunks of FQ k pairs: a chunk's 2*FQ operand loads are issued
+        // together, then its FQ MFMAs run (two waves per SIMD overlap one
+        // wave's loads with the other's MFMAs; keeping 2 or 4 chunks in flight
+        // per wave measured slower, chunks of 4 to 32 pairs the same)
+        const long long chunks = p.m / (2 * FQ);
+        f32x16 acc = {};
+        for (long long c = 0; c < chunks; ++c) {
+            float a[FQ], b[FQ];
 #pragma unroll
-        for (int q = 0; q < FQ; ++q) {
-            const long long k = (c * FQ + q) * 2;
-            a[q] = x[k * p.d];
-            b[q] = dy[k * p.f];
+            for (int q = 0; q < FQ; ++q) {
+                const long long k = (c * FQ + q) * 2;
+                a[q] = x[k * p.d];
+                b[q] = dy[k * p.f];
+            }
+            // keep the scheduler from moving the loads down next to their MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < FQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
         }
-        // keep the scheduler from moving the loads down next to their MFMAs
-        __builtin_amdgcn_sched_barrier(0);
+        float *__restrict__ dwf = p.dw_full[r];
 #pragma unroll
-        for (int q = 0; q < FQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
-    }
-
-    float *__restrict__ dwf = p.dw_full[r];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int i = 8 * (q >> 2) + 4 * (int)kh + (q & 3);
-        dwf[(i0 + i) * p.f + j0 + col] = acc[q];
-        T[r][i * FB + col] = acc[q];
+        for (int q = 0; q < 16; ++q) {
+            const int i = 8 * (q >> 2) + 4 * (int)kh + (q & 3);
+            dwf[(i0 + i) * p.f + j0 + col] = acc[q];
+            T[r][i * FB + col] = acc[q];
+        }
     }
     __syncthreads();
 
     // shard c holds rows c*R ..; its fold visits ranks c+1, c+2, ..., c (mod K)
     const int c = (int)(i0 / p.R);
     float *__restrict__ out = p.dw_shard[c] + (i0 - (long long)c * p.R) * p.f + j0;
-    for (int e = threadIdx.x; e < FB * FB; e += 64 * K) {
+    for (int e = threadIdx.x; e < FB * FB; e += NTH) {
         int rr = c + 1 >= K ? c + 1 - K : c + 1;
         float s = T[rr][e];
 #pragma unroll
@@ -88,10 +91,37 @@ __global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
 }
 
 template <int K>
+__global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
+{
+    fsdp_bwd_block<K, 64 * K>(p, (long long)blockIdx.x);
+}
+
+// The whole layer step in one launch: workgroups 0 .. n_fwd-1 are tiles of the
+// forward dot with the AllGather folded in (the 8-wave k-split fp32 tile, W's
+// rows read from the shards, the gathered copy written as it is loaded), the
+// rest are blocks of the backward half. The two halves share no data, so
+// they run side by side on the CUs instead of one after the other.
+template <int K>
+__global__ __launch_bounds__(512) void fsdp_step_kernel(const FsdpStepParams p)
+{
+    if ((int)blockIdx.x < p.n_fwd)
+        f32tile::gemm_f32_tile<0, 512, true, true>(p.fwd, p.tiles_x, (int)blockIdx.x);
+    else
+        fsdp_bwd_block<K, 512>(p.bwd, (long long)blockIdx.x - p.n_fwd);
+}
+
+template <int K>
 hipError_t go(const FsdpBwdParams &p, hipStream_t st)
 {
     const long long blocks = (p.d / FB) * (p.f / FB);
     hipLaunchKernelGGL((fsdp_bwd_kernel<K>), dim3((unsigned)blocks), dim3(64 * K), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int K>
+hipError_t go_step(const FsdpStepParams &p, long long blocks, hipStream_t st)
+{
+    hipLaunchKernelGGL((fsdp_step_kernel<K>), dim3((unsigned)blocks), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
@@ -117,6 +147,25 @@ hipError_t launch_fsdp_bwd_fused(const FsdpBwdParams &p, hipStream_t st)
     case 6: return go<6>(p, st);
     case 7: return go<7>(p, st);
     default: return go<8>(p, st);
+    }
+}
+
+hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t st)
+{
+    const int k = p.bwd.k;
+    if (k < 1 || k > 8 || p.fwd.nb != k || !fsdp_bwd_fusable(k, p.bwd.m, p.bwd.d, p.bwd.f))
+        return hipErrorInvalidValue;
+    const long long blocks = (long long)p.n_fwd + (p.bwd.d / FB) * (p.bwd.f / FB);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    switch (k) {
+    case 1: return go_step<1>(p, blocks, st);
+    case 2: return go_step<2>(p, blocks, st);
+    case 3: return go_step<3>(p, blocks, st);
+    case 4: return go_step<4>(p, blocks, st);
+    case 5: return go_step<5>(p, blocks, st);
+    case 6: return go_step<6>(p, blocks, st);
+    case 7: return go_step<7>(p, blocks, st);
+    default: return go_step<8>(p, blocks, st);
     }
 }
 
