@@ -46,13 +46,13 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 
 # HBM bytes per full-size launch from two rocprofv3 PMC passes (FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
-# sources they were taken on (sha256 of sync_kernels.hip + dps_internal.h).
+# sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "508daab374bccf8e04a0a84ce7d0c28e87d2c085e9471d058cb32e5d9d5e1b70"
-                      "97bb01548be6ad91cf58f0ee07b2e06de3efba446e85aa33d38aa8702d7b0932",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49738.8) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24809.4 + 390824.6) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220219.3 + 440376.9) * 1024,
+    "sources_sha256": "246aadf3cde199b205fe85c310f2f046586f823a0d93e58d5561f63ab48e5373"
+                      "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49740.1) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24809.4 + 390833.5) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220219.2 + 440396.5) * 1024,
 }
 
 
@@ -64,7 +64,7 @@ def kernel_sources_sha256() -> str:
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     out = ""
-    for f in ("sync_kernels.hip", "dps_internal.h"):
+    for f in ("sync_kernels.hip", "sync_internal.h"):
         with open(os.path.join(here, "gradient_sync_amd", "csrc", f), "rb") as fh:
             out += hashlib.sha256(fh.read()).hexdigest()
     return out

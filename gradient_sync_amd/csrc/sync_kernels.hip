@@ -25,7 +25,7 @@
 // vectors) and the unaligned head and the tail are done element by element;
 // otherwise the tile is done element by element with consecutive lanes on
 // consecutive elements (still coalesced).
-#include "dps_internal.h"
+#include "sync_internal.h"
 
 #pragma clang fp contract(off)
 
