@@ -323,26 +323,36 @@ def bench_fsdp(args):
     y = [torch.empty(ml, f, device="cuda") for _ in range(k)]
     dwf = [torch.empty(d, f, device="cuda") for _ in range(k)]
     dws = [torch.empty(R, f, device="cuda") for _ in range(k)]
-    dps.dp_fsdp_layer(xl, ws, dyl, wf, y, dwf, dws)      # checks shapes once
+    dx = [torch.empty(ml, d, device="cuda") for _ in range(k)]
+    dps.dp_fsdp_layer(xl, ws, dyl, wf, y, dwf, dws, dx_local=dx)     # checks shapes once
     P = lambda ts: dps.ptr_array([t.data_ptr() for t in ts])
     args_c = (k, ml, d, f, P(xl), P(ws), P(dyl), P(wf), P(y), P(dwf), P(dws))
+    args_x = (k, ml, d, f, P(xl), P(ws), P(dyl), P(wf), P(y), P(dx), P(dwf), P(dws))
     lib = dps.lib()
     batch = 20
-
-    def steps():
-        st = dps._stream(None)
-        for _ in range(batch):
-            rc = lib.dp_fsdp_layer(*args_c, st)
-            if rc:
-                raise dps.DpsyncError(rc, "dp_fsdp_layer")
-    ms = [t / batch for t in _time_ms(steps, warm=2, reps=9)]
-    med = statistics.median(ms)
-    flops = 2 * (2 * k * ml * d * f)
+    res = {}
+    for name, fn, args_ in (("step", lib.dp_fsdp_layer, args_c),
+                            ("step_with_dx", lib.dp_fsdp_layer_ex, args_x)):
+        def steps():
+            st = dps._stream(None)
+            for _ in range(batch):
+                rc = fn(*args_, st)
+                if rc:
+                    raise dps.DpsyncError(rc, name)
+        ms = [t / batch for t in _time_ms(steps, warm=2, reps=9)]
+        med = statistics.median(ms)
+        gemms = 2 if name == "step" else 3
+        flops = gemms * (2 * k * ml * d * f)
+        res[name] = {"median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
+                     "gemm_flops": flops,
+                     "effective_tflops": round(flops / (med * 1e-3) / 1e12, 2)}
     return {"metric": "FSDP layer step (AG w, y=xW, dW=x^T dy, RS dW), K=8",
             "timing": f"{batch} back-to-back calls between two HIP events, per call",
-            "unit": "us", "median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
-            "gemm_flops": flops,
-            "effective_tflops": round(flops / (med * 1e-3) / 1e12, 2),
+            "unit": "us", "median_us": res["step"]["median_us"], "min_us": res["step"]["min_us"],
+            "gemm_flops": res["step"]["gemm_flops"],
+            "effective_tflops": res["step"]["effective_tflops"],
+            "with_dx": dict(res["step_with_dx"], what="the same plus the input gradient "
+                                                       "dx = dy W^T (dp_fsdp_layer_ex)"),
             "mfma_peak_tflops": MFMA_F32_TFLOPS,
             "config": {"workload": "K=8, x[1024,512] N(0,1), w[512,512] N(0,0.02^2), "
                                    "dy[1024,512] N(0,1), fp32"}}

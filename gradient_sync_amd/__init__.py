@@ -13,7 +13,8 @@ Calls (same names and meaning as the C ABI):
   dp_all_gather(send, recv, n=None, s_chunks=1, stream=None)
   dp_all_reduce(send, recv, op="sum", s_chunks=1, stream=None)
   dp_weighted_reduce(send, recv, tokens, s_chunks=1, stream=None)
-  dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full, dw_shard, stream=None)
+  dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full, dw_shard, stream=None,
+                dx_local=None)                # dx_local: dp_fsdp_layer_ex
   dp_gemm_bf16(a, b, c, stream=None)          # c = a @ b.T
 """
 from __future__ import annotations
@@ -46,7 +47,7 @@ EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version"
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
            "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex",
            "dp_scatter_accumulate", "dp_settle", "dp_backward_allreduce_overlap",
-           "dp_reduce_scatter_all_gather")
+           "dp_reduce_scatter_all_gather", "dp_fsdp_layer_ex")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
@@ -155,6 +156,8 @@ def lib():
         L.dp_weighted_reduce.argtypes = [_vp, _vp, _vp, _sz, _int, _int, _int, _vp]
         L.dp_fsdp_layer.restype = _int
         L.dp_fsdp_layer.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.dp_fsdp_layer_ex.restype = _int
+        L.dp_fsdp_layer_ex.argtypes = [_int, _i64, _i64, _i64] + [_vp] * 9
         L.dp_gemm_bf16.restype = _int
         L.dp_gemm_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
         P = ctypes.POINTER(LaunchOpts)
@@ -370,8 +373,9 @@ def dp_weighted_reduce_ex(send, recv, tokens, s_chunks: int = 1, max_workgroups:
 
 
 def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_shard=None,
-                  stream=None):
-    """FSDP layer step over K ranks (fp32): gather W, y = x W, dW = x^T dy, RS(dW)."""
+                  stream=None, dx_local=None):
+    """FSDP layer step over K ranks (fp32): gather W, y = x W, dW = x^T dy, RS(dW);
+    with dx_local (needs dy_local) also the input gradient dx = dy W^T."""
     f32 = torch.float32
     x_local = _tensors(x_local, "x_local", f32)
     w_shard = _tensors(w_shard, "w_shard", f32)
@@ -385,14 +389,25 @@ def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_
         dy_local = _tensors(dy_local, "dy_local", f32)
         dw_full = _tensors(dw_full, "dw_full", f32)
         dw_shard = _tensors(dw_shard, "dw_shard", f32)
+    want_dx = dx_local is not None
+    if want_dx:
+        if not bwd:
+            raise ValueError("dx_local needs dy_local")
+        dx_local = _tensors(dx_local, "dx_local", f32)
     R = dp_shard_len(d, k)
-    for name, ts, shape in (("x_local", x_local, (m_local, d)), ("w_shard", w_shard, (R, f)),
+    for name, ts, shape in ((("dx_local", dx_local, (m_local, d)),) if want_dx else ()) + (
+            ("x_local", x_local, (m_local, d)), ("w_shard", w_shard, (R, f)),
                             ("w_full", w_full, (d, f)), ("y_local", y_local, (m_local, f))) + (
             (("dy_local", dy_local, (m_local, f)), ("dw_full", dw_full, (d, f)),
              ("dw_shard", dw_shard, (R, f))) if bwd else ()):
         if len(ts) != k or any(tuple(t.shape) != shape for t in ts):
             raise ValueError(f"{name}: expected {k} tensors of shape {shape}")
     P = lambda ts: ptr_array([t.data_ptr() for t in ts])
+    if want_dx:
+        _check(lib().dp_fsdp_layer_ex(k, m_local, d, f, P(x_local), P(w_shard), P(dy_local),
+                                      P(w_full), P(y_local), P(dx_local), P(dw_full),
+                                      P(dw_shard), _stream(stream)), "dp_fsdp_layer_ex")
+        return
     _check(lib().dp_fsdp_layer(k, m_local, d, f, P(x_local), P(w_shard),
                                P(dy_local) if bwd else None, P(w_full), P(y_local),
                                P(dw_full) if bwd else None, P(dw_shard) if bwd else None,

@@ -439,6 +439,16 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
                           float *const *y_local, float *const *dw_full, float *const *dw_shard,
                           void *stream)
 {
+    return dp_fsdp_layer_ex(k, m_local, d, f, x_local, w_shard, dy_local, w_full, y_local,
+                            nullptr, dw_full, dw_shard, stream);
+}
+
+dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
+                             const float *const *x_local, const float *const *w_shard,
+                             const float *const *dy_local, float *const *w_full,
+                             float *const *y_local, float *const *dx_local,
+                             float *const *dw_full, float *const *dw_shard, void *stream)
+{
     if (!valid_k(k) || m_local < 1 || d < 1 || f < 1) return DP_ERR_INVALID_ARG;
     if (m_local > (1 << 24) || d > (1 << 24) || f > (1 << 24)) return DP_ERR_INVALID_ARG;
     if (!ptrs_ok((const void *const *)x_local, k, 4) || !ptrs_ok((const void *const *)w_shard, k, 4) ||
@@ -449,11 +459,13 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
                 !ptrs_ok((const void *const *)dw_full, k, 4) ||
                 !ptrs_ok((const void *const *)dw_shard, k, 4)))
         return DP_ERR_INVALID_ARG;
+    const bool want_dx = dx_local != nullptr;
+    if (want_dx && (!bwd || !ptrs_ok((const void *const *)dx_local, k, 4))) return DP_ERR_INVALID_ARG;
     const int64_t R = (d + k - 1) / k;
     const size_t bx = (size_t)(m_local * d) * 4, bws = (size_t)(R * f) * 4, bdy = (size_t)(m_local * f) * 4;
     const size_t bwf = (size_t)(d * f) * 4, by = (size_t)(m_local * f) * 4;
     // outputs must be disjoint from every input and from each other
-    Range ins[3 * DP_MAX_K], outs[4 * DP_MAX_K];
+    Range ins[3 * DP_MAX_K], outs[5 * DP_MAX_K];
     int ni = 0, no = 0;
     for (int r = 0; r < k; ++r) {
         ins[ni++] = span(x_local[r], bx);
@@ -465,6 +477,7 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
             outs[no++] = span(dw_full[r], bwf);
             outs[no++] = span(dw_shard[r], bws);
         }
+        if (want_dx) outs[no++] = span(dx_local[r], bx);
     }
     for (int a = 0; a < no; ++a) {
         for (int b = 0; b < ni; ++b)
@@ -488,11 +501,28 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
     g.Kd = d;
     g.trans_a = 0;
     g.b_rows = R;
+    // dx_r = dy_r . W^T: [m_local, d], W^T's columns are W's rows (shards)
+    dps::GemmF32Batch gx;
+    memset(&gx, 0, sizeof(gx));
+    for (int r = 0; r < k && want_dx; ++r) {
+        gx.a[r] = dy_local[r];
+        gx.b[r] = w_full[r];
+        gx.c[r] = dx_local[r];
+        gx.b_shard[r] = w_shard[r];
+    }
+    gx.nb = k;
+    gx.M = m_local;
+    gx.N = d;
+    gx.Kd = f;
+    gx.trans_b = 1;
+    gx.b_rows = R;
     dp_status_t s;
     const bool fwd_fused = dps::gemm_f32_fusable_gather(g, k);
+    const bool dx_fused = want_dx && dps::gemm_f32_fusable_gather(gx, k);
     const int64_t n_fwd = (m_local / 64) * (f / 64) * k;
+    const int64_t n_dx = want_dx ? (m_local / 64) * (d / 64) * k : 0;
     if (fwd_fused && bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
-        n_fwd + (d / 32) * (f / 32) <= 0x7fffffffLL) {
+        (!want_dx || dx_fused) && n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
         // the whole step in one launch: forward tiles (AllGather folded into
         // the dot) beside backward blocks (ReduceScatter folded into the dW
         // kernel); the two halves share no data
@@ -520,6 +550,21 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
         p.bwd.R = R;
         p.tiles_x = (int)(f / 64);
         p.n_fwd = (int)n_fwd;
+        if (want_dx) {
+            for (int r = 0; r < k; ++r) {
+                p.dx.a[r] = dy_local[r];
+                p.dx.c[r] = dx_local[r];
+                p.dx.b_shard[r] = w_shard[r];
+            }
+            p.dx.nb = k;
+            p.dx.M = m_local;
+            p.dx.N = d;
+            p.dx.Kd = f;
+            p.dx.b_rows = R;
+            p.dx.trans_b = 1;
+            p.tiles_x_dx = (int)(d / 64);
+            p.n_dx = (int)n_dx;
+        }
         return hip_status(dps::launch_fsdp_step(p, st));
     }
     if (fwd_fused) {
@@ -536,6 +581,13 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
         s = hip_status(dps::launch_gemm_f32(g, st));
     }
     if (s != DP_OK || !bwd) return s;
+    // dx = dy . W^T, from the shards where the shapes allow, else from the
+    // gathered W (written above)
+    if (want_dx) {
+        if (!dx_fused) gx.b_rows = 0;
+        s = hip_status(dps::launch_gemm_f32(gx, st));
+        if (s != DP_OK) return s;
+    }
     // 3+4 in one launch where the shapes allow: dW_r = x_r^T . dy_r for every
     // rank and the ReduceScatter of dW from the K blocks in LDS
     if (dps::fsdp_bwd_fusable(k, m_local, d, f)) {

@@ -6,8 +6,9 @@
 namespace dps {
 
 // Batched fp32 GEMM on MFMA: for each batch b < nb,
-// C_b[M,N] = op(A_b)[M,Kd] * B_b[Kd,N], row-major; op(A) = A ([M,Kd]) or, with
-// trans_a, A^T where A_b is stored [Kd,M].
+// C_b[M,N] = op(A_b)[M,Kd] * op(B_b)[Kd,N], row-major; op(A) = A ([M,Kd]) or,
+// with trans_a, A^T where A_b is stored [Kd,M]; op(B) = B ([Kd,N]) or, with
+// trans_b, B^T where B_b is stored [N,Kd] (not both transposed).
 struct GemmF32Batch {
     const float *a[kMaxK];
     const float *b[kMaxK];
@@ -15,13 +16,14 @@ struct GemmF32Batch {
     int nb;
     long long M, N, Kd;
     int trans_a;
-    // b_rows > 0 (trans_a == 0): B is the same for every entry and given as row
-    // shards, row k in b_shard[k / b_rows] (b ignored); entries with b_copy[i]
-    // set also receive a copy of B there (the gathered matrix). Shapes:
-    // gemm_f32_fusable_gather().
+    // b_rows > 0 (trans_a == 0): the stored B is the same for every entry and
+    // given as row shards, row k in b_shard[k / b_rows] (b ignored); without
+    // trans_b, entries with b_copy[i] set also receive a copy of B there (the
+    // gathered matrix). Shapes: gemm_f32_fusable_gather().
     const float *b_shard[kMaxK];
     long long b_rows;
     float *b_copy[kMaxK];
+    int trans_b;
 };
 hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t stream);
 bool gemm_f32_fusable_gather(const GemmF32Batch &g, int n_shards);
@@ -55,6 +57,7 @@ struct FsdpFwd8 {
     const float *b_shard[8];
     long long b_rows;
     float *b_copy[8];
+    int trans_b;
 };
 struct FsdpBwd8 {
     const float *x[8];
@@ -65,9 +68,11 @@ struct FsdpBwd8 {
     long long m, d, f, R;
 };
 struct FsdpStepParams {
-    FsdpFwd8 fwd;
+    FsdpFwd8 fwd;       // y = x . W, W's rows from the shards, gathered copy written
+    FsdpFwd8 dx;        // dx = dy . W^T, W's rows from the shards (n_dx = 0: none)
     FsdpBwd8 bwd;
     int n_fwd, tiles_x;
+    int n_dx, tiles_x_dx;
 };
 hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t stream);
 

@@ -32,11 +32,12 @@ constexpr int FB = 32;       // block edge
 constexpr int FQ = 16;       // k pairs per chunk of operands
 
 // Block id of the backward half for NTH threads (NTH >= 64 K; waves K.. only
-// join the fold). P is FsdpBwdParams or a struct with the same fields.
+// join the fold). P is FsdpBwdParams or a struct with the same fields. T: the
+// caller's LDS, K blocks of 32x32 floats (rank r's block, element i*32 + j).
 template <int K, int NTH, class P>
-__device__ __forceinline__ void fsdp_bwd_block(const P &p, const long long id)
+__device__ __forceinline__ void fsdp_bwd_block(const P &p, const long long id,
+                                               float (*__restrict__ T)[FB * FB])
 {
-    __shared__ float T[K][FB * FB];          // rank r's block, element i*32 + j
     const int lane = threadIdx.x & 63;
     const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long long nbj = p.f / FB;
@@ -93,21 +94,36 @@ __device__ __forceinline__ void fsdp_bwd_block(const P &p, const long long id)
 template <int K>
 __global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
 {
-    fsdp_bwd_block<K, 64 * K>(p, (long long)blockIdx.x);
+    __shared__ float T[K][FB * FB];
+    fsdp_bwd_block<K, 64 * K>(p, (long long)blockIdx.x, T);
 }
 
 // The whole layer step in one launch: workgroups 0 .. n_fwd-1 are tiles of the
 // forward dot with the AllGather folded in (the 8-wave k-split fp32 tile, W's
-// rows read from the shards, the gathered copy written as it is loaded), the
-// rest are blocks of the backward half. The two halves share no data, so
-// they run side by side on the CUs instead of one after the other.
+// rows read from the shards, the gathered copy written as it is loaded); the
+// next n_dx are tiles of the input gradient dx = dy . W^T (W's rows read from
+// the shards as the columns of W^T); the rest are blocks of the backward
+// weight gradient with its ReduceScatter. The parts share no data, so they run
+// side by side on the CUs instead of one after the other; the ReduceScatter of
+// dW overlaps the dx dot (the FSDP backward overlap). A workgroup runs one
+// part, so the parts share one LDS allocation.
 template <int K>
 __global__ __launch_bounds__(512) void fsdp_step_kernel(const FsdpStepParams p)
 {
-    if ((int)blockIdx.x < p.n_fwd)
-        f32tile::gemm_f32_tile<0, 512, true, true>(p.fwd, p.tiles_x, (int)blockIdx.x);
+    using namespace f32tile;
+    constexpr int kOp = 2 * BK * LDP;                    // floats of one operand's buffers
+    constexpr int kWords = 2 * kOp > K * FB * FB ? 2 * kOp : K * FB * FB;
+    __shared__ __attribute__((aligned(16))) float smem[kWords];
+    auto As = reinterpret_cast<float (*)[BK][LDP]>(smem);
+    auto Bs = reinterpret_cast<float (*)[BK][LDP]>(smem + kOp);
+    const int id = (int)blockIdx.x;
+    if (id < p.n_fwd)
+        gemm_f32_tile<0, 512, true, 1>(p.fwd, p.tiles_x, id, As, Bs);
+    else if (id < p.n_fwd + p.n_dx)
+        gemm_f32_tile<2, 512, true, 2>(p.dx, p.tiles_x_dx, id - p.n_fwd, As, Bs);
     else
-        fsdp_bwd_block<K, 512>(p.bwd, (long long)blockIdx.x - p.n_fwd);
+        fsdp_bwd_block<K, 512>(p.bwd, (long long)id - p.n_fwd - p.n_dx,
+                               reinterpret_cast<float (*)[FB * FB]>(smem));
 }
 
 template <int K>
@@ -155,7 +171,7 @@ hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t st)
     const int k = p.bwd.k;
     if (k < 1 || k > 8 || p.fwd.nb != k || !fsdp_bwd_fusable(k, p.bwd.m, p.bwd.d, p.bwd.f))
         return hipErrorInvalidValue;
-    const long long blocks = (long long)p.n_fwd + (p.bwd.d / FB) * (p.bwd.f / FB);
+    const long long blocks = (long long)p.n_fwd + p.n_dx + (p.bwd.d / FB) * (p.bwd.f / FB);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (k) {
     case 1: return go_step<1>(p, blocks, st);

@@ -43,13 +43,17 @@ static_assert(kDepth >= 2 && kDepth % 2 == 0, "an even number of register stages
 // Stage loader: the 64x32 A and 32x64 B tiles of one stage as 2 x 256 float4
 // each; with NT threads every thread takes 512/NT of them (h = 0, 1 for 256
 // threads; h = threadIdx.x / 256 for 512).
+// TA: bit 0 = A stored [Kd][M] (else [M][Kd]); bit 1 = B stored [N][Kd] (else
+// [Kd][N]). LDS always holds A k-major (As[k][i]) and B k-major (Bs[k][j]).
 template <int TA, int NT>
 struct Stage {
     static constexpr int NH = 512 / NT;
+    static constexpr bool TRA = TA & 1, TRB = (TA & 2) != 0;
     f32x4 a[NH], b[NH];
     long long kb;                       // k0 of the stage held
 
-    // the B tile held, written to rows kb.. of the [Kd][N] matrix W (whole tiles)
+    // the B tile held, written to rows kb.. of the [Kd][N] matrix W (whole
+    // tiles, B not transposed)
     __device__ __forceinline__ void copy_b(float *__restrict__ W, long long N, long long n0) const
     {
         const int t = threadIdx.x & 255;
@@ -64,7 +68,8 @@ struct Stage {
     // WHOLE: every tile is inside the matrices and 16-byte aligned, so all
     // loads are unconditional 16-byte loads (the guarded form, if-converted by
     // the compiler, would issue both forms and wait on all of them)
-    // Bk0: address of row k0 of B (B may be split into row shards).
+    // Bk0: address of row k0 of B, or with B transposed of row n0 (B may be
+    // split into row shards).
     template <bool WHOLE>
     __device__ __forceinline__ void load(const float *__restrict__ A, const float *__restrict__ Bk0,
                                          long long M, long long N, long long Kd, long long m0,
@@ -76,7 +81,7 @@ struct Stage {
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const int h = NH == 2 ? hh : (int)(threadIdx.x >> 8);
-            if (TA == 0) {
+            if (!TRA) {
                 // A stored [M][Kd]: row m0 + t/8 + 32h, k k0 + (t%8)*4 .. +3
                 const long long i = m0 + (t >> 3) + 32 * h, k = k0 + (t & 7) * 4;
                 if (vec_a) {
@@ -95,13 +100,24 @@ struct Stage {
                     for (int e = 0; e < 4; ++e) a[hh][e] = (k < Kd && i + e < M) ? A[k * M + i + e] : 0.0f;
                 }
             }
-            // B stored [Kd][N]: k row k0 + t/16 + 16h, j n0 + (t%16)*4 .. +3
-            const long long kr = (t >> 4) + 16 * h, k = k0 + kr, j = n0 + (t & 15) * 4;
-            if (vec_b) {
-                b[hh] = *reinterpret_cast<const f32x4 *>(Bk0 + kr * N + j);
-            } else {
+            if (TRB) {
+                // B stored [N][Kd]: row n0 + t/8 + 32h, k k0 + (t%8)*4 .. +3
+                const long long jr = (t >> 3) + 32 * h, j = n0 + jr, k = k0 + (t & 7) * 4;
+                if (vec_b) {
+                    b[hh] = *reinterpret_cast<const f32x4 *>(Bk0 + jr * Kd + k);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b[hh][e] = (k < Kd && j + e < N) ? Bk0[kr * N + j + e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) b[hh][e] = (j < N && k + e < Kd) ? Bk0[jr * Kd + k + e] : 0.0f;
+                }
+            } else {
+                // B stored [Kd][N]: k row k0 + t/16 + 16h, j n0 + (t%16)*4 .. +3
+                const long long kr = (t >> 4) + 16 * h, k = k0 + kr, j = n0 + (t & 15) * 4;
+                if (vec_b) {
+                    b[hh] = *reinterpret_cast<const f32x4 *>(Bk0 + kr * N + j);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) b[hh][e] = (k < Kd && j + e < N) ? Bk0[kr * N + j + e] : 0.0f;
+                }
             }
         }
     }
@@ -112,14 +128,20 @@ struct Stage {
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const int h = NH == 2 ? hh : (int)(threadIdx.x >> 8);
-            if (TA == 0) {
+            if (!TRA) {
                 const int i = (t >> 3) + 32 * h, k = (t & 7) * 4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) As[k + e][i] = a[hh][e];
             } else {
                 *reinterpret_cast<f32x4 *>(&As[(t >> 4) + 16 * h][(t & 15) * 4]) = a[hh];
             }
-            *reinterpret_cast<f32x4 *>(&Bs[(t >> 4) + 16 * h][(t & 15) * 4]) = b[hh];
+            if (TRB) {
+                const int j = (t >> 3) + 32 * h, k = (t & 7) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Bs[k + e][j] = b[hh][e];
+            } else {
+                *reinterpret_cast<f32x4 *>(&Bs[(t >> 4) + 16 * h][(t & 15) * 4]) = b[hh];
+            }
         }
     }
 };
@@ -129,16 +151,24 @@ struct Stage {
 // upper half of every 32-deep stage for the same quadrants, and their partial
 // tiles are added to those of waves 0-3 through LDS at the end (a fixed order:
 // lower half + upper half), so twice as many SIMDs run half-length MFMA chains.
-// FUSE (whole tiles, A not transposed): B's rows come from row shards
-// (row k in b_shard[k / b_rows], each k stage inside one shard) and every B
-// tile loaded is also written to b_copy[entry] by one of the tiles that load
-// it, so one launch does the AllGather of the shards and the dot that
-// consumes it.
+// FUSE = 1 (whole tiles, B not transposed): B's rows come from row shards (row
+// k in b_shard[k / b_rows], each k stage inside one shard) and every B tile
+// loaded is also written to b_copy[entry] by one of the tiles that load it, so
+// one launch does the AllGather of the shards and the dot that consumes it.
+// FUSE = 2 (whole tiles, B transposed): B^T's rows (the N dimension) come from
+// row shards (row j in b_shard[j / b_rows], each 64-row tile inside one
+// shard): a dot with the transpose of a row-sharded matrix, without gathering
+// it first.
+// The LDS stage buffers (As, Bs: 2 x BK x LDP floats each) are the caller's, so
+// different tile kinds in one kernel can share them.
 // One tile of C, for workgroup number id of the launch (NT threads). Batch is
 // GemmF32Batch or a struct with the same fields and fewer entries.
-template <int TA, int NT, bool WHOLE, bool FUSE, class Batch>
-__device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x, const int id)
+template <int TA, int NT, bool WHOLE, int FUSE, class Batch>
+__device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x, const int id,
+                                              float (*__restrict__ As)[BK][LDP],
+                                              float (*__restrict__ Bs)[BK][LDP])
 {
+    constexpr bool TRA = TA & 1, TRB = (TA & 2) != 0;
     // 1-D grid, batch entry = id mod nb: with 8 ranks, workgroup ids round-robin
     // over the 8 XCDs put every tile of rank r on XCD r, so a rank's A and B
     // stay in one XCD's L2
@@ -150,9 +180,6 @@ __device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x,
     const long long M = g.M, N = g.N, Kd = g.Kd;
     const long long m0 = (long long)(tile / tiles_x) * BM, n0 = (long long)(tile % tiles_x) * BN;
 
-    __shared__ __attribute__((aligned(16))) float As[2][BK][LDP];   // As[buf][k][i]
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDP];   // Bs[buf][k][j]
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wi = (wave & 3) >> 1, wj = wave & 1;
     constexpr int KSPAN = NT == 512 ? BK / 2 : BK;     // k values of a stage per wave
@@ -160,8 +187,9 @@ __device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x,
     // whole-tile 16-byte loads need the tile inside the matrix, 16-byte aligned
     // base pointers and row lengths that keep every row 16-byte aligned
     const bool rows_a = ((uintptr_t)A & 15) == 0 && m0 + BM <= M &&
-                        (TA == 0 ? (Kd & 3) == 0 : (M & 3) == 0);
-    const bool rows_b = ((uintptr_t)B & 15) == 0 && n0 + BN <= N && (N & 3) == 0;
+                        (!TRA ? (Kd & 3) == 0 : (M & 3) == 0);
+    const bool rows_b = ((uintptr_t)B & 15) == 0 && n0 + BN <= N &&
+                        (TRB ? (Kd & 3) == 0 : (N & 3) == 0);
     const long long stages = (Kd + BK - 1) / BK;
 
     f32x16 acc = {};
@@ -172,10 +200,13 @@ __device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x,
     Stage<TA, NT> r[kDepth];
     auto load = [&](Stage<TA, NT> &st, long long s) {
         const long long k0 = s * BK;
-        const float *Bk0 = B + k0 * N;
-        if (FUSE) {
+        const float *Bk0 = TRB ? B + n0 * Kd : B + k0 * N;
+        if (FUSE == 1) {
             const long long c = k0 / g.b_rows;
             Bk0 = g.b_shard[c] + (k0 - c * g.b_rows) * N;
+        } else if (FUSE == 2) {
+            const long long c = n0 / g.b_rows;
+            Bk0 = g.b_shard[c] + (n0 - c * g.b_rows) * Kd;
         }
         st.template load<WHOLE>(A, Bk0, M, N, Kd, m0, n0, k0, rows_a && k0 + BK <= Kd,
                                 rows_b && k0 + BK <= Kd);
@@ -183,11 +214,11 @@ __device__ __forceinline__ void gemm_f32_tile(const Batch &g, const int tiles_x,
     // the copy of a B tile is written by one of the tiles_y tiles that load
     // it: stage s by the tile in tile row s mod tiles_y, so the extra writes
     // are spread evenly over the tile rows
-    float *__restrict__ Wc = FUSE ? g.b_copy[bz] : nullptr;
+    float *__restrict__ Wc = FUSE == 1 ? g.b_copy[bz] : nullptr;
     const long long tiles_y = (M + BM - 1) / BM, ty = m0 / BM;
     auto put = [&](const Stage<TA, NT> &st, int buf) {
         st.store(As[buf], Bs[buf]);
-        if (FUSE && Wc && (st.kb / BK) % tiles_y == ty) st.copy_b(Wc, N, n0);
+        if (FUSE == 1 && Wc && (st.kb / BK) % tiles_y == ty) st.copy_b(Wc, N, n0);
     };
     auto mma = [&](int buf) {
 #pragma unroll

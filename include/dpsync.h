@@ -191,6 +191,27 @@ dp_status_t dp_fsdp_layer(int k, int64_t m_local, int64_t d, int64_t f,
                           void *stream);
 
 /*
+ * dp_fsdp_layer with the input gradient of the backward pass as well
+ * ("Sharding and Parallelism", section "FSDP and ZeRO": the backward pass
+ * needs the gathered weight for the gradient that flows to the previous layer
+ * while the weight gradient is reduce-scattered):
+ *   dx_local[r] : [m_local, d] = dy_local[r] . W^T (fp32 MFMA), or NULL (then
+ *                 exactly dp_fsdp_layer). Requires dy_local; must be disjoint
+ *                 from every other buffer (DP_ERR_ALIAS).
+ * Where the shapes allow (K <= 8; m_local, d, f multiples of 64; shards of a
+ * multiple of 64 rows; d divisible by K; 16-byte aligned buffers) the whole
+ * step is one launch in which the dx dot, the forward dot and the weight
+ * gradient with its ReduceScatter run side by side; other shapes run separate
+ * launches. The results are the same either way up to the summation order of
+ * the dots (dw_shard is always the ring-order ReduceScatter of dw_full).
+ */
+dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
+                             const float *const *x_local, const float *const *w_shard,
+                             const float *const *dy_local, float *const *w_full,
+                             float *const *y_local, float *const *dx_local,
+                             float *const *dw_full, float *const *dw_shard, void *stream);
+
+/*
  * Dense bf16 GEMM used as the compute side of concurrent computation and
  * communication (the GEMM kernel of a (GEMM, collective) pair, "Optimizing ML
  * Concurrent Computation and Communication with GPU DMA Engines", section

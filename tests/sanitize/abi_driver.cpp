@@ -80,6 +80,10 @@ int main()
     expect(dp_fsdp_layer(0, 8, 8, 8, (const float *const *)a, (const float *const *)b,
                          (const float *const *)c, (float *const *)d, (float *const *)d,
                          (float *const *)d, (float *const *)d, nullptr), DP_ERR_INVALID_ARG, "fsdp k");
+    expect(dp_fsdp_layer_ex(2, 8, 8, 8, (const float *const *)a, (const float *const *)b, nullptr,
+                            (float *const *)c, (float *const *)d, (float *const *)d,
+                            (float *const *)d, (float *const *)d, nullptr),
+           DP_ERR_INVALID_ARG, "fsdp_ex dx without dy");
     expect(dp_gemm_bf16(a[0], b[0], c[0], 0, 8, 8, nullptr), DP_ERR_INVALID_ARG, "gemm m");
     expect(dp_gemm_bf16(a[0], b[0], c[0], 8, 8, 12, nullptr), DP_ERR_UNSUPPORTED, "gemm k");
     expect(dp_gemm_bf16(a[0], b[0], (char *)a[0] + 16, 8, 8, 8, nullptr), DP_ERR_ALIAS, "gemm alias");

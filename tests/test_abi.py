@@ -146,6 +146,15 @@ def test_fsdp_validation():
     assert call(x_=[x[0], 0]) == INVALID
     assert call(y_=[x[0], y[1]]) == ALIAS             # output on top of an input
     assert call(wf_=[wf[0], wf[0] + 4]) == ALIAS      # outputs overlap each other
+    dx = fake(k, 1 << 47)
+
+    def call_ex(dx_=dx, dy_=dy, x_=x):
+        return L.dp_fsdp_layer_ex(k, 8, 8, 8, P(x_), P(ws), P(dy_) if dy_ else None, P(wf), P(y),
+                                  P(dx_) if dx_ else None, P(dwf), P(dws), None)
+    assert call_ex(dy_=None) == INVALID                # dx needs the backward pass
+    assert call_ex(dx_=[dx[0], 0]) == INVALID
+    assert call_ex(dx_=[dx[0], x[1] + 8]) == ALIAS     # dx on top of an input
+    assert call_ex(dx_=[dx[0], dwf[0]]) == ALIAS       # dx on top of another output
 
 
 def test_gemm_validation():

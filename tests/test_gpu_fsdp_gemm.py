@@ -38,7 +38,7 @@ def shard_rows(w, k):
     return out
 
 
-def run_fsdp(x, w, dy, k, backward=True):
+def run_fsdp(x, w, dy, k, backward=True, with_dx=False):
     m, d = x.shape
     f = w.shape[1]
     ml = m // k
@@ -50,21 +50,22 @@ def run_fsdp(x, w, dy, k, backward=True):
     y = [torch.full((ml, f), float("nan"), device=DEV) for _ in range(k)]
     dwf = [torch.full((d, f), float("nan"), device=DEV) for _ in range(k)]
     dws = [torch.full((R, f), float("nan"), device=DEV) for _ in range(k)]
+    dx = [torch.full((ml, d), float("nan"), device=DEV) for _ in range(k)] if with_dx else None
     dps.dp_fsdp_layer(xl, ws, dyl if backward else None, wf, y,
-                      dwf if backward else None, dws if backward else None)
+                      dwf if backward else None, dws if backward else None, dx_local=dx)
     torch.cuda.synchronize()
     host = dict(xl=[to_np(t) for t in xl], ws=[to_np(t) for t in ws],
                 dyl=[to_np(t) for t in dyl])
     return dict(wf=[to_np(t) for t in wf], y=[to_np(t) for t in y], dwf=[to_np(t) for t in dwf],
-                dws=[to_np(t) for t in dws]), host
+                dws=[to_np(t) for t in dws], dx=[to_np(t) for t in dx] if with_dx else None), host
 
 
-def check_fsdp(x, w, dy, k, exact=False):
+def check_fsdp(x, w, dy, k, exact=False, with_dx=False):
     m, d = x.shape
     f = w.shape[1]
     ml = m // k
     R = -(-d // k)
-    got, host = run_fsdp(x, w, dy, k)
+    got, host = run_fsdp(x, w, dy, k, with_dx=with_dx)
     want = oracle.fsdp_layer(host["xl"], host["ws"], host["dyl"], d=d, nthreads=8)
     wn, xn, dyn = w.numpy(), x.numpy(), dy.numpy()
     for r in range(k):
@@ -102,6 +103,16 @@ def check_fsdp(x, w, dy, k, exact=False):
     rs = oracle.reduce_scatter([g.ravel() for g in got["dwf"]], op="sum", L=R * f)
     for c in range(k):
         assert bits_equal(got["dws"][c].ravel(), rs[c])
+    # dx_r = dy_r W^T (the gathered W, from the oracle), within the summation bound
+    if with_dx:
+        wt = np.ascontiguousarray(want["w_full"][0].T)
+        for r in range(k):
+            ref, ab = oracle.gemm_f64(host["dyl"][r], wt)
+            if exact:
+                assert bits_equal(got["dx"][r], ref.astype(np.float32))
+            else:
+                err = np.abs(got["dx"][r].astype(np.float64) - ref)
+                assert np.all(err <= gamma(f + 2) * ab), float((err / (ab + 1e-300)).max())
     # global view: concatenated y is x @ w (normwise)
     ycat = np.concatenate(got["y"]).astype(np.float64)
     ref = xn.astype(np.float64) @ wn.astype(np.float64)
@@ -116,6 +127,8 @@ def test_fsdp_fixture_k8():
     say("fsdp fixture k=8")
     fx = gen.fsdp_fixture(seed=2, k=8)
     check_fsdp(fx["x"], fx["w"], fx["dy"], 8)
+    say("fsdp fixture k=8 with dx")
+    check_fsdp(fx["x"], fx["w"], fx["dy"], 8, with_dx=True)
 
 
 def test_fsdp_integer_values_exact():
@@ -125,6 +138,7 @@ def test_fsdp_integer_values_exact():
     w = torch.randint(-4, 5, (512, 512), generator=g).float()
     dy = torch.randint(-4, 5, (1024, 512), generator=g).float()
     check_fsdp(x, w, dy, 8, exact=True)
+    check_fsdp(x, w, dy, 8, exact=True, with_dx=True)
 
 
 @pytest.mark.parametrize("k,m,d,f", [(3, 111, 45, 29), (8, 64, 100, 70), (1, 5, 3, 2),
@@ -145,10 +159,11 @@ def test_fsdp_ragged_shapes(k, m, d, f):
     w = torch.randn(d, f, generator=g) * 0.02
     dy = torch.randn(m, f, generator=g)
     check_fsdp(x, w, dy, k)
+    check_fsdp(x, w, dy, k, with_dx=True)
     xi = torch.randint(-3, 4, (m, d), generator=g).float()
     wi = torch.randint(-3, 4, (d, f), generator=g).float()
     dyi = torch.randint(-3, 4, (m, f), generator=g).float()
-    check_fsdp(xi, wi, dyi, k, exact=True)
+    check_fsdp(xi, wi, dyi, k, exact=True, with_dx=True)
 
 
 def test_fsdp_forward_only():
