@@ -519,10 +519,19 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
     dp_status_t s;
     const bool fwd_fused = dps::gemm_f32_fusable_gather(g, k);
     const bool dx_fused = want_dx && dps::gemm_f32_fusable_gather(gx, k);
-    const int64_t n_fwd = (m_local / 64) * (f / 64) * k;
+    // forward blocks of the one-launch step: 32x32 without dx, 64x64 tiles with it
+    const int64_t n_fwd = want_dx ? (m_local / 64) * (f / 64) * k : (m_local / 32) * (f / 32) * k;
     const int64_t n_dx = want_dx ? (m_local / 64) * (d / 64) * k : 0;
+    dps::FsdpFwd8 fw8;
+    memset(&fw8, 0, sizeof(fw8));
+    fw8.nb = k;
+    fw8.M = m_local;
+    fw8.N = f;
+    fw8.Kd = d;
+    fw8.b_rows = R;
     if (fwd_fused && bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
-        (!want_dx || dx_fused) && n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
+        (want_dx ? dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
+        n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
         // the whole step in one launch: forward tiles (AllGather folded into
         // the dot) beside backward blocks (ReduceScatter folded into the dW
         // kernel); the two halves share no data
@@ -548,7 +557,7 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
         p.bwd.d = d;
         p.bwd.f = f;
         p.bwd.R = R;
-        p.tiles_x = (int)(f / 64);
+        p.tiles_x = (int)(want_dx ? f / 64 : f / 32);
         p.n_fwd = (int)n_fwd;
         if (want_dx) {
             for (int r = 0; r < k; ++r) {

@@ -75,6 +75,10 @@ struct FsdpStepParams {
     int n_dx, tiles_x_dx;
 };
 hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t stream);
+// the step kernel's forward blocks (32x32, x block in LDS, W from the shards):
+// fwd.M, fwd.N multiples of 32, fwd.Kd 256 or 512, shards
+// of a multiple of 32 rows
+bool fsdp_fwd_direct_ok(const FsdpFwd8 &p);
 
 // bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
 // GEMM variants: kGemmFast = the 4-wave kernel (every register of each SIMD)

@@ -91,6 +91,105 @@ __device__ __forceinline__ void fsdp_bwd_block(const P &p, const long long id,
     }
 }
 
+// Forward block with the AllGather folded in: one workgroup (8 waves) computes a
+// 32x32 block (rows i0.., columns j0..) of y_r = x_r . W. The block's 32 rows of
+// x_r are loaded into LDS once, k-major (Xs[k][i], odd row pitch: the 4-byte
+// stores of consecutive k and the reads of 32 consecutive i are free of bank
+// conflicts); wave w then runs the MFMA chain over its eighth of the k range
+// with the B operand read straight from W's row shards into registers (lanes
+// 0-31 and 32-63 read 128-byte row pieces of W, the 32x32x2 operand layout),
+// and the eight partial blocks are added through LDS in wave order. There is
+// no k-stage loop, so no per-stage barrier and LDS round trip. Wave w of block
+// row it also writes the W rows it loaded to the gathered copy w_full[r] when
+// w mod (m/32) == it, so every W element is written once per rank.
+constexpr int XP = FB + 1;   // LDS row pitch of the x block (floats)
+
+template <class P>
+__device__ __forceinline__ void fsdp_fwd_block(const P &p, const int id, float *__restrict__ smem)
+{
+    const int K = p.nb;
+    const int r = id % K;                     // with K = 8 a rank's blocks share an XCD
+    const long long t = id / K;
+    const long long nbj = p.N / FB, nbi = p.M / FB;
+    const long long it = t / nbj, i0 = it * FB, j0 = (t % nbj) * FB;
+    const long long Kd = p.Kd, N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long kh = lane >> 5, col = lane & 31;
+
+    // x_r[i0 .. i0+31][0 .. Kd-1] -> Xs[k][i]: thread k loads column k of the
+    // block (Kd <= 512 threads), each row read by the workgroup as one
+    // coalesced 4-byte-per-lane sweep
+    // (buffer loads: one per-lane offset register, the row offset scalar)
+    if (threadIdx.x < Kd) {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.a[r] + i0 * Kd), (short)0, 0x7fffffff, 0x00020000);
+        const int vo = (int)threadIdx.x * 4;
+#pragma unroll
+        for (int h = 0; h < FB; h += 16) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, vo, (int)((h + i) * Kd * 4), 0));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) smem[threadIdx.x * XP + h + i] = v[i];
+        }
+    }
+    __syncthreads();
+
+    const long long span = Kd / 8, kb = w * span;
+    float *__restrict__ wc = (w % nbi) == it ? p.b_copy[r] : nullptr;
+    f32x16 acc = {};
+    for (long long c0 = kb; c0 < kb + span; c0 += 2 * FQ) {
+        // the chunk's 32 rows of W lie in one shard (R is a multiple of 32)
+        const long long sh = c0 / p.b_rows;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.b_shard[sh] + (c0 - sh * p.b_rows) * N + j0), (short)0, 0x7fffffff, 0x00020000);
+        const int vo = (int)((kh * N + col) * 4);
+        float b[FQ];
+#pragma unroll
+        for (int q = 0; q < FQ; ++q)
+            b[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, vo, (int)(2 * q * N * 4), 0));
+        __builtin_amdgcn_sched_barrier(0);
+        if (wc) {
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(wc + c0 * N + j0), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int q = 0; q < FQ; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, b[q]), rc, vo, (int)(2 * q * N * 4), 0);
+        }
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) {
+            const float a = smem[(c0 + 2 * q + kh) * XP + col];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[q], acc, 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    // partial blocks of the 8 waves, added in wave order
+#pragma unroll
+    for (int q = 0; q < 16; ++q) smem[(w * 16 + q) * 64 + lane] = acc[q];
+    __syncthreads();
+    float *__restrict__ y = p.c[r];
+    for (int e = threadIdx.x; e < 16 * 64; e += 512) {
+        const int q = e >> 6, l = e & 63;
+        float s = smem[q * 64 + l];
+#pragma unroll
+        for (int v = 1; v < 8; ++v) s = s + smem[(v * 16 + q) * 64 + l];
+        const int i = 8 * (q >> 2) + 4 * (l >> 5) + (q & 3), j = l & 31;
+        y[(i0 + i) * N + j0 + j] = s;
+    }
+}
+
+template <class P>
+bool fwd_direct_ok(const P &p)
+{
+    // whole 32x32 blocks, k split in 8 waves of whole 32-deep chunks, each chunk
+    // inside one shard, and one thread per k for the x block (Kd <= 512, which
+    // also keeps the block's LDS at 66 KiB: two workgroups per CU)
+    return p.M % FB == 0 && p.N % FB == 0 && p.Kd % (8 * 2 * FQ) == 0 && p.Kd <= 512 &&
+           p.b_rows % (2 * FQ) == 0 && p.N <= (1 << 20);   // buffer offsets in 31 bits
+}
+
 template <int K>
 __global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
 {
@@ -98,32 +197,45 @@ __global__ __launch_bounds__(64 * K) void fsdp_bwd_kernel(const FsdpBwdParams p)
     fsdp_bwd_block<K, 64 * K>(p, (long long)blockIdx.x, T);
 }
 
-// The whole layer step in one launch: workgroups 0 .. n_fwd-1 are tiles of the
-// forward dot with the AllGather folded in (the 8-wave k-split fp32 tile, W's
-// rows read from the shards, the gathered copy written as it is loaded); the
-// next n_dx are tiles of the input gradient dx = dy . W^T (W's rows read from
-// the shards as the columns of W^T); the rest are blocks of the backward
-// weight gradient with its ReduceScatter. The parts share no data, so they run
+// The whole layer step in one launch, three kinds of workgroups: tiles of the
+// input gradient dx = dy . W^T (W's rows read from the shards as the columns
+// of W^T; n_dx of them, none without dx), blocks of the backward weight
+// gradient with its ReduceScatter, and 32x32 blocks of the forward dot with
+// the AllGather folded in (fsdp_fwd_block: W's rows read from the shards, the
+// gathered copy written as it is loaded; n_fwd of them). The parts share no data, so they run
 // side by side on the CUs instead of one after the other; the ReduceScatter of
 // dW overlaps the dx dot (the FSDP backward overlap). A workgroup runs one
 // part, so the parts share one LDS allocation.
-template <int K>
+// DX: with the dx tiles. Their 16 dependent k stages are then the long pole,
+// and the forward runs as the same 64x64 k-stage tiles (34 KiB of LDS, so
+// more workgroups fit beside the dx tiles); without dx, the forward runs as
+// fsdp_fwd_block (66 KiB: the x block in LDS, no k-stage loop), which is
+// shorter alone (22.8 against 26.2 us for the step; with dx 26.5 against 29.0
+// the other way round).
+template <int K, bool DX>
 __global__ __launch_bounds__(512) void fsdp_step_kernel(const FsdpStepParams p)
 {
     using namespace f32tile;
     constexpr int kOp = 2 * BK * LDP;                    // floats of one operand's buffers
-    constexpr int kWords = 2 * kOp > K * FB * FB ? 2 * kOp : K * FB * FB;
+    constexpr int kA = 2 * kOp > K * FB * FB ? 2 * kOp : K * FB * FB;
+    constexpr int kWords = DX ? kA : (kA > 512 * XP ? kA : 512 * XP);
     __shared__ __attribute__((aligned(16))) float smem[kWords];
     auto As = reinterpret_cast<float (*)[BK][LDP]>(smem);
     auto Bs = reinterpret_cast<float (*)[BK][LDP]>(smem + kOp);
+    // longest parts first, so the workgroup dispatcher starts them first and
+    // the short forward blocks fill in behind them: the dx tiles (16 dependent
+    // k stages each), the backward blocks, then the forward blocks
     const int id = (int)blockIdx.x;
-    if (id < p.n_fwd)
-        gemm_f32_tile<0, 512, true, 1>(p.fwd, p.tiles_x, id, As, Bs);
-    else if (id < p.n_fwd + p.n_dx)
-        gemm_f32_tile<2, 512, true, 2>(p.dx, p.tiles_x_dx, id - p.n_fwd, As, Bs);
-    else
-        fsdp_bwd_block<K, 512>(p.bwd, (long long)id - p.n_fwd - p.n_dx,
+    const int n_bwd = (int)((p.bwd.d / FB) * (p.bwd.f / FB));
+    if (id < p.n_dx)
+        gemm_f32_tile<2, 512, true, 2>(p.dx, p.tiles_x_dx, id, As, Bs);
+    else if (id < p.n_dx + n_bwd)
+        fsdp_bwd_block<K, 512>(p.bwd, (long long)id - p.n_dx,
                                reinterpret_cast<float (*)[FB * FB]>(smem));
+    else if (DX)
+        gemm_f32_tile<0, 512, true, 1>(p.fwd, p.tiles_x, id - p.n_dx - n_bwd, As, Bs);
+    else
+        fsdp_fwd_block(p.fwd, id - p.n_dx - n_bwd, smem);
 }
 
 template <int K>
@@ -137,11 +249,16 @@ hipError_t go(const FsdpBwdParams &p, hipStream_t st)
 template <int K>
 hipError_t go_step(const FsdpStepParams &p, long long blocks, hipStream_t st)
 {
-    hipLaunchKernelGGL((fsdp_step_kernel<K>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+    if (p.n_dx > 0)
+        hipLaunchKernelGGL((fsdp_step_kernel<K, true>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+    else
+        hipLaunchKernelGGL((fsdp_step_kernel<K, false>), dim3((unsigned)blocks), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool fsdp_fwd_direct_ok(const FsdpFwd8 &p) { return fwd_direct_ok(p); }
 
 bool fsdp_bwd_fusable(int k, long long m, long long d, long long f)
 {
@@ -170,6 +287,11 @@ hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t st)
 {
     const int k = p.bwd.k;
     if (k < 1 || k > 8 || p.fwd.nb != k || !fsdp_bwd_fusable(k, p.bwd.m, p.bwd.d, p.bwd.f))
+        return hipErrorInvalidValue;
+    // forward as 32x32 blocks without dx, as 64x64 tiles with it
+    if (p.n_dx > 0 ? p.n_fwd != (p.fwd.M / 64) * (p.fwd.N / 64) * k || p.tiles_x != p.fwd.N / 64
+                   : !fwd_direct_ok(p.fwd) || p.n_fwd != (p.fwd.M / FB) * (p.fwd.N / FB) * k ||
+                         p.tiles_x != p.fwd.N / FB)
         return hipErrorInvalidValue;
     const long long blocks = (long long)p.n_fwd + p.n_dx + (p.bwd.d / FB) * (p.bwd.f / FB);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
