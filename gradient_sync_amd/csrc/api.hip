@@ -529,8 +529,10 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
     fw8.N = f;
     fw8.Kd = d;
     fw8.b_rows = R;
-    if (fwd_fused && bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
-        (want_dx ? dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
+    // the one-launch step: without dx its forward part is the 32x32 direct block,
+    // with dx the 64x64 k-stage tile (beside the dx tiles)
+    if (bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
+        (want_dx ? fwd_fused && dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
         n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
         // the whole step in one launch: forward tiles (AllGather folded into
         // the dot) beside backward blocks (ReduceScatter folded into the dW

@@ -145,14 +145,18 @@ def test_fsdp_integer_values_exact():
                                      (5, 5 * 33, 64, 130), (2, 256, 96, 64),
                                      (4, 4 * 64, 256, 96), (7, 7 * 32, 7 * 32, 64),
                                      (8, 8 * 32, 512, 32), (2, 256, 128, 128),
-                                     (4, 4 * 64, 256, 64), (8, 8 * 64, 256, 128)])
+                                     (4, 4 * 64, 256, 64), (8, 8 * 64, 256, 128),
+                                     (1, 64, 256, 64), (2, 64, 512, 96), (4, 128, 256, 32)])
 def test_fsdp_ragged_shapes(k, m, d, f):
     """The first five shapes take the separate launches (AllGather, GEMM, GEMM,
     ReduceScatter). The next three take the fused backward kernel (whole 32x32
     blocks, shards of a multiple of 32 rows, m_local a multiple of 32) with
-    K = 4, 7 and 8; the last three also the fused forward (whole 64x64 tiles,
+    K = 4, 7 and 8; the next three also the fused forward (whole 64x64 tiles,
     d a multiple of 64, shards of a multiple of 32 rows: the AllGather folded
-    into the GEMM's operand loads)."""
+    into the GEMM's operand loads); (4, 256, 256, 64), (8, 512, 256, 128) and
+    the last three (K = 1, 2, 4; d of 256 or 512) run the whole step in one
+    launch (with dx only where m_local is a multiple of 64: the last two take
+    the separate launches then)."""
     say(f"fsdp ragged k={k} m={m} d={d} f={f}")
     g = torch.Generator().manual_seed(k * m + d)
     x = torch.randn(m, d, generator=g)
