@@ -225,25 +225,26 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
 
-    // Staging: 16 registers of 16 bytes per lane; st[h] holds A row lr + 32h and
-    // st[8 + h] B row lr + 32h, at k chunk lk, of one stage. Byte offsets inside
-    // the tile's rows fit 31 bits (checked by the launcher).
+    // Staging: two sets of 16 registers of 16 bytes per lane; st[t][h] holds A
+    // row lr + 32h and st[t][8 + h] B row lr + 32h, at k chunk lk, of one
+    // stage. Byte offsets inside the tile's rows fit 31 bits (checked by the
+    // launcher).
     const int lr = tid / W4_CH, lk = (tid % W4_CH) * 8;
     const unsigned voff = (unsigned)((lr * Kd + lk) * 2);
     const __amdgpu_buffer_rsrc_t rA =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * Kd), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rB =
         __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * Kd), (short)0, 0x7fffffff, 0x00020000);
-    u32x4 st[2 * W4_HP];
-    auto gload1 = [&](int j, int k0) {
+    u32x4 st[2][2 * W4_HP];
+    auto gload1 = [&](int t, int j, int k0) __attribute__((always_inline)) {
         const int so = (W4_RPP * (j % W4_HP) * Kd + k0) * 2;
-        st[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              j < W4_HP ? rA : rB, voff, so, 0));
+        st[t][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 j < W4_HP ? rA : rB, voff, so, 0));
     };
-    auto sstore1 = [&](int buf, int j) {
+    auto sstore1 = [&](int t, int buf, int j) __attribute__((always_inline)) {
         unsigned short *row = j < W4_HP ? &As[buf][lr + W4_RPP * (j % W4_HP)][lk]
                                         : &Bs[buf][lr + W4_RPP * (j % W4_HP)][lk];
-        *reinterpret_cast<u32x4 *>(row) = st[j];
+        *reinterpret_cast<u32x4 *>(row) = st[t][j];
     };
 
     f32x16 acc[W4_B][W4_B];
@@ -255,16 +256,19 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
     // two fragment sets: k step ks computes from set ks & 1 while the next
     // step's fragments arrive in the other
     bf16x8 av[2][W4_B], bv[2][W4_B];
-    auto rd = [&](int set, int buf, int ks, int x) {
+    auto rd = [&](int set, int buf, int ks, int x) __attribute__((always_inline)) {
         const int r = lane & 31, kc = ks * 16 + 8 * (lane >> 5);
         av[set][x] = *reinterpret_cast<const bf16x8 *>(&As[buf][wi * 128 + x * 32 + r][kc]);
         bv[set][x] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * 128 + x * 32 + r][kc]);
     };
 
     // One stage from LDS buffer buf: 16 groups of 4 MFMAs (k step ks, A block a);
-    // group j also reads fragment pair a of step ks+1, stores staging register j
-    // (the next stage) into the idle buffer and reloads it from k offset kload.
-    auto stage = [&](int buf, int kload) {
+    // group j also reads fragment pair a of step ks+1, stores staging register
+    // st[buf][j] (the next stage, loaded two stages ago) into the idle buffer
+    // and reloads it from k offset kload (three stages ahead). Called with
+    // literal arguments only, so every register and LDS index is fixed at
+    // compile time; io = false (an odd last stage) leaves the staging alone.
+    auto stage = [&](int buf, int kload, bool io) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < W4_B; ++x) rd(0, buf, 0, x);
         W4_FENCE();
@@ -274,8 +278,10 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
             for (int a = 0; a < W4_B; ++a) {
                 const int j = ks * W4_B + a;
                 if (ks + 1 < W4_KS) rd((ks + 1) & 1, buf, ks + 1, a);
-                sstore1(buf ^ 1, j);
-                gload1(j, kload);
+                if (io) {
+                    sstore1(buf, buf ^ 1, j);
+                    gload1(buf, j, kload);
+                }
 #pragma unroll
                 for (int b = 0; b < W4_B; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][a], bv[ks & 1][b],
@@ -285,24 +291,30 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
         }
     };
 
+    // Stage s computes from LDS buffer s & 1. Before it, stage s+1 sits in
+    // staging set s & 1 and stage s+2 in the other set (or, for s = 0, stage 1
+    // in set 0 and stage 2 in set 1). Past the end the loads repeat the last
+    // stage and the stores land in a buffer that is never read again, so the
+    // loop body has no branch.
     const int stages = Kd / W4_TK;
+    const int last = (stages - 1) * W4_TK;
 #pragma unroll
-    for (int j = 0; j < 2 * W4_HP; ++j) gload1(j, 0);
+    for (int j = 0; j < 2 * W4_HP; ++j) gload1(0, j, 0);
 #pragma unroll
-    for (int j = 0; j < 2 * W4_HP; ++j) sstore1(0, j);
+    for (int j = 0; j < 2 * W4_HP; ++j) sstore1(0, 0, j);
 #pragma unroll
-    for (int j = 0; j < 2 * W4_HP; ++j) gload1(j, min(1, stages - 1) * W4_TK);
+    for (int j = 0; j < 2 * W4_HP; ++j) gload1(0, j, min(W4_TK, last));
+#pragma unroll
+    for (int j = 0; j < 2 * W4_HP; ++j) gload1(1, j, min(2 * W4_TK, last));
     __syncthreads();
-    int buf = 0;
-    for (int s = 0; s < stages; ++s) {
-        // Stage s+1 (staged during stage s-1) goes to the idle buffer, which
-        // every wave finished reading before the last barrier; stage s+2 is
-        // loaded. Past the end the loads repeat the last stage and the stores
-        // land in a buffer that is never read again, so the loop has no branch.
-        stage(buf, min(s + 2, stages - 1) * W4_TK);
+    int s = 0;
+    for (; s + 2 <= stages; s += 2) {
+        stage(0, min((s + 3) * W4_TK, last), true);
         __syncthreads();
-        buf ^= 1;
+        stage(1, min((s + 4) * W4_TK, last), true);
+        __syncthreads();
     }
+    if (s < stages) stage(0, 0, false);
 #pragma unroll
     for (int a = 0; a < W4_B; ++a)
 #pragma unroll
