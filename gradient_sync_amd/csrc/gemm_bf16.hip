@@ -21,10 +21,12 @@
 //   nothing hides an LDS wait, so the stage is software-pipelined by hand: the
 //   fragments of the next k step are read while the current step's MFMAs run
 //   (two fragment register sets), and each of the 16 groups of 4 MFMAs also
-//   carries one 16-byte LDS store of the next stage and one global load of the
-//   stage after it (scheduling fences keep that interleave). Global loads use a
-//   buffer descriptor on the tile's first row, so their addresses are one
-//   per-lane offset register plus a scalar offset.
+//   carries one 16-byte LDS store of the next stage and one global load three
+//   stages ahead (scheduling fences keep that interleave). The loads alternate
+//   between two staging register sets, so each has two stages to arrive before
+//   its LDS store needs it. Global loads use a buffer descriptor on the tile's
+//   first row, so their addresses are one per-lane offset register plus a
+//   scalar offset.
 //
 // * gemm_bf16_kernel: 8 waves arranged 2 (rows) x 4 (columns), each wave
 //   128x64 = 4x2 MFMA blocks (128 fp32 accumulators per lane), k stages of TK
