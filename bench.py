@@ -48,11 +48,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "246aadf3cde199b205fe85c310f2f046586f823a0d93e58d5561f63ab48e5373"
+    "sources_sha256": "804cb57e572f410273a24d214ecdd6ea09811efdc83651e55170937f4a6ac14b"
                       "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49740.1) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 24809.4 + 390833.5) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220219.2 + 440396.5) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49740.7) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 24807.4 + 390827.2) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220224.1 + 440387.1) * 1024,
 }
 
 

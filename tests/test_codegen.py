@@ -60,7 +60,7 @@ def test_no_scratch(kernels):
 
 
 def test_sync_kernels_use_16_byte_accesses(kernels):
-    for parts in (("rs_kernelILi1ELi1ELi8ELi2ELb0",), ("rs_kernelILi1ELi1ELi8ELi2ELb1",),
+    for parts in (("rs_kernelILi1ELi1ELi8ELi2ELb0",), ("rs_kernelILi1ELi1ELi8ELi1ELb1",),
                   ("ag_kernelILi2ELi8ELi2",), ("rsag_kernelILi1ELi1ELi8",),
                   ("scatter_accumulate_kernelILi1",)):
         for name, (_, body) in pick(kernels, *parts).items():
