@@ -423,6 +423,37 @@ def bench_fused_ar(args):
             "config": {"workload": "K=8, 218,103,808 bf16 per rank, 9 buckets of <=25,000,000"}}
 
 
+def _hip_runtime():
+    """The HIP runtime torch already loaded (stream calls torch does not wrap)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy.restype = ctypes.c_int
+    hip.hipGetErrorString.argtypes = [ctypes.c_int]
+    hip.hipGetErrorString.restype = ctypes.c_char_p
+    return hip
+
+
+def _cu_masked_stream(hip, first_cu, last_cu, n_cus):
+    """A stream (default priority) whose kernels run only on mask bits
+    [first_cu, last_cu). Mask bits go round-robin over the XCDs on this GPU,
+    so a contiguous range gives every XCD the same number of CUs, which the
+    driver requires of a mask. Returns the raw handle; raises on failure."""
+    import ctypes
+    words = (n_cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for b in range(first_cu, last_cu):
+        mask[b // 32] |= 1 << (b % 32)
+    st = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(st), words, mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask: {hip.hipGetErrorString(rc).decode()}")
+    return st
+
+
 def bench_c3(args):
     import torch
 
@@ -451,16 +482,17 @@ def bench_c3(args):
             dps.dp_gemm_bf16_ex(a, b, c, share_cu=share, stream=stream)
         return gemm
 
-    def concurrent(comm, gemm, first):
+    def concurrent(comm, gemm, first, streams=None):
+        sa_, sb_ = streams if streams else (sa, sb)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         ea = torch.cuda.Event(enable_timing=True)
         eb = torch.cuda.Event(enable_timing=True)
         cur = torch.cuda.current_stream()
         start.record(cur)
-        sa.wait_event(start)
-        sb.wait_event(start)
-        order = [(comm, sa, ea), (gemm, sb, eb)] if first == "comm" else [(gemm, sb, eb), (comm, sa, ea)]
+        sa_.wait_event(start)
+        sb_.wait_event(start)
+        order = [(comm, sa_, ea), (gemm, sb_, eb)] if first == "comm" else [(gemm, sb_, eb), (comm, sa_, ea)]
         for fn, st, ev in order:
             fn(stream=st)
             ev.record(st)
@@ -470,7 +502,8 @@ def bench_c3(args):
     # Schedules: c3_base = default grids, GEMM launched first; sp = the
     # collective launched first (schedule prioritisation) with its resident
     # workgroups capped so the GEMM still gets CUs; share = one persistent sync
-    # workgroup per CU beside one GEMM workgroup of the smaller-register variant.
+    # workgroup per CU beside one GEMM workgroup of the smaller-register variant;
+    # rp (below) = the collective and the GEMM on disjoint CU-masked streams.
     schedules = [("base", 0, False, "gemm"), ("base_comm_first", 0, False, "comm"),
                  ("sp_cap256", 256, False, "comm"), ("sp_cap128", 128, False, "comm"),
                  ("share_cu", 256, True, "comm"), ("share_cu_gemm_first", 256, True, "gemm")]
@@ -495,10 +528,47 @@ def bench_c3(args):
                      "S_ideal": round(s_ideal, 4), "S_over_S_ideal": round(s / s_ideal, 4),
                      "pct_of_ideal_gain": round(100 * (s - 1) / (s_ideal - 1), 1)
                      if s_ideal > 1 else None}
+    # RP (resource partitioning): the collective on a CU-masked stream holding
+    # CUs [0, n_comm) of the mask, the GEMM on one holding the rest. T_comm and
+    # T_gemm are the same kernels alone on the same masked streams.
+    hip = _hip_runtime()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n_comm in (128, 160, 192):
+        name = f"rp_comm{n_comm}"
+        raw = []
+        try:
+            raw.append(_cu_masked_stream(hip, 0, n_comm, n_cus))
+            raw.append(_cu_masked_stream(hip, n_comm, n_cus, n_cus))
+        except RuntimeError as e:
+            res[name] = {"error": str(e)}
+            torch.cuda.synchronize()
+            for st in raw:
+                hip.hipStreamDestroy(st)
+            continue
+        sc, sg = (torch.cuda.ExternalStream(st.value) for st in raw)
+        comm, gemm = make_comm(0), make_gemm(False)
+        t_comm = statistics.median(_time_ms(lambda: comm(stream=sc), stream=sc))
+        t_gemm = statistics.median(_time_ms(lambda: gemm(stream=sg), stream=sg))
+        for _ in range(6):
+            concurrent(comm, gemm, "gemm", streams=(sc, sg))
+        tc = statistics.median([concurrent(comm, gemm, "gemm", streams=(sc, sg)) for _ in range(9)])
+        torch.cuda.synchronize()
+        for st in raw:
+            hip.hipStreamDestroy(st)
+        s_ = (t_comm + t_gemm) / tc
+        s_ideal = (t_comm + t_gemm) / max(t_comm, t_gemm)
+        log(f"[c3] {name}: T_comm {t_comm:.3f} T_gemm {t_gemm:.3f} T_conc {tc:.3f} S {s_:.3f}")
+        res[name] = {"comm_cus": n_comm, "gemm_cus": n_cus - n_comm, "first": "gemm",
+                     "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
+                     "t_concurrent_ms": round(tc, 4), "S": round(s_, 4),
+                     "S_ideal": round(s_ideal, 4), "S_over_S_ideal": round(s_ / s_ideal, 4),
+                     "pct_of_ideal_gain": round(100 * (s_ - 1) / (s_ideal - 1), 1)
+                     if s_ideal > 1 else None}
     best_serial = min(v for (_, kind), v in iso.items() if kind == "comm") + \
         min(v for (_, kind), v in iso.items() if kind == "gemm")
     for v in res.values():
-        v["S_vs_best_serial"] = round(best_serial / v["t_concurrent_ms"], 4)
+        if "t_concurrent_ms" in v:
+            v["S_vs_best_serial"] = round(best_serial / v["t_concurrent_ms"], 4)
     t_comm0, t_gemm0 = iso[(0, "comm")], iso[(False, "gemm")]
     return {"metric": "C3: RS+AG (K=8, 1 GiB/rank fp32) concurrent with bf16 GEMM 8192^3",
             "t_comm_ms": round(t_comm0, 4), "t_gemm_ms": round(t_gemm0, 4),
