@@ -10,11 +10,14 @@ carried as numpy uint16 bit patterns. ring_sim.py is a second, literal
 message-passing model of the ring used to pin the closed-form fold order.
 
 Pins that tie this code to the pages and to mathematics (not to itself) are in
-tests/test_oracle_pins.py. Parity unpinned: the choices the pages leave open
-(which rank owns which chunk, the fp32 fold order, the pad value, bf16
-rounding, no fused multiply-add in the weighted fold, documents per rank in
-the token-count recipe) are fixed by the written readings that both sides
-follow independently; the pages cannot arbitrate them.
+tests/test_oracle_pins.py; every function here has at least one. Some
+choices are readings rather than facts the pages fix (which rank owns which
+chunk, and with it the fp32 fold order; the pad value; bf16 rounding; no
+fused multiply-add in the weighted fold; documents per rank in the
+token-count recipe). The pins check that the oracle computes each reading
+correctly (the literal ring adds in the closed-form order once rank c owns
+chunk c; bf16 rounding equals torch's conversion), but no pin can show that
+the pages meant that reading rather than another.
 """
 from __future__ import annotations
 
