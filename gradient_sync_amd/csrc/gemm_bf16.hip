@@ -13,7 +13,7 @@
 // Two designs over a 256x256 tile of C:
 //
 // * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
-//   multiple of 64 and at least 2048): 4 waves, one per SIMD, each owning a 128x128 quarter (4x4 MFMA
+//   multiple of 64 and at least 1024): 4 waves, one per SIMD, each owning a 128x128 quarter (4x4 MFMA
 //   blocks, 256 fp32 accumulators per lane held in the accumulation registers).
 //   A 128x128 wave tile reads 8 fragments from LDS per 16 MFMAs, against 6
 //   per 8 for a 128x64 wave tile, so the LDS read traffic per flop drops by a
@@ -206,7 +206,7 @@ constexpr int W4_RPP = W4_NT / W4_CH;       // rows loaded per pass (32)
 constexpr int W4_HP = TM / W4_RPP;          // passes per operand tile (8)
 constexpr int W4_KS = W4_TK / 16;           // MFMA k steps per stage (4)
 constexpr int W4_B = 4;                     // 32x32 MFMA blocks per wave side (128 = 4 x 32)
-constexpr long long kW4MinK = 2048;         // shortest k range given to the 4-wave kernel
+constexpr long long kW4MinK = 1024;         // shortest k range given to the 4-wave kernel
 static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of MFMAs");
 
 // keeps the compiler's scheduler from moving instructions across it, so the
@@ -356,8 +356,8 @@ hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, 
     // (512 * Kd) within its buffer descriptor's 31-bit range, and a k range long
     // enough that the main loop outweighs the per-tile prologue and epilogue,
     // which one wave per SIMD cannot overlap with another workgroup's MFMAs
-    // (measured: 1.19x the 8-wave kernel at 8192^3, 1.00x at kk = 1024, 0.8x at
-    // kk = 256)
+    // (measured: 1.2x the 8-wave kernel at 8192^3, 1.08x at kk = 1536,
+    // 1.02-1.07x at kk = 1024, 0.93x at kk = 512, 0.8x at kk = 256)
     const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
                     Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL;
     if (w4) {

@@ -225,7 +225,7 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
  *   (DP_ERR_ALIAS).
  *   The products are summed over k in ascending steps of 16 into fp32, the
  *   same order for every shape path and variant; m and n multiples of 256 and
- *   kk a multiple of 64 and >= 2048 run the 4-wave kernel (one wave per SIMD),
+ *   kk a multiple of 64 and >= 1024 run the 4-wave kernel (one wave per SIMD),
  *   other shapes the 8-wave kernel (guarded edge tiles where needed).
  */
 dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n,

@@ -232,13 +232,14 @@ def test_gemm_bf16_8192_sampled():
 
 
 @pytest.mark.parametrize("m,n,kk", [(256, 256, 2048), (512, 768, 2112), (1024, 256, 4096),
-                                    (768, 512, 320), (2048, 2048, 64)])
+                                    (512, 512, 1024), (256, 768, 1472),
+                                    (768, 512, 320), (2048, 2048, 64), (256, 256, 960)])
 def test_gemm_bf16_variants_bit_identical(m, n, kk):
-    """Whole 256x256 tiles with kk a multiple of 64 and >= 2048 run the 4-wave
+    """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run the 4-wave
     kernel; the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, so
     all agree bit for bit (shorter k ranges take the 8-wave kernel on every
-    path: the last two cases). The default result is also checked against the
+    path: the last three cases). The default result is also checked against the
     oracle (exactly on small-integer inputs, within the fp32 summation bound on
     N(0,1) inputs); an odd number of k stages (2112 = 33 x 64) and grids that
     are not a multiple of 8 tiles are among the cases."""
