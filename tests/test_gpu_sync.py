@@ -319,6 +319,30 @@ def test_layer_buckets_k8_bf16_full_size():
         assert torch.equal(out[0], out[r])
 
 
+def test_one_pass_layer_buckets_k8_bf16_full_size():
+    """The same layer buckets as one one-pass AllReduce per bucket
+    (BucketedSync.step_all_reduce, the launch configuration the one-pass
+    benchmark times): every element of every rank's output equals the oracle's
+    AllGather of its ReduceScatter, bit for bit."""
+    k, total = 8, gen.LAYER_PARAMS
+    say("one-pass layer: generating inputs")
+    grads = gen.layer_grads_bf16(3, k, device=DEV)
+    out = [torch.full((total,), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
+    say("one-pass layer: step")
+    sync.step_all_reduce()
+    torch.cuda.synchronize()
+    for r in range(1, k):
+        assert torch.equal(out[0], out[r]), r
+    host = [to_np(g) for g in grads]
+    got = to_np(out[0])
+    say("one-pass layer: oracle")
+    for b, (off, n) in enumerate(sync.plan):
+        xs = [np.ascontiguousarray(h[off:off + n]) for h in host]
+        want = oracle.all_reduce(xs, op="avg", nthreads=16)
+        assert bits_equal(got[off:off + n], want[0]), b
+
+
 def test_uneven_token_weighted_k8_10m():
     """K=8 ranks, N=10,000,019 fp32 (not divisible by 8: shards of 1,250,003,
     5 pads), token counts from sums of log-normal(7,1) document lengths,
