@@ -45,8 +45,10 @@ template <int DT> struct RsU { static constexpr int U = 2; };
 // vector per lane and rank measured best (25M bf16, K=8: 72.1% of peak against
 // 70.6% with 2 and 69.3% with 4).
 constexpr int kArU = 1;
+// The AllGather, too, stores each loaded vector K times; one vector per lane
+// measured best (the pipelined layer step 1.3508 -> 1.3382 ms against 2).
 #ifndef DPS_AG_U
-#define DPS_AG_U 2
+#define DPS_AG_U 1
 #endif
 constexpr int kAgU = DPS_AG_U;
 #ifndef DPS_AG_BLOCK

@@ -61,7 +61,7 @@ def test_no_scratch(kernels):
 
 def test_sync_kernels_use_16_byte_accesses(kernels):
     for parts in (("rs_kernelILi1ELi1ELi8ELi2ELb0",), ("rs_kernelILi1ELi1ELi8ELi1ELb1",),
-                  ("ag_kernelILi2ELi8ELi2",), ("rsag_kernelILi1ELi1ELi8",),
+                  ("ag_kernelILi2ELi8ELi1",), ("rsag_kernelILi1ELi1ELi8",),
                   ("scatter_accumulate_kernelILi1",)):
         for name, (_, body) in pick(kernels, *parts).items():
             assert "global_load_dwordx4" in body, name
