@@ -48,11 +48,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "078c1940d4997935fe25c801e684ccb91a72dcaba32b5eef51d493aaa78850fe"
+    "sources_sha256": "fbd8370a7e53718568233dc709ecd2a6e49090e4e40b5682af28530da2e8af67"
                       "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195402.6 + 49729.0) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25142.8 + 390812.4) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220598.0 + 440429.1) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195382.3 + 49393.7) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25142.7 + 390826.8) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220524.0 + 439863.3) * 1024,
 }
 
 

@@ -40,10 +40,14 @@ template <> struct Tr<kBF16> { using Acc = float;    static constexpr int ES = 2
 template <> struct Tr<kI32>  { using Acc = unsigned; static constexpr int ES = 4, V = 4; };
 
 // vectors per thread per tile
-template <int DT> struct RsU { static constexpr int U = 2; };
-// The one-pass AllReduce stores each folded vector to all K outputs; there one
-// vector per lane and rank measured best (25M bf16, K=8: 72.1% of peak against
-// 70.6% with 2 and 69.3% with 4).
+// One 16-byte vector per lane and rank in every ReduceScatter tile. In the
+// fused ReduceScatter + AllGather launch this makes the two kinds' tiles the
+// same size, so they pair up one for one across the grid (the pipelined layer
+// step 1.3483 -> 1.3128 ms against 2 per lane, interleaved in one process).
+template <int DT> struct RsU { static constexpr int U = 1; };
+// The one-pass AllReduce stores each folded vector to all K outputs; there, too,
+// one vector per lane and rank measured best (25M bf16, K=8: 72.1% of peak
+// against 70.6% with 2 and 69.3% with 4).
 constexpr int kArU = 1;
 // The AllGather, too, stores each loaded vector K times; one vector per lane
 // measured best (the pipelined layer step 1.3508 -> 1.3382 ms against 2).

@@ -60,7 +60,7 @@ def test_no_scratch(kernels):
 
 
 def test_sync_kernels_use_16_byte_accesses(kernels):
-    for parts in (("rs_kernelILi1ELi1ELi8ELi2ELb0",), ("rs_kernelILi1ELi1ELi8ELi1ELb1",),
+    for parts in (("rs_kernelILi1ELi1ELi8ELi1ELb0",), ("rs_kernelILi1ELi1ELi8ELi1ELb1",),
                   ("ag_kernelILi2ELi8ELi1",), ("rsag_kernelILi1ELi1ELi8",),
                   ("scatter_accumulate_kernelILi1",)):
         for name, (_, body) in pick(kernels, *parts).items():
@@ -82,7 +82,7 @@ def test_register_budgets(kernels):
         assert field(desc, "amdhsa_next_free_vgpr") <= 512, name
     # the CU-sharing GEMM leaves room for one default sync wave (<= 96)
     sync = max(field(d, "amdhsa_next_free_vgpr")
-               for d, _ in pick(kernels, "rs_kernelILi1ELi1ELi8ELi2").values())
+               for d, _ in pick(kernels, "rs_kernelILi1ELi1ELi8ELi1").values())
     for name, (desc, _) in pick(kernels, "gemm_bf16_kernelILb0ELi32").items():
         assert 2 * field(desc, "amdhsa_next_free_vgpr") + sync <= 512, name
 
