@@ -290,20 +290,49 @@ def bench_ring1m(args):
     xf = gen.ring_uniform_inputs(1, k, n, device="cuda")
     xi = [gen.int_copy(x) for x in xf]
     res = {}
+    lib = dps.lib()
     for name, xs, op in (("f32_avg", xf, "avg"), ("i32_sum", xi, "sum")):
         out = [torch.empty_like(x) for x in xs]
         call = lambda: dps.dp_all_reduce(xs, out, op=op, s_chunks=s)
         ms = _time_ms(call)
         med = statistics.median(ms)
         back = statistics.median(_time_batch_ms(call, batch=20))
+        # the same calls with the pointer arrays built once (no per-call
+        # marshalling), and recorded once into a HIP graph and replayed
+        dt = dps.DP_F32 if xs[0].dtype == torch.float32 else dps.DP_I32
+        opc = dps.DP_AVG if op == "avg" else dps.DP_SUM
+        sp, rp = dps.ptr_array([t.data_ptr() for t in xs]), dps.ptr_array([t.data_ptr() for t in out])
+
+        def abi():
+            rc = lib.dp_all_reduce(sp, rp, n, k, dt, opc, s, dps._stream(None))
+            if rc:
+                raise dps.DpsyncError(rc, "dp_all_reduce")
+        back_abi = statistics.median(_time_batch_ms(abi, batch=20))
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            abi()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for _ in range(20):
+                abi()
+        torch.cuda.synchronize()
+        back_graph = statistics.median(_time_ms(graph.replay)) / 20
         b = 2 * (k + 1) * n * 4
         res[name] = {"median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
                      "back_to_back_us": round(1e3 * back, 2),
-                     "gbs_rs_ag_bytes": round(b / (back * 1e-3) / 1e9, 1)}
+                     "back_to_back_abi_us": round(1e3 * back_abi, 2),
+                     "graph_replay_us": round(1e3 * back_graph, 2),
+                     "gbs_rs_ag_bytes": round(b / (back_graph * 1e-3) / 1e9, 1)}
     return {"metric": "ring AllReduce K=4 N=1,048,576 S=4 (cache-resident, launch-bound)",
             "unit": "us", "results": res,
             "timing": "median_us: one call between two events (host latency included); "
-                      "back_to_back_us: per call of 20 back-to-back calls; GB/s on the "
+                      "back_to_back_us: per call of 20 back-to-back calls through the Python "
+                      "binding; back_to_back_abi_us: the same through the C ABI with the "
+                      "pointer arrays built once; graph_replay_us: 20 calls recorded in a "
+                      "HIP graph, per call of a replay; GB/s (on the graph time) on the "
                       "ReduceScatter + AllGather bytes 2(K+1)Ns",
             "config": {"workload": "K=4, 1,048,576 fp32/int32, S=4"}}
 
