@@ -406,6 +406,55 @@ def test_one_gib_per_rank_k8_fp32_sampled():
         assert torch.equal(out[0], out[r])
 
 
+def _uniform_chunked(seed, r, n, dtype, chunk=1 << 27):
+    """gen.uniform_pm1 of n elements written chunk by chunk into one buffer."""
+    t = torch.empty(n, dtype=dtype, device=DEV)
+    for s0 in range(0, n, chunk):
+        c = min(chunk, n - s0)
+        t[s0:s0 + c] = gen.uniform_pm1(seed, 0, r, c, start=s0, device=DEV).to(dtype)
+    return t
+
+
+@pytest.mark.parametrize("dtype,n", [(torch.bfloat16, (1 << 31) + 7), (torch.float32, (1 << 30) + 5)])
+def test_beyond_2g_elements_and_4gib_per_rank_sampled(dtype, n):
+    """K=2 ranks with more than 2^31 elements (bf16) or more than 4 GiB
+    (fp32) per buffer: ReduceScatter + AllGather and the one-pass AllReduce,
+    checked at every shard boundary, around the 2^31-element and 4 GiB marks,
+    at the ends and at random positions against the oracle's fold of the same
+    values (the shard starts and the marks exercise 64-bit addressing)."""
+    k = 2
+    say(f"beyond-4g {dtype} n={n}: generating inputs")
+    xs = [_uniform_chunked(9, r, n, dtype) for r in range(k)]
+    L = dps.dp_shard_len(n, k)
+    sh = [torch.empty(L, dtype=dtype, device=DEV) for _ in range(k)]
+    out = [torch.empty(n, dtype=dtype, device=DEV) for _ in range(k)]
+    rng = np.random.default_rng(1)
+    es = xs[0].element_size()
+    marks = [(1 << 31) // es, (1 << 32) // es, 1 << 31, L, n]
+    idx = np.concatenate([rng.integers(0, n, 100_000), np.arange(k) * L, np.arange(1, k + 1) * L - 1,
+                          np.arange(16), n - 1 - np.arange(16)] +
+                         [np.arange(m - 16, m + 16) for m in marks])
+    idx = np.unique(idx[(idx >= 0) & (idx < n)].astype(np.int64))
+    ti = torch.from_numpy(idx).to(DEV)
+    comp = [to_np(x[ti]) for x in xs]
+    want = oracle.fold_at(comp, idx // L, op="avg")
+    say(f"beyond-4g {dtype}: rs+ag")
+    dps.dp_reduce_scatter(xs, sh, op="avg")
+    dps.dp_all_gather(sh, out)
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(out[r][ti]), want), r
+    assert torch.equal(out[0], out[1])
+    say(f"beyond-4g {dtype}: one-pass all-reduce")
+    for o in out:
+        o.fill_(float("nan"))
+    dps.dp_all_reduce(xs, out, op="avg")
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(out[r][ti]), want), r
+    assert torch.equal(out[0], out[1])
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
 def test_capped_grid_is_bit_identical(dtype):
     """With a cap on resident workgroups the kernels walk their tiles
