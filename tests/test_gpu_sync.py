@@ -418,7 +418,8 @@ def _uniform_chunked(seed, r, n, dtype, chunk=1 << 27):
 @pytest.mark.parametrize("dtype,n", [(torch.bfloat16, (1 << 31) + 7), (torch.float32, (1 << 30) + 5)])
 def test_beyond_2g_elements_and_4gib_per_rank_sampled(dtype, n):
     """K=2 ranks with more than 2^31 elements (bf16) or more than 4 GiB
-    (fp32) per buffer: ReduceScatter + AllGather and the one-pass AllReduce,
+    (fp32) per buffer: ReduceScatter + AllGather, the one-pass AllReduce and
+    the fused ReduceScatter+AllGather launch,
     checked at every shard boundary, around the 2^31-element and 4 GiB marks,
     at the ends and at random positions against the oracle's fold of the same
     values (the shard starts and the marks exercise 64-bit addressing)."""
@@ -453,6 +454,16 @@ def test_beyond_2g_elements_and_4gib_per_rank_sampled(dtype, n):
     for r in range(k):
         assert bits_equal(to_np(out[r][ti]), want), r
     assert torch.equal(out[0], out[1])
+    say(f"beyond-4g {dtype}: fused launch (AllGather of the shards above beside a new ReduceScatter)")
+    sh2 = [torch.empty(L, dtype=dtype, device=DEV) for _ in range(k)]
+    for o in out:
+        o.fill_(float("nan"))
+    dps.dp_reduce_scatter_all_gather(xs, sh2, sh, out, op="avg")
+    torch.cuda.synchronize()
+    for r in range(k):
+        assert bits_equal(to_np(out[r][ti]), want), r
+    for c in range(k):
+        assert torch.equal(sh2[c], sh[c]), c
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
