@@ -48,11 +48,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "fbd8370a7e53718568233dc709ecd2a6e49090e4e40b5682af28530da2e8af67"
+    "sources_sha256": "e902b19e7c1816f0db92585a975e0dd8cf6b58fef22ac2704010bc75c4e97543"
                       "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195382.3 + 49393.7) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25142.7 + 390826.8) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220524.0 + 439863.3) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195382.8 + 49394.7) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25139.2 + 390816.5) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220531.6 + 439848.5) * 1024,
 }
 
 

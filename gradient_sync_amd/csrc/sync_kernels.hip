@@ -55,6 +55,11 @@ constexpr int kArU = 1;
 #define DPS_AG_U 1
 #endif
 constexpr int kAgU = DPS_AG_U;
+// With a capped grid (dp_launch_opts_t.max_workgroups) a few resident
+// workgroups walk many tiles, and two vectors per lane keep twice the loads in
+// flight per workgroup (1 GiB/rank fp32 RS + AG on 256 workgroups: 3.78 ms
+// against 4.01 with one; on the default grid one is faster: 3.42 against 3.53).
+constexpr int kUCapped = 2;
 #ifndef DPS_AG_BLOCK
 #define DPS_AG_BLOCK 256
 #endif
@@ -598,6 +603,8 @@ hipError_t rs_go(const RsParams &p, long long grid, bool lean, hipStream_t st)
 {
     if (lean)
         hipLaunchKernelGGL((rs_kernel_lean<DT, EP, KT, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    else if (p.max_blocks > 0)
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, kUCapped, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     else
         hipLaunchKernelGGL((rs_kernel<DT, EP, KT, AR ? kArU : RsU<DT>::U, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     return hipGetLastError();
@@ -639,7 +646,10 @@ hipError_t rs_dispatch(const RsParams &q, int dt, int ep, long long grid, bool l
 template <int ES, int KT>
 hipError_t ag_go(const AgParams &p, long long grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
+    if (p.max_blocks > 0)
+        hipLaunchKernelGGL((ag_kernel<ES, KT, kUCapped>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
+    else
+        hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
     return hipGetLastError();
 }
 
@@ -656,9 +666,11 @@ hipError_t ag_k(const AgParams &p, long long grid, hipStream_t st)
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-int rs_vectors_per_thread(int dt, bool lean)
+// vectors per lane of the tiles a launch will run (the kernel choice in rs_go)
+int rs_vectors_per_thread(int dt, bool lean, bool capped)
 {
     if (lean) return 1;
+    if (capped) return kUCapped;
     return dt == kF32 ? RsU<kF32>::U : dt == kBF16 ? RsU<kBF16>::U : RsU<kI32>::U;
 }
 
@@ -697,7 +709,7 @@ long long plan_rs(RsParams &p, int dt, bool lean)
     for (int c = 0; c < p.k; ++c)
         p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c], !DPS_RS_ALIGN_OUT);
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean) * (16 / es);
+    const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean, p.max_blocks > 0) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);
@@ -719,7 +731,7 @@ long long plan_ag(AgParams &p, int dt)
         if (same) p.meta[c] |= kOutAlignBit;
     }
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kAgBlock * kAgU * (16 / es);
+    const long long te = (long long)kAgBlock * (p.max_blocks > 0 ? kUCapped : kAgU) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);
@@ -746,7 +758,7 @@ long long plan_ar(RsParams &p, int dt, bool lean)
     }
     p.write_pads = 0;
     p.sub = ceil_div(p.L, p.S);
-    const long long te = (long long)kBlock * (lean ? 1 : kArU) * (16 / es);
+    const long long te = (long long)kBlock * (lean ? 1 : p.max_blocks > 0 ? kUCapped : kArU) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
     return grid_for(p.total_tiles, p.max_blocks);
