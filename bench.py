@@ -562,7 +562,7 @@ def bench_c3(args):
     # T_gemm are the same kernels alone on the same masked streams.
     hip = _hip_runtime()
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for n_comm in (128, 160, 192):
+    for n_comm in (128, 144, 160, 176, 192):
         name = f"rp_comm{n_comm}"
         raw = []
         try:
