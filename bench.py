@@ -759,7 +759,8 @@ def bench_overlap(args):
     soon as all its gradients exist), against the same work on one stream.
     Variants: default kernels; the lean AllReduce (64 VGPRs, fits beside a GEMM
     workgroup) capped at 256 workgroups; the GEMM variant that leaves room for a
-    default AllReduce workgroup."""
+    default AllReduce workgroup; and the two streams on disjoint CU-masked sets
+    (32 or 64 CUs for the AllReduces)."""
     import torch
 
     import gen
@@ -774,6 +775,8 @@ def bench_overlap(args):
     comm = torch.cuda.Stream()
     cur = torch.cuda.current_stream()
     sync = BucketedSync(grad, out, cap, op="avg")
+    hip = _hip_runtime()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     res = {}
     for t in (256, 1024):
         log(f"[bench] overlap t={t}")
@@ -808,7 +811,36 @@ def bench_overlap(args):
         r["t_serial_lean_ms"] = med(lambda: serial(lean=True))
         for name, o in variants:
             r[f"t_{name}_ms"] = med(lambda: overlapped(**o))
-        for name, _ in variants:
+        names = [name for name, _ in variants]
+        # RP: the GEMMs on a CU-masked stream with CUs [n_comm, all), the
+        # AllReduces on one with CUs [0, n_comm), default kernels
+        for n_comm in (32, 64):
+            name = f"overlap_rp_comm{n_comm}"
+            raw = []
+            try:
+                raw.append(_cu_masked_stream(hip, n_comm, n_cus, n_cus))
+                raw.append(_cu_masked_stream(hip, 0, n_comm, n_cus))
+            except RuntimeError as e:
+                r[f"error_{name}"] = str(e)
+                torch.cuda.synchronize()
+                for st in raw:
+                    hip.hipStreamDestroy(st)
+                continue
+            sc, sm = (torch.cuda.ExternalStream(st.value) for st in raw)
+
+            def rp():
+                sc.wait_stream(cur)
+                sm.wait_stream(cur)
+                dps.dp_backward_allreduce_overlap(pieces, t, dy, x, grad, out, cap, op="avg",
+                                                  compute_stream=sc, comm_stream=sm, events=ev)
+                cur.wait_stream(sc)
+                cur.wait_stream(sm)
+            r[f"t_{name}_ms"] = med(rp)
+            torch.cuda.synchronize()
+            for st in raw:
+                hip.hipStreamDestroy(st)
+            names.append(name)
+        for name in names:
             r[f"hidden_comm_frac_{name}"] = round(
                 (r["t_serial_ms"] - r[f"t_{name}_ms"]) / r["t_comm_ms"], 4)
             r[f"speedup_{name}"] = round(r["t_serial_ms"] / r[f"t_{name}_ms"], 4)
