@@ -229,6 +229,48 @@ def test_side_stream():
     assert bits_equal(to_np(outs[2]), want[2])
 
 
+def test_cu_masked_stream():
+    """On a stream confined to 64 of the CUs (hipExtStreamCreateWithCUMask, the
+    resource partitioning the concurrency measurement uses) the pipelined
+    bucket step and the one-pass AllReduce give the oracle's bits."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n_cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for b in range(64):                  # bits go round-robin over the XCDs
+        mask[b // 32] |= 1 << (b % 32)
+    raw = ctypes.c_void_p()
+    assert hip.hipExtStreamCreateWithCUMask(ctypes.byref(raw), words, mask) == 0
+    try:
+        st = torch.cuda.ExternalStream(raw.value)
+        k, total, cap = 8, 2_500_003, 1_000_003
+        grads = [x.to(torch.bfloat16) for x in gen.ring_uniform_inputs(77, k, total, device=DEV)]
+        out = [torch.full((total,), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+        sync = BucketedSync(grads, out, cap, op="avg")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            sync.step_pipelined()
+        st.synchronize()
+        host = [to_np(g) for g in grads]
+        for off, n in sync.plan:
+            want = oracle.all_reduce([np.ascontiguousarray(h[off:off + n]) for h in host], op="avg")
+            assert bits_equal(to_np(out[5][off:off + n]), want[5])
+        for o in out:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            dps.dp_all_reduce(grads, out, op="sum")
+        st.synchronize()
+        assert bits_equal(to_np(out[0]), oracle.all_reduce(host, op="sum")[0])
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(raw)
+
+
 # ------------------------------------------------------------ weighted
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
