@@ -224,3 +224,39 @@ def test_minibatch_k8_bf16_25m_full_size():
     for c in range(k):
         assert bits_equal(to_np(out[c]), want[c]), c
         assert not torch.any(acc[c] != 0)
+
+
+def test_beyond_2g_elements_sampled():
+    """K=2 owners, two bf16 pushes of 2^31 + 7 elements (4 GiB each) and a
+    bf16 settle: accumulators and settled shards checked at every shard
+    boundary, around the 2^31-element mark, at the ends and at random
+    positions against the oracle's push and settle of the same values."""
+    from tests.test_gpu_sync import _uniform_chunked
+    k, n = 2, (1 << 31) + 7
+    say(f"odc beyond-2g n={n}: generating pushes")
+    grads = [_uniform_chunked(31 + i, 0, n, torch.bfloat16) for i in range(2)]
+    L = dps.dp_shard_len(n, k)
+    acc = [torch.zeros(L, dtype=torch.float32, device=DEV) for _ in range(k)]
+    out = [torch.empty(L, dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    dps.dp_scatter_accumulate(grads, acc)
+    dps.dp_settle(acc, out, n, divisor=2.0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    idx = np.concatenate([rng.integers(0, n, 100_000), np.arange(k) * L, np.arange(1, k + 1) * L - 1,
+                          np.arange(16), n - 1 - np.arange(16), np.arange((1 << 31) - 16, (1 << 31) + 7)])
+    idx = np.unique(idx[(idx >= 0) & (idx < n)].astype(np.int64))
+    ti = torch.from_numpy(idx).to(DEV)
+    s = idx.size
+    # the oracle on the compact samples: one owner holding all of them
+    want_acc = oracle.scatter_accumulate(to_np(grads[0][ti]), [np.zeros(s, np.float32)], 1)
+    want_acc = oracle.scatter_accumulate(to_np(grads[1][ti]), want_acc, 1)
+    want_out = oracle.settle(want_acc, s, 1, dtype=np.uint16, divisor=2.0)[0]
+    got_acc = np.empty(s, np.float32)
+    got_out = np.empty(s, np.uint16)
+    for c in range(k):
+        m = (idx // L) == c
+        j = torch.from_numpy(idx[m] - c * L).to(DEV)
+        got_acc[m] = to_np(acc[c][j])
+        got_out[m] = to_np(out[c][j])
+    assert bits_equal(got_acc, want_acc[0])
+    assert bits_equal(got_out, want_out)
