@@ -50,9 +50,9 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 MEASURED_TRAFFIC = {
     "sources_sha256": "e902b19e7c1816f0db92585a975e0dd8cf6b58fef22ac2704010bc75c4e97543"
                       "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195382.8 + 49394.7) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25139.2 + 390816.5) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220531.6 + 439848.5) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195382.8 + 49390.7) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25139.2 + 390817.2) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220531.7 + 439830.1) * 1024,
 }
 
 
@@ -93,6 +93,23 @@ def bf16_bits(t):
 
 # ----------------------------------------------------------------- headline
 
+def _in_rank_layout(ts):
+    """The generated per-rank tensors copied into one allocation with the ranks
+    a fixed gap apart (buckets.rank_buffers), the layout the sync steps are
+    measured in; the separately allocated originals are freed by the caller."""
+    from gradient_sync_amd.buckets import rank_buffers
+    out = rank_buffers(len(ts), ts[0].numel(), ts[0].dtype, device=ts[0].device)
+    for o, t in zip(out, ts):
+        o.copy_(t)
+    return out
+
+
+def _rank_layout_note():
+    from gradient_sync_amd.buckets import RANK_STAGGER_BYTES, SHARD_STAGGER_BYTES
+    return (f"each of grads/shards/out in one allocation, ranks {RANK_STAGGER_BYTES // 1024} KiB "
+            f"apart (bucket shards {SHARD_STAGGER_BYTES // 1024} KiB apart)")
+
+
 def bench_layer(args):
     import torch
 
@@ -102,8 +119,8 @@ def bench_layer(args):
     k = 8
     total = gen.LAYER_PARAMS
     log(f"[bench] generating {k} x {total} bf16 gradients on the GPU")
-    grads = gen.layer_grads_bf16(3, k, device="cuda")
-    out = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    grads = _in_rank_layout(gen.layer_grads_bf16(3, k, device="cuda"))
+    out = _in_rank_layout([torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)])
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
     step_bytes = sync.algorithmic_bytes()
 
@@ -175,7 +192,8 @@ def bench_layer(args):
                                "averaged ReduceScatter then AllGather per bucket, the "
                                "ReduceScatter of bucket b+1 fused with the AllGather of b",
                    "ranks": k, "params_per_rank": total, "bucket_elems": gen.BUCKET_ELEMS,
-                   "buckets": len(sync.plan), "op": "avg", "accumulate": "fp32, ring order"},
+                   "buckets": len(sync.plan), "op": "avg", "accumulate": "fp32, ring order",
+                   "rank_layout": _rank_layout_note()},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
         "plain_step": {"value": round(value_plain, 2),
@@ -429,8 +447,9 @@ def bench_fused_ar(args):
     import gen
     from gradient_sync_amd.buckets import BucketedSync
     k = 8
-    grads = gen.layer_grads_bf16(3, k, device="cuda")
-    out = [torch.empty(gen.LAYER_PARAMS, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    grads = _in_rank_layout(gen.layer_grads_bf16(3, k, device="cuda"))
+    out = _in_rank_layout([torch.empty(gen.LAYER_PARAMS, dtype=torch.bfloat16, device="cuda")
+                           for _ in range(k)])
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
     res = {}
     for name, fn, b in (("one_pass_all_reduce", sync.step_all_reduce, sync.all_reduce_bytes()),
@@ -449,7 +468,8 @@ def bench_fused_ar(args):
                            res["one_pass_all_reduce"]["ms_per_step"], 4)
     return {"metric": "averaged AllReduce of the K=8 bf16 layer buckets: one pass vs RS+AG",
             "unit": "ms", "results": res,
-            "config": {"workload": "K=8, 218,103,808 bf16 per rank, 9 buckets of <=25,000,000"}}
+            "config": {"workload": "K=8, 218,103,808 bf16 per rank, 9 buckets of <=25,000,000",
+                       "rank_layout": _rank_layout_note()}}
 
 
 def _hip_runtime():
@@ -490,10 +510,11 @@ def bench_c3(args):
     import gradient_sync_amd as dps
     k, n = 8, 268_435_456
     log("[c3] generating 8 x 1 GiB fp32 and 2 x 8192^2 bf16")
-    xs = gen.ring_uniform_inputs(5, k, n, device="cuda")
+    xs = _in_rank_layout(gen.ring_uniform_inputs(5, k, n, device="cuda"))
     L = dps.dp_shard_len(n, k)
-    sh = [torch.empty(L, device="cuda") for _ in range(k)]
-    out = [torch.empty(n, device="cuda") for _ in range(k)]
+    from gradient_sync_amd.buckets import rank_buffers
+    sh = rank_buffers(k, L, torch.float32)
+    out = rank_buffers(k, n, torch.float32)
     a, b = gen.gemm_bf16_inputs(5, 8192, 8192, 8192, device="cuda")
     c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
@@ -610,7 +631,8 @@ def bench_c3(args):
                             "pct_of_ideal_gain = (S-1)/(S_ideal-1)",
             "results": res,
             "config": {"workload": "K=8 x 268,435,456 fp32 RS(sum)+AG on stream A, "
-                                   "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured"}}
+                                   "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured",
+                       "rank_layout": _rank_layout_note()}}
 
 
 def _odc_kernel_rooflines(rounds8, singles, acc, out, n, div, with_np1):

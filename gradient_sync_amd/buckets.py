@@ -26,6 +26,33 @@ def bucket_plan(total: int, cap: int) -> list[tuple[int, int]]:
     return [(o, min(cap, total - o)) for o in range(0, total, cap)]
 
 
+# Extra bytes between consecutive emulated ranks' buffers in one allocation,
+# and between consecutive shards of a bucket. Every sync kernel touches the K
+# ranks at the same offset at the same time. Measured on MI355X (same bits in
+# every layout; medians of 10 shuffled rounds, three allocations):
+#   K = 8 bf16 layer step, 218,103,808 values per rank in 25,000,000-value
+#   buckets: 75.4-75.5% of HBM peak with separately allocated buffers or one
+#   allocation with no gaps; 75.9-76.6% with rank gaps of 64-128 KiB;
+#   8 x 1 GiB fp32 ReduceScatter + AllGather: 72.1% separately allocated,
+#   76.5-76.8% with gaps of 96-160 KiB (64 KiB: 76.1% in one allocation,
+#   71.6% in another).
+RANK_STAGGER_BYTES = 128 * 1024
+SHARD_STAGGER_BYTES = 64 * 1024
+
+
+def rank_buffers(k: int, n: int, dtype=torch.bfloat16, device="cuda",
+                 stagger: int = RANK_STAGGER_BYTES) -> list[torch.Tensor]:
+    """K contiguous length-n tensors, one per emulated rank, carved from one
+    allocation: rank r starts at r * (n * element_size rounded up to 256 bytes
+    + stagger) bytes. `stagger` must be a multiple of 256."""
+    if k < 1 or n < 0 or stagger < 0 or stagger % 256:
+        raise ValueError("rank_buffers: need k >= 1, n >= 0 and a stagger that is a multiple of 256")
+    es = torch.empty(0, dtype=dtype).element_size()
+    stride = (-(-n * es // 256) * 256 + stagger) // es
+    slab = torch.empty(max(1, (k - 1) * stride + n), dtype=dtype, device=device)
+    return [slab[r * stride:r * stride + n] for r in range(k)]
+
+
 class BucketedSync:
     """Averaged (or summed) AllReduce of K flat gradients, bucket by bucket,
     as ReduceScatter into per-bucket shard buffers and AllGather into `out`.
@@ -33,10 +60,12 @@ class BucketedSync:
     grads, out : K contiguous device tensors of the same dtype and length.
     cap        : bucket size in elements.
     The shards of bucket b for rank c live in one preallocated buffer; each
-    shard starts on a 256-byte boundary.
+    shard starts on a 256-byte boundary, `shard_stagger` bytes after the end
+    of the previous one (the gap of `rank_buffers`).
     """
 
-    def __init__(self, grads, out, cap: int, op: str = "avg", s_chunks: int = 1):
+    def __init__(self, grads, out, cap: int, op: str = "avg", s_chunks: int = 1,
+                 shard_stagger: int = SHARD_STAGGER_BYTES):
         self.k = k = len(grads)
         if len(out) != k:
             raise ValueError("grads and out need one tensor per rank")
@@ -50,9 +79,11 @@ class BucketedSync:
         self.op = {"sum": DP_SUM, "avg": DP_AVG}[op]
         self.s_chunks = s_chunks
         self.plan = bucket_plan(total, cap)
+        if shard_stagger < 0 or shard_stagger % 256:
+            raise ValueError("shard_stagger must be a non-negative multiple of 256")
         align = max(1, 256 // self.es)
         self.shard_len = [dp_shard_len(n, k) for _, n in self.plan]
-        self.slot = [-(-L // align) * align for L in self.shard_len]
+        self.slot = [-(-L // align) * align + shard_stagger // self.es for L in self.shard_len]
         self.shards = torch.empty(k * sum(self.slot), dtype=dt, device=grads[0].device)
         base = self.shards.data_ptr()
         self.calls = []

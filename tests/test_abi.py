@@ -9,7 +9,7 @@ import re
 import pytest
 
 import gradient_sync_amd as dps
-from gradient_sync_amd.buckets import bucket_plan
+from gradient_sync_amd.buckets import bucket_plan, rank_buffers
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dpsync.h")
@@ -176,6 +176,26 @@ def test_bucket_plan():
     assert bucket_plan(0, 10) == []
     with pytest.raises(ValueError):
         bucket_plan(10, 0)
+
+
+def test_rank_buffers_layout():
+    import torch
+    for dt, n, st in ((torch.bfloat16, 1001, 131072), (torch.float32, 64, 0), (torch.int32, 3, 256)):
+        bufs = rank_buffers(3, n, dt, device="cpu", stagger=st)
+        es = bufs[0].element_size()
+        stride = (-(-n * es // 256) * 256 + st)
+        base = bufs[0].data_ptr()
+        for r, b in enumerate(bufs):
+            assert b.numel() == n and b.is_contiguous() and b.dtype == dt
+            assert b.data_ptr() - base == r * stride
+            assert (b.data_ptr() - base) % 256 == 0
+        for b in bufs:
+            b.zero_()
+        bufs[1].fill_(1)                              # no overlap between ranks
+        assert bufs[0].eq(0).all() and bufs[2].eq(0).all()
+    assert [b.numel() for b in rank_buffers(2, 0, device="cpu")] == [0, 0]
+    with pytest.raises(ValueError):
+        rank_buffers(2, 10, stagger=100)
 
 
 def test_binding_rejects_host_tensors():

@@ -11,7 +11,7 @@ import torch
 import gen
 import gradient_sync_amd as dps
 import oracle
-from gradient_sync_amd.buckets import BucketedSync
+from gradient_sync_amd.buckets import BucketedSync, rank_buffers
 from tests.helpers import bits_equal, from_np, say, to_np
 
 pytestmark = pytest.mark.gpu
@@ -337,15 +337,19 @@ def test_ring_allreduce_k4_1m_fp32_and_int32():
 def test_layer_buckets_k8_bf16_full_size():
     """K=8 ranks, one GQA+SwiGLU layer of bf16 gradients (218,103,808 per rank,
     N(0, 1e-3)), 9 buckets of at most 25,000,000, averaged ReduceScatter then
-    AllGather, in the bucketed launch configuration the benchmark times.
-    Compared bit-exactly with the oracle for every element."""
+    AllGather, in the bucketed launch configuration and the rank layout the
+    benchmark times (the pipelined step; ranks in one allocation, a fixed gap
+    apart). Compared bit-exactly with the oracle for every element; the plain
+    step must give the same bits."""
     k, total = 8, gen.LAYER_PARAMS
     say("layer-buckets: generating inputs")
-    grads = gen.layer_grads_bf16(3, k, device=DEV)
-    out = [torch.empty(total, dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    grads = rank_buffers(k, total, torch.bfloat16, device=DEV)
+    for g, src in zip(grads, gen.layer_grads_bf16(3, k, device=DEV)):
+        g.copy_(src)
+    out = rank_buffers(k, total, torch.bfloat16, device=DEV)
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
-    say("layer-buckets: step")
-    sync.step()
+    say("layer-buckets: pipelined step")
+    sync.step_pipelined()
     torch.cuda.synchronize()
     host = [to_np(g) for g in grads]
     say("layer-buckets: oracle")
@@ -359,6 +363,13 @@ def test_layer_buckets_k8_bf16_full_size():
             assert bits_equal(to_np(out[r][off:off + n]), full[r]), (b, r)
     for r in range(1, k):
         assert torch.equal(out[0], out[r])
+    say("layer-buckets: plain step")
+    piped = out[0].clone()
+    for o in out:
+        o.fill_(float("nan"))
+    sync.step()
+    for r in range(k):
+        assert torch.equal(out[r].view(torch.int16), piped.view(torch.int16)), r
 
 
 def test_one_pass_layer_buckets_k8_bf16_full_size():
