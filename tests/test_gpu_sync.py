@@ -375,12 +375,17 @@ def test_layer_buckets_k8_bf16_full_size():
 def test_one_pass_layer_buckets_k8_bf16_full_size():
     """The same layer buckets as one one-pass AllReduce per bucket
     (BucketedSync.step_all_reduce, the launch configuration the one-pass
-    benchmark times): every element of every rank's output equals the oracle's
-    AllGather of its ReduceScatter, bit for bit."""
+    benchmark times, ranks in its gapped layout): every element of every
+    rank's output equals the oracle's AllGather of its ReduceScatter, bit for
+    bit."""
     k, total = 8, gen.LAYER_PARAMS
     say("one-pass layer: generating inputs")
-    grads = gen.layer_grads_bf16(3, k, device=DEV)
-    out = [torch.full((total,), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    grads = rank_buffers(k, total, torch.bfloat16, device=DEV)
+    for g, src in zip(grads, gen.layer_grads_bf16(3, k, device=DEV)):
+        g.copy_(src)
+    out = rank_buffers(k, total, torch.bfloat16, device=DEV)
+    for o in out:
+        o.fill_(float("nan"))
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
     say("one-pass layer: step")
     sync.step_all_reduce()
