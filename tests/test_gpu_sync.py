@@ -524,6 +524,39 @@ def test_beyond_2g_elements_and_4gib_per_rank_sampled(dtype, n):
         assert torch.equal(sh2[c], sh[c]), c
 
 
+def test_fp32_1gib_pipelined_buckets_full_size_sampled():
+    """The pipelined bucket step in fp32 at 1 GiB per rank: K=8 ranks of
+    268,435,456 fp32 (ranks in the gapped layout), 8 buckets of 33,554,432
+    with the ReduceScatter of bucket b+1 fused with the AllGather of bucket b,
+    summed. Each bucket is its own AllReduce, so the
+    ring order of an element follows its shard within its bucket; checked
+    against the oracle's fold at bucket and shard boundaries, the ends and
+    random positions, and every rank's output equal."""
+    k, n = 8, 268_435_456
+    cap = n // 8
+    say("fp32 1 GiB pipelined buckets: generating inputs")
+    xs = rank_buffers(k, n, torch.float32, device=DEV)
+    for x, src in zip(xs, gen.ring_uniform_inputs(5, k, n, device=DEV)):
+        x.copy_(src)
+    out = rank_buffers(k, n, torch.float32, device=DEV)
+    for o in out:
+        o.fill_(float("nan"))
+    sync = BucketedSync(xs, out, cap, op="sum")
+    sync.step_pipelined()
+    torch.cuda.synchronize()
+    Lb = dps.dp_shard_len(cap, k)
+    rng = np.random.default_rng(3)
+    edges = np.concatenate([b * cap + c * Lb + np.array([-1, 0, 1]) for b in range(8) for c in range(k)])
+    idx = np.concatenate([rng.integers(0, n, 200_000), edges, np.arange(8), n - 1 - np.arange(8)])
+    idx = np.unique(idx[(idx >= 0) & (idx < n)].astype(np.int64))
+    ti = torch.from_numpy(idx).to(DEV)
+    owner = (idx % cap) // Lb
+    want = oracle.fold_at([to_np(x[ti]) for x in xs], owner, op="sum")
+    for r in range(k):
+        assert bits_equal(to_np(out[r][ti]), want), r
+        assert torch.equal(out[r].view(torch.int32), out[0].view(torch.int32)), r
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int32])
 def test_capped_grid_is_bit_identical(dtype):
     """With a cap on resident workgroups the kernels walk their tiles
