@@ -48,11 +48,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
 # sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "e902b19e7c1816f0db92585a975e0dd8cf6b58fef22ac2704010bc75c4e97543"
-                      "820d128eb8ae4b3b8f3ae32bcab1f3903fd4bc381b64895e7adf4e9f6d896ba0",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195382.8 + 49390.7) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25139.2 + 390817.2) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220531.7 + 439830.1) * 1024,
+    "sources_sha256": "6b4258669b13664da75507a59562c91a93d78cc66363b982c71a6faa18e74bd3"
+                      "b850e90b15c363987deced1fc1305e093b5a658a6f7105e7927a82440a46a8fb",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195384.1 + 49019.4) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25139.0 + 390956.5) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220533.0 + 439713.4) * 1024,
 }
 
 

@@ -38,6 +38,7 @@ struct RsParams {
     long long total_tiles;      // S * K * tiles_per_seg
     int max_blocks;             // persistent grid size (0: library default)
     int k, S;
+    int cache_out;              // store the shards with ordinary (cached) stores
 };
 
 // AllGather kernel arguments. Shard c's valid elements go to element c*L + j
@@ -50,6 +51,7 @@ struct AgParams {
     long long n, L, sub, tiles_per_seg, total_tiles;
     int max_blocks;
     int k, S;
+    int stream_in;              // load the shards with the nontemporal hint
 };
 
 // Fill the phase table and tiling of the parameter blocks; returns the grid size.

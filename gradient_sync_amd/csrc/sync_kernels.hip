@@ -67,9 +67,13 @@ constexpr int kAgBlock = DPS_AG_BLOCK;   // threads per AllGather workgroup
 #ifndef DPS_AG_NT_STORE
 #define DPS_AG_NT_STORE 1
 #endif
-#ifndef DPS_AG_NT_LOAD
-#define DPS_AG_NT_LOAD 0
-#endif
+// AllGather shard sets that fit in kCacheOutBytes (those a ReduceScatter
+// leaves in the caches) are loaded with the nontemporal hint, as each shard is
+// read once: K = 8 bf16 layer step, pipelined 78.59% -> 79.08% and 81.52% ->
+// 82.27% of HBM peak in two runs on two machines. Larger sets, read from
+// HBM, keep ordinary loads. The output stores stay nontemporal: with ordinary
+// stores the 400 MB a bucket's AllGather writes displace the next bucket's
+// shards from the Infinity Cache (pipelined 81.52% -> 74.70%).
 // persistent grid: workgroups per CU and the CU count the default assumes
 // Default grid: one workgroup per tile (a wave that finishes its tile exits
 // instead of waiting for its stores before loading the next tile). A positive
@@ -83,9 +87,18 @@ constexpr int kBlocksPerCU = DPS_BLOCKS_PER_CU;
 #endif
 constexpr int kCUs = DPS_CUS;
 
-#ifndef DPS_RS_NT_STORE
-#define DPS_RS_NT_STORE 1
+// ReduceScatter shards whose K together fit in kCacheOutBytes are stored with
+// ordinary stores: an AllGather reads them soon after (in the bucket pipeline,
+// in the next launch), and ordinary stores leave them in the caches (the 256 MB
+// Infinity Cache holds a 25,000,000-value bf16 bucket's 50 MB of shards) where
+// nontemporal stores do not. Measured on MI355X, K = 8 bf16 layer step:
+// pipelined 75.98% -> 78.59% of HBM peak, plain 70.35% -> 71.89% (same bits).
+// Larger shard sets cannot stay cached until they are read, so ordinary
+// stores would only displace other data; they stay nontemporal.
+#ifndef DPS_RS_CACHE_OUT_BYTES
+#define DPS_RS_CACHE_OUT_BYTES (128ll << 20)
 #endif
+constexpr long long kCacheOutBytes = DPS_RS_CACHE_OUT_BYTES;
 
 // Tile bodies start on a kAlign-byte boundary of the dominant stream: the K
 // inputs for ReduceScatter (unless DPS_RS_ALIGN_OUT), the K outputs for
@@ -106,13 +119,10 @@ __device__ __forceinline__ u32x4 load_stream(const char *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
-__device__ __forceinline__ void store_rs(char *p, u32x4 v)
+__device__ __forceinline__ void store_rs(char *p, u32x4 v, bool cached)
 {
-#if DPS_RS_NT_STORE
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-#else
-    *reinterpret_cast<u32x4 *>(p) = v;
-#endif
+    if (cached) *reinterpret_cast<u32x4 *>(p) = v;
+    else __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
 __device__ __forceinline__ void store_ag(char *p, u32x4 v)
@@ -322,7 +332,7 @@ __device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const
                 if (FULL || q < nv) store_ag(p.dst[fold_rank(c, i, K)] + off + q * 16, o);
             }
         } else {
-            if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]));
+            if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]), p.cache_out != 0);
         }
     }
 }
@@ -421,11 +431,8 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const long long q = FULL ? (long long)tid + u * kAgBlock : min((long long)tid + u * kAgBlock, nv - 1);
-#if DPS_AG_NT_LOAD
-        v[u] = load_stream(src + q * 16);
-#else
-        v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
-#endif
+        if (p.stream_in) v[u] = load_stream(src + q * 16);
+        else v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
     }
     const int nr = SKIP_OWN ? K - 1 : K;
 #pragma unroll
@@ -712,6 +719,7 @@ long long plan_rs(RsParams &p, int dt, bool lean)
     const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean, p.max_blocks > 0) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
+    p.cache_out = (long long)p.k * p.L * es <= kCacheOutBytes;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
@@ -734,6 +742,7 @@ long long plan_ag(AgParams &p, int dt)
     const long long te = (long long)kAgBlock * (p.max_blocks > 0 ? kUCapped : kAgU) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
+    p.stream_in = (long long)p.k * p.L * es <= kCacheOutBytes;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
