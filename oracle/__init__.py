@@ -82,8 +82,6 @@ def lib():
         L.orc_ar_weighted.argtypes = [_int, _vp, _vp, _vp, _i64, _int, _int, _int]
         L.orc_gemm_f64.restype = None
         L.orc_gemm_f64.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int]
-        L.orc_gemm_f32.restype = None
-        L.orc_gemm_f32.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int]
         L.orc_gemm_bf16_at.restype = None
         L.orc_gemm_bf16_at.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _int]
         L.orc_fsdp_layer.restype = None
@@ -260,18 +258,6 @@ def gemm_f64(a: np.ndarray, b: np.ndarray, trans_a: bool = False, nthreads: int 
     lib().orc_gemm_f64(a.ctypes.data, b.ctypes.data, c.ctypes.data, ab.ctypes.data, m, n, kk,
                        int(trans_a), nthreads)
     return c, ab
-
-
-def gemm_f32(a: np.ndarray, b: np.ndarray, trans_a: bool = False, nthreads: int = 1):
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    b = np.ascontiguousarray(b, dtype=np.float32)
-    m = a.shape[1] if trans_a else a.shape[0]
-    kk = a.shape[0] if trans_a else a.shape[1]
-    n = b.shape[1]
-    c = np.zeros((m, n), dtype=np.float32)
-    lib().orc_gemm_f32(a.ctypes.data, b.ctypes.data, c.ctypes.data, m, n, kk, int(trans_a),
-                       nthreads)
-    return c
 
 
 def gemm_bf16_at(a_bits: np.ndarray, b_bits: np.ndarray, rows, cols, nthreads: int = 1):

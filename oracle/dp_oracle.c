@@ -483,24 +483,6 @@ void orc_gemm_f64(const float *a, const float *b, double *c, double *abs_c, int6
     }
 }
 
-/* plain fp32 k-loop (kept for timing the CPU baseline) */
-void orc_gemm_f32(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t kk,
-                  int trans_a, int nthreads)
-{
-    set_threads(nthreads);
-#pragma omp parallel for schedule(static) if (nthreads > 1)
-    for (int64_t i = 0; i < m; ++i) {
-        for (int64_t j = 0; j < n; ++j) {
-            float s = 0.0f;
-            for (int64_t p = 0; p < kk; ++p) {
-                float av = trans_a ? a[p * m + i] : a[i * kk + p];
-                s = s + av * b[p * n + j];
-            }
-            c[i * n + j] = s;
-        }
-    }
-}
-
 /* bf16 inputs, fp64 result at sampled (rows[s], cols[s]); abs_c as above */
 void orc_gemm_bf16_at(const uint16_t *a, const uint16_t *b, int64_t n, int64_t kk,
                       const int64_t *rows, const int64_t *cols, int64_t count, double *vals,

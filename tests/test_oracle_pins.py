@@ -268,6 +268,157 @@ def test_weighted_rejects_bad_tokens():
         oracle.weighted_reduce_scatter(xs, [-1, 5])
 
 
+# ---------------------------------------------------------- bf16 weighted
+# The bf16 token-weighted reduction widens each bf16 gradient exactly to fp32,
+# multiplies by f32(t_r), folds the products in ring order in fp32 and rounds
+# once to bf16 after one division by f32(sum t). The pins below reach that
+# value without the oracle: the literal ring on the widened inputs, then
+# torch's round-to-nearest-even conversion; special token sets that reduce to
+# the average or to one rank's gradient; and an fp64 bound.
+
+def _bf16_grads(k, n, seed, std=1e-3):
+    return [gen.bf16_normal(seed, 7, r, n, std).view(torch.int16).numpy().view(np.uint16)
+            for r in range(k)]
+
+
+def _widen(b):
+    """bf16 bits -> fp32, exactly (the bf16 pattern is the top half of the fp32 one)."""
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _torch_bf16_bits(f32):
+    return torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _ring_weighted_bf16(xb, tokens):
+    """Independent value of the bf16 weighted ReduceScatter: literal ring over
+    f32(t_r) * widened g_r, division by f32(sum t) at the owner, library RNE."""
+    wf = np.array(tokens, dtype=np.float32)
+    ring = ring_sim.rs_f32([_widen(x) for x in xb], weights=wf, total=np.float32(sum(tokens)))
+    return [_torch_bf16_bits(r) for r in ring]
+
+
+@pytest.mark.parametrize("k,n", [(8, 3001), (3, 200), (5, 41)])
+def test_weighted_bf16_constant_power_of_two_tokens_equal_avg(k, n):
+    xb = _bf16_grads(k, n, 60 + k)
+    avg = oracle.reduce_scatter(xb, op="avg")
+    for c_tok in (1, 4, 64):
+        w = oracle.weighted_reduce_scatter(xb, [c_tok] * k)
+        for c in range(k):
+            assert w[c].tobytes() == avg[c].tobytes(), (k, c_tok, c)
+
+
+def test_weighted_bf16_one_hot_returns_that_ranks_bits():
+    k, n = 8, 2001
+    xb = _bf16_grads(k, n, 61, std=1.0)
+    L = oracle.shard_len(n, k)
+    for j in range(k):
+        for m in (0, 3, 10):
+            t = [0] * k
+            t[j] = 2 ** m
+            w = oracle.weighted_reduce_scatter(xb, t)
+            full = np.concatenate([w[c][:oracle.shard_valid(n, L, c)] for c in range(k)])
+            nz = (xb[j] & 0x7FFF) != 0
+            assert np.array_equal(full[nz], xb[j][nz]), (j, m)
+            assert not (full[~nz] & 0x7FFF).any()            # zeros stay zero (sign may differ)
+
+
+@pytest.mark.parametrize("k,n,seed", [(8, 10_019, 62), (6, 4097, 63), (2, 999, 64)])
+def test_weighted_bf16_general_tokens_ring_then_library_rounding(k, n, seed):
+    xb = _bf16_grads(k, n, seed)
+    t = gen.token_counts(seed, k)
+    got = oracle.weighted_reduce_scatter(xb, t)
+    want = _ring_weighted_bf16(xb, t)
+    L = oracle.shard_len(n, k)
+    for c in range(k):
+        nc = oracle.shard_valid(n, L, c)
+        assert np.array_equal(got[c][:nc], want[c]), c
+        assert not got[c][nc:].any()
+        # within the fp32 accumulation bound plus one bf16 rounding of the result
+        seg = slice(c * L, c * L + nc)
+        xs = [_widen(x[seg]).astype(np.float64) for x in xb]
+        ex = sum(np.float64(t[r]) * xs[r] for r in range(k)) / sum(t)
+        ab = sum(np.float64(t[r]) * np.abs(xs[r]) for r in range(k)) / sum(t)
+        g = _widen(got[c][:nc]).astype(np.float64)
+        assert np.all(np.abs(g - ex) <= _gamma(k + 2) * ab + 2.0 ** -8 * np.abs(ex))
+
+
+def test_weighted_bf16_all_reduce_is_rs_then_ag():
+    k, n = 8, 5003
+    xb = _bf16_grads(k, n, 65)
+    t = gen.token_counts(65, k)
+    ar = oracle.weighted_all_reduce(xb, t)
+    ag = oracle.all_gather(oracle.weighted_reduce_scatter(xb, t), n)
+    want = np.concatenate(_ring_weighted_bf16(xb, t))
+    for r in range(k):
+        assert ar[r].tobytes() == ag[r].tobytes() == want.tobytes()
+
+
+# Planted mistakes in the bf16 weighted reduction, each computed here in numpy
+# from the widened inputs; the ring-then-library pin above must reject every
+# one of them and accept the oracle.
+
+def _mutant_weighted_bf16(xb, tokens, kind):
+    k = len(xb)
+    n = xb[0].size
+    L = oracle.shard_len(n, k)
+    wf = np.array(tokens, dtype=np.float32)
+    total = np.float32(sum(tokens))
+    out = []
+    for c in range(k):
+        seg = slice(c * L, c * L + oracle.shard_valid(n, L, c))
+        order = [oracle.fold_rank(c, m, k, "rank" if kind == "rank_order" else "ring")
+                 for m in range(k)]
+        acc = None
+        for r in order:
+            g = _widen(xb[r][seg])
+            if kind == "product_rounded_to_bf16":
+                p = _widen(_torch_bf16_bits(wf[r] * g))
+            elif kind == "divide_before_fold":
+                p = (wf[r] / total) * g
+            else:
+                p = wf[r] * g
+            acc = p if acc is None else (acc + p).astype(np.float32)
+        if kind != "divide_before_fold":
+            acc = (acc / total).astype(np.float32)
+        out.append(_torch_bf16_bits(acc))
+    return out
+
+
+def _cancelling_bf16(k, n, seed):
+    """bf16 gradients in which, at every index, two ranks hold +2^30 and -2^30
+    and the others values in [-1, 1): the fp32 fold then depends on the order
+    far beyond its last bit (what is added before the pair cancels is lost)."""
+    rng = np.random.default_rng(seed)
+    small = [_torch_bf16_bits(rng.uniform(-1, 1, n).astype(np.float32)) for _ in range(k)]
+    big = np.uint16(0x4E80)                                  # 2^30
+    for i in range(n):
+        p, q = rng.choice(k, 2, replace=False)
+        small[p][i] = big
+        small[q][i] = big | np.uint16(0x8000)
+    return small
+
+
+@pytest.mark.parametrize("kind", ["product_rounded_to_bf16", "divide_before_fold", "rank_order"])
+def test_mutant_weighted_bf16_is_caught(kind):
+    k, n = 8, 20_011
+    if kind == "rank_order":
+        # equal tokens keep each cancelling pair's products equal and opposite
+        xb, t = _cancelling_bf16(k, n, 66), [5] * k
+    else:
+        xb, t = _bf16_grads(k, n, 66, std=1.0), gen.token_counts(66, k)
+    want = _ring_weighted_bf16(xb, t)
+    L = oracle.shard_len(n, k)
+    got = oracle.weighted_reduce_scatter(xb, t)
+    assert all(np.array_equal(got[c][:oracle.shard_valid(n, L, c)], want[c]) for c in range(k))
+    bad = _mutant_weighted_bf16(xb, t, kind)
+    assert not all(np.array_equal(bad[c], want[c]) for c in range(k))
+    # the correct computation written the same way passes the pin
+    good = _mutant_weighted_bf16(xb, t, "none")
+    assert all(np.array_equal(good[c], want[c]) for c in range(k))
+
+
 # -------------------------------------------------- AllGather / AllReduce
 
 @pytest.mark.parametrize("k,n", [(1, 7), (3, 10), (4, 1 << 12), (8, 8 * 33 + 5), (8, 3)])
@@ -324,6 +475,39 @@ def test_fold_at_matches_full():
     comp = [np.ascontiguousarray(x[idx]) for x in xs]
     got = oracle.fold_at(comp, idx // L, op="avg")
     assert np.array_equal(got, np.array([full[i // L][i % L] for i in idx], np.float32))
+
+
+def test_fold_bf16_at_matches_full_and_ring():
+    """The compact bf16 fold at sampled indices, shard boundaries included,
+    equals the full bf16 ReduceScatter and the literal ring on the widened
+    inputs followed by the library's rounding."""
+    k, n = 8, 4001
+    xb = _bf16_grads(k, n, 67, std=1.0)
+    L = oracle.shard_len(n, k)
+    idx = np.array([0, 1, L - 1, L, 2 * L - 1, 2 * L, 7 * L - 1, 7 * L, n - 1, 1234, 3001],
+                   np.int64)
+    comp = [np.ascontiguousarray(x[idx]) for x in xb]
+    for op in ("sum", "avg"):
+        full = oracle.reduce_scatter(xb, op=op)
+        ring = ring_sim.rs_f32([_widen(x) for x in xb], op=op)
+        got = oracle.fold_at(comp, idx // L, op=op)
+        for s_, i in enumerate(idx):
+            c, j = int(i // L), int(i % L)
+            assert got[s_] == full[c][j], (op, i)
+            assert got[s_] == _torch_bf16_bits(ring[c][j:j + 1])[0], (op, i)
+
+
+def test_rs_f32_at_matches_full():
+    k, n = 6, 9_001
+    xs = _rand_f32(k, n, 68)
+    L = oracle.shard_len(n, k)
+    idx = np.array([0, L - 1, L, 3 * L + 5, n - 1, 4000], np.int64)
+    for op in ("sum", "avg"):
+        full = oracle.reduce_scatter(xs, op=op)
+        ring = ring_sim.rs_f32(xs, op=op)
+        got = oracle.rs_at(xs, idx, op=op)
+        for s_, i in enumerate(idx):
+            assert got[s_] == full[i // L][i % L] == ring[i // L][i % L]
 
 
 # ------------------------------------------------------------------ shapes
