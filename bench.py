@@ -70,8 +70,18 @@ def kernel_sources_sha256() -> str:
     return out
 
 
+# The oracle baselines use at most this many threads: a one-GPU machine is
+# allotted 16 host cores, whatever the affinity mask of the process shows.
+HOST_CORE_CAP = 16
+
+
 def host_cores() -> int:
-    return min(len(os.sched_getaffinity(0)), 16)
+    return min(len(os.sched_getaffinity(0)), HOST_CORE_CAP)
+
+
+def cores_note() -> str:
+    return (f"oracle threads = min(affinity {len(os.sched_getaffinity(0))}, "
+            f"cap {HOST_CORE_CAP}: the host cores a one-GPU box is allotted)")
 
 
 def cpu_model() -> str:
@@ -123,6 +133,8 @@ def bench_layer(args):
     out = _in_rank_layout([torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)])
     sync = BucketedSync(grads, out, gen.BUCKET_ELEMS, op="avg")
     step_bytes = sync.algorithmic_bytes()
+    # shard bytes: written by each bucket's ReduceScatter, read by its AllGather
+    shard_bytes = sum(2 * n * 2 for _, n in sync.plan)
 
     def timed(step):
         for _ in range(args.warmup):
@@ -196,11 +208,24 @@ def bench_layer(args):
                    "rank_layout": _rank_layout_note()},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "bytes": "algorithmic: per bucket of n elements and phase, (K+1)*n*2 (each input "
+                 "element read once, each output element written once). In the pipelined "
+                 "step the shards (2*n*2 of the 2*(K+1)*n*2 bytes of a bucket) go through the "
+                 "256 MB Infinity Cache between the two phases, so not all counted bytes "
+                 "cross the HBM interface; plain_step below has no such reuse",
         "plain_step": {"value": round(value_plain, 2),
                        "pct_of_peak": round(100 * value_plain / HBM_PEAK_GBS, 2),
                        "ms_per_step": round(1e3 * wall_plain / args.steps, 4),
                        "schedule": "ReduceScatter then AllGather, one launch each, bucket by "
-                                   "bucket"},
+                                   "bucket, shards stored and loaded with nontemporal hints: "
+                                   "no cache reuse between the phases, every byte from or to "
+                                   "HBM (the figure the 70%-of-HBM-peak target is judged on)"},
+        "pipelined_excluding_shard_bytes": {
+            "value": round((step_bytes - shard_bytes) * args.steps / wall / 1e9, 2),
+            "pct_of_peak": round(100 * (step_bytes - shard_bytes) * args.steps / wall / 1e9
+                                 / HBM_PEAK_GBS, 2),
+            "what": "the pipelined step with the shard round trip left out of the bytes: a "
+                    "lower bound on its HBM-only rate"},
         "kernel_timing": "HIP events around every launch in a second pass of the same steps",
         "bytes_per_step": step_bytes,
         "kernels": {names[k_]: {kk: (round(v, 2) if isinstance(v, float) else v)
@@ -209,6 +234,13 @@ def bench_layer(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                     "traffic_source": "not measured in this run: the per-launch counters of "
+                                       "profiles/sync_kernels_layer_k8_bf16.md, used only "
+                                       "while the sync kernel sources hash to the value they "
+                                       "were taken on (else null). FETCH_SIZE and WRITE_SIZE "
+                                       "count L2-to-fabric bytes, so they include bytes the "
+                                       "Infinity Cache serves and cannot separate them from "
+                                       "HBM bytes",
                      "bytes_per_launch": launch_bytes,
                      "unit_bytes": "(K+1)*n*2 per bucket of n bf16 elements and phase; the "
                                    "fused launch carries one ReduceScatter and one AllGather"},
@@ -267,7 +299,39 @@ def cpu_baseline_layer(grads, k, seconds):
                       f"(K=8 x 25,000,000 bf16), {t:.1f} s",
             "single_thread_value": round(b / t1 / 1e9, 3),
             "single_thread_bits_equal": same,
-            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
+            "cpu_model": cpu_model(), "cores_note": cores_note()}
+
+
+def _timed_reps(fn, seconds):
+    """Run fn until ~seconds of CPU time have passed (at least once); returns
+    (reps, seconds taken)."""
+    reps, t = 0, 0.0
+    while reps == 0 or t < seconds:
+        t0 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t0
+        reps += 1
+    return reps, t
+
+
+def cpu_baseline_rs_ag(xs, op, nbytes, seconds, sample, tokens=None):
+    """The oracle's ReduceScatter + AllGather (token-weighted when tokens are
+    given) of the host arrays xs, repeated for ~seconds; GB/s on nbytes per
+    repetition."""
+    import oracle
+    cores = host_cores()
+    n = int(xs[0].size)
+
+    def once():
+        if tokens is None:
+            sh = oracle.reduce_scatter(xs, op=op, nthreads=cores)
+        else:
+            sh = oracle.weighted_reduce_scatter(xs, tokens, nthreads=cores)
+        oracle.all_gather(sh, n, nthreads=cores)
+    reps, t = _timed_reps(once, seconds)
+    return {"value": round(reps * nbytes / t / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "sample": f"{reps} x {sample}, {t:.1f} s",
+            "cores_note": cores_note(), "cpu_model": cpu_model()}
 
 
 # ------------------------------------------------------------ other configs
@@ -344,8 +408,18 @@ def bench_ring1m(args):
                      "back_to_back_abi_us": round(1e3 * back_abi, 2),
                      "graph_replay_us": round(1e3 * back_graph, 2),
                      "gbs_rs_ag_bytes": round(b / (back_graph * 1e-3) / 1e9, 1)}
-    return {"metric": "ring AllReduce K=4 N=1,048,576 S=4 (cache-resident, launch-bound)",
+    b = 2 * (k + 1) * n * 4
+    line = {"metric": "ring AllReduce K=4 N=1,048,576 S=4 (cache-resident, launch-bound)",
             "unit": "us", "results": res,
+            "roofline": {"bound": "hbm", "kernel": "rs_kernel<f32, avg, K=4, AllReduce> (one "
+                                                   "pass), per call of a graph replay",
+                         "achieved": res["f32_avg"]["gbs_rs_ag_bytes"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s",
+                         "frac": round(res["f32_avg"]["gbs_rs_ag_bytes"] / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "note": "41.9 MB per call: inputs and outputs stay in the 256 MB "
+                                 "Infinity Cache and a call lasts a few microseconds, so this "
+                                 "measures launch latency, not HBM; GB/s on 2(K+1)N*4 bytes"},
             "timing": "median_us: one call between two events (host latency included); "
                       "back_to_back_us: per call of 20 back-to-back calls through the Python "
                       "binding; back_to_back_abi_us: the same through the C ABI with the "
@@ -353,6 +427,13 @@ def bench_ring1m(args):
                       "HIP graph, per call of a replay; GB/s (on the graph time) on the "
                       "ReduceScatter + AllGather bytes 2(K+1)Ns",
             "config": {"workload": "K=4, 1,048,576 fp32/int32, S=4"}}
+    if not args.no_cpu_baseline:
+        hx = [x.cpu().numpy() for x in xf]
+        line["cpu_baseline"] = cpu_baseline_rs_ag(
+            hx, "avg", b, args.cpu_seconds,
+            "ReduceScatter (avg) + AllGather of the same K=4 x 1,048,576 fp32; GB/s on "
+            "2(K+1)N*4 bytes")
+    return line
 
 
 def bench_fsdp(args):
@@ -393,7 +474,7 @@ def bench_fsdp(args):
         res[name] = {"median_us": round(1e3 * med, 2), "min_us": round(1e3 * min(ms), 2),
                      "gemm_flops": flops,
                      "effective_tflops": round(flops / (med * 1e-3) / 1e12, 2)}
-    return {"metric": "FSDP layer step (AG w, y=xW, dW=x^T dy, RS dW), K=8",
+    line = {"metric": "FSDP layer step (AG w, y=xW, dW=x^T dy, RS dW), K=8",
             "timing": f"{batch} back-to-back calls between two HIP events, per call",
             "unit": "us", "median_us": res["step"]["median_us"], "min_us": res["step"]["min_us"],
             "gemm_flops": res["step"]["gemm_flops"],
@@ -401,8 +482,32 @@ def bench_fsdp(args):
             "with_dx": dict(res["step_with_dx"], what="the same plus the input gradient "
                                                        "dx = dy W^T (dp_fsdp_layer_ex)"),
             "mfma_peak_tflops": MFMA_F32_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "fsdp_step_kernel (the one-launch step)",
+                         "achieved": res["step"]["effective_tflops"], "peak": MFMA_F32_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": round(res["step"]["effective_tflops"] / MFMA_F32_TFLOPS, 4),
+                         "traffic": None,
+                         "unit_flops": "2 GEMMs of 2*m_local*d*f per rank (y = x W, dW = x^T dy), "
+                                       "K=8: 1,073,741,824 per step; the AllGather and "
+                                       "ReduceScatter bytes are folded into the operand loads"},
             "config": {"workload": "K=8, x[1024,512] N(0,1), w[512,512] N(0,0.02^2), "
                                    "dy[1024,512] N(0,1), fp32"}}
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = host_cores()
+        hxl = [t.cpu().numpy() for t in xl]
+        hws = [t.cpu().numpy() for t in ws]
+        hdy = [t.cpu().numpy() for t in dyl]
+        reps, t = _timed_reps(lambda: oracle.fsdp_layer(hxl, hws, hdy, nthreads=cores),
+                              args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(reps * res["step"]["gemm_flops"] / t / 1e9, 3), "unit": "GFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x the oracle's FSDP layer step (AllGather, fp64 y and dW, "
+                      f"fp64 ReduceScatter) on the same K=8 fixture, {t:.1f} s; GFLOP/s on the "
+                      f"same 2-GEMM flop count",
+            "cores_note": cores_note(), "cpu_model": cpu_model()}
+    return line
 
 
 def bench_weighted(args):
@@ -431,12 +536,26 @@ def bench_weighted(args):
                      "gbs": round(b / (med * 1e-3) / 1e9, 1),
                      "pct_of_peak": round(100 * b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                      "single_call_us": round(1e3 * single, 2)}
-    return {"metric": "token-weighted AllReduce K=8 N=10,000,019 fp32", "unit": "GB/s",
+    line = {"metric": "token-weighted AllReduce K=8 N=10,000,019 fp32", "unit": "GB/s",
             "value": res["one_pass"]["gbs"], "results": res, "tokens": toks,
+            "roofline": {"bound": "hbm", "kernel": "rs_kernel<f32, weighted, K=8, AllReduce> "
+                                                   "(one pass)",
+                         "achieved": res["one_pass"]["gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(res["one_pass"]["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "unit_bytes": "2*K*n*4 per call (each input read once, each output "
+                                       "written once), n = 10,000,019"},
             "timing": "median per call of 10 back-to-back calls between two events; "
                       "single_call_us: one call between two events (host latency included)",
             "config": {"workload": "K=8, 10,000,019 fp32 uniform[-1,1), log-normal(7,1) "
                                    "token counts, 2 docs/rank"}}
+    if not args.no_cpu_baseline:
+        hx = [x.cpu().numpy() for x in xs]
+        line["cpu_baseline"] = cpu_baseline_rs_ag(
+            hx, None, 2 * k * n * 4, args.cpu_seconds,
+            "token-weighted ReduceScatter + AllGather of the same K=8 x 10,000,019 fp32; GB/s "
+            "on the one-pass bytes 2*K*n*4", tokens=toks)
+    return line
 
 
 def bench_fused_ar(args):
@@ -472,167 +591,120 @@ def bench_fused_ar(args):
                        "rank_layout": _rank_layout_note()}}
 
 
-def _hip_runtime():
-    """The HIP runtime torch already loaded (stream calls torch does not wrap)."""
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_uint32)]
-    hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
-    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
-    hip.hipStreamDestroy.restype = ctypes.c_int
-    hip.hipGetErrorString.argtypes = [ctypes.c_int]
-    hip.hipGetErrorString.restype = ctypes.c_char_p
-    return hip
-
-
-def _cu_masked_stream(hip, first_cu, last_cu, n_cus):
-    """A stream (default priority) whose kernels run only on mask bits
-    [first_cu, last_cu). Mask bits go round-robin over the XCDs on this GPU,
-    so a contiguous range gives every XCD the same number of CUs, which the
-    driver requires of a mask. Returns the raw handle; raises on failure."""
-    import ctypes
-    words = (n_cus + 31) // 32
-    mask = (ctypes.c_uint32 * words)()
-    for b in range(first_cu, last_cu):
-        mask[b // 32] |= 1 << (b % 32)
-    st = ctypes.c_void_p()
-    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(st), words, mask)
-    if rc != 0:
-        raise RuntimeError(f"hipExtStreamCreateWithCUMask: {hip.hipGetErrorString(rc).decode()}")
-    return st
-
-
 def bench_c3(args):
     import torch
 
     import gen
     import gradient_sync_amd as dps
+    from gradient_sync_amd.buckets import rank_buffers
+    from gradient_sync_amd.concurrency import SCHEDULES, C3Pair
     k, n = 8, 268_435_456
     log("[c3] generating 8 x 1 GiB fp32 and 2 x 8192^2 bf16")
-    xs = _in_rank_layout(gen.ring_uniform_inputs(5, k, n, device="cuda"))
+    xs = rank_buffers(k, n, torch.float32)
+    for r in range(k):
+        xs[r].copy_(gen.uniform_pm1(5, 0, r, n, device="cuda"))
     L = dps.dp_shard_len(n, k)
-    from gradient_sync_amd.buckets import rank_buffers
     sh = rank_buffers(k, L, torch.float32)
     out = rank_buffers(k, n, torch.float32)
     a, b = gen.gemm_bf16_inputs(5, 8192, 8192, 8192, device="cuda")
     c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    pair = C3Pair(xs, sh, out, a, b, c)
     comm_bytes = 2 * (k + 1) * n * 4
     flops = 2 * 8192 ** 3
 
-    def make_comm(cap):
-        def comm(stream=None):
-            dps.dp_reduce_scatter_ex(xs, sh, op="sum", max_workgroups=cap, stream=stream)
-            dps.dp_all_gather_ex(sh, out, max_workgroups=cap, stream=stream)
-        return comm
-
-    def make_gemm(share):
-        def gemm(stream=None):
-            dps.dp_gemm_bf16_ex(a, b, c, share_cu=share, stream=stream)
-        return gemm
-
-    def concurrent(comm, gemm, first, streams=None):
-        sa_, sb_ = streams if streams else (sa, sb)
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        ea = torch.cuda.Event(enable_timing=True)
-        eb = torch.cuda.Event(enable_timing=True)
-        cur = torch.cuda.current_stream()
-        start.record(cur)
-        sa_.wait_event(start)
-        sb_.wait_event(start)
-        order = [(comm, sa_, ea), (gemm, sb_, eb)] if first == "comm" else [(gemm, sb_, eb), (comm, sa_, ea)]
-        for fn, st, ev in order:
-            fn(stream=st)
-            ev.record(st)
-        torch.cuda.synchronize()
-        return max(start.elapsed_time(ea), start.elapsed_time(eb))
-
-    # Schedules: c3_base = default grids, GEMM launched first; sp = the
-    # collective launched first (schedule prioritisation) with its resident
-    # workgroups capped so the GEMM still gets CUs; share = one persistent sync
-    # workgroup per CU beside one GEMM workgroup of the smaller-register variant;
-    # rp (below) = the collective and the GEMM on disjoint CU-masked streams.
-    schedules = [("base", 0, False, "gemm"), ("base_comm_first", 0, False, "comm"),
-                 ("sp_cap256", 256, False, "comm"), ("sp_cap128", 128, False, "comm"),
-                 ("share_cu", 256, True, "comm"), ("share_cu_gemm_first", 256, True, "gemm")]
+    # T_comm and T_gemm: each kernel alone on the streams the schedule uses
+    # (the CU-masked ones for RP); T_concurrent: start event to the later of
+    # the two completion events. 6 warm-up + 9 measured runs, median.
     iso = {}
     res = {}
-    for name, cap, share, first in schedules:
-        comm, gemm = make_comm(cap), make_gemm(share)
-        if (cap, "comm") not in iso:
-            iso[(cap, "comm")] = statistics.median(_time_ms(comm))
-        if (share, "gemm") not in iso:
-            iso[(share, "gemm")] = statistics.median(_time_ms(gemm))
-        t_comm, t_gemm = iso[(cap, "comm")], iso[(share, "gemm")]
-        for _ in range(6):
-            concurrent(comm, gemm, first)
-        tc = statistics.median([concurrent(comm, gemm, first) for _ in range(9)])
-        s = (t_comm + t_gemm) / tc
-        s_ideal = (t_comm + t_gemm) / max(t_comm, t_gemm)
-        log(f"[c3] {name}: T_comm {t_comm:.3f} T_gemm {t_gemm:.3f} T_conc {tc:.3f} S {s:.3f}")
-        res[name] = {"comm_max_workgroups": cap, "gemm_share_cu": share, "first": first,
-                     "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
-                     "t_concurrent_ms": round(tc, 4), "S": round(s, 4),
-                     "S_ideal": round(s_ideal, 4), "S_over_S_ideal": round(s / s_ideal, 4),
-                     "pct_of_ideal_gain": round(100 * (s - 1) / (s_ideal - 1), 1)
-                     if s_ideal > 1 else None}
-    # RP (resource partitioning): the collective on a CU-masked stream holding
-    # CUs [0, n_comm) of the mask, the GEMM on one holding the rest. T_comm and
-    # T_gemm are the same kernels alone on the same masked streams.
-    hip = _hip_runtime()
-    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for n_comm in (128, 144, 160, 176, 192):
-        name = f"rp_comm{n_comm}"
-        raw = []
+    for name, sched in SCHEDULES.items():
         try:
-            raw.append(_cu_masked_stream(hip, 0, n_comm, n_cus))
-            raw.append(_cu_masked_stream(hip, n_comm, n_cus, n_cus))
+            sc, sg, closers = pair.streams(sched)
         except RuntimeError as e:
             res[name] = {"error": str(e)}
-            torch.cuda.synchronize()
-            for st in raw:
-                hip.hipStreamDestroy(st)
             continue
-        sc, sg = (torch.cuda.ExternalStream(st.value) for st in raw)
-        comm, gemm = make_comm(0), make_gemm(False)
-        t_comm = statistics.median(_time_ms(lambda: comm(stream=sc), stream=sc))
-        t_gemm = statistics.median(_time_ms(lambda: gemm(stream=sg), stream=sg))
-        for _ in range(6):
-            concurrent(comm, gemm, "gemm", streams=(sc, sg))
-        tc = statistics.median([concurrent(comm, gemm, "gemm", streams=(sc, sg)) for _ in range(9)])
-        torch.cuda.synchronize()
-        for st in raw:
-            hip.hipStreamDestroy(st)
+        try:
+            key_c = ("comm", sched.comm_max_workgroups, sched.comm_cus)
+            key_g = ("gemm", sched.gemm_share_cu, sched.comm_cus)
+            if key_c not in iso:
+                iso[key_c] = statistics.median(_time_ms(
+                    lambda: pair.comm(sc, sched.comm_max_workgroups), stream=sc))
+            if key_g not in iso:
+                iso[key_g] = statistics.median(_time_ms(
+                    lambda: pair.gemm(sg, sched.gemm_share_cu), stream=sg))
+
+            def conc():
+                start, ec, eg = pair.launch(sched, sc, sg)
+                torch.cuda.synchronize()
+                return max(start.elapsed_time(ec), start.elapsed_time(eg))
+            for _ in range(6):
+                conc()
+            tc = statistics.median([conc() for _ in range(9)])
+        finally:
+            for st in closers:
+                st.close()
+        t_comm, t_gemm = iso[key_c], iso[key_g]
         s_ = (t_comm + t_gemm) / tc
         s_ideal = (t_comm + t_gemm) / max(t_comm, t_gemm)
         log(f"[c3] {name}: T_comm {t_comm:.3f} T_gemm {t_gemm:.3f} T_conc {tc:.3f} S {s_:.3f}")
-        res[name] = {"comm_cus": n_comm, "gemm_cus": n_cus - n_comm, "first": "gemm",
-                     "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
-                     "t_concurrent_ms": round(tc, 4), "S": round(s_, 4),
-                     "S_ideal": round(s_ideal, 4), "S_over_S_ideal": round(s_ / s_ideal, 4),
-                     "pct_of_ideal_gain": round(100 * (s_ - 1) / (s_ideal - 1), 1)
-                     if s_ideal > 1 else None}
-    best_serial = min(v for (_, kind), v in iso.items() if kind == "comm") + \
-        min(v for (_, kind), v in iso.items() if kind == "gemm")
+        r = {"first": sched.first, "t_comm_ms": round(t_comm, 4), "t_gemm_ms": round(t_gemm, 4),
+             "t_concurrent_ms": round(tc, 4), "S": round(s_, 4), "S_ideal": round(s_ideal, 4),
+             "S_over_S_ideal": round(s_ / s_ideal, 4),
+             "pct_of_ideal_gain": round(100 * (s_ - 1) / (s_ideal - 1), 1) if s_ideal > 1 else None}
+        if sched.comm_cus:
+            r["comm_cus"] = sched.comm_cus
+            r["gemm_cus"] = torch.cuda.get_device_properties(0).multi_processor_count - sched.comm_cus
+        else:
+            r["comm_max_workgroups"] = sched.comm_max_workgroups
+            r["gemm_share_cu"] = sched.gemm_share_cu
+        res[name] = r
+    comm_iso = [v for key, v in iso.items() if key[0] == "comm" and key[2] == 0]
+    gemm_iso = [v for key, v in iso.items() if key[0] == "gemm" and key[2] == 0]
+    best_serial = min(comm_iso) + min(gemm_iso)
     for v in res.values():
         if "t_concurrent_ms" in v:
             v["S_vs_best_serial"] = round(best_serial / v["t_concurrent_ms"], 4)
-    t_comm0, t_gemm0 = iso[(0, "comm")], iso[(False, "gemm")]
-    return {"metric": "C3: RS+AG (K=8, 1 GiB/rank fp32) concurrent with bf16 GEMM 8192^3",
+    t_comm0, t_gemm0 = iso[("comm", 0, 0)], iso[("gemm", False, 0)]
+    best_name = max((kk for kk, v in res.items() if "S" in v),
+                    key=lambda kk: res[kk]["S_vs_best_serial"])
+    best = res[best_name]
+    line = {"metric": "C3: RS+AG (K=8, 1 GiB/rank fp32) concurrent with bf16 GEMM 8192^3",
+            "unit": "x (S = T_serial / T_concurrent)", "value": res["base"]["S"],
+            "higher_is_better": True,
             "t_comm_ms": round(t_comm0, 4), "t_gemm_ms": round(t_gemm0, 4),
             "comm_gbs": round(comm_bytes / (t_comm0 * 1e-3) / 1e9, 1),
             "gemm_tflops": round(flops / (t_gemm0 * 1e-3) / 1e12, 1),
-            "gemm_frac_of_bf16_peak": round(flops / (t_gemm0 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
             "best_serial_ms": round(best_serial, 4),
+            "best_schedule": {"name": best_name, "t_concurrent_ms": best["t_concurrent_ms"],
+                              "S_vs_best_serial": best["S_vs_best_serial"]},
             "S_definition": "S = (T_comm + T_gemm) / T_concurrent with T_comm, T_gemm of the "
-                            "same kernels run alone; S_ideal = (T_comm + T_gemm) / max; "
-                            "pct_of_ideal_gain = (S-1)/(S_ideal-1)",
+                            "same kernels run alone on the same streams; S_ideal = "
+                            "(T_comm + T_gemm) / max; pct_of_ideal_gain = (S-1)/(S_ideal-1); "
+                            "S_vs_best_serial = (fastest T_comm + fastest T_gemm, default "
+                            "streams) / T_concurrent",
             "results": res,
+            "roofline": {"bound": "hbm", "kernel": "the collective alone: rs_kernel<f32, sum, "
+                                                   "K=8> then ag_kernel<4-byte, K=8>",
+                         "achieved": round(comm_bytes / (t_comm0 * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(comm_bytes / (t_comm0 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "unit_bytes": "(K+1)*n*4 per phase, n = 268,435,456, two phases"},
+            "roofline_gemm": {"bound": "mfma", "kernel": "dp_gemm_bf16 8192^3",
+                              "achieved": round(flops / (t_gemm0 * 1e-3) / 1e12, 1),
+                              "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(flops / (t_gemm0 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4)},
             "config": {"workload": "K=8 x 268,435,456 fp32 RS(sum)+AG on stream A, "
-                                   "C=A.B^T bf16 8192^3 on stream B; 6 warm-up + 9 measured",
+                                   "bf16 GEMM 8192^3 on stream B; 6 warm-up + 9 measured",
                        "rank_layout": _rank_layout_note()}}
+    if not args.no_cpu_baseline:
+        n_s = 1 << 24
+        hx = [xs[r][:n_s].cpu().numpy() for r in range(k)]
+        line["cpu_baseline"] = cpu_baseline_rs_ag(
+            hx, "sum", 2 * (k + 1) * n_s * 4, args.cpu_seconds,
+            "ReduceScatter (sum) + AllGather of the first 16,777,216 elements of each rank "
+            "(K=8 fp32); GB/s on the same (K+1)*n*4 bytes per phase")
+    return line
 
 
 def _odc_kernel_rooflines(rounds8, singles, acc, out, n, div, with_np1):
@@ -788,6 +860,7 @@ def bench_overlap(args):
     import gen
     import gradient_sync_amd as dps
     from gradient_sync_amd.buckets import BucketedSync
+    from gradient_sync_amd.concurrency import CuMaskedStream
     k, total, cap = 8, gen.LAYER_PARAMS, gen.BUCKET_ELEMS
     pieces = gen.layer_backward_pieces()
     grad = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
@@ -797,7 +870,6 @@ def bench_overlap(args):
     comm = torch.cuda.Stream()
     cur = torch.cuda.current_stream()
     sync = BucketedSync(grad, out, cap, op="avg")
-    hip = _hip_runtime()
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     res = {}
     for t in (256, 1024):
@@ -840,15 +912,14 @@ def bench_overlap(args):
             name = f"overlap_rp_comm{n_comm}"
             raw = []
             try:
-                raw.append(_cu_masked_stream(hip, n_comm, n_cus, n_cus))
-                raw.append(_cu_masked_stream(hip, 0, n_comm, n_cus))
+                raw.append(CuMaskedStream(n_comm, n_cus))
+                raw.append(CuMaskedStream(0, n_comm))
             except RuntimeError as e:
                 r[f"error_{name}"] = str(e)
-                torch.cuda.synchronize()
                 for st in raw:
-                    hip.hipStreamDestroy(st)
+                    st.close()
                 continue
-            sc, sm = (torch.cuda.ExternalStream(st.value) for st in raw)
+            sc, sm = (st.stream for st in raw)
 
             def rp():
                 sc.wait_stream(cur)
@@ -858,9 +929,8 @@ def bench_overlap(args):
                 cur.wait_stream(sc)
                 cur.wait_stream(sm)
             r[f"t_{name}_ms"] = med(rp)
-            torch.cuda.synchronize()
             for st in raw:
-                hip.hipStreamDestroy(st)
+                st.close()
             names.append(name)
         for name in names:
             r[f"hidden_comm_frac_{name}"] = round(

@@ -38,7 +38,10 @@ struct RsParams {
     long long total_tiles;      // S * K * tiles_per_seg
     int max_blocks;             // persistent grid size (0: library default)
     int k, S;
-    int cache_out;              // store the shards with ordinary (cached) stores
+    // set by the caller when an AllGather reads the shards next: then shard
+    // sets small enough to stay in the caches are stored with ordinary
+    // (cached) stores (the planner clears it for larger sets)
+    int cache_out;
 };
 
 // AllGather kernel arguments. Shard c's valid elements go to element c*L + j
@@ -51,7 +54,10 @@ struct AgParams {
     long long n, L, sub, tiles_per_seg, total_tiles;
     int max_blocks;
     int k, S;
-    int stream_in;              // load the shards with the nontemporal hint
+    // set by the caller when a ReduceScatter left the shards in the caches:
+    // they are then loaded with the nontemporal hint (cleared by the planner
+    // for shard sets too large to have stayed cached)
+    int stream_in;
 };
 
 // Fill the phase table and tiling of the parameter blocks; returns the grid size.

@@ -67,9 +67,9 @@ constexpr int kAgBlock = DPS_AG_BLOCK;   // threads per AllGather workgroup
 #ifndef DPS_AG_NT_STORE
 #define DPS_AG_NT_STORE 1
 #endif
-// AllGather shard sets that fit in kCacheOutBytes (those a ReduceScatter
-// leaves in the caches) are loaded with the nontemporal hint, as each shard is
-// read once: K = 8 bf16 layer step, pipelined 78.59% -> 79.08% and 81.52% ->
+// AllGather shard sets that a ReduceScatter left in the caches (see
+// kCacheOutBytes) are loaded with the nontemporal hint, as each shard is read
+// once: K = 8 bf16 layer step, pipelined 78.59% -> 79.08% and 81.52% ->
 // 82.27% of HBM peak in two runs on two machines. Larger sets, read from
 // HBM, keep ordinary loads. The output stores stay nontemporal: with ordinary
 // stores the 400 MB a bucket's AllGather writes displace the next bucket's
@@ -87,14 +87,17 @@ constexpr int kBlocksPerCU = DPS_BLOCKS_PER_CU;
 #endif
 constexpr int kCUs = DPS_CUS;
 
-// ReduceScatter shards whose K together fit in kCacheOutBytes are stored with
-// ordinary stores: an AllGather reads them soon after (in the bucket pipeline,
-// in the next launch), and ordinary stores leave them in the caches (the 256 MB
-// Infinity Cache holds a 25,000,000-value bf16 bucket's 50 MB of shards) where
-// nontemporal stores do not. Measured on MI355X, K = 8 bf16 layer step:
-// pipelined 75.98% -> 78.59% of HBM peak, plain 70.35% -> 71.89% (same bits).
-// Larger shard sets cannot stay cached until they are read, so ordinary
-// stores would only displace other data; they stay nontemporal.
+// Where an AllGather reads the shards next (the fused ReduceScatter + AllGather
+// launch of the bucket pipeline, whose AllGather half reads the previous
+// launch's shards, and the two-phase AllReduce), shard sets whose K shards
+// together fit in kCacheOutBytes are stored with ordinary stores, which leave
+// them in the caches (the 256 MB Infinity Cache holds a 25,000,000-value bf16
+// bucket's 50 MB of shards) where nontemporal stores do not. Measured on
+// MI355X, K = 8 bf16 layer step: pipelined 75.98% -> 78.59% of HBM peak (same
+// bits). A ReduceScatter whose shards are not read next keeps nontemporal
+// stores: ordinary ones slowed the standalone kernel from 76.75 to 84.32 us
+// per 25M bf16 bucket (K = 8). Larger shard sets cannot stay cached until they
+// are read, so they stay nontemporal too.
 #ifndef DPS_RS_CACHE_OUT_BYTES
 #define DPS_RS_CACHE_OUT_BYTES (128ll << 20)
 #endif
@@ -719,7 +722,7 @@ long long plan_rs(RsParams &p, int dt, bool lean)
     const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean, p.max_blocks > 0) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
-    p.cache_out = (long long)p.k * p.L * es <= kCacheOutBytes;
+    p.cache_out = p.cache_out && (long long)p.k * p.L * es <= kCacheOutBytes;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
@@ -742,7 +745,7 @@ long long plan_ag(AgParams &p, int dt)
     const long long te = (long long)kAgBlock * (p.max_blocks > 0 ? kUCapped : kAgU) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
-    p.stream_in = (long long)p.k * p.L * es <= kCacheOutBytes;
+    p.stream_in = p.stream_in && (long long)p.k * p.L * es <= kCacheOutBytes;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
@@ -800,6 +803,10 @@ hipError_t launch_rsag(const RsParams &rp0, const AgParams &ap0, int dt, int ep,
     AgParams ap = ap0;
     rp.max_blocks = 0;
     ap.max_blocks = 0;
+    // the AllGather half reads the shards the previous launch's ReduceScatter
+    // half left in the caches, and this launch's shards are read by the next
+    rp.cache_out = 1;
+    ap.stream_in = 1;
     plan_rs(rp, dt);
     plan_ag(ap, dt);
     const long long grid = rp.total_tiles + ap.total_tiles;

@@ -12,6 +12,7 @@ import gen
 import gradient_sync_amd as dps
 import oracle
 from gradient_sync_amd.buckets import BucketedSync, rank_buffers
+from gradient_sync_amd.concurrency import CuMaskedStream
 from tests.helpers import bits_equal, from_np, say, to_np
 
 pytestmark = pytest.mark.gpu
@@ -233,20 +234,8 @@ def test_cu_masked_stream():
     """On a stream confined to 64 of the CUs (hipExtStreamCreateWithCUMask, the
     resource partitioning the concurrency measurement uses) the pipelined
     bucket step and the one-pass AllReduce give the oracle's bits."""
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_uint32)]
-    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
-    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    words = (n_cus + 31) // 32
-    mask = (ctypes.c_uint32 * words)()
-    for b in range(64):                  # bits go round-robin over the XCDs
-        mask[b // 32] |= 1 << (b % 32)
-    raw = ctypes.c_void_p()
-    assert hip.hipExtStreamCreateWithCUMask(ctypes.byref(raw), words, mask) == 0
-    try:
-        st = torch.cuda.ExternalStream(raw.value)
+    with CuMaskedStream(0, 64) as ms:
+        st = ms.stream
         k, total, cap = 8, 2_500_003, 1_000_003
         grads = [x.to(torch.bfloat16) for x in gen.ring_uniform_inputs(77, k, total, device=DEV)]
         out = [torch.full((total,), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(k)]
@@ -266,9 +255,6 @@ def test_cu_masked_stream():
             dps.dp_all_reduce(grads, out, op="sum")
         st.synchronize()
         assert bits_equal(to_np(out[0]), oracle.all_reduce(host, op="sum")[0])
-    finally:
-        torch.cuda.synchronize()
-        hip.hipStreamDestroy(raw)
 
 
 # ------------------------------------------------------------ weighted

@@ -419,6 +419,63 @@ def test_mutant_weighted_bf16_is_caught(kind):
     assert all(np.array_equal(good[c], want[c]) for c in range(k))
 
 
+# ------------------------------------------------------ IEEE special values
+# The oracle's folds on the special-value scenarios that the GPU parity tests
+# use, against what IEEE binary32 arithmetic and round-to-nearest-even fix for
+# each scenario, whatever the fold order.
+
+def _special_case(dtype, k, n, seed, op):
+    from tests.special_values import scenarios, special_inputs
+    bits = special_inputs(dtype, k, n, seed)
+    host = [b if dtype == torch.bfloat16 else b.view(np.float32) for b in bits]
+    out = np.concatenate(oracle.reduce_scatter(host, op=op))[:n]
+    return bits, scenarios(n, seed), (out if dtype == torch.bfloat16 else out.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("k,op", [(8, "sum"), (8, "avg"), (6, "avg")])
+def test_oracle_on_special_values(dtype, k, op):
+    from tests.special_values import BF16, F32, _is_nan
+    bf = dtype == torch.bfloat16
+    S = BF16 if bf else F32
+    n = 40_000
+    bits, scen, out = _special_case(dtype, k, n, 7, op)
+    mag = out & (0x7FFF if bf else 0x7FFFFFFF)
+    inf = mag == (S["pinf"])
+    nan = _is_nan(out, out.dtype)
+    sign = (out >> (15 if bf else 31)) & 1
+    # every rank -0.0: the fold keeps -0.0 (no +0.0 seed), and so does 1/K
+    assert np.all(out[scen == 4] == S["nz"])
+    # +Inf with -Inf, or any NaN operand: NaN
+    assert np.all(nan[scen == 7]) and np.all(nan[scen == 8]) and np.all(nan[scen == 9])
+    # one infinity among finite values: that infinity
+    assert np.all(inf[scen == 6])
+    # all subnormal operands: the exact sum is a subnormal or the smallest
+    # normals, never zero unless it cancels, and never NaN or Inf
+    assert not np.any(nan[scen == 10] | inf[scen == 10])
+    if op == "sum":
+        if bf:
+            # max + 2^119 is the tie above max: rounds to even, i.e. to Inf;
+            # max + 2^118 stays max
+            assert np.all(inf[scen == 12]) and np.all(mag[scen == 13] == S["max"])
+            # 1 + 2^-8 -> 1, (1 + 2^-7) + 2^-8 -> 1 + 2^-6 (ties to even)
+            t = mag[scen == 14]
+            assert np.all((t == 0x3F80) | (t == 0x3F82))
+        else:
+            assert np.all(inf[(scen == 12) | (scen == 13)])
+            t = mag[scen == 14]
+            # 1 + 2^-24 -> 1, (1 + 2^-23) + 2^-24 -> 1 + 2^-22
+            assert np.all((t == 0x3F800000) | (t == 0x3F800002))
+    # the sign of a tie or overflow follows its operands' common sign
+    for sc in (12, 13, 14):
+        m = scen == sc
+        src_sign = np.zeros(n, np.int64)
+        for b in bits:
+            v = b & (0x7FFF if bf else 0x7FFFFFFF)
+            src_sign = np.where(v != 0, (b >> (15 if bf else 31)) & 1, src_sign)
+        assert np.array_equal(sign[m], src_sign[m])
+
+
 # -------------------------------------------------- AllGather / AllReduce
 
 @pytest.mark.parametrize("k,n", [(1, 7), (3, 10), (4, 1 << 12), (8, 8 * 33 + 5), (8, 3)])
