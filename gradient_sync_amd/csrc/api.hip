@@ -118,9 +118,11 @@ dp_status_t validate_rs_ag_common(const void *const *send, void *const *recv, si
 
 // ReduceScatter launch shared by the RS and AR entry points.
 // out[c] = element 0 of shard c's output region.
+// keep_cached: an AllGather reads the shards next (two-phase AllReduce, bucket
+// pipeline), so small shard sets are left in the caches.
 dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t L, int k, int dt,
                    int ep, float scale, const float *w, int write_pads, int s_chunks,
-                   hipStream_t st, int max_wg = 0, bool lean = false)
+                   hipStream_t st, int max_wg = 0, bool lean = false, bool keep_cached = false)
 {
     dps::RsParams p;
     memset(&p, 0, sizeof(p));
@@ -136,11 +138,15 @@ dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t
     p.k = k;
     p.S = s_chunks;
     p.max_blocks = max_wg;
+    p.cache_out = keep_cached ? 1 : 0;
     return hip_status(dps::launch_rs(p, dt, ep, st, lean));
 }
 
+// shards_cached: the shards were just written by a ReduceScatter that left
+// them in the caches.
 dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_t L, int k, int dt,
-                   int skip_own, int s_chunks, hipStream_t st, int max_wg = 0)
+                   int skip_own, int s_chunks, hipStream_t st, int max_wg = 0,
+                   bool shards_cached = false)
 {
     dps::AgParams p;
     memset(&p, 0, sizeof(p));
@@ -154,6 +160,7 @@ dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_
     p.k = k;
     p.S = s_chunks;
     p.max_blocks = max_wg;
+    p.stream_in = shards_cached ? 1 : 0;
     return hip_status(dps::launch_ag(p, dt, st));
 }
 
@@ -195,11 +202,11 @@ dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, 
     }
     char *rs_out[DP_MAX_K];
     for (int c = 0; c < k; ++c) rs_out[c] = (char *)recv[c] + (size_t)c * (size_t)L * (size_t)es;
-    dp_status_t s =
-        run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st, max_wg, lean);
+    dp_status_t s = run_rs(send, rs_out, (int64_t)n, L, k, dt, ep, scale, w, 0, s_chunks, st,
+                           max_wg, lean, true);
     if (s != DP_OK) return s;
     return run_ag((const void *const *)rs_out, (char *const *)recv, (int64_t)n, L, k, dt, 1,
-                  s_chunks, st, max_wg);
+                  s_chunks, st, max_wg, true);
 }
 
 // ReduceScatter argument checks (shared by the single and the fused call);
@@ -345,12 +352,14 @@ dp_status_t dp_reduce_scatter_all_gather(const void *const *rs_send, void *const
     float scale;
     pick_epilogue(op, k, ep, scale);
     hipStream_t st = (hipStream_t)stream;
+    // a pipeline step: the shards written here are gathered by the next step,
+    // and the shards gathered here were written by the previous one
     if (ag_n == 0)
         return run_rs(rs_send, (char *const *)rs_recv, (int64_t)rs_n, (int64_t)Lr, k, dt, ep, scale,
-                      nullptr, 1, s_chunks, st);
+                      nullptr, 1, s_chunks, st, 0, false, true);
     if (rs_n == 0)
         return run_ag(ag_send, (char *const *)ag_recv, (int64_t)ag_n, (int64_t)La, k, dt,
-                      ag_in_place ? 1 : 0, s_chunks, st);
+                      ag_in_place ? 1 : 0, s_chunks, st, 0, true);
     dps::RsParams rp;
     dps::AgParams ap;
     memset(&rp, 0, sizeof(rp));
