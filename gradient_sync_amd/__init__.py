@@ -30,13 +30,15 @@ __all__ = [
     "dp_fsdp_layer", "dp_gemm_bf16", "DP_MAX_K", "EXPORTS", "LaunchOpts",
     "dp_reduce_scatter_ex", "dp_all_gather_ex", "dp_all_reduce_ex", "dp_gemm_bf16_ex",
     "dp_weighted_reduce_ex", "dp_scatter_accumulate", "dp_settle", "GradPiece", "HipEvents",
-    "dp_backward_allreduce_overlap", "dp_reduce_scatter_all_gather",
+    "dp_backward_allreduce_overlap", "dp_reduce_scatter_all_gather", "dp_fsdp_layer_static",
+    "DP_STATIC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdpsync.so")
 
-DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_ALIAS, DP_ERR_HIP = range(5)
+DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_ALIAS, DP_ERR_HIP, DP_ERR_SCRATCH = range(6)
+DP_STATIC_SCRATCH_BYTES = 32 << 20      # include/dpsync.h
 DP_F32, DP_BF16, DP_I32 = 0, 1, 2
 DP_SUM, DP_AVG = 0, 1
 DP_MAX_K = 64
@@ -47,7 +49,7 @@ EXPORTS = ("dp_shard_len", "dp_status_string", "dp_last_hip_error", "dp_version"
            "dp_fsdp_layer", "dp_gemm_bf16", "dp_reduce_scatter_ex", "dp_all_gather_ex",
            "dp_all_reduce_ex", "dp_gemm_bf16_ex", "dp_weighted_reduce_ex",
            "dp_scatter_accumulate", "dp_settle", "dp_backward_allreduce_overlap",
-           "dp_reduce_scatter_all_gather", "dp_fsdp_layer_ex")
+           "dp_reduce_scatter_all_gather", "dp_fsdp_layer_ex", "dp_fsdp_layer_static")
 
 _DTYPES = {torch.float32: DP_F32, torch.bfloat16: DP_BF16, torch.int32: DP_I32}
 _OPS = {"sum": DP_SUM, "avg": DP_AVG}
@@ -158,6 +160,8 @@ def lib():
         L.dp_fsdp_layer.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dp_fsdp_layer_ex.restype = _int
         L.dp_fsdp_layer_ex.argtypes = [_int, _i64, _i64, _i64] + [_vp] * 9
+        L.dp_fsdp_layer_static.restype = _int
+        L.dp_fsdp_layer_static.argtypes = [_int, _i64, _i64, _i64] + [_vp] * 7
         L.dp_gemm_bf16.restype = _int
         L.dp_gemm_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
         P = ctypes.POINTER(LaunchOpts)
@@ -412,6 +416,41 @@ def dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full=None, dw_
                                P(dy_local) if bwd else None, P(w_full), P(y_local),
                                P(dw_full) if bwd else None, P(dw_shard) if bwd else None,
                                _stream(stream)), "dp_fsdp_layer")
+
+
+def dp_fsdp_layer_static(x_local, w_shard, dy_local, y_local, dw_shard=None, dx_local=None,
+                         stream=None):
+    """dp_fsdp_layer (with dx_local: dp_fsdp_layer_ex) without caller
+    workspaces: the gathered W and the per-rank dW live in the library's
+    static device buffer, so the call allocates nothing. Calls on one GPU that
+    can overlap race on that buffer."""
+    f32 = torch.float32
+    x_local = _tensors(x_local, "x_local", f32)
+    w_shard = _tensors(w_shard, "w_shard", f32)
+    y_local = _tensors(y_local, "y_local", f32)
+    k = len(x_local)
+    m_local, d = x_local[0].shape
+    f = y_local[0].shape[1]
+    bwd = dy_local is not None
+    if bwd:
+        dy_local = _tensors(dy_local, "dy_local", f32)
+        dw_shard = _tensors(dw_shard, "dw_shard", f32)
+    if dx_local is not None:
+        dx_local = _tensors(dx_local, "dx_local", f32)
+    R = dp_shard_len(d, k)
+    shapes = [("x_local", x_local, (m_local, d)), ("w_shard", w_shard, (R, f)),
+              ("y_local", y_local, (m_local, f))]
+    if bwd:
+        shapes += [("dy_local", dy_local, (m_local, f)), ("dw_shard", dw_shard, (R, f))]
+    if dx_local is not None:
+        shapes.append(("dx_local", dx_local, (m_local, d)))
+    for name, ts, shape in shapes:
+        if len(ts) != k or any(tuple(t.shape) != shape for t in ts):
+            raise ValueError(f"{name}: expected {k} tensors of shape {shape}")
+    P = lambda ts: ptr_array([t.data_ptr() for t in ts]) if ts is not None else None
+    _check(lib().dp_fsdp_layer_static(k, m_local, d, f, P(x_local), P(w_shard), P(dy_local),
+                                      P(y_local), P(dx_local), P(dw_shard), _stream(stream)),
+           "dp_fsdp_layer_static")
 
 
 def _gemm(a, b, c, stream, opts):

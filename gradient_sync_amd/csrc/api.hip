@@ -4,11 +4,21 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "dps_internal.h"
 #include "odc_internal.h"
 #include "dpsync.h"
 
 static_assert(dps::kMaxK == DP_MAX_K, "kernel and ABI rank limits differ");
+
+// Device memory of dp_fsdp_layer_static: the K gathered weights and the K
+// per-rank weight gradients, for callers that cannot allocate. Each GPU the
+// library runs on holds its own copy until the process ends. In host code the
+// array's name is only a stand-in; its device address comes from
+// hipGetSymbolAddress, once per device (scratch_base below).
+static __device__ __align__(256) unsigned char scratch[DP_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -256,6 +266,240 @@ dp_status_t check_ag(const void *const *send, void *const *recv, size_t n, int k
     return DP_OK;
 }
 
+// FSDP step argument checks. with_ws: the caller passes the w_full and dw_full
+// workspaces (checked like outputs); without, they are the library's static
+// scratch, which no caller buffer can overlap.
+dp_status_t check_fsdp(int k, int64_t m_local, int64_t d, int64_t f, const float *const *x_local,
+                       const float *const *w_shard, const float *const *dy_local,
+                       float *const *w_full, float *const *y_local, float *const *dx_local,
+                       float *const *dw_full, float *const *dw_shard, bool with_ws)
+{
+    if (!valid_k(k) || m_local < 1 || d < 1 || f < 1) return DP_ERR_INVALID_ARG;
+    if (m_local > (1 << 24) || d > (1 << 24) || f > (1 << 24)) return DP_ERR_INVALID_ARG;
+    if (!ptrs_ok((const void *const *)x_local, k, 4) || !ptrs_ok((const void *const *)w_shard, k, 4) ||
+        (with_ws && !ptrs_ok((const void *const *)w_full, k, 4)) ||
+        !ptrs_ok((const void *const *)y_local, k, 4))
+        return DP_ERR_INVALID_ARG;
+    const bool bwd = dy_local != nullptr;
+    if (bwd && (!ptrs_ok((const void *const *)dy_local, k, 4) ||
+                (with_ws && !ptrs_ok((const void *const *)dw_full, k, 4)) ||
+                !ptrs_ok((const void *const *)dw_shard, k, 4)))
+        return DP_ERR_INVALID_ARG;
+    const bool want_dx = dx_local != nullptr;
+    if (want_dx && (!bwd || !ptrs_ok((const void *const *)dx_local, k, 4))) return DP_ERR_INVALID_ARG;
+    const int64_t R = (d + k - 1) / k;
+    const size_t bx = (size_t)(m_local * d) * 4, bws = (size_t)(R * f) * 4, bdy = (size_t)(m_local * f) * 4;
+    const size_t bwf = (size_t)(d * f) * 4, by = (size_t)(m_local * f) * 4;
+    // outputs must be disjoint from every input and from each other
+    Range ins[3 * DP_MAX_K], outs[5 * DP_MAX_K];
+    int ni = 0, no = 0;
+    for (int r = 0; r < k; ++r) {
+        ins[ni++] = span(x_local[r], bx);
+        ins[ni++] = span(w_shard[r], bws);
+        if (bwd) ins[ni++] = span(dy_local[r], bdy);
+        if (with_ws) outs[no++] = span(w_full[r], bwf);
+        outs[no++] = span(y_local[r], by);
+        if (bwd) {
+            if (with_ws) outs[no++] = span(dw_full[r], bwf);
+            outs[no++] = span(dw_shard[r], bws);
+        }
+        if (want_dx) outs[no++] = span(dx_local[r], bx);
+    }
+    for (int a = 0; a < no; ++a) {
+        for (int b = 0; b < ni; ++b)
+            if (overlap(outs[a], ins[b])) return DP_ERR_ALIAS;
+        for (int b = a + 1; b < no; ++b)
+            if (overlap(outs[a], outs[b])) return DP_ERR_ALIAS;
+    }
+    return DP_OK;
+}
+
+// The FSDP step on validated arguments (see dp_fsdp_layer_ex).
+dp_status_t run_fsdp(int k, int64_t m_local, int64_t d, int64_t f, const float *const *x_local,
+                     const float *const *w_shard, const float *const *dy_local,
+                     float *const *w_full, float *const *y_local, float *const *dx_local,
+                     float *const *dw_full, float *const *dw_shard, hipStream_t st)
+{
+    const bool bwd = dy_local != nullptr;
+    const bool want_dx = dx_local != nullptr;
+    const int64_t R = (d + k - 1) / k;
+    dps::GemmF32Batch g;
+    memset(&g, 0, sizeof(g));
+    for (int r = 0; r < k; ++r) {
+        g.a[r] = x_local[r];
+        g.b[r] = w_full[r];
+        g.c[r] = y_local[r];
+        g.b_shard[r] = w_shard[r];
+        g.b_copy[r] = w_full[r];
+    }
+    g.nb = k;
+    g.M = m_local;
+    g.N = f;
+    g.Kd = d;
+    g.trans_a = 0;
+    g.b_rows = R;
+    // dx_r = dy_r . W^T: [m_local, d], W^T's columns are W's rows (shards)
+    dps::GemmF32Batch gx;
+    memset(&gx, 0, sizeof(gx));
+    for (int r = 0; r < k && want_dx; ++r) {
+        gx.a[r] = dy_local[r];
+        gx.b[r] = w_full[r];
+        gx.c[r] = dx_local[r];
+        gx.b_shard[r] = w_shard[r];
+    }
+    gx.nb = k;
+    gx.M = m_local;
+    gx.N = d;
+    gx.Kd = f;
+    gx.trans_b = 1;
+    gx.b_rows = R;
+    dp_status_t s;
+    const bool fwd_fused = dps::gemm_f32_fusable_gather(g, k);
+    const bool dx_fused = want_dx && dps::gemm_f32_fusable_gather(gx, k);
+    // forward blocks of the one-launch step: 32x32 without dx, 64x64 tiles with it
+    const int64_t n_fwd = want_dx ? (m_local / 64) * (f / 64) * k : (m_local / 32) * (f / 32) * k;
+    const int64_t n_dx = want_dx ? (m_local / 64) * (d / 64) * k : 0;
+    dps::FsdpFwd8 fw8;
+    memset(&fw8, 0, sizeof(fw8));
+    fw8.nb = k;
+    fw8.M = m_local;
+    fw8.N = f;
+    fw8.Kd = d;
+    fw8.b_rows = R;
+    // the one-launch step: without dx its forward part is the 32x32 direct block,
+    // with dx the 64x64 k-stage tile (beside the dx tiles)
+    if (bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
+        (want_dx ? fwd_fused && dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
+        n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
+        // the whole step in one launch: forward tiles (AllGather folded into
+        // the dot) beside backward blocks (ReduceScatter folded into the dW
+        // kernel); the two halves share no data
+        dps::FsdpStepParams p;
+        memset(&p, 0, sizeof(p));
+        for (int r = 0; r < k; ++r) {
+            p.fwd.a[r] = x_local[r];
+            p.fwd.c[r] = y_local[r];
+            p.fwd.b_shard[r] = w_shard[r];
+            p.fwd.b_copy[r] = w_full[r];
+            p.bwd.x[r] = x_local[r];
+            p.bwd.dy[r] = dy_local[r];
+            p.bwd.dw_full[r] = dw_full[r];
+            p.bwd.dw_shard[r] = dw_shard[r];
+        }
+        p.fwd.nb = k;
+        p.fwd.M = m_local;
+        p.fwd.N = f;
+        p.fwd.Kd = d;
+        p.fwd.b_rows = R;
+        p.bwd.k = k;
+        p.bwd.m = m_local;
+        p.bwd.d = d;
+        p.bwd.f = f;
+        p.bwd.R = R;
+        p.tiles_x = (int)(want_dx ? f / 64 : f / 32);
+        p.n_fwd = (int)n_fwd;
+        if (want_dx) {
+            for (int r = 0; r < k; ++r) {
+                p.dx.a[r] = dy_local[r];
+                p.dx.c[r] = dx_local[r];
+                p.dx.b_shard[r] = w_shard[r];
+            }
+            p.dx.nb = k;
+            p.dx.M = m_local;
+            p.dx.N = d;
+            p.dx.Kd = f;
+            p.dx.b_rows = R;
+            p.dx.trans_b = 1;
+            p.tiles_x_dx = (int)(d / 64);
+            p.n_dx = (int)n_dx;
+        }
+        return hip_status(dps::launch_fsdp_step(p, st));
+    }
+    if (fwd_fused) {
+        // 1+2 in one launch: the dot reads W's rows from the shards, and the
+        // tiles of the first tile row write the gathered W into every w_full
+        s = hip_status(dps::launch_gemm_f32(g, st));
+    } else {
+        // 1. forward: all-gather the weight row shards into every rank's W
+        s = run_ag((const void *const *)w_shard, (char *const *)w_full, d * f, R * f, k, DP_F32, 0,
+                   1, st);
+        if (s != DP_OK) return s;
+        // 2. local dot y_r = x_r . W
+        g.b_rows = 0;
+        s = hip_status(dps::launch_gemm_f32(g, st));
+    }
+    if (s != DP_OK || !bwd) return s;
+    // dx = dy . W^T, from the shards where the shapes allow, else from the
+    // gathered W (written above)
+    if (want_dx) {
+        if (!dx_fused) gx.b_rows = 0;
+        s = hip_status(dps::launch_gemm_f32(gx, st));
+        if (s != DP_OK) return s;
+    }
+    // 3+4 in one launch where the shapes allow: dW_r = x_r^T . dy_r for every
+    // rank and the ReduceScatter of dW from the K blocks in LDS
+    if (dps::fsdp_bwd_fusable(k, m_local, d, f)) {
+        dps::FsdpBwdParams p;
+        memset(&p, 0, sizeof(p));
+        for (int r = 0; r < k; ++r) {
+            p.x[r] = x_local[r];
+            p.dy[r] = dy_local[r];
+            p.dw_full[r] = dw_full[r];
+            p.dw_shard[r] = dw_shard[r];
+        }
+        p.k = k;
+        p.m = m_local;
+        p.d = d;
+        p.f = f;
+        p.R = R;
+        return hip_status(dps::launch_fsdp_bwd_fused(p, st));
+    }
+    // 3. backward: dW_r = x_r^T . dy_r
+    for (int r = 0; r < k; ++r) {
+        g.a[r] = x_local[r];
+        g.b[r] = dy_local[r];
+        g.c[r] = dw_full[r];
+    }
+    g.M = d;
+    g.N = f;
+    g.Kd = m_local;
+    g.trans_a = 1;
+    g.b_rows = 0;
+    s = hip_status(dps::launch_gemm_f32(g, st));
+    if (s != DP_OK) return s;
+    // 4. reduce-scatter dW back to the row shards (sum, pad rows zero)
+    return run_rs((const void *const *)dw_full, (char *const *)dw_shard, d * f, R * f, k, DP_F32,
+                  dps::kSum, 1.0f, nullptr, 1, 1, st);
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device afterwards.
+constexpr int kMaxDevices = 64;
+std::atomic<char *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+dp_status_t scratch_base(char **base)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return DP_ERR_UNSUPPORTED;
+    char *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *q = nullptr;
+            e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e);
+            p = (char *)q;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *base = p;
+    return DP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,6 +518,8 @@ const char *dp_status_string(int status)
     case DP_ERR_UNSUPPORTED: return "DP_ERR_UNSUPPORTED: unsupported dtype or op";
     case DP_ERR_ALIAS: return "DP_ERR_ALIAS: buffers overlap outside the in-place forms";
     case DP_ERR_HIP: return "DP_ERR_HIP: HIP launch failed";
+    case DP_ERR_SCRATCH:
+        return "DP_ERR_SCRATCH: the workspaces exceed the library's static scratch buffer";
     default: return "unknown dpsync status";
     }
 }
@@ -458,190 +704,36 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
                              float *const *y_local, float *const *dx_local,
                              float *const *dw_full, float *const *dw_shard, void *stream)
 {
-    if (!valid_k(k) || m_local < 1 || d < 1 || f < 1) return DP_ERR_INVALID_ARG;
-    if (m_local > (1 << 24) || d > (1 << 24) || f > (1 << 24)) return DP_ERR_INVALID_ARG;
-    if (!ptrs_ok((const void *const *)x_local, k, 4) || !ptrs_ok((const void *const *)w_shard, k, 4) ||
-        !ptrs_ok((const void *const *)w_full, k, 4) || !ptrs_ok((const void *const *)y_local, k, 4))
-        return DP_ERR_INVALID_ARG;
-    const bool bwd = dy_local != nullptr;
-    if (bwd && (!ptrs_ok((const void *const *)dy_local, k, 4) ||
-                !ptrs_ok((const void *const *)dw_full, k, 4) ||
-                !ptrs_ok((const void *const *)dw_shard, k, 4)))
-        return DP_ERR_INVALID_ARG;
-    const bool want_dx = dx_local != nullptr;
-    if (want_dx && (!bwd || !ptrs_ok((const void *const *)dx_local, k, 4))) return DP_ERR_INVALID_ARG;
-    const int64_t R = (d + k - 1) / k;
-    const size_t bx = (size_t)(m_local * d) * 4, bws = (size_t)(R * f) * 4, bdy = (size_t)(m_local * f) * 4;
-    const size_t bwf = (size_t)(d * f) * 4, by = (size_t)(m_local * f) * 4;
-    // outputs must be disjoint from every input and from each other
-    Range ins[3 * DP_MAX_K], outs[5 * DP_MAX_K];
-    int ni = 0, no = 0;
-    for (int r = 0; r < k; ++r) {
-        ins[ni++] = span(x_local[r], bx);
-        ins[ni++] = span(w_shard[r], bws);
-        if (bwd) ins[ni++] = span(dy_local[r], bdy);
-        outs[no++] = span(w_full[r], bwf);
-        outs[no++] = span(y_local[r], by);
-        if (bwd) {
-            outs[no++] = span(dw_full[r], bwf);
-            outs[no++] = span(dw_shard[r], bws);
-        }
-        if (want_dx) outs[no++] = span(dx_local[r], bx);
-    }
-    for (int a = 0; a < no; ++a) {
-        for (int b = 0; b < ni; ++b)
-            if (overlap(outs[a], ins[b])) return DP_ERR_ALIAS;
-        for (int b = a + 1; b < no; ++b)
-            if (overlap(outs[a], outs[b])) return DP_ERR_ALIAS;
-    }
-    hipStream_t st = (hipStream_t)stream;
-    dps::GemmF32Batch g;
-    memset(&g, 0, sizeof(g));
-    for (int r = 0; r < k; ++r) {
-        g.a[r] = x_local[r];
-        g.b[r] = w_full[r];
-        g.c[r] = y_local[r];
-        g.b_shard[r] = w_shard[r];
-        g.b_copy[r] = w_full[r];
-    }
-    g.nb = k;
-    g.M = m_local;
-    g.N = f;
-    g.Kd = d;
-    g.trans_a = 0;
-    g.b_rows = R;
-    // dx_r = dy_r . W^T: [m_local, d], W^T's columns are W's rows (shards)
-    dps::GemmF32Batch gx;
-    memset(&gx, 0, sizeof(gx));
-    for (int r = 0; r < k && want_dx; ++r) {
-        gx.a[r] = dy_local[r];
-        gx.b[r] = w_full[r];
-        gx.c[r] = dx_local[r];
-        gx.b_shard[r] = w_shard[r];
-    }
-    gx.nb = k;
-    gx.M = m_local;
-    gx.N = d;
-    gx.Kd = f;
-    gx.trans_b = 1;
-    gx.b_rows = R;
-    dp_status_t s;
-    const bool fwd_fused = dps::gemm_f32_fusable_gather(g, k);
-    const bool dx_fused = want_dx && dps::gemm_f32_fusable_gather(gx, k);
-    // forward blocks of the one-launch step: 32x32 without dx, 64x64 tiles with it
-    const int64_t n_fwd = want_dx ? (m_local / 64) * (f / 64) * k : (m_local / 32) * (f / 32) * k;
-    const int64_t n_dx = want_dx ? (m_local / 64) * (d / 64) * k : 0;
-    dps::FsdpFwd8 fw8;
-    memset(&fw8, 0, sizeof(fw8));
-    fw8.nb = k;
-    fw8.M = m_local;
-    fw8.N = f;
-    fw8.Kd = d;
-    fw8.b_rows = R;
-    // the one-launch step: without dx its forward part is the 32x32 direct block,
-    // with dx the 64x64 k-stage tile (beside the dx tiles)
-    if (bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
-        (want_dx ? fwd_fused && dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
-        n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
-        // the whole step in one launch: forward tiles (AllGather folded into
-        // the dot) beside backward blocks (ReduceScatter folded into the dW
-        // kernel); the two halves share no data
-        dps::FsdpStepParams p;
-        memset(&p, 0, sizeof(p));
-        for (int r = 0; r < k; ++r) {
-            p.fwd.a[r] = x_local[r];
-            p.fwd.c[r] = y_local[r];
-            p.fwd.b_shard[r] = w_shard[r];
-            p.fwd.b_copy[r] = w_full[r];
-            p.bwd.x[r] = x_local[r];
-            p.bwd.dy[r] = dy_local[r];
-            p.bwd.dw_full[r] = dw_full[r];
-            p.bwd.dw_shard[r] = dw_shard[r];
-        }
-        p.fwd.nb = k;
-        p.fwd.M = m_local;
-        p.fwd.N = f;
-        p.fwd.Kd = d;
-        p.fwd.b_rows = R;
-        p.bwd.k = k;
-        p.bwd.m = m_local;
-        p.bwd.d = d;
-        p.bwd.f = f;
-        p.bwd.R = R;
-        p.tiles_x = (int)(want_dx ? f / 64 : f / 32);
-        p.n_fwd = (int)n_fwd;
-        if (want_dx) {
-            for (int r = 0; r < k; ++r) {
-                p.dx.a[r] = dy_local[r];
-                p.dx.c[r] = dx_local[r];
-                p.dx.b_shard[r] = w_shard[r];
-            }
-            p.dx.nb = k;
-            p.dx.M = m_local;
-            p.dx.N = d;
-            p.dx.Kd = f;
-            p.dx.b_rows = R;
-            p.dx.trans_b = 1;
-            p.tiles_x_dx = (int)(d / 64);
-            p.n_dx = (int)n_dx;
-        }
-        return hip_status(dps::launch_fsdp_step(p, st));
-    }
-    if (fwd_fused) {
-        // 1+2 in one launch: the dot reads W's rows from the shards, and the
-        // tiles of the first tile row write the gathered W into every w_full
-        s = hip_status(dps::launch_gemm_f32(g, st));
-    } else {
-        // 1. forward: all-gather the weight row shards into every rank's W
-        s = run_ag((const void *const *)w_shard, (char *const *)w_full, d * f, R * f, k, DP_F32, 0,
-                   1, st);
-        if (s != DP_OK) return s;
-        // 2. local dot y_r = x_r . W
-        g.b_rows = 0;
-        s = hip_status(dps::launch_gemm_f32(g, st));
-    }
-    if (s != DP_OK || !bwd) return s;
-    // dx = dy . W^T, from the shards where the shapes allow, else from the
-    // gathered W (written above)
-    if (want_dx) {
-        if (!dx_fused) gx.b_rows = 0;
-        s = hip_status(dps::launch_gemm_f32(gx, st));
-        if (s != DP_OK) return s;
-    }
-    // 3+4 in one launch where the shapes allow: dW_r = x_r^T . dy_r for every
-    // rank and the ReduceScatter of dW from the K blocks in LDS
-    if (dps::fsdp_bwd_fusable(k, m_local, d, f)) {
-        dps::FsdpBwdParams p;
-        memset(&p, 0, sizeof(p));
-        for (int r = 0; r < k; ++r) {
-            p.x[r] = x_local[r];
-            p.dy[r] = dy_local[r];
-            p.dw_full[r] = dw_full[r];
-            p.dw_shard[r] = dw_shard[r];
-        }
-        p.k = k;
-        p.m = m_local;
-        p.d = d;
-        p.f = f;
-        p.R = R;
-        return hip_status(dps::launch_fsdp_bwd_fused(p, st));
-    }
-    // 3. backward: dW_r = x_r^T . dy_r
-    for (int r = 0; r < k; ++r) {
-        g.a[r] = x_local[r];
-        g.b[r] = dy_local[r];
-        g.c[r] = dw_full[r];
-    }
-    g.M = d;
-    g.N = f;
-    g.Kd = m_local;
-    g.trans_a = 1;
-    g.b_rows = 0;
-    s = hip_status(dps::launch_gemm_f32(g, st));
+    dp_status_t s0 = check_fsdp(k, m_local, d, f, x_local, w_shard, dy_local, w_full, y_local,
+                                dx_local, dw_full, dw_shard, true);
+    if (s0 != DP_OK) return s0;
+    return run_fsdp(k, m_local, d, f, x_local, w_shard, dy_local, w_full, y_local, dx_local,
+                    dw_full, dw_shard, (hipStream_t)stream);
+}
+
+dp_status_t dp_fsdp_layer_static(int k, int64_t m_local, int64_t d, int64_t f,
+                                 const float *const *x_local, const float *const *w_shard,
+                                 const float *const *dy_local, float *const *y_local,
+                                 float *const *dx_local, float *const *dw_shard, void *stream)
+{
+    dp_status_t s = check_fsdp(k, m_local, d, f, x_local, w_shard, dy_local, nullptr, y_local,
+                               dx_local, nullptr, dw_shard, false);
     if (s != DP_OK) return s;
-    // 4. reduce-scatter dW back to the row shards (sum, pad rows zero)
-    return run_rs((const void *const *)dw_full, (char *const *)dw_shard, d * f, R * f, k, DP_F32,
-                  dps::kSum, 1.0f, nullptr, 1, 1, st);
+    // K gathered weights and K weight gradients, each [d, f] fp32, every one
+    // starting on a 256-byte boundary (the alignment a caller's allocations
+    // have, so the same kernels are chosen as with caller workspaces)
+    const size_t region = ((size_t)(d * f) * 4 + 255) / 256 * 256;
+    if ((size_t)(2 * k) * region > (size_t)DP_STATIC_SCRATCH_BYTES) return DP_ERR_SCRATCH;
+    char *base = nullptr;
+    s = scratch_base(&base);
+    if (s != DP_OK) return s;
+    float *w_full[DP_MAX_K], *dw_full[DP_MAX_K];
+    for (int r = 0; r < k; ++r) {
+        w_full[r] = (float *)(base + (size_t)r * region);
+        dw_full[r] = (float *)(base + (size_t)(k + r) * region);
+    }
+    return run_fsdp(k, m_local, d, f, x_local, w_shard, dy_local, w_full, y_local, dx_local,
+                    dw_full, dw_shard, (hipStream_t)stream);
 }
 
 dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, int64_t n,

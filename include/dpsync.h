@@ -60,7 +60,9 @@ typedef enum {
                                 misaligned pointer, size overflow, bad token counts */
     DP_ERR_UNSUPPORTED = 2,  /* dtype/op outside the enums, or AVG/weighted on DP_I32 */
     DP_ERR_ALIAS = 3,        /* buffers overlap other than in the documented in-place forms */
-    DP_ERR_HIP = 4           /* a HIP launch failed; see dp_last_hip_error() */
+    DP_ERR_HIP = 4,          /* a HIP launch failed; see dp_last_hip_error() */
+    DP_ERR_SCRATCH = 5       /* the call's workspaces exceed DP_STATIC_SCRATCH_BYTES
+                                (dp_fsdp_layer_static only) */
 } dp_status_t;
 
 typedef enum { DP_F32 = 0, DP_BF16 = 1, DP_I32 = 2 } dp_dtype_t;
@@ -210,6 +212,32 @@ dp_status_t dp_fsdp_layer_ex(int k, int64_t m_local, int64_t d, int64_t f,
                              const float *const *dy_local, float *const *w_full,
                              float *const *y_local, float *const *dx_local,
                              float *const *dw_full, float *const *dw_shard, void *stream);
+
+/*
+ * dp_fsdp_layer_ex for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the gathered weights w_full[r] and the per-rank weight
+ * gradients dw_full[r] are kept in a static device buffer of the library
+ * instead of caller workspaces. Same arguments, results and validation as
+ * dp_fsdp_layer_ex without w_full and dw_full (dy_local NULL: forward only,
+ * dw_shard is then ignored and dx_local must be NULL; dx_local NULL: no input
+ * gradient). The same kernels run, so the results are bit-identical to
+ * dp_fsdp_layer_ex with caller workspaces of the same shapes.
+ *   Limit: 2 * k * roundup256(d * f * 4 bytes) <= DP_STATIC_SCRATCH_BYTES
+ *   (32 MiB: e.g. K = 8 ranks with d = f = 512 use 16 MiB), else
+ *   DP_ERR_SCRATCH with nothing enqueued.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine). Each GPU holds one copy of the buffer, shared by every call on that
+ * GPU: calls on one GPU that can run at the same time (on different streams,
+ * or from different threads) race on it; serialise them. Every call
+ * overwrites the parts it uses, so nothing carries over from earlier calls.
+ */
+#define DP_STATIC_SCRATCH_BYTES (32u << 20)
+
+dp_status_t dp_fsdp_layer_static(int k, int64_t m_local, int64_t d, int64_t f,
+                                 const float *const *x_local, const float *const *w_shard,
+                                 const float *const *dy_local, float *const *y_local,
+                                 float *const *dx_local, float *const *dw_shard, void *stream);
 
 /*
  * Dense bf16 GEMM used as the compute side of concurrent computation and

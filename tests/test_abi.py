@@ -46,7 +46,7 @@ def test_shard_len_and_strings():
     assert dps.dp_shard_len(10_000_019, 8) == 1_250_003
     assert dps.dp_shard_len(1_048_576, 4) == 262_144
     assert dps.dp_shard_len(5, 0) == 0
-    for code in range(5):
+    for code in range(6):
         assert dps.dp_status_string(code).startswith("DP_")
     assert "unknown" in dps.dp_status_string(99)
     assert dps.dp_last_hip_error() == 0
@@ -155,6 +155,33 @@ def test_fsdp_validation():
     assert call_ex(dx_=[dx[0], 0]) == INVALID
     assert call_ex(dx_=[dx[0], x[1] + 8]) == ALIAS     # dx on top of an input
     assert call_ex(dx_=[dx[0], dwf[0]]) == ALIAS       # dx on top of another output
+
+
+def test_fsdp_static_validation():
+    """The allocation-free FSDP step checks the caller's buffers like
+    dp_fsdp_layer_ex and rejects workspaces beyond the static buffer, all
+    before it touches the device."""
+    L = dps.lib()
+    k = 8
+    x, ws, dy = fake(k, 1 << 40), fake(k, 1 << 41), fake(k, 1 << 42)
+    y, dws, dx = fake(k, 1 << 44), fake(k, 1 << 46), fake(k, 1 << 47)
+
+    def call(k_=k, m=64, d=64, f=64, x_=x, y_=y, dy_=dy, dx_=None):
+        return L.dp_fsdp_layer_static(k_, m, d, f, P(x_[:k_]), P(ws[:k_]),
+                                      P(dy_[:k_]) if dy_ else None, P(y_[:k_]),
+                                      P(dx_[:k_]) if dx_ else None, P(dws[:k_]), None)
+    assert call(k_=0) == INVALID
+    assert call(m=0) == INVALID
+    assert call(x_=[x[0], 0] + x[2:]) == INVALID
+    assert call(y_=[x[0]] + y[1:]) == ALIAS
+    assert call(dy_=None, dx_=dx) == INVALID            # dx needs the backward pass
+    # 2 * K * d * f * 4 bytes against the 32 MiB buffer
+    assert call(d=1024, f=1024) == dps.DP_ERR_SCRATCH
+    # just over the limit with K = 2 (each region rounded up to 256 bytes)
+    big = [fake(2, 1 << 40 + i, stride=64 * MB) for i in range(5)]
+    assert L.dp_fsdp_layer_static(2, 64, 2048, 1025, P(big[0]), P(big[1]), P(big[2]), P(big[3]),
+                                  None, P(big[4]), None) == dps.DP_ERR_SCRATCH
+    assert dps.DP_STATIC_SCRATCH_BYTES == 32 << 20
 
 
 def test_gemm_validation():
