@@ -166,10 +166,17 @@ def fsdp_fixture(seed: int = 2, k: int = 8, m: int = 1024, d: int = 512, f: int 
     return {"x": x, "w": w, "dy": dy}
 
 
-def gemm_bf16_inputs(seed: int, m: int, n: int, kk: int, device="cpu"):
-    """A[m,kk] and B[n,kk] (k-contiguous weight layout, C = A B^T), bf16 from N(0,1)."""
+def gemm_bf16_inputs(seed: int, m: int, n: int, kk: int, device="cpu", b_layout: str = "kn"):
+    """A[m,kk] and B, bf16 from N(0,1): B[kk,n] for C = A B (b_layout "kn"), or
+    B[n,kk] for C = A B^T ("nk", the k-contiguous weight layout). The same
+    draws fill B in both layouts: element (k, j) of the product's B is draw
+    j*kk + k, so the "kn" tensor is the transpose of the "nk" one."""
     a = bf16_normal(seed, 30, 0, m * kk, 1.0, device=device).view(m, kk)
     b = bf16_normal(seed, 31, 0, n * kk, 1.0, device=device).view(n, kk)
+    if b_layout == "kn":
+        b = b.t().contiguous()
+    elif b_layout != "nk":
+        raise ValueError("b_layout must be 'kn' or 'nk'")
     return a, b
 
 

@@ -15,7 +15,7 @@ Calls (same names and meaning as the C ABI):
   dp_weighted_reduce(send, recv, tokens, s_chunks=1, stream=None)
   dp_fsdp_layer(x_local, w_shard, dy_local, w_full, y_local, dw_full, dw_shard, stream=None,
                 dx_local=None)                # dx_local: dp_fsdp_layer_ex
-  dp_gemm_bf16(a, b, c, stream=None)          # c = a @ b.T
+  dp_gemm_bf16(a, b, c, stream=None)          # c = a @ b (b_layout="nk": a @ b.T)
 """
 from __future__ import annotations
 
@@ -56,6 +56,7 @@ _OPS = {"sum": DP_SUM, "avg": DP_AVG}
 DP_LAUNCH_SHARE_CU = 1
 DP_LAUNCH_TWO_PHASE = 2
 DP_LAUNCH_LEAN = 4
+DP_LAUNCH_B_NK = 8
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -453,13 +454,14 @@ def dp_fsdp_layer_static(x_local, w_shard, dy_local, y_local, dw_shard=None, dx_
            "dp_fsdp_layer_static")
 
 
-def _gemm(a, b, c, stream, opts):
+def _gemm(a, b, c, stream, opts, b_nk=False):
     for name, t in (("a", a), ("b", b), ("c", c)):
         _tensors([t], name, torch.bfloat16)
     m, kk = a.shape
-    n = b.shape[0]
-    if b.shape[1] != kk or tuple(c.shape) != (m, n):
-        raise ValueError("dp_gemm_bf16: shapes must be a[m,k], b[n,k], c[m,n]")
+    n = b.shape[0] if b_nk else b.shape[1]
+    if (b.shape[1] if b_nk else b.shape[0]) != kk or tuple(c.shape) != (m, n):
+        raise ValueError("dp_gemm_bf16: shapes must be a[m,k], " +
+                         ("b[n,k]" if b_nk else "b[k,n]") + ", c[m,n]")
     if opts is None:
         _check(lib().dp_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), m, n, kk,
                                   _stream(stream)), "dp_gemm_bf16")
@@ -469,15 +471,24 @@ def _gemm(a, b, c, stream, opts):
 
 
 def dp_gemm_bf16(a, b, c, stream=None):
-    """c[m,n] = a[m,kk] @ b[n,kk]^T in bf16 with fp32 accumulation."""
+    """c[m,n] = a[m,kk] @ b[kk,n] in bf16 with fp32 accumulation."""
     _gemm(a, b, c, stream, None)
 
 
-def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None, lean: bool = False):
-    """dp_gemm_bf16 with a variant choice: share_cu selects the variant that
-    leaves room for a default sync workgroup on every CU, lean the one beside
-    which a lean sync workgroup fits; neither, the fastest (same bits)."""
-    _gemm(a, b, c, stream, ctypes.byref(LaunchOpts.make(0, share_cu, lean=lean)))
+def dp_gemm_bf16_ex(a, b, c, share_cu: bool = False, stream=None, lean: bool = False,
+                    b_layout: str = "kn"):
+    """dp_gemm_bf16 with a variant choice and B's layout: b_layout "kn" (b is
+    [kk,n], c = a @ b) or "nk" (b is [n,kk], c = a @ b.T). share_cu selects
+    the variant that leaves room for a default sync workgroup on every CU,
+    lean the one beside which a lean sync workgroup fits; neither, the fastest
+    (same bits)."""
+    if b_layout not in ("kn", "nk"):
+        raise ValueError("b_layout must be 'kn' or 'nk'")
+    b_nk = b_layout == "nk"
+    o = LaunchOpts.make(0, share_cu, lean=lean)
+    if b_nk:
+        o.flags |= DP_LAUNCH_B_NK
+    _gemm(a, b, c, stream, ctypes.byref(o), b_nk)
 
 
 def dp_scatter_accumulate(grads, acc, stream=None, n=None):

@@ -51,17 +51,20 @@ int gemm_variant(bool share_cu, bool lean)
 }
 
 bool opts_ok(const dp_launch_opts_t *o, int &max_wg, bool *share_cu = nullptr,
-             bool *two_phase = nullptr, bool *lean = nullptr)
+             bool *two_phase = nullptr, bool *lean = nullptr, bool *b_nk = nullptr)
 {
     max_wg = 0;
     if (share_cu) *share_cu = false;
     if (two_phase) *two_phase = false;
     if (lean) *lean = false;
+    if (b_nk) *b_nk = false;
     if (!o) return true;
     if (o->max_workgroups < 0 ||
-        (o->flags & ~(DP_LAUNCH_SHARE_CU | DP_LAUNCH_TWO_PHASE | DP_LAUNCH_LEAN)) ||
+        (o->flags &
+         ~(DP_LAUNCH_SHARE_CU | DP_LAUNCH_TWO_PHASE | DP_LAUNCH_LEAN | DP_LAUNCH_B_NK)) ||
         o->reserved[0] || o->reserved[1])
         return false;
+    if (b_nk) *b_nk = (o->flags & DP_LAUNCH_B_NK) != 0;
     max_wg = o->max_workgroups;
     if (share_cu) *share_cu = (o->flags & DP_LAUNCH_SHARE_CU) != 0;
     if (two_phase) *two_phase = (o->flags & DP_LAUNCH_TWO_PHASE) != 0;
@@ -740,17 +743,16 @@ dp_status_t dp_gemm_bf16_ex(const void *a, const void *b, void *c, int64_t m, in
                             int64_t kk, const dp_launch_opts_t *opts, void *stream)
 {
     int max_wg;
-    bool share_cu, lean;
-    if (!opts_ok(opts, max_wg, &share_cu, nullptr, &lean)) return DP_ERR_INVALID_ARG;
+    bool share_cu, lean, b_nk;
+    if (!opts_ok(opts, max_wg, &share_cu, nullptr, &lean, &b_nk)) return DP_ERR_INVALID_ARG;
     if (!a || !b || !c || m < 1 || n < 1 || kk < 1) return DP_ERR_INVALID_ARG;
     if (m > (1 << 24) || n > (1 << 24) || kk > (1 << 24)) return DP_ERR_INVALID_ARG;
-    if (kk % 8 != 0 || ((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)c & 1))
-        return DP_ERR_UNSUPPORTED;
+    if (((uintptr_t)a & 1) || ((uintptr_t)b & 1) || ((uintptr_t)c & 1)) return DP_ERR_INVALID_ARG;
     const Range rc = span(c, (size_t)(m * n) * 2);
     if (overlap(rc, span(a, (size_t)(m * kk) * 2)) || overlap(rc, span(b, (size_t)(n * kk) * 2)))
         return DP_ERR_ALIAS;
     return hip_status(dps::launch_gemm_bf16(a, b, c, m, n, kk, gemm_variant(share_cu, lean),
-                                            (hipStream_t)stream));
+                                            !b_nk, (hipStream_t)stream));
 }
 
 dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_piece_t *pieces,
@@ -820,7 +822,7 @@ dp_status_t dp_backward_allreduce_overlap(int k, int n_pieces, const dp_grad_pie
         for (int r = 0; r < k; ++r) {
             char *c = (char *)grad[r] + (size_t)p.offset * 2;
             hipError_t e = dps::launch_gemm_bf16(dy[g * k + r], x[g * k + r], c, p.m, p.n, t,
-                                                 gemm_variant(share_cu, lean), cs);
+                                                 gemm_variant(share_cu, lean), false, cs);
             if (e != hipSuccess) return hip_status(e);
         }
         const int64_t done = p.offset + p.m * p.n;

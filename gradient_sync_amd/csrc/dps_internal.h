@@ -80,7 +80,9 @@ hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t stream);
 // of a multiple of 32 rows
 bool fsdp_fwd_direct_ok(const FsdpFwd8 &p);
 
-// bf16 GEMM, C[M,N] = A[M,Kd] * B[N,Kd]^T, row-major, fp32 accumulation.
+// bf16 GEMM, row-major, fp32 accumulation: C[M,N] = A[M,Kd] * B[Kd,N] with
+// b_kn, else C = A[M,Kd] * B[N,Kd]^T. Any element-aligned pointers and shapes;
+// rows that are not 16-byte aligned take a slower kernel (same bits).
 // GEMM variants: kGemmFast = the 4-wave kernel (every register of each SIMD)
 // where the shape allows, else the 8-wave one; kGemmCoresident = the 8-wave
 // kernel with depth-64 stages (224 VGPRs: a lean sync workgroup fits beside it
@@ -88,6 +90,6 @@ bool fsdp_fwd_direct_ok(const FsdpFwd8 &p);
 // default sync workgroup fits beside it).
 enum GemmVariant { kGemmFast = 0, kGemmCoresident = 1, kGemmShareCU = 2 };
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, int variant, hipStream_t stream);
+                            long long Kd, int variant, bool b_kn, hipStream_t stream);
 
 }  // namespace dps

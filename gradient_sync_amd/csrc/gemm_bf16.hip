@@ -1,16 +1,27 @@
-// bf16 GEMM on CDNA4 matrix cores: C[M,N] = A[M,Kd] . B[N,Kd]^T, fp32
+// bf16 GEMM on CDNA4 matrix cores: C[M,N] = A[M,Kd] . op(B), fp32
 // accumulation, bf16 result (round to nearest even). This is the compute
 // kernel of a (GEMM, collective) pair run concurrently with the sync kernels
 // ("Optimizing ML Concurrent Computation and Communication with GPU DMA
 // Engines", section "Problem Formulation": a GEMM and a collective with no data
 // dependence between them).
 //
-// Both operands are k-contiguous (the linear-layer weight layout), so each
-// lane's MFMA operand is one 16-byte run of 8 bf16 values in LDS. Every variant
-// walks k in ascending 16-element steps with one v_mfma_f32_32x32x16_bf16 per
-// step and output block, so all variants produce the same bits.
+// B layouts (template parameter BKN):
+//   BKN = true : B stored [Kd, N] row-major (C = A . B, the plain product).
+//   BKN = false: B stored [N, Kd] row-major (C = A . B^T, both operands
+//                k-contiguous, the linear-layer weight layout).
+// A is always [M, Kd] (k-contiguous). The MFMA operands need 8 consecutive k
+// values per lane. A k-contiguous operand gives them as one 16-byte run in LDS;
+// for an n-contiguous B the stage is stored in LDS as [k][n] rows (coalesced
+// 16-byte global loads along n) and each lane's 8 k values are assembled with
+// two ds_read_b64_tr_b16 transposing reads, gfx950's LDS load that hands each
+// lane of a 16-lane group one 16-bit column of the 4 rows its neighbours
+// address (lane i of the group receives element i % 4 of the 8-byte rows
+// addressed by lanes 4e + i / 4, e = 0..3; verified on the GPU with an
+// in-bounds probe). Every variant and layout walks k in ascending 16-element
+// steps with one v_mfma_f32_32x32x16_bf16 per step and output block, zero-padded
+// past Kd, so all of them produce the same bits.
 //
-// Two designs over a 256x256 tile of C:
+// Three designs over a tile of C:
 //
 // * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
 //   multiple of 64 and at least 1024): 4 waves, one per SIMD, each owning a 128x128 quarter (4x4 MFMA
@@ -25,17 +36,23 @@
 //   stages ahead (scheduling fences keep that interleave). The loads alternate
 //   between two staging register sets, so each has two stages to arrive before
 //   its LDS store needs it. Global loads use a buffer descriptor on the tile's
-//   first row, so their addresses are one per-lane offset register plus a
-//   scalar offset.
+//   first row (first column for an n-contiguous B), so their addresses are one
+//   per-lane offset register plus a scalar offset.
 //
 // * gemm_bf16_kernel: 8 waves arranged 2 (rows) x 4 (columns), each wave
 //   128x64 = 4x2 MFMA blocks (128 fp32 accumulators per lane), k stages of TK
 //   (32 or 64) through double-buffered LDS. It fits in 224 (TK=64) or 198
 //   (TK=32) VGPRs, which leaves room for a sync workgroup on the same CU; it also
-//   takes any shape (edge tiles on a guarded path). With EARLY, a stage's
-//   operands are loaded into registers two stages ahead and written to the
-//   idle LDS buffer at the start of the next stage, so the LDS writes overlap
-//   that stage's MFMAs instead of standing between the MFMAs and the barrier.
+//   takes any shape whose rows are 16-byte aligned (edge tiles on a guarded
+//   path). With EARLY, a stage's operands are loaded into registers two stages
+//   ahead and written to the idle LDS buffer at the start of the next stage, so
+//   the LDS writes overlap that stage's MFMAs instead of standing between the
+//   MFMAs and the barrier.
+//
+// * gemm_bf16_any_kernel: any shape, any element-aligned pointers, any Kd: 64x64
+//   tiles of 4 waves, each lane gathering its MFMA operands straight from
+//   global memory with guarded 2-byte loads. Slow; it serves what the two
+//   kernels above cannot take (rows that are not 16-byte aligned).
 //
 // A 256x256 tile does 128 flop per byte loaded, which keeps the kernels off the
 // L2 bandwidth limit a 128x128 tile (64 flop/byte) runs into. Tiles are ordered
@@ -54,6 +71,31 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Padded LDS row of an n-contiguous B stage: 256 + 32 elements = 576 bytes, so
+// consecutive k rows start 64 bytes apart modulo 256 and the 8 rows x 64 bytes
+// one transposing read of a wave touches fall on every bank exactly twice.
+constexpr int BKN_LDN = 256 + 32;
+
+// MFMA B operand of lane `lane` for the 32 columns starting at column `col` of
+// an [k][n] LDS stage whose row `row0` is the block's first k: lane group g =
+// lane / 16 covers columns 16 (g % 2) .. + 15 and k 8 (g / 2) .. + 7; within
+// the group lane jj addresses row jj / 4 (+4 for the second read) at column
+// 4 (jj % 4), and receives its own column's 4 k values from each read.
+__device__ __forceinline__ bf16x8 b_operand_kn(const unsigned short *stage, int ldn, int row0,
+                                               int col, int lane)
+{
+    const int g = lane >> 4, jj = lane & 15;
+    const unsigned short *p = stage + (row0 + 8 * (g >> 1) + (jj >> 2)) * ldn + col +
+                              16 * (g & 1) + 4 * (jj & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * ldn));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
 
 constexpr int TM = 256, TN = 256;                           // workgroup tile of C
 constexpr int NT = 512;                                     // threads per workgroup
@@ -91,8 +133,9 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int &t
 
 // TK: k depth of one LDS stage (64: full 128-byte rows per load, 228 VGPRs,
 // 144 KiB LDS; 32: 198 VGPRs and 80 KiB, which leaves room on the CU for a
-// sync workgroup beside the GEMM workgroup).
-template <bool EDGE, int TK, bool EARLY>
+// sync workgroup beside the GEMM workgroup). BKN: B stored [Kd, N] (see above);
+// then N must be a multiple of 8 (16-byte rows) as Kd must for A.
+template <bool EDGE, int TK, bool EARLY, bool BKN>
 __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__restrict__ A,
                                                        const unsigned short *__restrict__ B,
                                                        unsigned short *__restrict__ C, int M, int N,
@@ -102,8 +145,13 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
     constexpr int CH = TK / 8;       // 16-byte chunks per tile row
     constexpr int RPP = NT / CH;     // rows loaded per pass
     constexpr int HP = TM / RPP;     // passes per tile
+    // B stage: [TN][LDK] (k-contiguous) or [TK][BKN_LDN] (n-contiguous)
+    constexpr int BR = BKN ? TK : TN, BC = BKN ? BKN_LDN : LDK;
+    // n-contiguous B: thread -> 16-byte chunk bc of k rows br + 16h
+    constexpr int BHP = BKN ? TK / 16 : HP;
+    static_assert(!BKN || BHP * 16 * 32 == TK * TN / 8, "B chunks per thread");
     __shared__ __attribute__((aligned(16))) unsigned short As[2][TM][LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][TN][LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][BR][BC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wi = wave >> 2, wj = wave & 3;
@@ -111,29 +159,53 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
 
-    // global -> register staging: rows lr + RPP*h of A and of B, 8 bf16 at k lk
+    // global -> register staging: rows lr + RPP*h of A (and of a k-contiguous
+    // B), 8 bf16 at k lk; an n-contiguous B: k rows br + 16h, 8 bf16 at column 8*bc
     const int lr = tid / CH, lk = (tid % CH) * 8;
-    u32x4 ra[HP], rb[HP];
+    const int bc = tid & 31, br = tid >> 5;
+    u32x4 ra[HP], rb[BHP];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int h = 0; h < HP; ++h) {
-            const long long gi = m0 + lr + RPP * h, gj = n0 + lr + RPP * h;
+            const long long gi = m0 + lr + RPP * h;
             const int gk = k0 + lk;
             if (EDGE) {
                 const bool kin = gk + 8 <= Kd;
                 ra[h] = (gi < M && kin) ? *reinterpret_cast<const u32x4 *>(A + gi * Kd + gk) : u32x4{0, 0, 0, 0};
-                rb[h] = (gj < N && kin) ? *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk) : u32x4{0, 0, 0, 0};
             } else {
                 ra[h] = *reinterpret_cast<const u32x4 *>(A + gi * Kd + gk);
-                rb[h] = *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < BHP; ++h) {
+            if constexpr (BKN) {
+                const long long gk = k0 + br + 16 * h, gj = n0 + 8 * bc;
+                if (EDGE)
+                    rb[h] = (gk < Kd && gj < N) ? *reinterpret_cast<const u32x4 *>(B + gk * N + gj)
+                                                : u32x4{0, 0, 0, 0};
+                else
+                    rb[h] = *reinterpret_cast<const u32x4 *>(B + gk * N + gj);
+            } else {
+                const long long gj = n0 + lr + RPP * h;
+                const int gk = k0 + lk;
+                if (EDGE)
+                    rb[h] = (gj < N && gk + 8 <= Kd) ? *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk)
+                                                     : u32x4{0, 0, 0, 0};
+                else
+                    rb[h] = *reinterpret_cast<const u32x4 *>(B + gj * Kd + gk);
             }
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int h = 0; h < HP; ++h) {
+        for (int h = 0; h < HP; ++h)
             *reinterpret_cast<u32x4 *>(&As[buf][lr + RPP * h][lk]) = ra[h];
-            *reinterpret_cast<u32x4 *>(&Bs[buf][lr + RPP * h][lk]) = rb[h];
+#pragma unroll
+        for (int h = 0; h < BHP; ++h) {
+            if constexpr (BKN)
+                *reinterpret_cast<u32x4 *>(&Bs[buf][br + 16 * h][8 * bc]) = rb[h];
+            else
+                *reinterpret_cast<u32x4 *>(&Bs[buf][lr + RPP * h][lk]) = rb[h];
         }
     };
 
@@ -169,8 +241,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const unsigned short *__r
             for (int a = 0; a < BI; ++a)
                 av[a] = *reinterpret_cast<const bf16x8 *>(&As[buf][wi * WM + a * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
 #pragma unroll
-            for (int b = 0; b < BJ; ++b)
-                bv[b] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * WN + b * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
+            for (int b = 0; b < BJ; ++b) {
+                if constexpr (BKN)
+                    bv[b] = b_operand_kn(&Bs[buf][0][0], BKN_LDN, ks * 16, wj * WN + b * 32, lane);
+                else
+                    bv[b] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * WN + b * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
+            }
 #pragma unroll
             for (int a = 0; a < BI; ++a)
 #pragma unroll
@@ -213,14 +289,18 @@ static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of M
 // interleave of LDS reads, LDS stores, global loads and MFMAs stays as written
 #define W4_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+template <bool BKN>
 __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned short *__restrict__ A,
                                                              const unsigned short *__restrict__ B,
                                                              unsigned short *__restrict__ C, int M,
                                                              int N, int Kd, int tiles_m,
                                                              int tiles_n)
 {
+    // B stage: [TN][W4_LDK] (k-contiguous) or [W4_TK][BKN_LDN] (n-contiguous);
+    // the same 73,728 bytes either way
+    constexpr int BR = BKN ? W4_TK : TN, BC = BKN ? BKN_LDN : W4_LDK;
     __shared__ __attribute__((aligned(16))) unsigned short As[2][TM][W4_LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][TN][W4_LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short Bs[2][BR][BC];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wi = wave >> 1, wj = wave & 1;
     int tm, tn;
@@ -228,24 +308,35 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
     const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
 
     // Staging: two sets of 16 registers of 16 bytes per lane; st[t][h] holds A
-    // row lr + 32h and st[t][8 + h] B row lr + 32h, at k chunk lk, of one
-    // stage. Byte offsets inside the tile's rows fit 31 bits (checked by the
-    // launcher).
+    // row lr + 32h at k chunk lk, and st[t][8 + h] B row lr + 32h at k chunk lk
+    // (k-contiguous B) or B's k row br + 8h at columns 8*bc (n-contiguous B),
+    // of one stage. Byte offsets from the descriptors' bases fit 31 bits
+    // (checked by the launcher).
     const int lr = tid / W4_CH, lk = (tid % W4_CH) * 8;
+    const int bc = tid & 31, br = tid >> 5;
     const unsigned voff = (unsigned)((lr * Kd + lk) * 2);
+    const unsigned voff_b = BKN ? (unsigned)((br * N + 8 * bc) * 2) : voff;
     const __amdgpu_buffer_rsrc_t rA =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * Kd), (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rB =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * Kd), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(BKN ? B + n0 : B + n0 * Kd), (short)0, 0x7fffffff, 0x00020000);
     u32x4 st[2][2 * W4_HP];
     auto gload1 = [&](int t, int j, int k0) __attribute__((always_inline)) {
-        const int so = (W4_RPP * (j % W4_HP) * Kd + k0) * 2;
-        st[t][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 j < W4_HP ? rA : rB, voff, so, 0));
+        if (j < W4_HP) {
+            const int so = (W4_RPP * j * Kd + k0) * 2;
+            st[t][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff, so, 0));
+        } else if (BKN) {
+            const int so = ((k0 + 8 * (j - W4_HP)) * N) * 2;
+            st[t][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff_b, so, 0));
+        } else {
+            const int so = (W4_RPP * (j - W4_HP) * Kd + k0) * 2;
+            st[t][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff_b, so, 0));
+        }
     };
     auto sstore1 = [&](int t, int buf, int j) __attribute__((always_inline)) {
-        unsigned short *row = j < W4_HP ? &As[buf][lr + W4_RPP * (j % W4_HP)][lk]
-                                        : &Bs[buf][lr + W4_RPP * (j % W4_HP)][lk];
+        unsigned short *row = j < W4_HP ? &As[buf][lr + W4_RPP * j][lk]
+                              : BKN     ? &Bs[buf][br + 8 * (j - W4_HP)][8 * bc]
+                                        : &Bs[buf][lr + W4_RPP * (j - W4_HP)][lk];
         *reinterpret_cast<u32x4 *>(row) = st[t][j];
     };
 
@@ -261,7 +352,10 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
     auto rd = [&](int set, int buf, int ks, int x) __attribute__((always_inline)) {
         const int r = lane & 31, kc = ks * 16 + 8 * (lane >> 5);
         av[set][x] = *reinterpret_cast<const bf16x8 *>(&As[buf][wi * 128 + x * 32 + r][kc]);
-        bv[set][x] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * 128 + x * 32 + r][kc]);
+        if constexpr (BKN)
+            bv[set][x] = b_operand_kn(&Bs[buf][0][0], BKN_LDN, ks * 16, wj * 128 + x * 32, lane);
+        else
+            bv[set][x] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wj * 128 + x * 32 + r][kc]);
     };
 
     // One stage from LDS buffer buf: 16 groups of 4 MFMAs (k step ks, A block a);
@@ -329,7 +423,47 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
             }
 }
 
-template <int TK, bool EARLY>
+// ------------------------------------------------------ any-shape kernel
+
+// 64x64 tile of C per workgroup of 4 waves (2x2 blocks of 32x32); every lane
+// gathers its 8 A and 8 B operand values of each 16-wide k step with guarded
+// 2-byte loads (zero past M, N or Kd), so any shape and any element alignment
+// works. Same MFMA sequence as the kernels above.
+template <bool BKN>
+__global__ __launch_bounds__(256) void gemm_bf16_any_kernel(const unsigned short *__restrict__ A,
+                                                            const unsigned short *__restrict__ B,
+                                                            unsigned short *__restrict__ C,
+                                                            long long M, long long N, long long Kd,
+                                                            long long tiles_n)
+{
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+    const long long i = tm * 64 + (wave >> 1) * 32 + (lane & 31);
+    const long long j = tn * 64 + (wave & 1) * 32 + (lane & 31);
+    const int kq = 8 * (lane >> 5);
+    f32x16 acc = f32x16{};
+    for (long long k0 = 0; k0 < Kd; k0 += 16) {
+        u16x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const long long k = k0 + kq + e;
+            const bool kin = k < Kd;
+            a[e] = (kin && i < M) ? A[i * Kd + k] : (unsigned short)0;
+            b[e] = (kin && j < N) ? (BKN ? B[k * N + j] : B[j * Kd + k]) : (unsigned short)0;
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const long long gi = tm * 64 + (wave >> 1) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const long long gj = tn * 64 + (wave & 1) * 32 + (lane & 31);
+        if (gi < M && gj < N) C[gi * N + gj] = f32_to_bf16_rne(acc[r]);
+    }
+}
+
+template <int TK, bool EARLY, bool BKN>
 void launch_tk(const void *a, const void *b, void *c, int M, int N, int Kd, int tm, int tn,
                hipStream_t st)
 {
@@ -339,37 +473,58 @@ void launch_tk(const void *a, const void *b, void *c, int M, int N, int Kd, int 
     const auto *B = (const unsigned short *)b;
     auto *C = (unsigned short *)c;
     if (edge)
-        hipLaunchKernelGGL((gemm_bf16_kernel<true, TK, EARLY>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<true, TK, EARLY, BKN>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<false, TK, EARLY>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<false, TK, EARLY, BKN>), dim3(grid), dim3(NT), 0, st, A, B, C, M, N, Kd, tm, tn);
+}
+
+template <bool BKN>
+hipError_t launch_layout(const void *a, const void *b, void *c, long long M, long long N,
+                         long long Kd, int variant, hipStream_t st)
+{
+    // rows of A (and of B) must be 16-byte aligned for the staged kernels
+    const bool rows16 = ((uintptr_t)a & 15) == 0 && ((uintptr_t)b & 15) == 0 && Kd % 8 == 0 &&
+                        (!BKN || N % 8 == 0);
+    if (!rows16) {
+        const long long tm = (M + 63) / 64, tn = (N + 63) / 64;
+        if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((gemm_bf16_any_kernel<BKN>), dim3((unsigned)(tm * tn)), dim3(256), 0, st,
+                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
+                           M, N, Kd, tn);
+        return hipGetLastError();
+    }
+    if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
+    if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // the 4-wave kernel: whole tiles only, byte offsets from its buffer
+    // descriptors' bases (a tile's 256 rows of A, 512 * Kd bytes; an
+    // n-contiguous B's Kd rows, 2 * Kd * N bytes) within 31 bits, and a k range
+    // long enough that the main loop outweighs the per-tile prologue and
+    // epilogue, which one wave per SIMD cannot overlap with another workgroup's
+    // MFMAs (measured: 1.2x the 8-wave kernel at 8192^3, 1.08x at kk = 1536,
+    // 1.02-1.07x at kk = 1024, 0.93x at kk = 512, 0.8x at kk = 256)
+    const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
+                    Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL &&
+                    (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
+    if (w4) {
+        hipLaunchKernelGGL(gemm_bf16_w4_kernel<BKN>, dim3((unsigned)(tm * tn)), dim3(W4_NT), 0, st,
+                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
+                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+    } else if (variant == kGemmShareCU) {
+        launch_tk<32, true, BKN>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
+    } else {
+        launch_tk<64, true, BKN>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const void *a, const void *b, void *c, long long M, long long N,
-                            long long Kd, int variant, hipStream_t st)
+                            long long Kd, int variant, bool b_kn, hipStream_t st)
 {
-    if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
-    const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
-    if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // the 4-wave kernel: whole tiles only, byte offsets inside a tile's 256 rows
-    // (512 * Kd) within its buffer descriptor's 31-bit range, and a k range long
-    // enough that the main loop outweighs the per-tile prologue and epilogue,
-    // which one wave per SIMD cannot overlap with another workgroup's MFMAs
-    // (measured: 1.2x the 8-wave kernel at 8192^3, 1.08x at kk = 1536,
-    // 1.02-1.07x at kk = 1024, 0.93x at kk = 512, 0.8x at kk = 256)
-    const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
-                    Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL;
-    if (w4) {
-        hipLaunchKernelGGL(gemm_bf16_w4_kernel, dim3((unsigned)(tm * tn)), dim3(W4_NT), 0, st,
-                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
-                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
-    } else if (variant == kGemmShareCU) {
-        launch_tk<32, true>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
-    } else {
-        launch_tk<64, true>(a, b, c, (int)M, (int)N, (int)Kd, (int)tm, (int)tn, st);
-    }
-    return hipGetLastError();
+    return b_kn ? launch_layout<true>(a, b, c, M, N, Kd, variant, st)
+                : launch_layout<false>(a, b, c, M, N, Kd, variant, st);
 }
 
 }  // namespace dps

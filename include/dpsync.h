@@ -244,17 +244,21 @@ dp_status_t dp_fsdp_layer_static(int k, int64_t m_local, int64_t d, int64_t f,
  * communication (the GEMM kernel of a (GEMM, collective) pair, "Optimizing ML
  * Concurrent Computation and Communication with GPU DMA Engines", section
  * "Problem Formulation").
- *   c[m,n] = a[m,kk] . b[n,kk]^T: a is [m,kk] and b is [n,kk] (both
- *   k-contiguous, the linear-layer weight layout), c is [m,n]; all row-major
- *   bf16 device buffers, fp32 accumulation on MFMA, result rounded to nearest
- *   even bf16.
- *   m, n, kk >= 1 (else DP_ERR_INVALID_ARG); kk must be a multiple of 8 and a,
- *   b 16-byte aligned (else DP_ERR_UNSUPPORTED); c must not overlap a or b
- *   (DP_ERR_ALIAS).
- *   The products are summed over k in ascending steps of 16 into fp32, the
- *   same order for every shape path and variant; m and n multiples of 256 and
- *   kk a multiple of 64 and >= 1024 run the 4-wave kernel (one wave per SIMD),
- *   other shapes the 8-wave kernel (guarded edge tiles where needed).
+ *   c[m,n] = a[m,kk] . b[kk,n]: a is [m,kk], b is [kk,n], c is [m,n], all
+ *   row-major bf16 device buffers; fp32 accumulation on MFMA, result rounded
+ *   to nearest even bf16. dp_gemm_bf16_ex with DP_LAUNCH_B_NK takes b as
+ *   [n,kk] instead (c = a . b^T, both operands k-contiguous: the linear-layer
+ *   weight layout).
+ *   m, n, kk in [1, 2^24] and every pointer aligned to its 2-byte element
+ *   (else DP_ERR_INVALID_ARG); c must not overlap a or b (DP_ERR_ALIAS).
+ *   The products are summed over k in ascending steps of 16 into fp32 (each
+ *   step one matrix-core instruction, zero-padded past kk), the same order for
+ *   every shape, layout and variant, so all give the same bits. Rows that are
+ *   16-byte aligned (a and b 16-byte aligned, kk a multiple of 8, and n a
+ *   multiple of 8 for b [kk,n]) take the staged kernels: m and n multiples of
+ *   256 and kk a multiple of 64 and >= 1024 the 4-wave kernel (one wave per
+ *   SIMD), other shapes the 8-wave kernel (guarded edge tiles where needed);
+ *   other rows a slower kernel that gathers operands element by element.
  */
 dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64_t n,
                          int64_t kk, void *stream);
@@ -284,7 +288,8 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
  *                    so the two kernels can be resident together. (The default
  *                    GEMM runs one wave per SIMD and uses all of its registers
  *                    where the shape allows; every GEMM variant gives the same
- *                    bits.) Other calls ignore the flags.
+ *                    bits.) DP_LAUNCH_B_NK: dp_gemm_bf16_ex's b is stored
+ *                    [n,kk] (c = a . b^T). Other calls ignore the flags.
  *   reserved       : must be zero.
  * A NULL opts pointer means all defaults. Invalid fields return
  * DP_ERR_INVALID_ARG.
@@ -292,6 +297,7 @@ dp_status_t dp_gemm_bf16(const void *a, const void *b, void *c, int64_t m, int64
 #define DP_LAUNCH_SHARE_CU 1
 #define DP_LAUNCH_TWO_PHASE 2
 #define DP_LAUNCH_LEAN 4
+#define DP_LAUNCH_B_NK 8
 
 typedef struct {
     int max_workgroups;

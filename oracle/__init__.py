@@ -83,7 +83,7 @@ def lib():
         L.orc_gemm_f64.restype = None
         L.orc_gemm_f64.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int]
         L.orc_gemm_bf16_at.restype = None
-        L.orc_gemm_bf16_at.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _int]
+        L.orc_gemm_bf16_at.argtypes = [_vp, _vp, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _int]
         L.orc_fsdp_layer.restype = None
         L.orc_fsdp_layer.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _int]
@@ -260,19 +260,26 @@ def gemm_f64(a: np.ndarray, b: np.ndarray, trans_a: bool = False, nthreads: int 
     return c, ab
 
 
-def gemm_bf16_at(a_bits: np.ndarray, b_bits: np.ndarray, rows, cols, nthreads: int = 1):
-    """fp64 (value, sum|a||b|) of (A B)[rows[s], cols[s]] for bf16 A, B (uint16 bits)."""
+def gemm_bf16_at(a_bits: np.ndarray, b_bits: np.ndarray, rows, cols, nthreads: int = 1,
+                 b_layout: str = "kn"):
+    """fp64 (value, sum|a||b|) of C[rows[s], cols[s]] for bf16 A [m,kk] (uint16
+    bits) and B stored [kk,n] (b_layout "kn": C = A B) or [n,kk] ("nk": C = A B^T)."""
     a = np.ascontiguousarray(a_bits, dtype=np.uint16)
     b = np.ascontiguousarray(b_bits, dtype=np.uint16)
-    kk, n = b.shape
+    if b_layout == "kn":
+        kk, n = b.shape
+    elif b_layout == "nk":
+        n, kk = b.shape
+    else:
+        raise ValueError("b_layout must be 'kn' or 'nk'")
     assert a.shape[1] == kk
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     vals = np.zeros(rows.size, dtype=np.float64)
     absv = np.zeros(rows.size, dtype=np.float64)
-    lib().orc_gemm_bf16_at(a.ctypes.data, b.ctypes.data, n, kk, rows.ctypes.data,
-                           cols.ctypes.data, rows.size, vals.ctypes.data, absv.ctypes.data,
-                           nthreads)
+    lib().orc_gemm_bf16_at(a.ctypes.data, b.ctypes.data, n, kk, int(b_layout == "nk"),
+                           rows.ctypes.data, cols.ctypes.data, rows.size, vals.ctypes.data,
+                           absv.ctypes.data, nthreads)
     return vals, absv
 
 

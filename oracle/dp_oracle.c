@@ -483,8 +483,10 @@ void orc_gemm_f64(const float *a, const float *b, double *c, double *abs_c, int6
     }
 }
 
-/* bf16 inputs, fp64 result at sampled (rows[s], cols[s]); abs_c as above */
-void orc_gemm_bf16_at(const uint16_t *a, const uint16_t *b, int64_t n, int64_t kk,
+/* bf16 inputs, fp64 result at sampled (rows[s], cols[s]) of C = A B with A
+ * [m, kk]; B stored [kk, n] (b_nk = 0) or [n, kk] (b_nk = 1, so C = A B^T);
+ * abs_c as above */
+void orc_gemm_bf16_at(const uint16_t *a, const uint16_t *b, int64_t n, int64_t kk, int b_nk,
                       const int64_t *rows, const int64_t *cols, int64_t count, double *vals,
                       double *abs_vals, int nthreads)
 {
@@ -494,7 +496,7 @@ void orc_gemm_bf16_at(const uint16_t *a, const uint16_t *b, int64_t n, int64_t k
         double acc = 0.0, sa = 0.0;
         for (int64_t p = 0; p < kk; ++p) {
             double av = (double)orc_bf16_to_f32(a[rows[s] * kk + p]);
-            double bv = (double)orc_bf16_to_f32(b[p * n + cols[s]]);
+            double bv = (double)orc_bf16_to_f32(b_nk ? b[cols[s] * kk + p] : b[p * n + cols[s]]);
             acc += av * bv;
             sa += fabs(av) * fabs(bv);
         }

@@ -189,9 +189,10 @@ def test_gemm_validation():
     a, b, c = 1 << 40, 1 << 41, 1 << 42
     assert L.dp_gemm_bf16(a, b, c, 0, 8, 8, None) == INVALID
     assert L.dp_gemm_bf16(None, b, c, 8, 8, 8, None) == INVALID
-    assert L.dp_gemm_bf16(a, b, c, 8, 8, 12, None) == UNSUPPORTED    # k not a multiple of 8
-    assert L.dp_gemm_bf16(a + 2, b, c, 8, 8, 8, None) == UNSUPPORTED
+    assert L.dp_gemm_bf16(a + 1, b, c, 8, 8, 8, None) == INVALID      # not element-aligned
+    assert L.dp_gemm_bf16(a, b, c + 3, 8, 8, 12, None) == INVALID
     assert L.dp_gemm_bf16(a, b, a + 16, 8, 8, 8, None) == ALIAS
+    assert L.dp_gemm_bf16(a, b, c, 1 << 25, 8, 8, None) == INVALID
 
 
 def test_bucket_plan():
@@ -236,7 +237,7 @@ def test_launch_options_validation():
     L = dps.lib()
     a, b = fake(4), fake(4, base=1 << 41)
     bad = [dps.LaunchOpts(-1, 0, (ctypes.c_int * 2)(0, 0)),
-           dps.LaunchOpts(0, 8, (ctypes.c_int * 2)(0, 0)),
+           dps.LaunchOpts(0, 16, (ctypes.c_int * 2)(0, 0)),
            dps.LaunchOpts(0, 0, (ctypes.c_int * 2)(1, 0))]
     for o in bad:
         r = ctypes.byref(o)
@@ -248,7 +249,9 @@ def test_launch_options_validation():
     # valid options, still rejected for the usual reasons (nothing is launched)
     assert L.dp_reduce_scatter_ex(P(a), P(b), 100, 0, F32, SUM, 1, ok, None) == INVALID
     assert L.dp_all_reduce_ex(P(a), P(b), 0, 4, F32, SUM, 1, ok, None) == OK
-    assert L.dp_gemm_bf16_ex(1 << 40, 1 << 41, 1 << 42, 8, 8, 12, ok, None) == UNSUPPORTED
+    assert L.dp_gemm_bf16_ex(1 << 40, (1 << 41) + 1, 1 << 42, 8, 8, 12, ok, None) == INVALID
+    nk = ctypes.byref(dps.LaunchOpts(0, dps.DP_LAUNCH_B_NK, (ctypes.c_int * 2)(0, 0)))
+    assert L.dp_gemm_bf16_ex(1 << 40, 1 << 41, (1 << 41) + 2, 8, 8, 8, nk, None) == ALIAS
     assert L.dp_reduce_scatter_ex(P(a), P(b), 0, 4, F32, SUM, 1, None, None) == OK
 
 
@@ -314,7 +317,7 @@ def test_overlap_validation():
     assert call(nev=2) == INVALID                           # 3 buckets need 3 events
     assert call(ev_=None, nev=0) == INVALID
     assert call(bucket=0) == INVALID
-    bad_opts = dps.LaunchOpts(0, 8, (ctypes.c_int * 2)(0, 0))
+    bad_opts = dps.LaunchOpts(0, 16, (ctypes.c_int * 2)(0, 0))
     assert call(opts=ctypes.byref(bad_opts)) == INVALID
 
 

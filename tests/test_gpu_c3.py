@@ -15,8 +15,9 @@ Checks after each concurrent run:
     ReduceScatter of the same inputs (fp64 per-shard checksums of both are
     compared as well, as a summary), every AllGather output equal to output 0
     on the device, and output 0 bit-exact against the oracle's AllGather;
-  - GEMM: bit-identical to the same GEMM run alone, which is itself checked
-    at sampled entries within the fp32 summation bound of the fp64 product.
+  - GEMM (C = A B, both operands [8192, 8192] row-major): bit-identical to
+    the same GEMM run alone, which is itself checked at sampled entries within
+    the fp32 summation bound of the fp64 product.
 """
 import numpy as np
 import pytest
@@ -71,9 +72,7 @@ def test_c3_gemm_alone_sampled(workload):
     rows = np.concatenate([rng.integers(0, MNK, 2000), [0, 0, MNK - 1, MNK - 1, 255, 256]])
     cols = np.concatenate([rng.integers(0, MNK, 2000), [0, MNK - 1, 0, MNK - 1, 256, 255]])
     rows, cols = rows.astype(np.int64), cols.astype(np.int64)
-    ab = to_np(w["a"])
-    bt = np.ascontiguousarray(to_np(w["b"]).T)
-    ref, absr = oracle.gemm_bf16_at(ab, bt, rows, cols, nthreads=16)
+    ref, absr = oracle.gemm_bf16_at(to_np(w["a"]), to_np(w["b"]), rows, cols, nthreads=16)
     got = oracle.bf16_to_f32(to_np(w["c_alone"])[rows, cols]).astype(np.float64)
     g = _gamma(MNK + 1) * absr
     assert np.all(np.abs(got - ref) <= U_BF16 * (np.abs(ref) + g) + g)

@@ -185,105 +185,164 @@ def _bits(t):
     return to_np(t)
 
 
-def check_gemm(a, b, rows=None, cols=None, exact=False):
-    m, kk = a.shape
-    n = b.shape[0]
+def run_gemm(a, b, layout="kn", **opts):
+    m = a.shape[0]
+    n = b.shape[1] if layout == "kn" else b.shape[0]
     c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
-    dps.dp_gemm_bf16(a, b, c)
+    dps.dp_gemm_bf16_ex(a, b, c, b_layout=layout, **opts)
     torch.cuda.synchronize()
+    return c
+
+
+def check_gemm(a, b, layout="kn", rows=None, cols=None, exact=False, c=None):
+    """The product against the oracle's fp64 value of the same bf16 operands,
+    read in the same layout (no transposition on either side)."""
+    m, kk = a.shape
+    n = b.shape[1] if layout == "kn" else b.shape[0]
+    if c is None:
+        c = run_gemm(a, b, layout)
     if rows is None:
         rows, cols = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
         rows, cols = rows.ravel(), cols.ravel()
-    ab = _bits(a)
-    bt = np.ascontiguousarray(_bits(b).T)
-    ref, absr = oracle.gemm_bf16_at(ab, bt, rows, cols, nthreads=16)
+    ref, absr = oracle.gemm_bf16_at(_bits(a), _bits(b), rows, cols, nthreads=16, b_layout=layout)
     got = oracle.bf16_to_f32(_bits(c)[rows, cols]).astype(np.float64)
     if exact:
         assert np.array_equal(got, ref)
-        return
+        return c
     g = gamma(kk + 1)
     bound = U_BF16 * (np.abs(ref) + g * absr) + g * absr
     err = np.abs(got - ref)
     assert np.all(err <= bound), float((err - bound).max())
+    return c
 
 
+def _small_int_inputs(m, n, kk, layout, seed, lo=-1, hi=2):
+    g = torch.Generator().manual_seed(seed)
+    ai = torch.randint(lo, hi, (m, kk), generator=g).to(torch.bfloat16).to(DEV)
+    shape = (kk, n) if layout == "kn" else (n, kk)
+    bi = torch.randint(lo, hi, shape, generator=g).to(torch.bfloat16).to(DEV)
+    return ai, bi
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("m,n,kk", [(128, 128, 32), (256, 384, 64), (200, 136, 40), (1, 1, 8),
                                     (129, 255, 1000), (512, 512, 4096)])
-def test_gemm_bf16_small(m, n, kk):
-    say(f"gemm bf16 {m}x{n}x{kk}")
-    a, b = gen.gemm_bf16_inputs(8, m, n, kk, device=DEV)
-    check_gemm(a, b)
-    g = torch.Generator().manual_seed(m + n)
-    ai = torch.randint(-1, 2, (m, kk), generator=g).to(torch.bfloat16).to(DEV)
-    bi = torch.randint(-1, 2, (n, kk), generator=g).to(torch.bfloat16).to(DEV)
+def test_gemm_bf16_small(m, n, kk, layout):
+    say(f"gemm bf16 {layout} {m}x{n}x{kk}")
+    a, b = gen.gemm_bf16_inputs(8, m, n, kk, device=DEV, b_layout=layout)
+    check_gemm(a, b, layout)
     if kk <= 256:
-        check_gemm(ai, bi, exact=True)
+        check_gemm(*_small_int_inputs(m, n, kk, layout, m + n), layout, exact=True)
 
 
 def test_gemm_bf16_8192_sampled():
-    """C = A B^T with A, B bf16 [8192,8192] ~ N(0,1): sampled entries."""
+    """C = A B with A, B bf16 [8192,8192] ~ N(0,1): sampled entries."""
     m = n = kk = 8192
     say("gemm bf16 8192^3")
     a, b = gen.gemm_bf16_inputs(5, m, n, kk, device=DEV)
     rng = np.random.default_rng(1)
     rows = np.concatenate([rng.integers(0, m, 3000), [0, 0, m - 1, m - 1, 127, 128]])
     cols = np.concatenate([rng.integers(0, n, 3000), [0, n - 1, 0, n - 1, 128, 127]])
-    check_gemm(a, b, rows.astype(np.int64), cols.astype(np.int64))
+    c = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+    dps.dp_gemm_bf16(a, b, c)
+    torch.cuda.synchronize()
+    check_gemm(a, b, "kn", rows.astype(np.int64), cols.astype(np.int64), c=c)
 
 
 @pytest.mark.parametrize("m,n,kk", [(256, 256, 2048), (512, 768, 2112), (1024, 256, 4096),
                                     (512, 512, 1024), (256, 768, 1472),
-                                    (768, 512, 320), (2048, 2048, 64), (256, 256, 960)])
-def test_gemm_bf16_variants_bit_identical(m, n, kk):
+                                    (768, 512, 320), (2048, 2048, 64), (256, 256, 960),
+                                    (264, 280, 1032)])
+def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run the 4-wave
     kernel; the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
-    DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, so
-    all agree bit for bit (shorter k ranges take the 8-wave kernel on every
-    path: the last three cases). The default result is also checked against the
-    oracle (exactly on small-integer inputs, within the fp32 summation bound on
-    N(0,1) inputs); an odd number of k stages (2112 = 33 x 64) and grids that
-    are not a multiple of 8 tiles are among the cases."""
+    DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
+    B stored [kk,n] (transposing LDS reads) and [n,kk] alike, so all six agree
+    bit for bit (shorter k ranges and edge tiles take the 8-wave kernel on
+    every path). The default result is also checked against the oracle
+    (exactly on small-integer inputs, within the fp32 summation bound on N(0,1)
+    inputs); an odd number of k stages (2112 = 33 x 64) and grids that are not a
+    multiple of 8 tiles are among the cases."""
     say(f"gemm bf16 variants {m}x{n}x{kk}")
-    a, b = gen.gemm_bf16_inputs(11, m, n, kk, device=DEV)
+    a, b_kn = gen.gemm_bf16_inputs(11, m, n, kk, device=DEV, b_layout="kn")
+    b_nk = b_kn.t().contiguous()
     outs = []
-    for opts in ({}, {"lean": True}, {"share_cu": True}):
-        c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
-        dps.dp_gemm_bf16_ex(a, b, c, **opts)
-        torch.cuda.synchronize()
-        outs.append(_bits(c))
-    assert np.array_equal(outs[0], outs[1])
-    assert np.array_equal(outs[0], outs[2])
+    for layout, b in (("kn", b_kn), ("nk", b_nk)):
+        for opts in ({}, {"lean": True}, {"share_cu": True}):
+            outs.append(_bits(run_gemm(a, b, layout, **opts)))
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
     rng = np.random.default_rng(kk)
     rows = np.concatenate([rng.integers(0, m, 1500), [0, m - 1, 255, 256 % m]]).astype(np.int64)
     cols = np.concatenate([rng.integers(0, n, 1500), [n - 1, 0, 256 % n, 255]]).astype(np.int64)
-    check_gemm(a, b, rows, cols)
+    check_gemm(a, b_kn, "kn", rows, cols)
     # small integers: every fp32 partial sum is exact (|sum| <= 4 kk < 2^24), so
     # the result is the exact sum rounded once to bf16
-    g = torch.Generator().manual_seed(m + kk)
-    ai = torch.randint(-2, 3, (m, kk), generator=g).to(torch.bfloat16).to(DEV)
-    bi = torch.randint(-2, 3, (n, kk), generator=g).to(torch.bfloat16).to(DEV)
-    c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
-    dps.dp_gemm_bf16(ai, bi, c)
-    torch.cuda.synchronize()
-    ref, _ = oracle.gemm_bf16_at(_bits(ai), np.ascontiguousarray(_bits(bi).T), rows, cols,
-                                 nthreads=16)
+    ai, bi = _small_int_inputs(m, n, kk, "kn", m + kk, -2, 3)
+    c = run_gemm(ai, bi, "kn")
+    ref, _ = oracle.gemm_bf16_at(_bits(ai), _bits(bi), rows, cols, nthreads=16)
     assert np.array_equal(_bits(c)[rows, cols], oracle.bf16_from_f32(ref.astype(np.float32)))
 
 
-@pytest.mark.parametrize("m,n,kk", [(256, 256, 32), (200, 136, 40), (512, 768, 1024), (8192, 8192, 8192)])
-def test_gemm_bf16_share_cu_variant(m, n, kk):
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("m,n,kk", [(256, 256, 32), (200, 136, 40), (512, 768, 1024),
+                                    (8192, 8192, 8192)])
+def test_gemm_bf16_share_cu_variant(m, n, kk, layout):
     """The depth-32 variant (DP_LAUNCH_SHARE_CU) against the oracle, including
     shapes with edge tiles."""
-    say(f"gemm bf16 share-cu {m}x{n}x{kk}")
-    a, b = gen.gemm_bf16_inputs(9, m, n, kk, device=DEV)
-    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
-    dps.dp_gemm_bf16_ex(a, b, c, share_cu=True)
-    torch.cuda.synchronize()
+    say(f"gemm bf16 share-cu {layout} {m}x{n}x{kk}")
+    a, b = gen.gemm_bf16_inputs(9, m, n, kk, device=DEV, b_layout=layout)
+    c = run_gemm(a, b, layout, share_cu=True)
     rng = np.random.default_rng(m + kk)
     rows = np.concatenate([rng.integers(0, m, 2000), [0, m - 1]]).astype(np.int64)
     cols = np.concatenate([rng.integers(0, n, 2000), [n - 1, 0]]).astype(np.int64)
-    ref, absr = oracle.gemm_bf16_at(_bits(a), np.ascontiguousarray(_bits(b).T), rows, cols,
-                                    nthreads=16)
-    got = oracle.bf16_to_f32(_bits(c)[rows, cols]).astype(np.float64)
-    g = gamma(kk + 1)
-    assert np.all(np.abs(got - ref) <= U_BF16 * (np.abs(ref) + g * absr) + g * absr)
+    check_gemm(a, b, layout, rows, cols, c=c)
+
+
+def _offset_copy(t, off):
+    """t's values in a fresh buffer starting `off` elements into its allocation."""
+    full = torch.empty(t.numel() + off, dtype=t.dtype, device=DEV)
+    v = full[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("m,n,kk,off", [(64, 64, 13, 0), (97, 45, 1003, 0), (256, 256, 1024, 1),
+                                        (33, 300, 77, 3), (1, 5, 1, 1), (130, 7, 200, 0)])
+def test_gemm_bf16_any_shape_and_alignment(m, n, kk, off, layout):
+    """Rows that are not 16-byte aligned (kk or n not a multiple of 8, or
+    operands at an odd element offset) take the element-gathering kernel: it
+    matches the oracle (exactly on small integers), and where the same values
+    also fit the staged kernels (copied to aligned buffers, kk padded with
+    zeros to a multiple of 8) both give the same bits."""
+    say(f"gemm bf16 any {layout} {m}x{n}x{kk} off={off}")
+    a, b = gen.gemm_bf16_inputs(12, m, n, kk, device=DEV, b_layout=layout)
+    a_o, b_o = _offset_copy(a, off), _offset_copy(b, off)
+    c_full = torch.empty((m * n + off + 8,), dtype=torch.bfloat16, device=DEV)
+    c_full.view(torch.int16).fill_(0x5A5A)                 # canary around the output
+    c = c_full[off:off + m * n].view(m, n)
+    dps.dp_gemm_bf16_ex(a_o, b_o, c, b_layout=layout)
+    torch.cuda.synchronize()
+    check_gemm(a, b, layout, c=c)
+    guard = np.concatenate([to_np(c_full[:off]), to_np(c_full[off + m * n:])])
+    assert np.all(guard == 0x5A5A)
+    # the staged kernels on zero-padded, aligned copies of the same values
+    k8 = -(-kk // 8) * 8
+    n8 = -(-n // 8) * 8 if layout == "kn" else n
+    ap = torch.zeros(m, k8, dtype=torch.bfloat16, device=DEV)
+    ap[:, :kk] = a
+    if layout == "kn":
+        bp = torch.zeros(k8, n8, dtype=torch.bfloat16, device=DEV)
+        bp[:kk, :n] = b
+    else:
+        bp = torch.zeros(n, k8, dtype=torch.bfloat16, device=DEV)
+        bp[:, :kk] = b
+    cp = run_gemm(ap, bp, layout)
+    assert np.array_equal(_bits(cp)[:, :n], _bits(c))
+    if kk <= 256:
+        ai, bi = _small_int_inputs(m, n, kk, layout, 7 * m + kk)
+        ci = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+        dps.dp_gemm_bf16_ex(_offset_copy(ai, off), _offset_copy(bi, off), ci, b_layout=layout)
+        torch.cuda.synchronize()
+        check_gemm(ai, bi, layout, exact=True, c=ci)

@@ -58,10 +58,10 @@ def check_pieces(pieces, t, dy, x, grad_host, k, ranks, samples=None, exact=Fals
             else:
                 rows = np.concatenate([rng.integers(0, m, samples), [0, m - 1, 0, m - 1]])
                 cols = np.concatenate([rng.integers(0, n, samples), [0, n - 1, n - 1, 0]])
-            a = to_np(dy[g * k + r])
-            bt = np.ascontiguousarray(to_np(x[g * k + r]).T)
-            ref, absr = oracle.gemm_bf16_at(a, bt, rows.astype(np.int64), cols.astype(np.int64),
-                                            nthreads=16)
+            # dW = dY X^T with X stored [n, t]: the [n, kk] layout of B
+            ref, absr = oracle.gemm_bf16_at(to_np(dy[g * k + r]), to_np(x[g * k + r]),
+                                            rows.astype(np.int64), cols.astype(np.int64),
+                                            nthreads=16, b_layout="nk")
             got = oracle.bf16_to_f32(grad_host[r][off:off + m * n].reshape(m, n)[rows, cols])
             got = got.astype(np.float64)
             if exact:

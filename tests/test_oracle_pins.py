@@ -596,14 +596,25 @@ def test_gemm_f64_matches_numpy():
 
 
 def test_gemm_bf16_at_matches_numpy():
-    a, b = gen.gemm_bf16_inputs(5, 40, 24, 96)          # b is [n, k]
+    """Both B layouts against numpy's fp64 product of the exactly widened bf16
+    values, with the |A||B| sums."""
+    a = gen.bf16_normal(5, 30, 0, 40 * 96, 1.0).view(40, 96)
+    b_kn = gen.bf16_normal(5, 31, 0, 96 * 24, 1.0).view(96, 24)
+    b_nk = b_kn.t().contiguous()
     ab = a.view(torch.int16).numpy().view(np.uint16)
-    bb = np.ascontiguousarray(b.view(torch.int16).numpy().view(np.uint16).T)
     rows = np.array([0, 3, 39, 17], np.int64)
     cols = np.array([0, 23, 5, 11], np.int64)
-    vals, _ = oracle.gemm_bf16_at(ab, bb, rows, cols)
-    ref = a.double().numpy() @ b.double().numpy().T
-    assert np.allclose(vals, ref[rows, cols], rtol=0, atol=1e-12)
+    ref = a.double().numpy() @ b_kn.double().numpy()
+    refa = np.abs(a.double().numpy()) @ np.abs(b_kn.double().numpy())
+    for layout, b in (("kn", b_kn), ("nk", b_nk)):
+        vals, absv = oracle.gemm_bf16_at(ab, b.view(torch.int16).numpy().view(np.uint16), rows,
+                                         cols, b_layout=layout)
+        assert np.allclose(vals, ref[rows, cols], rtol=0, atol=1e-12), layout
+        assert np.allclose(absv, refa[rows, cols], rtol=1e-15), layout
+    # the [n,kk] array read as if it were [kk,n] (a layout mix-up) is caught
+    nk_bits = b_nk.view(torch.int16).numpy().view(np.uint16)
+    bad, _ = oracle.gemm_bf16_at(ab, nk_bits.reshape(96, 24), rows, cols, b_layout="kn")
+    assert not np.allclose(bad, ref[rows, cols], atol=1e-6)
 
 
 def test_fsdp_global_view_invariance():
