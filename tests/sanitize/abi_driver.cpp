@@ -84,8 +84,17 @@ int main()
                             (float *const *)c, (float *const *)d, (float *const *)d,
                             (float *const *)d, (float *const *)d, nullptr),
            DP_ERR_INVALID_ARG, "fsdp_ex dx without dy");
+    void *e[DP_MAX_K];
+    fake(e, DP_MAX_K, (uintptr_t)1 << 44);
+    expect(dp_fsdp_layer_static(0, 8, 8, 8, (const float *const *)a, (const float *const *)b,
+                                (const float *const *)c, (float *const *)d, nullptr,
+                                (float *const *)e, nullptr), DP_ERR_INVALID_ARG, "fsdp static k");
+    expect(dp_fsdp_layer_static(8, 8, 1024, 1024, (const float *const *)a, (const float *const *)b,
+                                (const float *const *)c, (float *const *)d, nullptr,
+                                (float *const *)e, nullptr), DP_ERR_SCRATCH, "fsdp static size");
     expect(dp_gemm_bf16(a[0], b[0], c[0], 0, 8, 8, nullptr), DP_ERR_INVALID_ARG, "gemm m");
-    expect(dp_gemm_bf16(a[0], b[0], c[0], 8, 8, 12, nullptr), DP_ERR_UNSUPPORTED, "gemm k");
+    expect(dp_gemm_bf16(a[0], (char *)b[0] + 1, c[0], 8, 8, 12, nullptr), DP_ERR_INVALID_ARG,
+           "gemm b alignment");
     expect(dp_gemm_bf16(a[0], b[0], (char *)a[0] + 16, 8, 8, 8, nullptr), DP_ERR_ALIAS, "gemm alias");
 
     float *acc[4];
