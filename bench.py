@@ -45,14 +45,16 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 
 
 # HBM bytes per full-size launch from two rocprofv3 PMC passes (FETCH_SIZE x 2.0,
-# WRITE_SIZE x 1.0, factors from a plain 1 GiB copy), valid only for the kernel
-# sources they were taken on (sha256 of sync_kernels.hip + sync_internal.h).
+# WRITE_SIZE x 1.0, factors from a plain 1 GiB copy) recorded in
+# profiles/sync_kernels_layer_k8_bf16.md, valid only for the kernel sources they
+# were taken on (sha256 of sync_kernels.hip + sync_internal.h; the gfx950 code of
+# these sources is the same as that of the tree the counters were taken on).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "6b4258669b13664da75507a59562c91a93d78cc66363b982c71a6faa18e74bd3"
-                      "b850e90b15c363987deced1fc1305e093b5a658a6f7105e7927a82440a46a8fb",
+    "sources_sha256": "ee2c112dd5dba12d58a9d63dba859e2b6c01a3e7bd43c0fb5af5a562eee40b0d"
+                      "a4d8bd48c142ae6134854361dbdbf9eadcada43974efa00bf403909f6b226495",
     "rs_kernel<bf16, avg, K=8>": (2 * 195384.1 + 49019.4) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25139.0 + 390956.5) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220533.0 + 439713.4) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25138.9 + 390957.6) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220533.0 + 439711.3) * 1024,
 }
 
 
@@ -617,7 +619,12 @@ def bench_c3(args):
     # the two completion events. 6 warm-up + 9 measured runs, median.
     iso = {}
     res = {}
-    for name, sched in SCHEDULES.items():
+    wanted = args.schedules.split(",") if args.schedules else list(SCHEDULES)
+    for name in wanted:
+        if name not in SCHEDULES:
+            raise SystemExit(f"bench.py: unknown C3 schedule {name!r}; known: {', '.join(SCHEDULES)}")
+    for name in ["base"] + [w for w in wanted if w != "base"]:
+        sched = SCHEDULES[name]
         try:
             sc, sg, closers = pair.streams(sched)
         except RuntimeError as e:
@@ -1050,6 +1057,9 @@ def main():
     ap.add_argument("--config", default="layer", choices=["layer", "all", *CONFIGS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--schedules", default="",
+                    help="--config c3: comma-separated schedule names (default: all; the "
+                         "base schedule always runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU (K ranks are emulated as K buffers in "

@@ -69,7 +69,7 @@ hipError_t launch_gemm_f32(const GemmF32Batch &g, hipStream_t st)
                          (g.trans_b ? g.b_rows % BN != 0 : g.b_rows % BK != 0)))
         return hipErrorInvalidValue;
     // grids that leave CUs idle get eight waves per tile (k split in two)
-    const bool split = blocks <= DPS_GEMM_F32_SPLIT_MAX;
+    const bool split = blocks <= kSplitMax;
     if (g.trans_a) {
         if (split) launch_f32<1, 512>(g, blocks, gx, whole, st);
         else launch_f32<1, 256>(g, blocks, gx, whole, st);

@@ -30,15 +30,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64, BN = 64, BK = 32, LDP = 64 + 4;
 
-#ifndef DPS_GEMM_F32_DEPTH
-#define DPS_GEMM_F32_DEPTH 2            // k stages in flight from global memory (even)
-#endif
-constexpr int kDepth = DPS_GEMM_F32_DEPTH;
+constexpr int kDepth = 2;            // k stages in flight from global memory (even)
 static_assert(kDepth >= 2 && kDepth % 2 == 0, "an even number of register stages");
 
-#ifndef DPS_GEMM_F32_SPLIT_MAX
-#define DPS_GEMM_F32_SPLIT_MAX 256      // largest grid that gets eight waves per tile
-#endif
+constexpr int kSplitMax = 256;       // largest grid that gets eight waves per tile
 
 // Stage loader: the 64x32 A and 32x64 B tiles of one stage as 2 x 256 float4
 // each; with NT threads every thread takes 512/NT of them (h = 0, 1 for 256

@@ -29,55 +29,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Tuning knobs (measured at layer size on MI355X; defaults are the best found)
-#ifndef DPS_ODC_TILE
-#define DPS_ODC_TILE 4096          // elements of one shard per workgroup tile
-#endif
-#ifndef DPS_ODC_PUSH_UNROLL
-#define DPS_ODC_PUSH_UNROLL 4      // gradients whose loads are in flight together
-#endif
-#ifndef DPS_ODC_NT_ACC
-#define DPS_ODC_NT_ACC 1           // 1: nontemporal accumulator stores, 2: loads and stores
-#endif
-#ifndef DPS_ODC_NT_OUT
-#define DPS_ODC_NT_OUT 1           // nontemporal stores of the settled shards
-#endif
-
+// Sizes measured best at layer size on MI355X
 constexpr int kOdcBlock = 256;
-constexpr long long kOdcTile = DPS_ODC_TILE;
-constexpr int kPushUnroll = DPS_ODC_PUSH_UNROLL;
+constexpr long long kOdcTile = 4096;      // elements of one shard per workgroup tile
+constexpr int kPushUnroll = 4;            // gradients whose loads are in flight together
 
+// Accumulators: ordinary loads, nontemporal stores (nontemporal loads as well
+// measured slower); settled shards: nontemporal stores.
 __device__ __forceinline__ f32x4 ld_acc(const float *p)
 {
-#if DPS_ODC_NT_ACC >= 2
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-#else
     return *reinterpret_cast<const f32x4 *>(p);
-#endif
 }
 
 __device__ __forceinline__ void st_acc(float *p, f32x4 v)
 {
-#if DPS_ODC_NT_ACC >= 1
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
-#else
-    *reinterpret_cast<f32x4 *>(p) = v;
-#endif
 }
 
 template <typename V>
 __device__ __forceinline__ void st_out(V *p, V v)
 {
-#if DPS_ODC_NT_OUT
     __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
 }
-
-#ifndef DPS_ODC_BF16_GROUP
-#define DPS_ODC_BF16_GROUP 8       // bf16 elements per thread group: 8 (16-byte loads) or 4 (8-byte)
-#endif
 
 // G elements per thread group (the gradient load is G*s bytes, the
 // accumulator G*4 bytes); U groups per thread per tile. With G = 4 every
@@ -86,7 +59,7 @@ __device__ __forceinline__ void st_out(V *p, V v)
 // loads, two 16-byte accumulator stores per group) writes about 12% more
 // partial lines but runs faster on MI355X.
 template <int DT> struct Grp {
-    static constexpr int G = DT == kBF16 ? DPS_ODC_BF16_GROUP : 4;
+    static constexpr int G = DT == kBF16 ? 8 : 4;
     static constexpr int U = (int)(kOdcTile / (kOdcBlock * G));
     static constexpr int W = G * (DT == kBF16 ? 2 : 4) / 4;     // 32-bit words per gradient load
 };

@@ -51,22 +51,13 @@ template <int DT> struct RsU { static constexpr int U = 1; };
 constexpr int kArU = 1;
 // The AllGather, too, stores each loaded vector K times; one vector per lane
 // measured best (the pipelined layer step 1.3508 -> 1.3382 ms against 2).
-#ifndef DPS_AG_U
-#define DPS_AG_U 1
-#endif
-constexpr int kAgU = DPS_AG_U;
+constexpr int kAgU = 1;
 // With a capped grid (dp_launch_opts_t.max_workgroups) a few resident
 // workgroups walk many tiles, and two vectors per lane keep twice the loads in
 // flight per workgroup (1 GiB/rank fp32 RS + AG on 256 workgroups: 3.78 ms
 // against 4.01 with one; on the default grid one is faster: 3.42 against 3.53).
 constexpr int kUCapped = 2;
-#ifndef DPS_AG_BLOCK
-#define DPS_AG_BLOCK 256
-#endif
-constexpr int kAgBlock = DPS_AG_BLOCK;   // threads per AllGather workgroup
-#ifndef DPS_AG_NT_STORE
-#define DPS_AG_NT_STORE 1
-#endif
+constexpr int kAgBlock = 256;   // threads per AllGather workgroup
 // AllGather shard sets that a ReduceScatter left in the caches (see
 // kCacheOutBytes) are loaded with the nontemporal hint, as each shard is read
 // once: K = 8 bf16 layer step, pipelined 78.59% -> 79.08% and 81.52% ->
@@ -74,18 +65,10 @@ constexpr int kAgBlock = DPS_AG_BLOCK;   // threads per AllGather workgroup
 // HBM, keep ordinary loads. The output stores stay nontemporal: with ordinary
 // stores the 400 MB a bucket's AllGather writes displace the next bucket's
 // shards from the Infinity Cache (pipelined 81.52% -> 74.70%).
-// persistent grid: workgroups per CU and the CU count the default assumes
 // Default grid: one workgroup per tile (a wave that finishes its tile exits
-// instead of waiting for its stores before loading the next tile). A positive
-// DPS_BLOCKS_PER_CU caps the grid at that many workgroups per CU instead.
-#ifndef DPS_BLOCKS_PER_CU
-#define DPS_BLOCKS_PER_CU 0
-#endif
-constexpr int kBlocksPerCU = DPS_BLOCKS_PER_CU;
-#ifndef DPS_CUS
-#define DPS_CUS 256
-#endif
-constexpr int kCUs = DPS_CUS;
+// instead of waiting for its stores before loading the next tile); measured
+// faster than persistent grids of 1, 2 or 4 workgroups per CU. A caller's
+// dp_launch_opts_t.max_workgroups caps it instead.
 
 // Where an AllGather reads the shards next (the fused ReduceScatter + AllGather
 // launch of the bucket pipeline, whose AllGather half reads the previous
@@ -98,21 +81,12 @@ constexpr int kCUs = DPS_CUS;
 // stores: ordinary ones slowed the standalone kernel from 76.75 to 84.32 us
 // per 25M bf16 bucket (K = 8). Larger shard sets cannot stay cached until they
 // are read, so they stay nontemporal too.
-#ifndef DPS_RS_CACHE_OUT_BYTES
-#define DPS_RS_CACHE_OUT_BYTES (128ll << 20)
-#endif
-constexpr long long kCacheOutBytes = DPS_RS_CACHE_OUT_BYTES;
+constexpr long long kCacheOutBytes = 128ll << 20;
 
 // Tile bodies start on a kAlign-byte boundary of the dominant stream: the K
-// inputs for ReduceScatter (unless DPS_RS_ALIGN_OUT), the K outputs for
-// AllGather.
-#ifndef DPS_ALIGN
-#define DPS_ALIGN 128
-#endif
-#ifndef DPS_RS_ALIGN_OUT
-#define DPS_RS_ALIGN_OUT 0
-#endif
-constexpr int kAlign = DPS_ALIGN;
+// inputs for ReduceScatter, the K outputs for AllGather (anchoring the
+// ReduceScatter on its output measured slower).
+constexpr int kAlign = 128;
 constexpr int kFastBit = 256;
 constexpr int kOutAlignBit = 512;   // AllGather: the K outputs share one 16-byte phase
 static_assert(kAlign >= 16 && kAlign <= 256 && (kAlign & (kAlign - 1)) == 0, "alignment");
@@ -130,11 +104,7 @@ __device__ __forceinline__ void store_rs(char *p, u32x4 v, bool cached)
 
 __device__ __forceinline__ void store_ag(char *p, u32x4 v)
 {
-#if DPS_AG_NT_STORE
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-#else
-    *reinterpret_cast<u32x4 *>(p) = v;
-#endif
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned h) { return __uint_as_float(h << 16); }
@@ -583,14 +553,11 @@ static_assert(kAgBlock == kBlock, "the fused kernel runs both tile kinds with on
 // workgroup ids the first 8 (one per XCD, ids go round-robin over the 8 XCDs)
 // take ReduceScatter tiles and the next 8 AllGather tiles; the tiles left over
 // when one kind runs out go to the other.
-#ifndef DPS_RSAG_GROUP
-#define DPS_RSAG_GROUP 8
-#endif
 template <int DT, int EP, int KT>
 __global__ __launch_bounds__(kBlock) void rsag_kernel(const RsParams rp, const AgParams ap)
 {
     constexpr int ES = Tr<DT>::ES;
-    constexpr long long G = DPS_RSAG_GROUP;
+    constexpr long long G = 8;
     const int K = KT ? KT : rp.k;
     const long long nr = rp.total_tiles, na = ap.total_tiles;
     const long long paired = ((nr < na ? nr : na) / G) * G;
@@ -706,8 +673,7 @@ int phase_meta(const char *const *ins, long long in_off_bytes, int k, const char
 
 long long grid_for(long long total_tiles, int max_blocks)
 {
-    long long cap = max_blocks > 0 ? max_blocks
-                    : kBlocksPerCU > 0 ? (long long)kBlocksPerCU * kCUs : 0x7fffffffLL;
+    const long long cap = max_blocks > 0 ? max_blocks : 0x7fffffffLL;
     return total_tiles < cap ? total_tiles : cap;
 }
 
@@ -717,7 +683,7 @@ long long plan_rs(RsParams &p, int dt, bool lean)
 {
     const int es = elem_size(dt);
     for (int c = 0; c < p.k; ++c)
-        p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c], !DPS_RS_ALIGN_OUT);
+        p.meta[c] = phase_meta(p.src, (long long)c * p.L * es, p.k, p.dst[c], true);
     p.sub = ceil_div(p.L, p.S);
     const long long te = (long long)kBlock * rs_vectors_per_thread(dt, lean, p.max_blocks > 0) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
