@@ -369,10 +369,13 @@ dp_status_t run_fsdp(int k, int64_t m_local, int64_t d, int64_t f, const float *
     fw8.N = f;
     fw8.Kd = d;
     fw8.b_rows = R;
+    // without dx, where the shapes allow: the step as one wave of workgroups,
+    // each wave running a forward and a backward chain side by side
+    const bool step2 = bwd && !want_dx && k <= 8 && dps::fsdp_step2_ok(k, m_local, d, f);
     // the one-launch step: without dx its forward part is the 32x32 direct block,
     // with dx the 64x64 k-stage tile (beside the dx tiles)
     if (bwd && k <= 8 && dps::fsdp_bwd_fusable(k, m_local, d, f) &&
-        (want_dx ? fwd_fused && dx_fused : dps::fsdp_fwd_direct_ok(fw8)) &&
+        (want_dx ? fwd_fused && dx_fused : step2 || dps::fsdp_fwd_direct_ok(fw8)) &&
         n_fwd + n_dx + (d / 32) * (f / 32) <= 0x7fffffffLL) {
         // the whole step in one launch: forward tiles (AllGather folded into
         // the dot) beside backward blocks (ReduceScatter folded into the dW
@@ -415,6 +418,10 @@ dp_status_t run_fsdp(int k, int64_t m_local, int64_t d, int64_t f, const float *
             p.dx.trans_b = 1;
             p.tiles_x_dx = (int)(d / 64);
             p.n_dx = (int)n_dx;
+        }
+        if (step2) {
+            p.n_fwd = (int)((k * m_local / 32) * (f / 64));
+            return hip_status(dps::launch_fsdp_step2(p, st));
         }
         return hip_status(dps::launch_fsdp_step(p, st));
     }

@@ -79,6 +79,12 @@ hipError_t launch_fsdp_step(const FsdpStepParams &p, hipStream_t stream);
 // fwd.M, fwd.N multiples of 32, fwd.Kd 256 or 512, shards
 // of a multiple of 32 rows
 bool fsdp_fwd_direct_ok(const FsdpFwd8 &p);
+// The step without dx as one wave of workgroups, each wave running a forward
+// chain and a backward chain (fsdp_step2_kernel): the backward blocks'
+// shapes, f a multiple of 64, d a multiple of 128 and at most 512. p.n_fwd =
+// (k*m/32)*(f/64), p.n_dx = 0.
+bool fsdp_step2_ok(int k, long long m, long long d, long long f);
+hipError_t launch_fsdp_step2(const FsdpStepParams &p, hipStream_t stream);
 
 // bf16 GEMM, row-major, fp32 accumulation: C[M,N] = A[M,Kd] * B[Kd,N] with
 // b_kn, else C = A[M,Kd] * B[N,Kd]^T. Any element-aligned pointers and shapes;

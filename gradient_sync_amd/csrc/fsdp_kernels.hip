@@ -238,6 +238,207 @@ __global__ __launch_bounds__(512) void fsdp_step_kernel(const FsdpStepParams p)
         fsdp_fwd_block(p.fwd, id - p.n_dx - n_bwd, smem);
 }
 
+// The FSDP step (without dx) in one wave of workgroups: G = max(n_fwd, n_bwd)
+// workgroups of 8 waves, where n_fwd = (K*m/32)*(f/64) forward tiles of 32x64
+// and n_bwd = (d/32)*(f/32) backward positions; with the fixture's shapes both
+// are 256, one workgroup per CU, all resident from the start (no second round
+// of workgroups). Every wave runs two independent MFMA chains side by side:
+//   forward: a 32x32 block (column half w & 1 of the tile) over a quarter
+//     (w >> 1) of the k range, A from the tile's x rows staged once in LDS
+//     (k-major, odd pitch), B straight from W's row shards into registers; the
+//     four quarter partials are added in quarter order through LDS. The waves
+//     also write the W rows they load to the gathered copy w_full (each chunk
+//     of 32 rows by one tile row of each rank, so each element once per rank);
+//   backward: rank w's 32x32 block of dW_w = x_w^T dy_w over the tokens in
+//     ascending pairs (the same chain as the stand-alone GEMM, so the same
+//     bits), written to dw_full[w] and to LDS; after one barrier the block's K
+//     rank blocks are folded in the ring order of its shard into dw_shard (the
+//     ReduceScatter's fold, same bits).
+// Operands move in chunks of 16 k pairs, the next chunk's loads issued before
+// the current chunk's MFMAs. Workgroup ids go round-robin over the 8 XCDs; the
+// tiles are permuted so that an XCD's workgroups take one rank's forward tiles
+// (its x rows and all of W in that XCD's L2) and adjacent backward positions.
+constexpr int S2_XP = FB + 1;     // LDS pitch of the x block (floats)
+
+__device__ __forceinline__ long long xcd_major(long long id, long long n, long long grid)
+{
+    return (grid == n && n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+}
+
+template <int K>
+__global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
+{
+    const FsdpFwd8 &fw = p.fwd;
+    const FsdpBwd8 &bw = p.bwd;
+    const long long m = bw.m, d = bw.d, f = bw.f, R = bw.R;
+    const long long grid = gridDim.x;
+    const long long n_bwd = (d / FB) * (f / FB);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long kh = lane >> 5, col = lane & 31;
+    __shared__ float Xs[512 * S2_XP];          // forward tile's x rows, k-major
+    __shared__ float Pf[8][16 * 64];            // forward partial blocks
+    __shared__ float T[K][FB * FB];             // backward rank blocks
+
+    // ---- forward tile
+    const bool has_f = blockIdx.x < p.n_fwd;
+    const long long tf = has_f ? xcd_major(blockIdx.x, p.n_fwd, grid) : 0;
+    const long long nbj2 = f / 64, rows_per_rank = m / FB;
+    const long long trow = tf / nbj2, jb = tf % nbj2;
+    const int rf = (int)(trow / rows_per_rank);
+    const long long it = trow % rows_per_rank;
+    const long long jf = jb * 64 + (w & 1) * FB;            // this wave's 32 columns
+    const long long pq = d / 8;                              // k pairs per quarter
+    const long long pf0 = (w >> 1) * pq;                     // first k pair of the quarter
+    // ---- backward position
+    const bool has_b = blockIdx.x < n_bwd && w < K;
+    const long long tb = blockIdx.x < n_bwd ? xcd_major(blockIdx.x, n_bwd, grid) : 0;
+    const long long i0 = (tb / (f / FB)) * FB, j0 = (tb % (f / FB)) * FB;
+
+    // x rows of the forward tile into LDS: thread t loads column t of the 32 rows
+    if (has_f && (long long)threadIdx.x < d) {
+        const float *xr = fw.a[rf] + it * FB * d + threadIdx.x;
+        float v[FB];
+#pragma unroll
+        for (int i = 0; i < FB; ++i) v[i] = xr[i * d];
+#pragma unroll
+        for (int i = 0; i < FB; ++i) Xs[threadIdx.x * S2_XP + i] = v[i];
+    }
+
+    const long long nfc = has_f ? pq / FQ : 0;               // forward chunks
+    const long long nbc = has_b ? m / (2 * FQ) : 0;          // backward chunks
+    const long long nc = nfc > nbc ? nfc : nbc;
+    // Buffer descriptors on this wave's columns: a lane's offset is fixed
+    // (row kh, column col) and a load's row offset is a scalar. The backward
+    // operands of rank w: x_w[.][i0 + col] and dy_w[.][j0 + col]; byte offsets
+    // stay below 2^31 (checked by the launcher).
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(has_b ? bw.x[w] + i0 : bw.x[0]), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(has_b ? bw.dy[w] + j0 : bw.dy[0]), (short)0, 0x7fffffff, 0x00020000);
+    const int vox = (int)((kh * d + col) * 4), voy = (int)((kh * f + col) * 4);
+    const int vow = (int)((kh * f + jf + col) * 4);
+    // staging: two sets (chunk parity) of FQ forward B values and FQ pairs of
+    // backward operands per lane
+    float fb0[FQ], ba0[FQ], bb0[FQ], fb1[FQ], ba1[FQ], bb1[FQ];
+    auto load = [&](long long c, float (&fb)[FQ], float (&ba)[FQ], float (&bb)[FQ])
+        __attribute__((always_inline)) {
+        if (c < nfc) {
+            // W rows 2*(pf0 + c*FQ) .. + 31 lie in one shard
+            const long long k0 = 2 * (pf0 + c * FQ);
+            const long long sh = k0 / R;
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(fw.b_shard[sh] + (k0 - sh * R) * f), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int q = 0; q < FQ; ++q)
+                fb[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rw, vow, (int)(2 * q * f * 4), 0));
+        }
+        if (c < nbc) {
+#pragma unroll
+            for (int q = 0; q < FQ; ++q) {
+                const int k = (int)((c * FQ + q) * 2);
+                ba[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rx, vox, (int)(k * d * 4), 0));
+                bb[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rdy, voy, (int)(k * f * 4), 0));
+            }
+        }
+    };
+    load(0, fb0, ba0, bb0);
+    __syncthreads();                                         // the x block is in LDS
+
+    f32tile::f32x16 accf = {}, accb = {};
+    // chunk cc from one staging set: the two chains' MFMAs alternate (each
+    // depends only on the one two back), then the W rows go to the gathered
+    // copy where this tile row writes them
+    auto chunk = [&](long long cc, const float (&fb)[FQ], const float (&ba)[FQ],
+                     const float (&bb)[FQ]) __attribute__((always_inline)) {
+        const bool on_b = cc < nbc, on_f = cc < nfc;
+        const long long k0 = 2 * (pf0 + cc * FQ);
+        const float *xs = &Xs[(k0 + kh) * S2_XP + col];
+        if (on_b && on_f) {
+#pragma unroll
+            for (int q = 0; q < FQ; ++q) {
+                accb = __builtin_amdgcn_mfma_f32_32x32x2f32(ba[q], bb[q], accb, 0, 0, 0);
+                accf = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[2 * q * S2_XP], fb[q], accf, 0, 0, 0);
+            }
+        } else if (on_b) {
+#pragma unroll
+            for (int q = 0; q < FQ; ++q)
+                accb = __builtin_amdgcn_mfma_f32_32x32x2f32(ba[q], bb[q], accb, 0, 0, 0);
+        } else if (on_f) {
+#pragma unroll
+            for (int q = 0; q < FQ; ++q)
+                accf = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[2 * q * S2_XP], fb[q], accf, 0, 0, 0);
+        }
+        if (on_f && (k0 / FB) % rows_per_rank == it) {
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(fw.b_copy[rf] + k0 * f), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int q = 0; q < FQ; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, fb[q]), rc, vow,
+                                                      (int)(2 * q * f * 4), 0);
+        }
+    };
+    for (long long c = 0; c < nc; c += 2) {
+        load(c + 1, fb1, ba1, bb1);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk(c, fb0, ba0, bb0);
+        load(c + 2, fb0, ba0, bb0);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk(c + 1, fb1, ba1, bb1);
+    }
+    if (has_f) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) Pf[w][q * 64 + lane] = accf[q];
+    }
+    if (has_b) {
+        float *__restrict__ dwf = bw.dw_full[w];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = 8 * (q >> 2) + 4 * (int)kh + (q & 3);
+            dwf[(i0 + i) * f + j0 + col] = accb[q];
+            T[w][i * FB + col] = accb[q];
+        }
+    }
+    __syncthreads();
+    if (has_f) {
+        // y block (column half ch): the quarters' partials in quarter order
+        float *__restrict__ y = fw.c[rf];
+        for (int e = threadIdx.x; e < 2 * 16 * 64; e += 512) {
+            const int ch = e >> 10, q = (e >> 6) & 15, l = e & 63;
+            float s = Pf[ch][q * 64 + l];
+#pragma unroll
+            for (int h = 1; h < 4; ++h) s = s + Pf[2 * h + ch][q * 64 + l];
+            const int i = 8 * (q >> 2) + 4 * (l >> 5) + (q & 3), j = l & 31;
+            y[(it * FB + i) * f + jb * 64 + ch * FB + j] = s;
+        }
+    }
+    if (blockIdx.x < n_bwd) {
+        // shard c holds rows c*R ..; its fold visits ranks c+1, c+2, ..., c (mod K)
+        const int c = (int)(i0 / R);
+        float *__restrict__ out = bw.dw_shard[c] + (i0 - (long long)c * R) * f + j0;
+        for (int e = threadIdx.x; e < FB * FB; e += 512) {
+            int rr = c + 1 >= K ? c + 1 - K : c + 1;
+            float s = T[rr][e];
+#pragma unroll
+            for (int mm = 1; mm < K; ++mm) {
+                rr = rr + 1 >= K ? 0 : rr + 1;
+                s = s + T[rr][e];
+            }
+            out[(e / FB) * f + (e % FB)] = s;
+        }
+    }
+}
+
+template <int K>
+hipError_t go_step2(const FsdpStepParams &p, long long grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((fsdp_step2_kernel<K>), dim3((unsigned)grid), dim3(512), 0, st, p);
+    return hipGetLastError();
+}
+
 template <int K>
 hipError_t go(const FsdpBwdParams &p, hipStream_t st)
 {
@@ -259,6 +460,36 @@ hipError_t go_step(const FsdpStepParams &p, long long blocks, hipStream_t st)
 }  // namespace
 
 bool fsdp_fwd_direct_ok(const FsdpFwd8 &p) { return fwd_direct_ok(p); }
+
+bool fsdp_step2_ok(int k, long long m, long long d, long long f)
+{
+    // the backward blocks' shape conditions, forward tiles of 32x64 with a k
+    // quarter of whole 16-pair chunks, and the x rows of a tile in LDS (d <= 512)
+    return fsdp_bwd_fusable(k, m, d, f) && f % 64 == 0 && d % 128 == 0 && d <= 512 &&
+           (k * m / FB) * (f / 64) <= 0x7fffffffLL &&
+           m * d * 4 < 0x7fffffffLL && m * f * 4 < 0x7fffffffLL && d * f * 4 < 0x7fffffffLL;
+}
+
+hipError_t launch_fsdp_step2(const FsdpStepParams &p, hipStream_t st)
+{
+    const int k = p.bwd.k;
+    if (k < 1 || k > 8 || p.fwd.nb != k || p.n_dx != 0 ||
+        !fsdp_step2_ok(k, p.bwd.m, p.bwd.d, p.bwd.f) ||
+        p.n_fwd != (k * p.bwd.m / FB) * (p.bwd.f / 64))
+        return hipErrorInvalidValue;
+    const long long n_bwd = (p.bwd.d / FB) * (p.bwd.f / FB);
+    const long long grid = p.n_fwd > n_bwd ? p.n_fwd : n_bwd;
+    switch (k) {
+    case 1: return go_step2<1>(p, grid, st);
+    case 2: return go_step2<2>(p, grid, st);
+    case 3: return go_step2<3>(p, grid, st);
+    case 4: return go_step2<4>(p, grid, st);
+    case 5: return go_step2<5>(p, grid, st);
+    case 6: return go_step2<6>(p, grid, st);
+    case 7: return go_step2<7>(p, grid, st);
+    default: return go_step2<8>(p, grid, st);
+    }
+}
 
 bool fsdp_bwd_fusable(int k, long long m, long long d, long long f)
 {

@@ -148,15 +148,14 @@ def test_fsdp_integer_values_exact():
                                      (4, 4 * 64, 256, 64), (8, 8 * 64, 256, 128),
                                      (1, 64, 256, 64), (2, 64, 512, 96), (4, 128, 256, 32)])
 def test_fsdp_ragged_shapes(k, m, d, f):
-    """The first five shapes take the separate launches (AllGather, GEMM, GEMM,
-    ReduceScatter). The next three take the fused backward kernel (whole 32x32
-    blocks, shards of a multiple of 32 rows, m_local a multiple of 32) with
-    K = 4, 7 and 8; the next three also the fused forward (whole 64x64 tiles,
-    d a multiple of 64, shards of a multiple of 32 rows: the AllGather folded
-    into the GEMM's operand loads); (4, 256, 256, 64), (8, 512, 256, 128) and
-    the last three (K = 1, 2, 4; d of 256 or 512) run the whole step in one
-    launch (with dx only where m_local is a multiple of 64: the last two take
-    the separate launches then)."""
+    """The shapes span every path of the call: the first five take the
+    separate launches (AllGather, GEMM, GEMM, ReduceScatter); the others the
+    fused backward kernel (whole 32x32 blocks, shards of a multiple of 32 rows,
+    m_local a multiple of 32) with K = 4, 7 and 8, the fused forward (whole 64x64
+    tiles: the AllGather folded into the GEMM's operand loads), and the whole
+    step in one launch: with dx where m_local is a multiple of 64, without dx
+    as the one-wave step where f is a multiple of 64 and d of 128 (at most
+    512), else with 32x32 forward blocks."""
     say(f"fsdp ragged k={k} m={m} d={d} f={f}")
     g = torch.Generator().manual_seed(k * m + d)
     x = torch.randn(m, d, generator=g)
@@ -168,6 +167,26 @@ def test_fsdp_ragged_shapes(k, m, d, f):
     wi = torch.randint(-3, 4, (d, f), generator=g).float()
     dyi = torch.randint(-3, 4, (m, f), generator=g).float()
     check_fsdp(xi, wi, dyi, k, exact=True, with_dx=True)
+
+
+@pytest.mark.parametrize("k,m,d,f", [(1, 32, 128, 64), (2, 2 * 96, 384, 192), (4, 4 * 32, 512, 128),
+                                     (8, 8 * 64, 256, 320), (6, 6 * 32, 384, 64),
+                                     (8, 1024, 512, 512)])
+def test_fsdp_one_wave_step(k, m, d, f):
+    """The step without dx as one wave of workgroups (each wave a forward and a
+    backward chain): forward tile and backward position counts equal (with the
+    XCD-major tile order: (8, 512, 256, 320) and the fixture's shape) or not
+    (the other workgroups then run one part only)."""
+    say(f"fsdp one-wave step k={k} m={m} d={d} f={f}")
+    g = torch.Generator().manual_seed(k * m + d + f)
+    x = torch.randn(m, d, generator=g)
+    w = torch.randn(d, f, generator=g) * 0.02
+    dy = torch.randn(m, f, generator=g)
+    check_fsdp(x, w, dy, k)
+    xi = torch.randint(-3, 4, (m, d), generator=g).float()
+    wi = torch.randint(-3, 4, (d, f), generator=g).float()
+    dyi = torch.randint(-3, 4, (m, f), generator=g).float()
+    check_fsdp(xi, wi, dyi, k, exact=True)
 
 
 def test_fsdp_forward_only():
