@@ -155,11 +155,8 @@ dp_status_t run_rs(const void *const *send, char *const *out, int64_t n, int64_t
     return hip_status(dps::launch_rs(p, dt, ep, st, lean));
 }
 
-// shards_cached: the shards were just written by a ReduceScatter that left
-// them in the caches.
 dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_t L, int k, int dt,
-                   int skip_own, int s_chunks, hipStream_t st, int max_wg = 0,
-                   bool shards_cached = false)
+                   int skip_own, int s_chunks, hipStream_t st, int max_wg = 0)
 {
     dps::AgParams p;
     memset(&p, 0, sizeof(p));
@@ -173,7 +170,6 @@ dp_status_t run_ag(const void *const *shard, char *const *out, int64_t n, int64_
     p.k = k;
     p.S = s_chunks;
     p.max_blocks = max_wg;
-    p.stream_in = shards_cached ? 1 : 0;
     return hip_status(dps::launch_ag(p, dt, st));
 }
 
@@ -219,7 +215,7 @@ dp_status_t run_ar(const void *const *send, void *const *recv, size_t n, int k, 
                            max_wg, lean, true);
     if (s != DP_OK) return s;
     return run_ag((const void *const *)rs_out, (char *const *)recv, (int64_t)n, L, k, dt, 1,
-                  s_chunks, st, max_wg, true);
+                  s_chunks, st, max_wg);
 }
 
 // ReduceScatter argument checks (shared by the single and the fused call);
@@ -615,7 +611,7 @@ dp_status_t dp_reduce_scatter_all_gather(const void *const *rs_send, void *const
                       nullptr, 1, s_chunks, st, 0, false, true);
     if (rs_n == 0)
         return run_ag(ag_send, (char *const *)ag_recv, (int64_t)ag_n, (int64_t)La, k, dt,
-                      ag_in_place ? 1 : 0, s_chunks, st, 0, true);
+                      ag_in_place ? 1 : 0, s_chunks, st, 0);
     dps::RsParams rp;
     dps::AgParams ap;
     memset(&rp, 0, sizeof(rp));

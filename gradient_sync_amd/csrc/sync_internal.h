@@ -40,7 +40,8 @@ struct RsParams {
     int k, S;
     // set by the caller when an AllGather reads the shards next: then shard
     // sets small enough to stay in the caches are stored with ordinary
-    // (cached) stores (the planner clears it for larger sets)
+    // (cached) stores (the planner clears it for larger sets; capped-grid and
+    // lean launches store nontemporally)
     int cache_out;
 };
 
@@ -54,10 +55,6 @@ struct AgParams {
     long long n, L, sub, tiles_per_seg, total_tiles;
     int max_blocks;
     int k, S;
-    // set by the caller when a ReduceScatter left the shards in the caches:
-    // they are then loaded with the nontemporal hint (cleared by the planner
-    // for shard sets too large to have stayed cached)
-    int stream_in;
 };
 
 // Fill the phase table and tiling of the parameter blocks; returns the grid size.

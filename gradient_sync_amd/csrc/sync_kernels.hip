@@ -58,29 +58,28 @@ constexpr int kAgU = 1;
 // against 4.01 with one; on the default grid one is faster: 3.42 against 3.53).
 constexpr int kUCapped = 2;
 constexpr int kAgBlock = 256;   // threads per AllGather workgroup
-// AllGather shard sets that a ReduceScatter left in the caches (see
-// kCacheOutBytes) are loaded with the nontemporal hint, as each shard is read
-// once: K = 8 bf16 layer step, pipelined 78.59% -> 79.08% and 81.52% ->
-// 82.27% of HBM peak in two runs on two machines. Larger sets, read from
-// HBM, keep ordinary loads. The output stores stay nontemporal: with ordinary
-// stores the 400 MB a bucket's AllGather writes displace the next bucket's
-// shards from the Infinity Cache (pipelined 81.52% -> 74.70%).
+// AllGather shards are loaded with ordinary loads and the outputs stored with
+// the nontemporal hint: with ordinary output stores the 400 MB a bucket's
+// AllGather writes displace the next bucket's shards from the Infinity Cache
+// (pipelined layer step 81.52% -> 74.70% of HBM peak).
 // Default grid: one workgroup per tile (a wave that finishes its tile exits
 // instead of waiting for its stores before loading the next tile); measured
 // faster than persistent grids of 1, 2 or 4 workgroups per CU. A caller's
 // dp_launch_opts_t.max_workgroups caps it instead.
 
-// Where an AllGather reads the shards next (the fused ReduceScatter + AllGather
-// launch of the bucket pipeline, whose AllGather half reads the previous
-// launch's shards, and the two-phase AllReduce), shard sets whose K shards
-// together fit in kCacheOutBytes are stored with ordinary stores, which leave
-// them in the caches (the 256 MB Infinity Cache holds a 25,000,000-value bf16
-// bucket's 50 MB of shards) where nontemporal stores do not. Measured on
-// MI355X, K = 8 bf16 layer step: pipelined 75.98% -> 78.59% of HBM peak (same
-// bits). A ReduceScatter whose shards are not read next keeps nontemporal
-// stores: ordinary ones slowed the standalone kernel from 76.75 to 84.32 us
-// per 25M bf16 bucket (K = 8). Larger shard sets cannot stay cached until they
-// are read, so they stay nontemporal too.
+// Where an AllGather reads the shards next, the ReduceScatter stores them with
+// ordinary stores, which leave them in the caches (the 256 MB Infinity Cache
+// holds a 25,000,000-value bf16 bucket's 50 MB of shards) where nontemporal
+// stores do not: always in the fused ReduceScatter + AllGather launch of the
+// bucket pipeline (its AllGather half reads the previous launch's shards), and
+// in a ReduceScatter launched with cache_out (the two-phase AllReduce, the
+// pipeline call's single phases) when the K shards together fit in
+// kCacheOutBytes. Measured on MI355X, K = 8 bf16 layer step: pipelined 75.98%
+// -> 78.59% of HBM peak (same bits). Every other ReduceScatter stores
+// nontemporally: ordinary stores slowed the standalone kernel from 76.75 to
+// 84.32 us per 25M bf16 bucket (K = 8). The store kind is a template
+// parameter: chosen at run time inside the kernel, the two stores were merged
+// into one ordinary store by the compiler.
 constexpr long long kCacheOutBytes = 128ll << 20;
 
 // Tile bodies start on a kAlign-byte boundary of the dominant stream: the K
@@ -96,9 +95,10 @@ __device__ __forceinline__ u32x4 load_stream(const char *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
-__device__ __forceinline__ void store_rs(char *p, u32x4 v, bool cached)
+template <bool CACHED>
+__device__ __forceinline__ void store_rs(char *p, u32x4 v)
 {
-    if (cached) *reinterpret_cast<u32x4 *>(p) = v;
+    if constexpr (CACHED) *reinterpret_cast<u32x4 *>(p) = v;
     else __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
@@ -237,7 +237,7 @@ __device__ __forceinline__ void rs_scalar_range(const RsParams &p, int K, int c,
 // the stores are not separated by waits on earlier memory operations. With AR
 // the packed result goes to offset `off` of all K outputs (ranks c+1, c+2, ...,
 // c, no per-rank branch) instead of to `dst`.
-template <int DT, int EP, int KT, int U, bool FULL, bool AR>
+template <int DT, int EP, int KT, int U, bool FULL, bool AR, bool CACHED>
 __device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const int c,
                                            const long long off, char *dst, const long long nv)
 {
@@ -305,12 +305,12 @@ __device__ __forceinline__ void rs_vectors(const RsParams &p, const int K, const
                 if (FULL || q < nv) store_ag(p.dst[fold_rank(c, i, K)] + off + q * 16, o);
             }
         } else {
-            if (FULL || q < nv) store_rs(dst + q * 16, pack<DT>(acc[u]), p.cache_out != 0);
+            if (FULL || q < nv) store_rs<CACHED>(dst + q * 16, pack<DT>(acc[u]));
         }
     }
 }
 
-template <int DT, int EP, int KT, int U, bool AR>
+template <int DT, int EP, int KT, int U, bool AR, bool CACHED>
 __device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const long long bid)
 {
     using A = typename Tr<DT>::Acc;
@@ -344,18 +344,18 @@ __device__ __forceinline__ void rs_tile(const RsParams &p, const int K, const lo
     char *dst = AR ? nullptr : p.dst[c] + e0 * ES;
     const long long off = (base + e0) * ES;
     if (nv == (long long)kBlock * U)
-        rs_vectors<DT, EP, KT, U, true, AR>(p, K, c, off, dst, nv);
+        rs_vectors<DT, EP, KT, U, true, AR, CACHED>(p, K, c, off, dst, nv);
     else if (nv > 0)
-        rs_vectors<DT, EP, KT, U, false, AR>(p, K, c, off, dst, nv);
+        rs_vectors<DT, EP, KT, U, false, AR, CACHED>(p, K, c, off, dst, nv);
     rs_scalar_range<DT, EP, KT, AR>(p, K, c, base, nc, e0 + nv * V, e1);
 }
 
-template <int DT, int EP, int KT, int U, bool AR>
+template <int DT, int EP, int KT, int U, bool AR, bool CACHED>
 __global__ __launch_bounds__(kBlock) void rs_kernel(const RsParams p)
 {
     const int K = KT ? KT : p.k;
     for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
-        rs_tile<DT, EP, KT, U, AR>(p, K, bid);
+        rs_tile<DT, EP, KT, U, AR, CACHED>(p, K, bid);
 }
 
 // Lean variant: one vector per lane per rank and at most 64 VGPRs (8 waves per
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kBlock, 8) void rs_kernel_lean(const RsParams p)
 {
     const int K = KT ? KT : p.k;
     for (long long bid = blockIdx.x; bid < p.total_tiles; bid += gridDim.x)
-        rs_tile<DT, EP, KT, 1, AR>(p, K, bid);
+        rs_tile<DT, EP, KT, 1, AR, false>(p, K, bid);
 }
 
 // ------------------------------------------------------------------ AllGather
@@ -404,8 +404,7 @@ __device__ __forceinline__ void ag_vectors(const AgParams &p, const int K, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const long long q = FULL ? (long long)tid + u * kAgBlock : min((long long)tid + u * kAgBlock, nv - 1);
-        if (p.stream_in) v[u] = load_stream(src + q * 16);
-        else v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
+        v[u] = *reinterpret_cast<const u32x4 *>(src + q * 16);
     }
     const int nr = SKIP_OWN ? K - 1 : K;
 #pragma unroll
@@ -565,11 +564,11 @@ __global__ __launch_bounds__(kBlock) void rsag_kernel(const RsParams rp, const A
     if (bid < 2 * paired) {
         const long long idx = (bid / (2 * G)) * G + bid % G;
         if ((bid / G) & 1) ag_tile<ES, KT, kAgU>(ap, K, idx);
-        else rs_tile<DT, EP, KT, RsU<DT>::U, false>(rp, K, idx);
+        else rs_tile<DT, EP, KT, RsU<DT>::U, false, true>(rp, K, idx);
         return;
     }
     const long long rem = bid - 2 * paired;
-    if (rem < nr - paired) rs_tile<DT, EP, KT, RsU<DT>::U, false>(rp, K, paired + rem);
+    if (rem < nr - paired) rs_tile<DT, EP, KT, RsU<DT>::U, false, true>(rp, K, paired + rem);
     else ag_tile<ES, KT, kAgU>(ap, K, paired + rem - (nr - paired));
 }
 
@@ -581,9 +580,11 @@ hipError_t rs_go(const RsParams &p, long long grid, bool lean, hipStream_t st)
     if (lean)
         hipLaunchKernelGGL((rs_kernel_lean<DT, EP, KT, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     else if (p.max_blocks > 0)
-        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, kUCapped, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, kUCapped, AR, false>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+    else if (!AR && p.cache_out)
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U, false, true>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     else
-        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, AR ? kArU : RsU<DT>::U, AR>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, AR ? kArU : RsU<DT>::U, AR, false>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 
@@ -711,7 +712,6 @@ long long plan_ag(AgParams &p, int dt)
     const long long te = (long long)kAgBlock * (p.max_blocks > 0 ? kUCapped : kAgU) * (16 / es);
     p.tiles_per_seg = p.sub > 0 ? ceil_div(p.sub, te) : 1;
     p.total_tiles = (long long)p.S * p.k * p.tiles_per_seg;
-    p.stream_in = p.stream_in && (long long)p.k * p.L * es <= kCacheOutBytes;
     return grid_for(p.total_tiles, p.max_blocks);
 }
 
@@ -769,10 +769,6 @@ hipError_t launch_rsag(const RsParams &rp0, const AgParams &ap0, int dt, int ep,
     AgParams ap = ap0;
     rp.max_blocks = 0;
     ap.max_blocks = 0;
-    // the AllGather half reads the shards the previous launch's ReduceScatter
-    // half left in the caches, and this launch's shards are read by the next
-    rp.cache_out = 1;
-    ap.stream_in = 1;
     plan_rs(rp, dt);
     plan_ag(ap, dt);
     const long long grid = rp.total_tiles + ap.total_tiles;

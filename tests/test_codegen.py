@@ -93,3 +93,35 @@ def test_no_packed_fp32_and_no_scalar_stores(kernels):
     for name, (_, body) in kernels.items():
         m = banned.search(body)
         assert m is None, (name, m.group(0) if m else None)
+
+
+def _stores(body):
+    return re.findall(r"^\s*global_store_dwordx4 [^\n]*", body, re.M)
+
+
+def _loads(body):
+    return re.findall(r"^\s*global_load_dwordx4 [^\n]*", body, re.M)
+
+
+def test_cache_hints_reach_the_code(kernels):
+    """The nontemporal hints the sync kernels choose are in the compiled code:
+    a standalone ReduceScatter streams its inputs and stores its shards
+    nontemporally, the variant for shards an AllGather reads next stores them
+    with ordinary stores, the AllGather stores its outputs nontemporally. (A
+    store kind chosen by a run-time flag inside the kernel was once merged by
+    the compiler into one ordinary store; the kinds are template parameters.)"""
+    nt = re.compile(r"\bnt\b")
+    # bf16, avg by x1/8, K = 8, one vector per lane, not AllReduce
+    for name, (_, body) in pick(kernels, "rs_kernelILi1ELi1ELi8ELi1ELb0ELb0E").items():
+        assert _stores(body) and all(nt.search(s) for s in _stores(body)), name
+        assert _loads(body) and all(nt.search(s) for s in _loads(body)), name
+    for name, (_, body) in pick(kernels, "rs_kernelILi1ELi1ELi8ELi1ELb0ELb1E").items():
+        assert _stores(body) and not any(nt.search(s) for s in _stores(body)), name
+        assert _loads(body) and all(nt.search(s) for s in _loads(body)), name
+    for name, (_, body) in pick(kernels, "ag_kernelILi2ELi8ELi1E").items():
+        assert _stores(body) and all(nt.search(s) for s in _stores(body)), name
+    # the fused launch: ordinary shard stores (ReduceScatter half) beside
+    # nontemporal output stores (AllGather half)
+    for name, (_, body) in pick(kernels, "rsag_kernelILi1ELi1ELi8E").items():
+        st = _stores(body)
+        assert any(nt.search(s) for s in st) and not all(nt.search(s) for s in st), name
