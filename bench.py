@@ -50,11 +50,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # were taken on (sha256 of sync_kernels.hip + sync_internal.h; the gfx950 code of
 # these sources is the same as that of the tree the counters were taken on).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "ee2c112dd5dba12d58a9d63dba859e2b6c01a3e7bd43c0fb5af5a562eee40b0d"
-                      "a4d8bd48c142ae6134854361dbdbf9eadcada43974efa00bf403909f6b226495",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195384.1 + 49019.4) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25138.9 + 390957.6) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220533.0 + 439711.3) * 1024,
+    "sources_sha256": "068cee16680959fdf53ff7e56614a75e0eb3f6fbab476d7523ba953d679ec891"
+                      "f16581e6b16ca798c1f240711e1e80c1a3d4fdf4628ca177e96c534422299b95",
+    "rs_kernel<bf16, avg, K=8>": (2 * 195384.3 + 49408.9) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25142.6 + 390841.3) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220517.3 + 439715.3) * 1024,
 }
 
 
@@ -219,9 +219,10 @@ def bench_layer(args):
                        "pct_of_peak": round(100 * value_plain / HBM_PEAK_GBS, 2),
                        "ms_per_step": round(1e3 * wall_plain / args.steps, 4),
                        "schedule": "ReduceScatter then AllGather, one launch each, bucket by "
-                                   "bucket, shards stored and loaded with nontemporal hints: "
-                                   "no cache reuse between the phases, every byte from or to "
-                                   "HBM (the figure the 70%-of-HBM-peak target is judged on)"},
+                                   "bucket (dp_reduce_scatter, dp_all_gather): shards stored "
+                                   "with the nontemporal hint and read back from HBM, no cache "
+                                   "reuse between the phases, every byte from or to HBM (the "
+                                   "figure the 70%-of-HBM-peak target is judged on)"},
         "pipelined_excluding_shard_bytes": {
             "value": round((step_bytes - shard_bytes) * args.steps / wall / 1e9, 2),
             "pct_of_peak": round(100 * (step_bytes - shard_bytes) * args.steps / wall / 1e9

@@ -129,7 +129,13 @@ dp_status_t dp_all_gather(const void *const *send, void *const *recv, size_t n, 
  *   s_chunks), bit for bit; each operation follows that call's buffer and
  *   in-place rules, and no buffer of one operation may overlap a buffer of
  *   the other (DP_ERR_ALIAS). rs_n or ag_n may be 0 (then only the other
- *   operation runs).
+ *   operation runs; the arrays of the empty one must be non-NULL but are not
+ *   read).
+ *   Cache use: the ReduceScatter stores its shards with ordinary stores, so
+ *   that they can stay in the caches for the AllGather that reads them next
+ *   (this call's AllGather half in the next pipeline step); in the
+ *   ReduceScatter-only form only when the K shards fit in 128 MiB, else with
+ *   the nontemporal hint, as dp_reduce_scatter always stores them.
  */
 dp_status_t dp_reduce_scatter_all_gather(const void *const *rs_send, void *const *rs_recv,
                                          size_t rs_n, const void *const *ag_send,
