@@ -960,9 +960,10 @@ def bench_overlap(args):
 def bench_gemm(args):
     """The bf16 GEMM of the concurrency measurement alone (C = A B, 8192^3,
     B stored [k, n]): the default (4-wave) kernel, the same with B stored [n, k]
-    (C = A B^T), and the two 8-wave variants that leave room for a sync
-    workgroup on each CU, against the MFMA roofline; the vendor library GEMM
-    (torch.matmul, hipBLASLt) on the same operands for context. The variants
+    (C = A B^T, the direct-to-LDS kernel), and the two 8-wave variants that
+    leave room for a sync workgroup on each CU, against the MFMA roofline; the
+    vendor library GEMM (torch.matmul, hipBLASLt) on the same operands in both
+    layouts for context. The variants
     are timed in interleaved rounds of 8 back-to-back calls after ~1 s of
     warm-up, so that they see the same clock and power state."""
     import torch
@@ -978,7 +979,8 @@ def bench_gemm(args):
            "dp_gemm_bf16_b_nk": lambda: dps.dp_gemm_bf16_ex(a, b_nk, c, b_layout="nk"),
            "dp_gemm_bf16_lean": lambda: dps.dp_gemm_bf16_ex(a, b, c, lean=True),
            "dp_gemm_bf16_share_cu": lambda: dps.dp_gemm_bf16_ex(a, b, c, share_cu=True),
-           "library_torch_matmul": lambda: torch.matmul(a, b, out=c)}
+           "library_torch_matmul": lambda: torch.matmul(a, b, out=c),
+           "library_torch_matmul_b_nk": lambda: torch.matmul(a, b_nk.t(), out=c)}
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 1.0:
         for fn in fns.values():
@@ -1002,6 +1004,12 @@ def bench_gemm(args):
                          "achieved": res["dp_gemm_bf16"]["tflops"],
                          "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": res["dp_gemm_bf16"]["frac_of_peak"], "traffic": None},
+            "roofline_b_nk": {"bound": "mfma",
+                              "kernel": "gemm_bf16_w4d_kernel (B stored [n, k], operands loaded "
+                                        "straight into LDS, 16x16x32 MFMAs)",
+                              "achieved": res["dp_gemm_bf16_b_nk"]["tflops"],
+                              "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": res["dp_gemm_bf16_b_nk"]["frac_of_peak"], "traffic": None},
             "config": {"workload": "A [8192, 8192], B [8192, 8192] bf16 ~ N(0,1), row-major"}}
     if not args.no_cpu_baseline:
         import numpy as np

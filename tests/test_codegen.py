@@ -77,7 +77,8 @@ def test_register_budgets(kernels):
         assert field(desc, "amdhsa_next_free_vgpr") <= 224, name
     # the 4-wave GEMM: 256 accumulators in the accumulation registers, the
     # rest within the 256 architectural VGPRs (one wave per SIMD)
-    for name, (desc, _) in pick(kernels, "gemm_bf16_w4_kernel").items():
+    for name, (desc, _) in list(pick(kernels, "gemm_bf16_w4_kernel").items()) + \
+            list(pick(kernels, "gemm_bf16_w4d_kernel").items()):
         assert field(desc, "amdhsa_accum_offset") == 256, name
         assert field(desc, "amdhsa_next_free_vgpr") <= 512, name
     # the CU-sharing GEMM leaves room for one default sync wave (<= 96)

@@ -255,7 +255,8 @@ def test_gemm_bf16_small(m, n, kk, layout):
 
 
 def test_gemm_bf16_8192_sampled():
-    """C = A B with A, B bf16 [8192,8192] ~ N(0,1): sampled entries."""
+    """C = A B with A, B bf16 [8192,8192] ~ N(0,1): sampled entries; then B
+    stored [n,k] (the direct-to-LDS kernel) gives the same bits."""
     m = n = kk = 8192
     say("gemm bf16 8192^3")
     a, b = gen.gemm_bf16_inputs(5, m, n, kk, device=DEV)
@@ -266,6 +267,10 @@ def test_gemm_bf16_8192_sampled():
     dps.dp_gemm_bf16(a, b, c)
     torch.cuda.synchronize()
     check_gemm(a, b, "kn", rows.astype(np.int64), cols.astype(np.int64), c=c)
+    b_nk = b.t().contiguous()
+    del b
+    c_nk = run_gemm(a, b_nk, "nk")
+    assert torch.equal(c.view(torch.int16), c_nk.view(torch.int16))
 
 
 @pytest.mark.parametrize("m,n,kk", [(256, 256, 2048), (512, 768, 2112), (1024, 256, 4096),
@@ -273,8 +278,9 @@ def test_gemm_bf16_8192_sampled():
                                     (768, 512, 320), (2048, 2048, 64), (256, 256, 960),
                                     (264, 280, 1032)])
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
-    """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run the 4-wave
-    kernel; the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
+    """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run a 4-wave
+    kernel (with B stored [n,kk] and an even number of depth-64 stages the
+    direct-to-LDS one, 16x16x32 MFMAs); the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
     B stored [kk,n] (transposing LDS reads) and [n,kk] alike, so all six agree
     bit for bit (shorter k ranges and edge tiles take the 8-wave kernel on
