@@ -295,15 +295,11 @@ __global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
     const long long tb = blockIdx.x < n_bwd ? xcd_major(blockIdx.x, n_bwd, grid) : 0;
     const long long i0 = (tb / (f / FB)) * FB, j0 = (tb % (f / FB)) * FB;
 
-    // x rows of the forward tile into LDS: thread t loads column t of the 32 rows
-    if (has_f && (long long)threadIdx.x < d) {
-        const float *xr = fw.a[rf] + it * FB * d + threadIdx.x;
-        float v[FB];
-#pragma unroll
-        for (int i = 0; i < FB; ++i) v[i] = xr[i * d];
-#pragma unroll
-        for (int i = 0; i < FB; ++i) Xs[threadIdx.x * S2_XP + i] = v[i];
-    }
+    // x rows of the forward tile: thread t loads column t of the 32 rows; they
+    // go into LDS after the backward chain's first chunk, which does not need
+    // them, so the loads' latency is spent on MFMAs
+    const bool xcol = has_f && (long long)threadIdx.x < d;
+    float xv[FB];
 
     const long long nfc = has_f ? pq / FQ : 0;               // forward chunks
     const long long nbc = has_b ? m / (2 * FQ) : 0;          // backward chunks
@@ -321,9 +317,9 @@ __global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
     // staging: two sets (chunk parity) of FQ forward B values and FQ pairs of
     // backward operands per lane
     float fb0[FQ], ba0[FQ], bb0[FQ], fb1[FQ], ba1[FQ], bb1[FQ];
-    auto load = [&](long long c, float (&fb)[FQ], float (&ba)[FQ], float (&bb)[FQ])
+    auto load = [&](long long c, float (&fb)[FQ], float (&ba)[FQ], float (&bb)[FQ], int parts = 3)
         __attribute__((always_inline)) {
-        if (c < nfc) {
+        if ((parts & 1) && c < nfc) {
             // W rows 2*(pf0 + c*FQ) .. + 31 lie in one shard
             const long long k0 = 2 * (pf0 + c * FQ);
             const long long sh = k0 / R;
@@ -334,7 +330,7 @@ __global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
                 fb[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                       rw, vow, (int)(2 * q * f * 4), 0));
         }
-        if (c < nbc) {
+        if ((parts & 2) && c < nbc) {
 #pragma unroll
             for (int q = 0; q < FQ; ++q) {
                 const int k = (int)((c * FQ + q) * 2);
@@ -345,16 +341,39 @@ __global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
             }
         }
     };
-    load(0, fb0, ba0, bb0);
-    __syncthreads();                                         // the x block is in LDS
+    // loads in the order their results are needed (vmcnt counts in order):
+    // the backward operands of chunk 0, the x columns, the forward operands
+    load(0, fb0, ba0, bb0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (xcol) {
+        const float *xr = fw.a[rf] + it * FB * d + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < FB; ++i) xv[i] = xr[i * d];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, fb0, ba0, bb0, 1);
 
     f32tile::f32x16 accf = {}, accb = {};
+    if (nbc > 0) {
+#pragma unroll
+        for (int q = 0; q < FQ; ++q)
+            accb = __builtin_amdgcn_mfma_f32_32x32x2f32(ba0[q], bb0[q], accb, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (xcol) {
+#pragma unroll
+        for (int i = 0; i < FB; ++i) Xs[threadIdx.x * S2_XP + i] = xv[i];
+    }
+    __syncthreads();                                         // the x block is in LDS
+    load(1, fb1, ba1, bb1);
+
     // chunk cc from one staging set: the two chains' MFMAs alternate (each
     // depends only on the one two back), then the W rows go to the gathered
-    // copy where this tile row writes them
+    // copy where this tile row writes them; bwd = false: the backward part of
+    // the chunk is already done
     auto chunk = [&](long long cc, const float (&fb)[FQ], const float (&ba)[FQ],
-                     const float (&bb)[FQ]) __attribute__((always_inline)) {
-        const bool on_b = cc < nbc, on_f = cc < nfc;
+                     const float (&bb)[FQ], bool bwd = true) __attribute__((always_inline)) {
+        const bool on_b = bwd && cc < nbc, on_f = cc < nfc;
         const long long k0 = 2 * (pf0 + cc * FQ);
         const float *xs = &Xs[(k0 + kh) * S2_XP + col];
         if (on_b && on_f) {
@@ -381,7 +400,12 @@ __global__ __launch_bounds__(512) void fsdp_step2_kernel(const FsdpStepParams p)
                                                       (int)(2 * q * f * 4), 0);
         }
     };
-    for (long long c = 0; c < nc; c += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(0, fb0, ba0, bb0, false);
+    load(2, fb0, ba0, bb0);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(1, fb1, ba1, bb1);
+    for (long long c = 2; c < nc; c += 2) {
         load(c + 1, fb1, ba1, bb1);
         __builtin_amdgcn_sched_barrier(0);
         chunk(c, fb0, ba0, bb0);
