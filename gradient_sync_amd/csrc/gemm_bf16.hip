@@ -449,11 +449,12 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
 // Stage t computes from buffer t & 1 in two k steps of 32: step 0 while the
 // fragments of step 1 are read (one read per 4 MFMAs); then each wave waits
 // for its own loads of stage t + 1 and the workgroup meets at the barrier;
-// then step 1 while the step-0 fragments of stage t + 1 are read and the 16
-// loads of stage t + 2 go into buffer t & 1 (all its reads finished before
-// the barrier), one read and one load per 4 MFMAs. Spreading the loads over
-// the step keeps the address unit's queues from filling (all 16 in a quarter
-// of the step: 3% slower). The k steps add the same products in the same
+// then step 1 while the step-0 fragments of stage t + 1 are read (one per 4
+// MFMAs) and the 16 loads of stage t + 2 go into buffer t & 1 (all its reads
+// finished before the barrier), one per 3 MFMAs over the first 46 of the
+// step's 64: early enough to land before the next barrier, spread enough to
+// keep the address unit's queues from filling (one per 4 MFMAs: 2.4% slower;
+// one per 2 or 1: 21% slower). The k steps add the same products in the same
 // order as the 32x32x16 kernels, and the results are the same bits.
 // Measured at 8192^3: 724 us (1518 TFLOP/s) against 804 us for the
 // register-staged kernel and 673 us for the vendor library on the same GPU.
@@ -543,10 +544,8 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
         W4_FENCE();
 #pragma unroll
         for (int i = 0; i < 64; ++i) {
-            if ((i & 3) == 0) {
-                rdq(0, buf ^ 1, 0, i >> 2);
-                dtl(buf, k2, i >> 2);
-            }
+            if ((i & 3) == 0) rdq(0, buf ^ 1, 0, i >> 2);
+            if (i % 3 == 0 && i / 3 < 16) dtl(buf, k2, i / 3);
             mf(1, i >> 3, i & 7);
             W4_FENCE();
         }
