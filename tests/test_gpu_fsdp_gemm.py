@@ -333,6 +333,28 @@ def _offset_copy(t, off):
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("off", [1, 3, 8])
+def test_gemm_bf16_output_at_any_element_offset(layout, off):
+    """The 4-wave kernels (B [n,k] with an even number of k stages: the
+    direct-to-LDS one) with aligned operands and C at an element offset that
+    is not 16-byte aligned: the same bits as an aligned C, and the elements
+    around C untouched."""
+    m = n = 512
+    kk = 1024
+    say(f"gemm bf16 output offset {layout} off={off}")
+    a, b = gen.gemm_bf16_inputs(13, m, n, kk, device=DEV, b_layout=layout)
+    want = run_gemm(a, b, layout)
+    c_full = torch.empty((m * n + off + 8,), dtype=torch.bfloat16, device=DEV)
+    c_full.view(torch.int16).fill_(0x5A5A)
+    c = c_full[off:off + m * n].view(m, n)
+    dps.dp_gemm_bf16_ex(a, b, c, b_layout=layout)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(c), _bits(want))
+    guard = np.concatenate([to_np(c_full[:off]), to_np(c_full[off + m * n:])])
+    assert np.all(guard == 0x5A5A)
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("m,n,kk,off", [(64, 64, 13, 0), (97, 45, 1003, 0), (256, 256, 1024, 1),
                                         (33, 300, 77, 3), (1, 5, 1, 1), (130, 7, 200, 0)])
 def test_gemm_bf16_any_shape_and_alignment(m, n, kk, off, layout):
