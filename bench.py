@@ -485,7 +485,7 @@ def bench_fsdp(args):
             "with_dx": dict(res["step_with_dx"], what="the same plus the input gradient "
                                                        "dx = dy W^T (dp_fsdp_layer_ex)"),
             "mfma_peak_tflops": MFMA_F32_TFLOPS,
-            "roofline": {"bound": "mfma", "kernel": "fsdp_step2_kernel (the one-launch step: one workgroup per CU, forward and backward chains side by side)",
+            "roofline": {"bound": "mfma", "kernel": "fsdp_step_k8_kernel (the one-launch step with every size fixed at compile time: one workgroup per CU, each wave a backward then a forward MFMA chain)",
                          "achieved": res["step"]["effective_tflops"], "peak": MFMA_F32_TFLOPS,
                          "unit": "TFLOP/s",
                          "frac": round(res["step"]["effective_tflops"] / MFMA_F32_TFLOPS, 4),

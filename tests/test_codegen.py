@@ -81,6 +81,10 @@ def test_register_budgets(kernels):
             list(pick(kernels, "gemm_bf16_w4d_kernel").items()):
         assert field(desc, "amdhsa_accum_offset") == 256, name
         assert field(desc, "amdhsa_next_free_vgpr") <= 512, name
+    # the FSDP step kernels: 8 waves per workgroup, two per SIMD (<= 256 each)
+    for name, (desc, _) in list(pick(kernels, "fsdp_step_k8_kernel").items()) + \
+            list(pick(kernels, "fsdp_step2_kernel").items()):
+        assert field(desc, "amdhsa_next_free_vgpr") <= 256, name
     # the CU-sharing GEMM leaves room for one default sync wave (<= 96)
     sync = max(field(d, "amdhsa_next_free_vgpr")
                for d, _ in pick(kernels, "rs_kernelILi1ELi1ELi8ELi1").values())
@@ -126,3 +130,9 @@ def test_cache_hints_reach_the_code(kernels):
     for name, (_, body) in pick(kernels, "rsag_kernelILi1ELi1ELi8E").items():
         st = _stores(body)
         assert any(nt.search(s) for s in st) and not all(nt.search(s) for s in st), name
+    # the FSDP step of the compile-time sizes: every output store is a
+    # nontemporal 16-byte store (y, the W copies, dw_full, dw_shard)
+    for name, (_, body) in pick(kernels, "fsdp_step_k8_kernel").items():
+        st = _stores(body)
+        assert len(st) >= 4 and all(nt.search(x) for x in st), name
+        assert not re.search(r"^\s*(global|buffer)_store_dword\b", body, re.M), name

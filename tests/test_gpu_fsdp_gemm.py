@@ -189,6 +189,39 @@ def test_fsdp_one_wave_step(k, m, d, f):
     check_fsdp(xi, wi, dyi, k, exact=True)
 
 
+def _fsdp_outputs_at(off, k, ml, d, f, R):
+    """Output tensors whose first element is off floats past a 256-byte boundary."""
+    def mk(*shape):
+        n = int(np.prod(shape))
+        return torch.full((n + off,), float("nan"), device=DEV)[off:].view(*shape)
+    return dict(wf=[mk(d, f) for _ in range(k)], y=[mk(ml, f) for _ in range(k)],
+                dwf=[mk(d, f) for _ in range(k)], dws=[mk(R, f) for _ in range(k)])
+
+
+def test_fsdp_step_outputs_not_16_byte_aligned():
+    """The fixture's step (K = 8, 128 tokens, d = f = 512) runs the kernel with
+    every size fixed at compile time (16-byte output stores) when the W shards
+    and all outputs are 16-byte aligned, else the runtime-shaped step kernel:
+    the same bits either way, and both within the bounds."""
+    say("fsdp step, outputs aligned and 4 bytes off")
+    k, m, d, f = 8, 1024, 512, 512
+    fx = gen.fsdp_fixture(seed=5, k=k)
+    ml, R = m // k, d // k
+    xl = [fx["x"][r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    dyl = [fx["dy"][r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    ws = [s.to(DEV) for s in shard_rows(fx["w"], k)]
+    outs = []
+    for off in (0, 1):
+        o = _fsdp_outputs_at(off, k, ml, d, f, R)
+        dps.dp_fsdp_layer(xl, ws, dyl, o["wf"], o["y"], o["dwf"], o["dws"])
+        torch.cuda.synchronize()
+        outs.append({n: [to_np(t) for t in ts] for n, ts in o.items()})
+    for n in ("wf", "y", "dwf", "dws"):
+        for r in range(k):
+            assert bits_equal(outs[0][n][r], outs[1][n][r]), (n, r)
+    check_fsdp(fx["x"], fx["w"], fx["dy"], k)
+
+
 def test_fsdp_forward_only():
     fx = gen.fsdp_fixture(seed=7, k=8, m=256, d=128, f=64)
     got, host = run_fsdp(fx["x"], fx["w"], fx["dy"], 8, backward=False)
