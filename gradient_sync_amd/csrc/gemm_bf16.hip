@@ -22,15 +22,19 @@
 // v_mfma_f32_16x16x32_bf16, which accumulate the same products in the same
 // order), zero-padded past Kd, so all of them produce the same bits.
 //
-// Four designs over a tile of C:
+// Five designs over a tile of C:
 //
 // * gemm_bf16_w4d_kernel (the default for B stored [N, Kd] where M and N are
 //   multiples of 256 and Kd a multiple of 128, at least 1024): the operands go
 //   from global memory straight into LDS, 4 waves of 128x128 with 16x16x32
 //   MFMAs; described at the kernel.
 //
+// * gemm_bf16_w4dn_kernel (the same for B stored [Kd, N]): the same loads
+//   into LDS, B's fragments assembled with transposing LDS reads, 32x32x16
+//   MFMAs; described at the kernel.
+//
 // * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
-//   multiple of 64 and at least 1024, and the direct-to-LDS kernel does not
+//   multiple of 64 and at least 1024, and the direct-to-LDS kernels do not
 //   apply): 4 waves, one per SIMD, each owning a 128x128 quarter (4x4 MFMA
 //   blocks, 256 fp32 accumulators per lane held in the accumulation registers).
 //   A 128x128 wave tile reads 8 fragments from LDS per 16 MFMAs, against 6
@@ -458,10 +462,7 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
 // order as the 32x32x16 kernels, and the results are the same bits.
 // Measured at 8192^3: 724 us (1518 TFLOP/s) against 804 us for the
 // register-staged kernel and 673 us for the vendor library on the same GPU.
-// An n-contiguous B through the same scheme (transposing LDS reads) was
-// slower than the register-staged kernel: the compiler makes each
-// transposing read wait for every direct-to-LDS load in flight, since it
-// cannot tell the addresses apart.
+// An n-contiguous B takes the kernel after this one.
 constexpr int D_NT = 256, D_TK = 64;
 constexpr int D_ELEMS = TM * D_TK;          // one operand's stage: 16,384 bf16 = 32 KiB
 
@@ -584,6 +585,189 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
                                                       ((a * 16 + r) * N + b * 16) * 2, 0);
 }
 
+// ------------------------------------------- 4-wave direct-to-LDS kernel, B stored [Kd, N]
+
+// For B stored [Kd, N] (the plain product). Same tile, waves, LDS buffers
+// and direct-to-LDS loads as the kernel above; what differs:
+// - B's stage is 64 k rows of 256 n (512 bytes each, one load instruction
+//   moving two rows), 16-byte chunk c of row r at position c ^ 4 (r % 4)
+//   (SQ_LDS_BANK_CONFLICT: 33.6M cycles per 8192^3 product, against 67.2M
+//   with c ^ 2 (r % 4); the same time either way);
+// - the B operand of each MFMA is assembled with two ds_read_b64_tr_b16 reads
+//   (as in the register-staged kernel) issued as inline assembly: the compiler
+//   cannot tell a transposing read from the direct-to-LDS loads in flight and
+//   would otherwise make each one wait for all of them. The wait for a
+//   fragment set's reads is written out at the start of the k step that uses
+//   it (one s_waitcnt naming the set's registers, so the MFMAs depend on it);
+// - v_mfma_f32_32x32x16_bf16 in 4x4 blocks per wave (64 fragment registers
+//   for two sets; the 16x16x32 form's 128 left the register allocator moving
+//   accumulators inside the loop), k steps of 16, four per stage: steps 0-2,
+//   the barrier, step 3; each step's 12 fragment reads of the next step go one
+//   per MFMA over its first 12;
+// - a stage's 16 loads go one per 2 MFMAs, 8 in step 3 of the stage two
+//   before (after its barrier) and 8 in step 0 of the stage before (8 + 4 + 4
+//   or 4 + 6 + 6 over steps 3, 0, 1: 2-4% slower; all 16 in step 3: 5%).
+// Measured at 8192^3: 766-768 us (1432 TFLOP/s) against 810 us for the
+// register-staged kernel and 768-785 us for the vendor library on the same
+// GPU; the same bits (the same k order in every MFMA chain).
+template <int OFF>
+__device__ __forceinline__ i16x4 tr_read(unsigned addr)
+{
+    i16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+__global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned short *__restrict__ A,
+                                                              const unsigned short *__restrict__ B,
+                                                              unsigned short *__restrict__ C, int M,
+                                                              int N, int Kd, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned short A0[D_ELEMS], A1[D_ELEMS];
+    // B stages: [buffer][64 k rows][256 n], 16-byte chunk c of row r at position c ^ 4 (r % 4)
+    __shared__ __attribute__((aligned(1024))) unsigned short Bs[2 * D_ELEMS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wi = wave >> 1, wj = wave & 1;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const long long m0 = (long long)tm * TM, n0 = (long long)tn * TN;
+    const __amdgpu_buffer_rsrc_t rA =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * Kd), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0), (short)0, 0x7fffffff, 0x00020000);
+    auto abuf = [&](int buf) __attribute__((always_inline)) { return buf ? A1 : A0; };
+
+    // load q (0..15) of a stage: q < 8: A rows 64 wave + 8q (as the [N, Kd]
+    // kernel); q >= 8: B k rows r = 16 wave + 2 (q - 8) + h, h = lane / 32, the
+    // lane's LDS chunk p = lane % 32 holding global chunk p ^ 4 (r % 4)
+    const int lr = lane >> 3;
+    const int voff = lr * Kd * 2 + (((lane & 7) ^ lr) << 4);
+    const int vbh = (lane >> 5) * N * 2, vbc = lane & 31, vbf = 4 * (lane >> 5);
+    auto dtl = [&](int buf, int k0, int q) __attribute__((always_inline)) {
+        if (q < 8) {
+            const int row0 = wave * 64 + q * 8;
+            const int so = __builtin_amdgcn_readfirstlane((row0 * Kd + k0) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(abuf(buf) + row0 * D_TK), 16, voff, so, 0, 0);
+        } else {
+            const int qq = q - 8, r0 = wave * 16 + 2 * qq;
+            const int so = __builtin_amdgcn_readfirstlane((k0 + r0) * N * 2);
+            const int vb = vbh + 16 * (vbc ^ (vbf + 8 * (qq & 1)));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(Bs + buf * D_ELEMS + r0 * TN), 16, vb, so, 0, 0);
+        }
+    };
+
+    // fragments of a k step of 16 (v_mfma_f32_32x32x16_bf16), two sets
+    bf16x8 af[2][4], bf[2][4];
+    // A block a: rows wi*128 + 32a + lane % 32, k chunk 2 ks + lane / 32 (at chunk ^ row % 8)
+    const int ar = lane & 31, ah = lane >> 5;
+    // B block b (columns wj*128 + 32b ..): lane group g = lane / 16 takes columns
+    // 16 (g % 2) + 4 (lane % 4) .. + 3 of k rows 8 (g / 2) + e and + 4 (e = (lane % 16) / 4);
+    // its chunk 16 wj + 4b + 2 (g % 2) + (lane % 4) / 2 sits at 16 wj + 4 (b ^ e) + ..
+    const int g = lane >> 4, jj = lane & 15, e = jj >> 2;
+    const unsigned bs0 = (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned short *)Bs;
+    const unsigned bc = bs0 + ((8 * (g >> 1) + e) * TN + (16 * wj + 2 * (g & 1) + ((jj & 3) >> 1)) * 8 + 4 * (jj & 1)) * 2;
+    // read q (0..11) of k step ks into set: q < 4 A block q, else B block (q - 4) / 2, low or high rows
+    auto rdq = [&](int set, int buf, int ks, int q) __attribute__((always_inline)) {
+        if (q < 4) {
+            const int row = wi * 128 + 32 * q + ar;
+            af[set][q] = *reinterpret_cast<const bf16x8 *>(abuf(buf) + row * D_TK + (((2 * ks + ah) ^ (ar & 7)) * 8));
+        } else {
+            const int b = (q - 4) >> 1, hi = (q - 4) & 1;
+            const unsigned ad = bc + ((unsigned)(b ^ e) << 6);
+            i16x4 v;
+            // immediate: buffer, k step (16 rows of 512 bytes), high rows (+4 rows)
+#define TRR(BUF, KS, HI) v = tr_read<(BUF) * 32768 + (KS) * 8192 + (HI) * 2048>(ad)
+            if (buf == 0) {
+                if (ks == 0) { if (hi) TRR(0, 0, 1); else TRR(0, 0, 0); }
+                else if (ks == 1) { if (hi) TRR(0, 1, 1); else TRR(0, 1, 0); }
+                else if (ks == 2) { if (hi) TRR(0, 2, 1); else TRR(0, 2, 0); }
+                else { if (hi) TRR(0, 3, 1); else TRR(0, 3, 0); }
+            } else {
+                if (ks == 0) { if (hi) TRR(1, 0, 1); else TRR(1, 0, 0); }
+                else if (ks == 1) { if (hi) TRR(1, 1, 1); else TRR(1, 1, 0); }
+                else if (ks == 2) { if (hi) TRR(1, 2, 1); else TRR(1, 2, 0); }
+                else { if (hi) TRR(1, 3, 1); else TRR(1, 3, 0); }
+            }
+#undef TRR
+            i16x8 w = __builtin_bit_cast(i16x8, bf[set][b]);
+            if (hi) { w[4] = v[0]; w[5] = v[1]; w[6] = v[2]; w[7] = v[3]; }
+            else    { w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3]; }
+            bf[set][b] = __builtin_bit_cast(bf16x8, w);
+        }
+    };
+    // the reads of a set have returned (issued during the previous k step);
+    // the A fragments are named too, so the compiler adds no waits of its own
+    auto wait_b = [&](int set) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(bf[set][0]), "+v"(bf[set][1]), "+v"(bf[set][2]), "+v"(bf[set][3]),
+                       "+v"(af[set][0]), "+v"(af[set][1]), "+v"(af[set][2]), "+v"(af[set][3]));
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    auto mf = [&](int set, int a, int b) __attribute__((always_inline)) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][a], bf[set][b], acc[a][b], 0, 0, 0);
+    };
+    // one k step: 16 MFMAs from set `set`, the 12 reads of the next step into the other set
+    auto kstep = [&](int set, int nbuf, int nks, auto &&extra) __attribute__((always_inline)) {
+        wait_b(set);
+        W4_FENCE();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < 12) rdq(set ^ 1, nbuf, nks, i);
+            extra(i);
+            mf(set, i >> 2, i & 3);
+            W4_FENCE();
+        }
+    };
+    auto none = [](int) {};
+
+    const int stages = Kd / D_TK;
+    const int last = (stages - 1) * D_TK;
+    // stage t from buffer buf: k steps 0-2 (the rest of stage t+1's loads
+    // into buf ^ 1 during steps 0-1), then the barrier, then step 3 while the
+    // first loads of stage t+2 go into buf; k1, k2: k offsets of stages t+1, t+2
+    auto stage = [&](int buf, int k1, int k2) __attribute__((always_inline)) {
+        kstep(0, buf, 1, [&](int i) __attribute__((always_inline)) { if (i % 2 == 0) dtl(buf ^ 1, k1, 8 + i / 2); });
+        kstep(1, buf, 2, none);
+        kstep(0, buf, 3, none);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of stage t + 1 landed
+        __syncthreads();
+        kstep(1, buf ^ 1, 0, [&](int i) __attribute__((always_inline)) { if (i % 2 == 0) dtl(buf, k2, i / 2); });
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dtl(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dtl(1, min(D_TK, last), q);
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): this wave's loads of stage 0 landed
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 12; ++q) rdq(0, 0, 0, q);
+    W4_FENCE();
+    for (int s = 0; s < stages; s += 2) {
+        stage(0, min((s + 1) * D_TK, last), min((s + 2) * D_TK, last));
+        stage(1, min((s + 2) * D_TK, last), min((s + 3) * D_TK, last));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // D register r of a 32x32 block: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+    const __amdgpu_buffer_rsrc_t rC =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
+    // the lane index recomputed here rather than kept live through the loop
+    const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int coff = ((wi * 128 + 4 * (el >> 5)) * N + wj * 128 + (el & 31)) * 2;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[a][b][r]), rC, coff,
+                                                      ((a * 32 + 8 * (r >> 2) + (r & 3)) * N + b * 32) * 2, 0);
+}
+
 // ------------------------------------------------------ any-shape kernel
 
 // 64x64 tile of C per workgroup of 4 waves (2x2 blocks of 32x32); every lane
@@ -667,10 +851,14 @@ hipError_t launch_layout(const void *a, const void *b, void *c, long long M, lon
     const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
                     Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL &&
                     (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
-    // B stored [N, Kd] with an even number of k stages: the direct-to-LDS
-    // kernel (its C stores are 16-bit buffer stores of any alignment; 512 N
-    // bytes cover a tile's rows of C)
-    if (w4 && !BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
+    // an even number of k stages: the direct-to-LDS kernels (their C stores
+    // are 16-bit buffer stores of any alignment; 512 N bytes cover a tile's
+    // rows of C)
+    if (w4 && BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
+        hipLaunchKernelGGL(gemm_bf16_w4dn_kernel, dim3((unsigned)(tm * tn)), dim3(D_NT), 0, st,
+                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
+                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+    } else if (w4 && !BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
         hipLaunchKernelGGL(gemm_bf16_w4d_kernel, dim3((unsigned)(tm * tn)), dim3(D_NT), 0, st,
                            (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
                            (int)M, (int)N, (int)Kd, (int)tm, (int)tn);

@@ -78,7 +78,8 @@ def test_register_budgets(kernels):
     # the 4-wave GEMM: 256 accumulators in the accumulation registers, the
     # rest within the 256 architectural VGPRs (one wave per SIMD)
     for name, (desc, _) in list(pick(kernels, "gemm_bf16_w4_kernel").items()) + \
-            list(pick(kernels, "gemm_bf16_w4d_kernel").items()):
+            list(pick(kernels, "gemm_bf16_w4d_kernel").items()) + \
+            list(pick(kernels, "gemm_bf16_w4dn_kernel").items()):
         assert field(desc, "amdhsa_accum_offset") == 256, name
         assert field(desc, "amdhsa_next_free_vgpr") <= 512, name
     # the FSDP step kernels: 8 waves per workgroup, two per SIMD (<= 256 each)
@@ -136,3 +137,28 @@ def test_cache_hints_reach_the_code(kernels):
         st = _stores(body)
         assert len(st) >= 4 and all(nt.search(x) for x in st), name
         assert not re.search(r"^\s*(global|buffer)_store_dword\b", body, re.M), name
+
+
+def _loop_body(body):
+    """The instructions of the innermost loop (the block the compiler marks as
+    the loop header, up to the next label)."""
+    lines = body.splitlines()
+    start = next(i for i, ln in enumerate(lines) if "Inner Loop Header" in ln)
+    end = next(i for i in range(start + 1, len(lines)) if re.match(r"^\.LBB\d+_\d+:", lines[i]))
+    return "\n".join(lines[start:end])
+
+
+def test_direct_to_lds_gemm_loops(kernels):
+    """The main loops of both direct-to-LDS GEMM kernels keep every
+    accumulator in place (no accumulation-register moves inside the loop);
+    the kernel for B stored [k, n] assembles B's fragments with transposing LDS
+    reads and waits for the loads in flight only at its barriers."""
+    for parts in (("gemm_bf16_w4d_kernel",), ("gemm_bf16_w4dn_kernel",)):
+        for name, (_, body) in pick(kernels, *parts).items():
+            loop = _loop_body(body)
+            assert re.search(r"\bv_mfma_", loop), name
+            assert not re.search(r"\bv_accvgpr_(mov|write|read)", loop), name
+    for name, (_, body) in pick(kernels, "gemm_bf16_w4dn_kernel").items():
+        loop = _loop_body(body)
+        assert len(re.findall(r"\bds_read_b64_tr_b16\b", loop)) == 64, name
+        assert len(re.findall(r"s_waitcnt vmcnt\(0\)", loop)) == 2, name

@@ -288,8 +288,9 @@ def test_gemm_bf16_small(m, n, kk, layout):
 
 
 def test_gemm_bf16_8192_sampled():
-    """C = A B with A, B bf16 [8192,8192] ~ N(0,1): sampled entries; then B
-    stored [n,k] (the direct-to-LDS kernel) gives the same bits."""
+    """C = A B with A, B bf16 [8192,8192] ~ N(0,1) (B stored [k,n]: the
+    direct-to-LDS kernel with transposing LDS reads): sampled entries; then B
+    stored [n,k] (the other direct-to-LDS kernel) gives the same bits."""
     m = n = kk = 8192
     say("gemm bf16 8192^3")
     a, b = gen.gemm_bf16_inputs(5, m, n, kk, device=DEV)
@@ -312,8 +313,10 @@ def test_gemm_bf16_8192_sampled():
                                     (264, 280, 1032)])
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run a 4-wave
-    kernel (with B stored [n,kk] and an even number of depth-64 stages the
-    direct-to-LDS one, 16x16x32 MFMAs); the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
+    kernel (with an even number of depth-64 stages the direct-to-LDS ones:
+    16x16x32 MFMAs for B stored [n,kk], 32x32x16 MFMAs and transposing LDS
+    reads for B stored [kk,n]; with an odd number the register-staged one);
+    the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
     B stored [kk,n] (transposing LDS reads) and [n,kk] alike, so all six agree
     bit for bit (shorter k ranges and edge tiles take the 8-wave kernel on
@@ -368,8 +371,8 @@ def _offset_copy(t, off):
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("off", [1, 3, 8])
 def test_gemm_bf16_output_at_any_element_offset(layout, off):
-    """The 4-wave kernels (B [n,k] with an even number of k stages: the
-    direct-to-LDS one) with aligned operands and C at an element offset that
+    """The 4-wave direct-to-LDS kernels (both layouts, an even number of k
+    stages) with aligned operands and C at an element offset that
     is not 16-byte aligned: the same bits as an aligned C, and the elements
     around C untouched."""
     m = n = 512
