@@ -1000,7 +1000,7 @@ def bench_gemm(args):
             "value": res["dp_gemm_bf16"]["tflops"], "results": res,
             "timing": "interleaved rounds of 8 back-to-back calls between two events, "
                       "after ~1 s of warm-up; median per call",
-            "roofline": {"bound": "mfma", "kernel": "gemm_bf16_w4dn_kernel (B stored [k, n], operands loaded straight into LDS, transposing LDS reads, 32x32x16 MFMAs)",
+            "roofline": {"bound": "mfma", "kernel": "gemm_bf16_w4dn_kernel (B stored [k, n], operands loaded straight into LDS, transposing LDS reads, 16x16x32 MFMAs)",
                          "achieved": res["dp_gemm_bf16"]["tflops"],
                          "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": res["dp_gemm_bf16"]["frac_of_peak"], "traffic": None},

@@ -30,8 +30,8 @@
 //   MFMAs; described at the kernel.
 //
 // * gemm_bf16_w4dn_kernel (the same for B stored [Kd, N]): the same loads
-//   into LDS, B's fragments assembled with transposing LDS reads, 32x32x16
-//   MFMAs; described at the kernel.
+//   into LDS and 16x16x32 MFMAs, B's fragments assembled with transposing LDS
+//   reads; described at the kernel.
 //
 // * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
 //   multiple of 64 and at least 1024, and the direct-to-LDS kernels do not
@@ -587,45 +587,78 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
 
 // ------------------------------------------- 4-wave direct-to-LDS kernel, B stored [Kd, N]
 
-// For B stored [Kd, N] (the plain product). Same tile, waves, LDS buffers
-// and direct-to-LDS loads as the kernel above; what differs:
+// For B stored [Kd, N] (the plain product). Same tile, waves, LDS buffers,
+// 16x16x32 MFMAs (8x8 blocks per wave) and direct-to-LDS loads as the kernel
+// above; what differs:
 // - B's stage is 64 k rows of 256 n (512 bytes each, one load instruction
-//   moving two rows), 16-byte chunk c of row r at position c ^ 4 (r % 4)
-//   (SQ_LDS_BANK_CONFLICT: 33.6M cycles per 8192^3 product, against 67.2M
-//   with c ^ 2 (r % 4); the same time either way);
-// - the B operand of each MFMA is assembled with two ds_read_b64_tr_b16 reads
-//   (as in the register-staged kernel) issued as inline assembly: the compiler
-//   cannot tell a transposing read from the direct-to-LDS loads in flight and
-//   would otherwise make each one wait for all of them. The wait for a
-//   fragment set's reads is written out at the start of the k step that uses
-//   it (one s_waitcnt naming the set's registers, so the MFMAs depend on it);
-// - v_mfma_f32_32x32x16_bf16 in 4x4 blocks per wave (64 fragment registers
-//   for two sets; the 16x16x32 form's 128 left the register allocator moving
-//   accumulators inside the loop), k steps of 16, four per stage: steps 0-2,
-//   the barrier, step 3; each step's 12 fragment reads of the next step go one
-//   per MFMA over its first 12;
-// - a stage's 16 loads go one per 2 MFMAs, 8 in step 3 of the stage two
-//   before (after its barrier) and 8 in step 0 of the stage before (8 + 4 + 4
-//   or 4 + 6 + 6 over steps 3, 0, 1: 2-4% slower; all 16 in step 3: 5%).
-// Measured at 8192^3: 766-768 us (1432 TFLOP/s) against 810 us for the
-// register-staged kernel and 768-785 us for the vendor library on the same
-// GPU; the same bits (the same k order in every MFMA chain).
-template <int OFF>
-__device__ __forceinline__ i16x4 tr_read(unsigned addr)
+//   moving two rows), 16-byte chunk c of row r at position
+//   c ^ (4 (r % 4) + 2 ((r / 8) % 2)), which puts the four 16-lane groups of
+//   one transposing read on two disjoint halves of the banks
+//   (SQ_LDS_BANK_CONFLICT: 0 per 8192^3 product);
+// - each B fragment (the 8 k values of one column per lane) is two
+//   ds_read_b64_tr_b16 reads, gfx950's transposing LDS load: lane i of a
+//   16-lane group receives element i % 4 of the 8-byte rows addressed by lanes
+//   4e + i / 4 (e = 0..3) of its group, so lane 4e + h addresses k row e (+4
+//   for the second read) at columns 4h .. 4h + 3 and lane i receives 4 k
+//   values of column i;
+// - a k step walks the 8 column blocks in turn (8 MFMAs each, one per row
+//   block); all 8 A fragments of a step are read during the step before, the B
+//   fragment of block G two blocks ahead, each into a register set of its own;
+// - every LDS read is inline assembly and every wait for one is written out
+//   (s_waitcnt lgkmcnt naming the fragments it makes valid): the compiler
+//   counts neither the transposing reads nor, here, the others, and its own
+//   waits would wait for reads issued after the ones needed. The barrier sits
+//   after block 13 of a stage (the last reads of its buffer issued and waited
+//   for); the loads of stage t + 2 go into that buffer from then on, one per 3
+//   MFMAs, 6 in blocks 14-15 and 10 in step 0 of the next stage;
+// - the MFMAs are inline assembly too, with the accumulators as "+a"
+//   operands: with builtins the compiler keeps part of the 256 accumulators in
+//   architectural registers and copies them through the accumulation
+//   registers around every MFMA (~600 moves per loop pass). As it sees neither
+//   their latency nor their hazards, every read of the accumulators outside
+//   the MFMAs is ordered after a fence asm that names all of them and waits
+//   24 cycles.
+// Every MFMA chain adds the same products in the same order as the other
+// kernels (ascending k, 16x16x32 over 32-wide steps), so the results are the
+// same bits. Measured at 8192^3: 718-733 us (1500-1531 TFLOP/s) against
+// 759-768 us for the 32x32x16 form of this kernel on the same GPUs (which
+// holds a lower clock), level with it from kk = 1024 to 1152 and 3-6% faster
+// from 2048.
+
+__device__ __forceinline__ bf16x8 lds_read_b128(unsigned addr)
 {
-    i16x4 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
     return v;
 }
+__device__ __forceinline__ i16x4 lds_read_tr_b64(unsigned addr)
+{
+    i16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+#define DN_ACC_ROW(A, TXT)                                                                    \
+    asm volatile(TXT : "+a"(acc[A][0]), "+a"(acc[A][1]), "+a"(acc[A][2]), "+a"(acc[A][3]),    \
+                 "+a"(acc[A][4]), "+a"(acc[A][5]), "+a"(acc[A][6]), "+a"(acc[A][7]))
+#define DN_ACC_FENCE()                                                                        \
+    do {                                                                                      \
+        DN_ACC_ROW(0, "s_nop 7\n\ts_nop 7\n\ts_nop 7");                                         \
+        DN_ACC_ROW(1, ""); DN_ACC_ROW(2, ""); DN_ACC_ROW(3, ""); DN_ACC_ROW(4, "");             \
+        DN_ACC_ROW(5, ""); DN_ACC_ROW(6, ""); DN_ACC_ROW(7, "");                                \
+    } while (0)
+#define DN_WAIT_A(N, S, Q)                                                                    \
+    asm volatile("s_waitcnt lgkmcnt(" #N ")"                                                  \
+                 : "+v"(af[S][0]), "+v"(af[S][1]), "+v"(af[S][2]), "+v"(af[S][3]),             \
+                   "+v"(af[S][4]), "+v"(af[S][5]), "+v"(af[S][6]), "+v"(af[S][7]), "+v"(bq[Q]))
 
 __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned short *__restrict__ A,
                                                               const unsigned short *__restrict__ B,
                                                               unsigned short *__restrict__ C, int M,
                                                               int N, int Kd, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned short A0[D_ELEMS], A1[D_ELEMS];
-    // B stages: [buffer][64 k rows][256 n], 16-byte chunk c of row r at position c ^ 4 (r % 4)
-    __shared__ __attribute__((aligned(1024))) unsigned short Bs[2 * D_ELEMS];
+    // A stages at LDS bytes 0 and 32768, B stages at 65536 and 98304
+    __shared__ __attribute__((aligned(1024))) unsigned short L[4 * D_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = wave >> 1, wj = wave & 1;
@@ -636,137 +669,150 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned sho
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * Kd), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rB =
         __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0), (short)0, 0x7fffffff, 0x00020000);
-    auto abuf = [&](int buf) __attribute__((always_inline)) { return buf ? A1 : A0; };
+    const unsigned lb = (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned short *)L;
 
     // load q (0..15) of a stage: q < 8: A rows 64 wave + 8q (as the [N, Kd]
     // kernel); q >= 8: B k rows r = 16 wave + 2 (q - 8) + h, h = lane / 32, the
-    // lane's LDS chunk p = lane % 32 holding global chunk p ^ 4 (r % 4)
+    // lane's LDS chunk p = lane % 32 holding global chunk p ^ (4 (r % 4) + 2 ((r / 8) % 2))
     const int lr = lane >> 3;
     const int voff = lr * Kd * 2 + (((lane & 7) ^ lr) << 4);
-    const int vbh = (lane >> 5) * N * 2, vbc = lane & 31, vbf = 4 * (lane >> 5);
+    const int hb = lane >> 5;
+    const int vbh = hb * N * 2, vbc = lane & 31;
     auto dtl = [&](int buf, int k0, int q) __attribute__((always_inline)) {
         if (q < 8) {
             const int row0 = wave * 64 + q * 8;
             const int so = __builtin_amdgcn_readfirstlane((row0 * Kd + k0) * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(abuf(buf) + row0 * D_TK), 16, voff, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(L + buf * D_ELEMS + row0 * D_TK), 16, voff, so, 0, 0);
         } else {
             const int qq = q - 8, r0 = wave * 16 + 2 * qq;
             const int so = __builtin_amdgcn_readfirstlane((k0 + r0) * N * 2);
-            const int vb = vbh + 16 * (vbc ^ (vbf + 8 * (qq & 1)));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(Bs + buf * D_ELEMS + r0 * TN), 16, vb, so, 0, 0);
+            const int vb = vbh + 16 * (vbc ^ (8 * (qq & 1) + 4 * hb + 2 * (qq >> 2)));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(L + (2 + buf) * D_ELEMS + r0 * TN), 16, vb, so, 0, 0);
         }
     };
 
-    // fragments of a k step of 16 (v_mfma_f32_32x32x16_bf16), two sets
-    bf16x8 af[2][4], bf[2][4];
-    // A block a: rows wi*128 + 32a + lane % 32, k chunk 2 ks + lane / 32 (at chunk ^ row % 8)
-    const int ar = lane & 31, ah = lane >> 5;
-    // B block b (columns wj*128 + 32b ..): lane group g = lane / 16 takes columns
-    // 16 (g % 2) + 4 (lane % 4) .. + 3 of k rows 8 (g / 2) + e and + 4 (e = (lane % 16) / 4);
-    // its chunk 16 wj + 4b + 2 (g % 2) + (lane % 4) / 2 sits at 16 wj + 4 (b ^ e) + ..
-    const int g = lane >> 4, jj = lane & 15, e = jj >> 2;
-    const unsigned bs0 = (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned short *)Bs;
-    const unsigned bc = bs0 + ((8 * (g >> 1) + e) * TN + (16 * wj + 2 * (g & 1) + ((jj & 3) >> 1)) * 8 + 4 * (jj & 1)) * 2;
-    // read q (0..11) of k step ks into set: q < 4 A block q, else B block (q - 4) / 2, low or high rows
-    auto rdq = [&](int set, int buf, int ks, int q) __attribute__((always_inline)) {
-        if (q < 4) {
-            const int row = wi * 128 + 32 * q + ar;
-            af[set][q] = *reinterpret_cast<const bf16x8 *>(abuf(buf) + row * D_TK + (((2 * ks + ah) ^ (ar & 7)) * 8));
-        } else {
-            const int b = (q - 4) >> 1, hi = (q - 4) & 1;
-            const unsigned ad = bc + ((unsigned)(b ^ e) << 6);
-            i16x4 v;
-            // immediate: buffer, k step (16 rows of 512 bytes), high rows (+4 rows)
-#define TRR(BUF, KS, HI) v = tr_read<(BUF) * 32768 + (KS) * 8192 + (HI) * 2048>(ad)
-            if (buf == 0) {
-                if (ks == 0) { if (hi) TRR(0, 0, 1); else TRR(0, 0, 0); }
-                else if (ks == 1) { if (hi) TRR(0, 1, 1); else TRR(0, 1, 0); }
-                else if (ks == 2) { if (hi) TRR(0, 2, 1); else TRR(0, 2, 0); }
-                else { if (hi) TRR(0, 3, 1); else TRR(0, 3, 0); }
-            } else {
-                if (ks == 0) { if (hi) TRR(1, 0, 1); else TRR(1, 0, 0); }
-                else if (ks == 1) { if (hi) TRR(1, 1, 1); else TRR(1, 1, 0); }
-                else if (ks == 2) { if (hi) TRR(1, 2, 1); else TRR(1, 2, 0); }
-                else { if (hi) TRR(1, 3, 1); else TRR(1, 3, 0); }
-            }
-#undef TRR
-            i16x8 w = __builtin_bit_cast(i16x8, bf[set][b]);
-            if (hi) { w[4] = v[0]; w[5] = v[1]; w[6] = v[2]; w[7] = v[3]; }
-            else    { w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3]; }
-            bf[set][b] = __builtin_bit_cast(bf16x8, w);
-        }
+    // A fragment x of k step ks: row wi*128 + 16x + lane % 16, chunk 4 ks +
+    // lane / 16, stored at chunk ^ (row % 8)
+    const unsigned aa0 = lb + (wi * 128 + (lane & 15)) * 128 + 16 * ((lane >> 4) ^ (lane & 7));
+    const unsigned aa1 = lb + (wi * 128 + (lane & 15)) * 128 + 16 * ((4 + (lane >> 4)) ^ (lane & 7));
+    // B fragment of column block b (columns wj*128 + 16b ..) in k step ks:
+    // lane group g = lane / 16 covers k 8g .. 8g + 7; lane m = lane % 16
+    // addresses k row 8g + m / 4 (+4 for the second read) at columns 4 (m % 4)
+    // .. + 3, which sit 32 (b ^ s) + 16 ((m % 4) / 2) + 8 (m % 2) bytes into the
+    // row's 256-byte half wj, s = 2 (m / 4) + g % 2
+    const int g = lane >> 4, mm = lane & 15, e = mm >> 2, h4 = mm & 3;
+    const int sx = 2 * e + (g & 1);
+    const unsigned bb = lb + 65536 + 512 * (8 * g + e) + 256 * wj + 16 * (h4 >> 1) + 8 * (h4 & 1);
+
+    // af[ks][x]: A fragments of k step ks; bq[G]: B fragment of block G = 8 ks + b
+    bf16x8 af[2][8], bq[16];
+    auto rdA = [&](int set, int buf, int x) __attribute__((always_inline)) {
+        af[set][x] = lds_read_b128((set ? aa1 : aa0) + buf * 32768 + x * 2048);
     };
-    // the reads of a set have returned (issued during the previous k step);
-    // the A fragments are named too, so the compiler adds no waits of its own
-    auto wait_b = [&](int set) __attribute__((always_inline)) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(bf[set][0]), "+v"(bf[set][1]), "+v"(bf[set][2]), "+v"(bf[set][3]),
-                       "+v"(af[set][0]), "+v"(af[set][1]), "+v"(af[set][2]), "+v"(af[set][3]));
+    auto rdB = [&](int G, int buf, int hi) __attribute__((always_inline)) {
+        const int ks = G >> 3, b = G & 7;
+        const i16x4 v = lds_read_tr_b64(bb + ((unsigned)(b ^ sx) << 5) + buf * 32768 + ks * 16384 + hi * 2048);
+        i16x8 w = __builtin_bit_cast(i16x8, bq[G]);
+        if (hi) { w[4] = v[0]; w[5] = v[1]; w[6] = v[2]; w[7] = v[3]; }
+        else    { w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3]; }
+        bq[G] = __builtin_bit_cast(bf16x8, w);
     };
-    f32x16 acc[4][4];
+    f32x4 acc[8][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
-    auto mf = [&](int set, int a, int b) __attribute__((always_inline)) {
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][a], bf[set][b], acc[a][b], 0, 0, 0);
-    };
-    // one k step: 16 MFMAs from set `set`, the 12 reads of the next step into the other set
-    auto kstep = [&](int set, int nbuf, int nks, auto &&extra) __attribute__((always_inline)) {
-        wait_b(set);
-        W4_FENCE();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i < 12) rdq(set ^ 1, nbuf, nks, i);
-            extra(i);
-            mf(set, i >> 2, i & 3);
-            W4_FENCE();
-        }
-    };
-    auto none = [](int) {};
+        for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{};
+    DN_ACC_FENCE();
 
     const int stages = Kd / D_TK;
     const int last = (stages - 1) * D_TK;
-    // stage t from buffer buf: k steps 0-2 (the rest of stage t+1's loads
-    // into buf ^ 1 during steps 0-1), then the barrier, then step 3 while the
-    // first loads of stage t+2 go into buf; k1, k2: k offsets of stages t+1, t+2
+    // Block G (0..15) of stage t from buffer buf (literal): 8 MFMAs, one per
+    // row block. LDS reads issued in block G: G < 8: A fragment G of step 1 and
+    // the B fragment of block G + 2; 8 <= G < 14: the B fragment of block G + 2;
+    // G = 14, 15: A fragments 4 (G - 14) .. + 3 of stage t + 1's step 0 and its
+    // B fragment of block G - 14, from buf ^ 1. The wait at the start of a
+    // block counts the reads issued after the ones it needs (3 per block in
+    // step 0, 2 in step 1). k1: k of stage t + 1 (its loads 6..15 go into buf
+    // ^ 1 during step 0); k2: k of stage t + 2 (its loads 0..5 go into buf after
+    // the barrier).
+    auto block = [&](int buf, int k1, int k2, int G) __attribute__((always_inline)) {
+        const int ks = G >> 3, b = G & 7;
+        if (G == 0) DN_WAIT_A(2, 0, 0);
+        else if (G == 8) DN_WAIT_A(2, 1, 8);
+        else if (G < 8) asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(bq[G]));
+        else if (G <= 13) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(bq[G]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = 8 * G + j;
+            if (G < 8) {
+                if (j == 0) rdA(1, buf, G);
+                else if (j <= 2) rdB(G + 2, buf, j - 1);
+            } else if (G < 14) {
+                if (j <= 1) rdB(G + 2, buf, j);
+            } else {
+                if (j < 4) rdA(0, buf ^ 1, 4 * (G - 14) + j);
+                else if (j <= 5) rdB(G - 14, buf ^ 1, j - 4);
+            }
+            if (i >= 2 && i < 32 && (i - 2) % 3 == 0) dtl(buf ^ 1, k1, 6 + (i - 2) / 3);
+            if (i >= 112 && (i - 112) % 3 == 0) dtl(buf, k2, (i - 112) / 3);
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[j][b]) : "v"(af[ks][j]), "v"(bq[G]));
+            W4_FENCE();
+        }
+        if (G == 13) {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bq[12]), "+v"(bq[13]), "+v"(bq[14]), "+v"(bq[15]));
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of stage t + 1 landed
+            __syncthreads();
+            W4_FENCE();
+        }
+    };
     auto stage = [&](int buf, int k1, int k2) __attribute__((always_inline)) {
-        kstep(0, buf, 1, [&](int i) __attribute__((always_inline)) { if (i % 2 == 0) dtl(buf ^ 1, k1, 8 + i / 2); });
-        kstep(1, buf, 2, none);
-        kstep(0, buf, 3, none);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of stage t + 1 landed
-        __syncthreads();
-        kstep(1, buf ^ 1, 0, [&](int i) __attribute__((always_inline)) { if (i % 2 == 0) dtl(buf, k2, i / 2); });
+#pragma unroll
+        for (int G = 0; G < 16; ++G) block(buf, k1, k2, G);
     };
 #pragma unroll
     for (int q = 0; q < 16; ++q) dtl(0, 0, q);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dtl(1, min(D_TK, last), q);
-    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): this wave's loads of stage 0 landed
+    for (int q = 0; q < 6; ++q) dtl(1, min(D_TK, last), q);
+    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): this wave's loads of stage 0 landed
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 12; ++q) rdq(0, 0, 0, q);
+    for (int x = 0; x < 8; ++x) rdA(0, 0, x);
+    rdB(0, 0, 0);
+    rdB(0, 0, 1);
+    rdB(1, 0, 0);
+    rdB(1, 0, 1);
     W4_FENCE();
+    // an even number of stages (the launcher's condition); past the end the
+    // loads repeat the last stage into a buffer no MFMA reads again
     for (int s = 0; s < stages; s += 2) {
         stage(0, min((s + 1) * D_TK, last), min((s + 2) * D_TK, last));
         stage(1, min((s + 2) * D_TK, last), min((s + 3) * D_TK, last));
     }
+    // the reads issued for the stage past the end land before their registers
+    // are reused, and the loads before the workgroup's LDS is released
+    DN_WAIT_A(0, 0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bq[1]));
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    // D register r of a 32x32 block: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+    DN_ACC_FENCE();
+    // C through a buffer descriptor on the tile's first element. D register r
+    // of a 16x16 block: row 4 (l / 16) + r, column l % 16.
     const __amdgpu_buffer_rsrc_t rC =
         __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
-    // the lane index recomputed here rather than kept live through the loop
     const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const int coff = ((wi * 128 + 4 * (el >> 5)) * N + wj * 128 + (el & 31)) * 2;
+    const int coff = ((wi * 128 + 4 * (el >> 4)) * N + wj * 128 + (el & 15)) * 2;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 4; ++r)
                 __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[a][b][r]), rC, coff,
-                                                      ((a * 32 + 8 * (r >> 2) + (r & 3)) * N + b * 32) * 2, 0);
+                                                      ((a * 16 + r) * N + b * 16) * 2, 0);
 }
+#undef DN_ACC_ROW
+#undef DN_ACC_FENCE
+#undef DN_WAIT_A
 
 // ------------------------------------------------------ any-shape kernel
 

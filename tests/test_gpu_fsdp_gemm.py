@@ -314,7 +314,7 @@ def test_gemm_bf16_8192_sampled():
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run a 4-wave
     kernel (with an even number of depth-64 stages the direct-to-LDS ones:
-    16x16x32 MFMAs for B stored [n,kk], 32x32x16 MFMAs and transposing LDS
+    16x16x32 MFMAs for both, B's fragments assembled with transposing LDS
     reads for B stored [kk,n]; with an odd number the register-staged one);
     the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
