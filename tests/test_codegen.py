@@ -167,6 +167,12 @@ def test_direct_to_lds_gemm_loops(kernels):
         assert len(re.findall(r"\bv_mfma_f32_16x16x32_bf16\b", loop)) == 256, name
         assert len(re.findall(r"s_waitcnt vmcnt\(0\)", loop)) == 2, name
         assert len(re.findall(r"s_waitcnt lgkmcnt\(\d+\)", loop)) == 30, name
+        # the inline LDS reads' results go straight into the MFMA operand
+        # registers: no vector instruction in the loop but the MFMAs (a copy
+        # of a read's result would read it before it lands, and free its
+        # register while the read is still in flight)
+        valu = [m for m in re.findall(r"^\s*(v_\w+)", loop, re.M) if not m.startswith("v_mfma_")]
+        assert not valu, (name, sorted(set(valu)))
         tail = body[body.index(loop) + len(loop):]
         first_read = re.search(r"\bv_accvgpr_read_b32\b", tail).start()
         assert tail.rfind("s_nop 7", 0, first_read) > tail.rfind("v_mfma", 0, first_read), name
