@@ -88,6 +88,33 @@ constexpr long long kCacheOutBytes = 128ll << 20;
 constexpr int kAlign = 128;
 constexpr int kFastBit = 256;
 constexpr int kOutAlignBit = 512;   // AllGather: the K outputs share one 16-byte phase
+
+// Residency caps for launches over small shards. At full residency a launch
+// keeps ~2,048 workgroups of 4 KiB tiles in flight (8 waves per SIMD on 256
+// CUs); where a shard has fewer tiles than about twice that, the resident
+// workgroups span two shards most of the time, and the write-heavy kernels then
+// stream into twice as many output regions at once. Holding them to fewer
+// workgroups per CU keeps them mostly within one shard. The cap is LDS the
+// kernels never touch, reserved per workgroup at launch (160 KiB per CU,
+// allocated in 2 KiB blocks: 80 KiB -> 2 workgroups, 40 KiB -> 4). Measured on
+// MI355X, same bits, interleaved processes on one box per comparison
+// (25,000,000-value bf16 buckets, K = 8: 1,526 tiles per shard):
+//   AllGather 85.4-86.4 -> 79.7-80.1 us with 2 per CU (3: 80.3-80.6, 4: 84.3,
+//   1: 116; the plain layer step 70.4 -> 72.7-73.0% of HBM peak); one-pass
+//   AllReduce of the layer 1.191-1.193 -> 1.161-1.162 ms with 2 (3: 1.210-
+//   1.213, slower; 4 to 6: unchanged); fused ReduceScatter + AllGather, the
+//   pipelined layer step 78.4-78.5 -> 79.2-79.4% with 4 (2: 66%; 5, 6:
+//   78.8-79.0%); token-weighted fp32, 10,000,019 values (1,221 tiles per
+//   shard): two-phase 117.4-118.5 -> 114.2-115.0 us, one pass 111.8-114.2 ->
+//   110.8-112.6 us.
+// Shards of 131,072 tiles (1 GiB fp32 per rank) lose 1% with the cap, and the
+// standalone ReduceScatter (K reads per write) loses 5% (79 -> 83 us): both run
+// uncapped. A persistent grid of as few workgroups is no substitute (AllGather
+// on 512-1,024 workgroups: 90-97 us): the cap keeps one tile per workgroup.
+constexpr long long kCapSegTiles = 4096;   // shards of fewer tiles take the cap ...
+constexpr long long kCapMinTiles = 4096;   // ... in launches of at least this many tiles
+constexpr unsigned kCapLds2 = 80u << 10;   // AllGather and one-pass AllReduce: 2 per CU
+constexpr unsigned kCapLds4 = 40u << 10;   // fused ReduceScatter + AllGather: 4 per CU
 static_assert(kAlign >= 16 && kAlign <= 256 && (kAlign & (kAlign - 1)) == 0, "alignment");
 
 __device__ __forceinline__ u32x4 load_stream(const char *p)
@@ -574,6 +601,11 @@ __global__ __launch_bounds__(kBlock) void rsag_kernel(const RsParams rp, const A
 
 // ------------------------------------------------------------------ launchers
 
+bool small_shards(long long tiles_per_seg, long long total_tiles)
+{
+    return tiles_per_seg < kCapSegTiles && total_tiles >= kCapMinTiles;
+}
+
 template <int DT, int EP, int KT, bool AR>
 hipError_t rs_go(const RsParams &p, long long grid, bool lean, hipStream_t st)
 {
@@ -584,7 +616,8 @@ hipError_t rs_go(const RsParams &p, long long grid, bool lean, hipStream_t st)
     else if (!AR && p.cache_out)
         hipLaunchKernelGGL((rs_kernel<DT, EP, KT, RsU<DT>::U, false, true>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
     else
-        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, AR ? kArU : RsU<DT>::U, AR, false>), dim3((unsigned)grid), dim3(kBlock), 0, st, p);
+        hipLaunchKernelGGL((rs_kernel<DT, EP, KT, AR ? kArU : RsU<DT>::U, AR, false>), dim3((unsigned)grid), dim3(kBlock),
+                           AR && small_shards(p.tiles_per_seg, p.total_tiles) ? kCapLds2 : 0u, st, p);
     return hipGetLastError();
 }
 
@@ -627,7 +660,8 @@ hipError_t ag_go(const AgParams &p, long long grid, hipStream_t st)
     if (p.max_blocks > 0)
         hipLaunchKernelGGL((ag_kernel<ES, KT, kUCapped>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
     else
-        hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kAgBlock), 0, st, p);
+        hipLaunchKernelGGL((ag_kernel<ES, KT, kAgU>), dim3((unsigned)grid), dim3(kAgBlock),
+                           small_shards(p.tiles_per_seg, p.total_tiles) ? kCapLds2 : 0u, st, p);
     return hipGetLastError();
 }
 
@@ -754,11 +788,15 @@ hipError_t launch_ar(const RsParams &p, int dt, int ep, hipStream_t st, bool lea
 template <int DT, int EP>
 hipError_t rsag_k(const RsParams &rp, const AgParams &ap, long long grid, hipStream_t st)
 {
+    // both halves over small shards (an empty half counts as small)
+    const bool small = (rp.total_tiles == 0 || rp.tiles_per_seg < kCapSegTiles) &&
+                       (ap.total_tiles == 0 || ap.tiles_per_seg < kCapSegTiles) && grid >= kCapMinTiles;
+    const unsigned lds = small ? kCapLds4 : 0u;
     switch (rp.k) {
-    case 2: hipLaunchKernelGGL((rsag_kernel<DT, EP, 2>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
-    case 4: hipLaunchKernelGGL((rsag_kernel<DT, EP, 4>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
-    case 8: hipLaunchKernelGGL((rsag_kernel<DT, EP, 8>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
-    default: hipLaunchKernelGGL((rsag_kernel<DT, EP, 0>), dim3((unsigned)grid), dim3(kBlock), 0, st, rp, ap); break;
+    case 2: hipLaunchKernelGGL((rsag_kernel<DT, EP, 2>), dim3((unsigned)grid), dim3(kBlock), lds, st, rp, ap); break;
+    case 4: hipLaunchKernelGGL((rsag_kernel<DT, EP, 4>), dim3((unsigned)grid), dim3(kBlock), lds, st, rp, ap); break;
+    case 8: hipLaunchKernelGGL((rsag_kernel<DT, EP, 8>), dim3((unsigned)grid), dim3(kBlock), lds, st, rp, ap); break;
+    default: hipLaunchKernelGGL((rsag_kernel<DT, EP, 0>), dim3((unsigned)grid), dim3(kBlock), lds, st, rp, ap); break;
     }
     return hipGetLastError();
 }
