@@ -50,11 +50,11 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix
 # were taken on (sha256 of sync_kernels.hip + sync_internal.h; the gfx950 code of
 # these sources is the same as that of the tree the counters were taken on).
 MEASURED_TRAFFIC = {
-    "sources_sha256": "068cee16680959fdf53ff7e56614a75e0eb3f6fbab476d7523ba953d679ec891"
+    "sources_sha256": "3a3ca48c3af27a5b60f65de0d68051dea2c9c4b12ca009b940fbd130c74c80c7"
                       "f16581e6b16ca798c1f240711e1e80c1a3d4fdf4628ca177e96c534422299b95",
-    "rs_kernel<bf16, avg, K=8>": (2 * 195384.3 + 49408.9) * 1024,
-    "ag_kernel<2-byte, K=8>": (2 * 25142.6 + 390841.3) * 1024,
-    "rsag_kernel<bf16, avg, K=8>": (2 * 220517.3 + 439715.3) * 1024,
+    "rs_kernel<bf16, avg, K=8>": (2 * 195384.2 + 49415.8) * 1024,
+    "ag_kernel<2-byte, K=8>": (2 * 25142.5 + 390736.1) * 1024,
+    "rsag_kernel<bf16, avg, K=8>": (2 * 220517.3 + 439723.3) * 1024,
 }
 
 
