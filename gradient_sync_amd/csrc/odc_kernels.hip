@@ -33,6 +33,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kOdcBlock = 256;
 constexpr long long kOdcTile = 4096;      // elements of one shard per workgroup tile
 constexpr int kPushUnroll = 4;            // gradients whose loads are in flight together
+// Residency: the bf16 push and settle launches of at least kOdcCapMinGrid
+// workgroups reserve 52 KiB of LDS per workgroup (the kernels use none), so a
+// CU holds 3 of them instead of 8. Measured on MI355X at layer size (K = 8,
+// 27,262,976-value shards, 6,656 tiles each), interleaved processes on two
+// boxes, same bits: push of 8 gradients 908-916 -> 896-905 us (2 per CU:
+// 916-924, 4 per CU: 904-910), settle with reset 375-378 -> 358-361 us (2:
+// 364-366, 4: 379-381). The fp32 forms run uncapped (not measured).
+constexpr unsigned kOdcCapLds = 52u << 10;
+constexpr long long kOdcCapMinGrid = 4096;
 
 // Accumulators: ordinary loads, nontemporal stores (nontemporal loads as well
 // measured slower); settled shards: nontemporal stores.
@@ -252,7 +261,8 @@ hipError_t launch_scatter_accumulate(const SaParams &p0, int dt, hipStream_t st)
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dt == kBF16)
-        hipLaunchKernelGGL(scatter_accumulate_kernel<kBF16>, dim3((unsigned)grid), dim3(kOdcBlock), 0, st, p);
+        hipLaunchKernelGGL(scatter_accumulate_kernel<kBF16>, dim3((unsigned)grid), dim3(kOdcBlock),
+                           grid >= kOdcCapMinGrid ? kOdcCapLds : 0u, st, p);
     else
         hipLaunchKernelGGL(scatter_accumulate_kernel<kF32>, dim3((unsigned)grid), dim3(kOdcBlock), 0, st, p);
     return hipGetLastError();
@@ -271,8 +281,9 @@ hipError_t launch_settle(const SettleParams &p0, int dt, bool mul, hipStream_t s
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 g((unsigned)grid), b(kOdcBlock);
     if (dt == kBF16) {
-        if (mul) hipLaunchKernelGGL((settle_kernel<kBF16, true>), g, b, 0, st, p);
-        else hipLaunchKernelGGL((settle_kernel<kBF16, false>), g, b, 0, st, p);
+        const unsigned lds = grid >= kOdcCapMinGrid ? kOdcCapLds : 0u;
+        if (mul) hipLaunchKernelGGL((settle_kernel<kBF16, true>), g, b, lds, st, p);
+        else hipLaunchKernelGGL((settle_kernel<kBF16, false>), g, b, lds, st, p);
     } else {
         if (mul) hipLaunchKernelGGL((settle_kernel<kF32, true>), g, b, 0, st, p);
         else hipLaunchKernelGGL((settle_kernel<kF32, false>), g, b, 0, st, p);
