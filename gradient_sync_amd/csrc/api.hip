@@ -419,6 +419,12 @@ dp_status_t run_fsdp(int k, int64_t m_local, int64_t d, int64_t f, const float *
             p.n_fwd = (int)((k * m_local / 32) * (f / 64));
             return hip_status(dps::launch_fsdp_step2(p, st));
         }
+        // with dx at the fixture sizes: the compile-time-sized step, each wave
+        // running a backward, a forward and a dx chain
+        if (want_dx && dps::fsdp_step2_ok(k, m_local, d, f) && dps::fsdp_step_k8_ok(p)) {
+            p.n_fwd = (int)((k * m_local / 32) * (f / 64));
+            return hip_status(dps::launch_fsdp_step2(p, st));
+        }
         return hip_status(dps::launch_fsdp_step(p, st));
     }
     if (fwd_fused) {

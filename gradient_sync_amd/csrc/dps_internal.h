@@ -84,6 +84,10 @@ bool fsdp_fwd_direct_ok(const FsdpFwd8 &p);
 // shapes, f a multiple of 64, d a multiple of 128 and at most 512. p.n_fwd =
 // (k*m/32)*(f/64), p.n_dx = 0.
 bool fsdp_step2_ok(int k, long long m, long long d, long long f);
+// The fixture sizes (K = 8, m = 128, d = f = 512) with 16-byte aligned
+// shards and outputs: the step as a compile-time-sized kernel, with dx = dy . W^T
+// as well when p.n_dx != 0 (launch_fsdp_step2 then takes it).
+bool fsdp_step_k8_ok(const FsdpStepParams &p);
 hipError_t launch_fsdp_step2(const FsdpStepParams &p, hipStream_t stream);
 
 // bf16 GEMM, row-major, fp32 accumulation: C[M,N] = A[M,Kd] * B[Kd,N] with

@@ -491,6 +491,7 @@ static_assert(K * (D * F / kPiece) == kGrid && R * F % kPiece == 0, "one piece o
 static_assert(D == 512, "one thread per k column of the x block");
 }
 
+template <bool DX>
 __global__ __launch_bounds__(512) void fsdp_step_k8_kernel(const FsdpStepParams p)
 {
     using namespace k8;
@@ -573,6 +574,23 @@ __global__ __launch_bounds__(512) void fsdp_step_k8_kernel(const FsdpStepParams 
     mfb(ba1, bb1);
     loadf(1, fb1);
     __builtin_amdgcn_sched_barrier(0);
+    // dx = dy . W^T (DX): wave w's partial of the dx tile's column half w % 2
+    // over the f quarter w / 2, in 4 chunks of 32 f. A k step pairs f0 + s
+    // with f0 + 16 + s (s = 0..15), so each lane's operands are 16 consecutive
+    // floats of one dy row and one W row: lane l loads row l % 32 at f0 + 16 (l / 32)
+    // with four 16-byte loads per operand.
+    const int fq = (w >> 1) * (F / 4), jd = jb * 64 + (w & 1) * FB;
+    const float *dyr = bw.dy[rf] + (it * FB + col) * F + fq + 16 * kh;
+    const float *wr = fw.b_shard[jd / R] + (jd % R + col) * F + fq + 16 * kh;
+    auto loadx = [&](int c, f32x4 (&da)[4], f32x4 (&db)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            da[u] = *reinterpret_cast<const f32x4 *>(dyr + c * 32 + 4 * u);
+            db[u] = *reinterpret_cast<const f32x4 *>(wr + c * 32 + 4 * u);
+        }
+    };
+    [[maybe_unused]] f32x4 da0[4], db0[4], da1[4], db1[4];
+    if constexpr (DX) loadx(0, da0, db0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) T[w][(8 * (q >> 2) + 4 * kh + (q & 3)) * FB + col] = accb[q];
     __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's block is in LDS
@@ -593,9 +611,23 @@ __global__ __launch_bounds__(512) void fsdp_step_k8_kernel(const FsdpStepParams 
 #pragma unroll
         for (int u = 0; u < kPiece / 4 / 512; ++u) wcp[u] = *reinterpret_cast<const f32x4 *>(src + (u * 512 + t) * 4);
     }
+    // with DX, the dx chain's chunks alternate with the forward chain's (two
+    // independent accumulators; each chunk's operands load behind the other
+    // chain's MFMAs)
+    [[maybe_unused]] f32tile::f32x16 accx = {};
+    auto mfx = [&](const f32x4 (&da)[4], const f32x4 (&db)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            accx = __builtin_amdgcn_mfma_f32_32x32x2f32(da[q >> 2][q & 3], db[q >> 2][q & 3], accx, 0, 0, 0);
+    };
     __builtin_amdgcn_sched_barrier(0);
     mff(0, fb0);
     loadf(2, fb0);
+    if constexpr (DX) {
+        loadx(1, da1, db1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfx(da0, db0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     mff(1, fb1);
     {
@@ -605,13 +637,33 @@ __global__ __launch_bounds__(512) void fsdp_step_k8_kernel(const FsdpStepParams 
             __builtin_nontemporal_store(wcp[u], reinterpret_cast<f32x4 *>(dst + (u * 512 + t) * 4));
     }
     loadf(3, fb1);
+    if constexpr (DX) {
+        loadx(2, da0, db0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfx(da1, db1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     mff(2, fb0);
+    if constexpr (DX) {
+        loadx(3, da1, db1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfx(da0, db0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     mff(3, fb1);
+    if constexpr (DX) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfx(da1, db1);
+    }
 #pragma unroll
     for (int q = 0; q < 16; ++q) Pf[w][q * 64 + lane] = accf[q];
     __syncthreads();
+    if constexpr (DX) {
+        // every forward chain is done with the x block: its LDS takes the dx partials
+        float *Px = Xs + w * (16 * 64);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) Px[q * 64 + lane] = accx[q];
+    }
 
     // 3. y tile: register q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32
     //    of column half ch; the quarters' partials in quarter order
@@ -635,6 +687,17 @@ __global__ __launch_bounds__(512) void fsdp_step_k8_kernel(const FsdpStepParams 
         }
         __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(
                                            &bw.dw_shard[c][(i0 - c * R + e / FB) * F + j0 + e % FB]));
+    }
+    if constexpr (DX) {
+        // 4. the dx tile, from the partials in the x block's LDS
+        __syncthreads();
+        // dx tile: the quarters' partials in quarter order, as the y tile
+        const int ch = t >> 8, q = (t >> 4) & 15, l = (t & 15) * 4;
+        f32x4 s = *reinterpret_cast<const f32x4 *>(&Xs[ch * (16 * 64) + q * 64 + l]);
+#pragma unroll
+        for (int h = 1; h < 4; ++h) s = s + *reinterpret_cast<const f32x4 *>(&Xs[(2 * h + ch) * (16 * 64) + q * 64 + l]);
+        const int i = 8 * (q >> 2) + 4 * (l >> 5) + (q & 3), j = l & 31;
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(&p.dx.c[rf][(it * FB + i) * D + jb * 64 + ch * FB + j]));
     }
 }
 
@@ -678,19 +741,29 @@ bool fsdp_step2_ok(int k, long long m, long long d, long long f)
 
 static bool aligned16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 
+bool fsdp_step_k8_ok(const FsdpStepParams &p)
+{
+    const int k = p.bwd.k;
+    bool ok = k == k8::K && p.fwd.nb == k && p.bwd.m == k8::M && p.bwd.d == k8::D && p.bwd.f == k8::F &&
+              p.bwd.R == k8::R;
+    for (int r = 0; ok && r < k; ++r) {
+        ok = aligned16(p.fwd.b_shard[r]) && aligned16(p.fwd.b_copy[r]) && aligned16(p.fwd.c[r]) &&
+             aligned16(p.bwd.dw_full[r]) && aligned16(p.bwd.dw_shard[r]);
+        if (p.n_dx != 0) ok = ok && aligned16(p.bwd.dy[r]) && aligned16(p.dx.c[r]);
+    }
+    return ok;
+}
+
 hipError_t launch_fsdp_step2(const FsdpStepParams &p, hipStream_t st)
 {
     const int k = p.bwd.k;
-    if (k < 1 || k > 8 || p.fwd.nb != k || p.n_dx != 0 ||
+    if (k < 1 || k > 8 || p.fwd.nb != k || (p.n_dx != 0 && !fsdp_step_k8_ok(p)) ||
         !fsdp_step2_ok(k, p.bwd.m, p.bwd.d, p.bwd.f) ||
         p.n_fwd != (k * p.bwd.m / FB) * (p.bwd.f / 64))
         return hipErrorInvalidValue;
-    bool fixed = k == k8::K && p.bwd.m == k8::M && p.bwd.d == k8::D && p.bwd.f == k8::F && p.bwd.R == k8::R;
-    for (int r = 0; fixed && r < k; ++r)
-        fixed = aligned16(p.fwd.b_shard[r]) && aligned16(p.fwd.b_copy[r]) && aligned16(p.fwd.c[r]) &&
-                aligned16(p.bwd.dw_full[r]) && aligned16(p.bwd.dw_shard[r]);
-    if (fixed) {
-        hipLaunchKernelGGL(fsdp_step_k8_kernel, dim3(k8::kGrid), dim3(512), 0, st, p);
+    if (fsdp_step_k8_ok(p)) {
+        if (p.n_dx != 0) hipLaunchKernelGGL(fsdp_step_k8_kernel<true>, dim3(k8::kGrid), dim3(512), 0, st, p);
+        else hipLaunchKernelGGL(fsdp_step_k8_kernel<false>, dim3(k8::kGrid), dim3(512), 0, st, p);
         return hipGetLastError();
     }
     const long long n_bwd = (p.bwd.d / FB) * (p.bwd.f / FB);
