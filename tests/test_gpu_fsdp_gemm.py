@@ -222,6 +222,42 @@ def test_fsdp_step_outputs_not_16_byte_aligned():
     check_fsdp(fx["x"], fx["w"], fx["dy"], k)
 
 
+def test_fsdp_step_with_dx_outputs_not_16_byte_aligned():
+    """With dx at the fixture's sizes: all outputs 16-byte aligned run the
+    compile-time-sized kernel with a dx chain per wave, dx 4 bytes off runs the
+    runtime-shaped step kernel. W copies, dW and its shards have the same bits
+    either way (the same backward chains); y and dx (other k orders) are each
+    within the fp32 summation bound of the fp64 oracle."""
+    say("fsdp step with dx, dx aligned and 4 bytes off")
+    k, m, d, f = 8, 1024, 512, 512
+    fx = gen.fsdp_fixture(seed=6, k=k)
+    ml, R = m // k, d // k
+    xl = [fx["x"][r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    dyl = [fx["dy"][r * ml:(r + 1) * ml].contiguous().to(DEV) for r in range(k)]
+    ws = [s.to(DEV) for s in shard_rows(fx["w"], k)]
+    outs = []
+    for off in (0, 1):
+        o = _fsdp_outputs_at(0, k, ml, d, f, R)
+        dx = [torch.full((ml * d + off,), float("nan"), device=DEV)[off:].view(ml, d) for _ in range(k)]
+        dps.dp_fsdp_layer(xl, ws, dyl, o["wf"], o["y"], o["dwf"], o["dws"], dx_local=dx)
+        torch.cuda.synchronize()
+        o["dx"] = dx
+        outs.append({n: [to_np(t) for t in ts] for n, ts in o.items()})
+    for n in ("wf", "dwf", "dws"):
+        for r in range(k):
+            assert bits_equal(outs[0][n][r], outs[1][n][r]), (n, r)
+    host_xl = [to_np(t) for t in xl]
+    host_dy = [to_np(t) for t in dyl]
+    wn = fx["w"].numpy()
+    wt = np.ascontiguousarray(wn.T)
+    for got in outs:
+        for r in range(k):
+            ref, ab = oracle.gemm_f64(host_xl[r], wn)
+            assert np.all(np.abs(got["y"][r].astype(np.float64) - ref) <= gamma(d + 2) * ab)
+            ref, ab = oracle.gemm_f64(host_dy[r], wt)
+            assert np.all(np.abs(got["dx"][r].astype(np.float64) - ref) <= gamma(f + 2) * ab)
+
+
 def test_fsdp_forward_only():
     fx = gen.fsdp_fixture(seed=7, k=8, m=256, d=128, f=64)
     got, host = run_fsdp(fx["x"], fx["w"], fx["dy"], 8, backward=False)
