@@ -493,6 +493,12 @@ def bench_fsdp(args):
                          "unit_flops": "2 GEMMs of 2*m_local*d*f per rank (y = x W, dW = x^T dy), "
                                        "K=8: 1,073,741,824 per step; the AllGather and "
                                        "ReduceScatter bytes are folded into the operand loads"},
+            "roofline_with_dx": {"bound": "mfma", "kernel": "fsdp_step_k8_kernel with dx (each wave a backward, a forward and a dx = dy W^T MFMA chain)",
+                                 "achieved": res["step_with_dx"]["effective_tflops"], "peak": MFMA_F32_TFLOPS,
+                                 "unit": "TFLOP/s",
+                                 "frac": round(res["step_with_dx"]["effective_tflops"] / MFMA_F32_TFLOPS, 4),
+                                 "traffic": None,
+                                 "unit_flops": "3 GEMMs of 2*m_local*d*f per rank, K=8: 1,610,612,736 per step"},
             "config": {"workload": "K=8, x[1024,512] N(0,1), w[512,512] N(0,0.02^2), "
                                    "dy[1024,512] N(0,1), fp32"}}
     if not args.no_cpu_baseline:
