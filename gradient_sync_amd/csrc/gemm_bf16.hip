@@ -462,13 +462,70 @@ __global__ __launch_bounds__(W4_NT) void gemm_bf16_w4_kernel(const unsigned shor
 // order as the 32x32x16 kernels, and the results are the same bits.
 // Measured at 8192^3: 724 us (1518 TFLOP/s) against 804 us for the
 // register-staged kernel and 673 us for the vendor library on the same GPU.
+// The MFMAs take B's fragment first, so each lane ends with four consecutive
+// columns of a row of C per block and C leaves in 16-byte stores (store_c_tr).
 // An n-contiguous B takes the kernel after this one.
 constexpr int D_NT = 256, D_TK = 64;
 constexpr int D_ELEMS = TM * D_TK;          // one operand's stage: 16,384 bf16 = 32 KiB
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// C of one wave's 128x128 block (rows wi*128.., columns wj*128.. of the tile at
+// rC) from accumulators holding transposed 16x16 blocks: the direct-to-LDS
+// kernels pass B's fragment as the MFMA's first operand and A's as its second,
+// which yields the same products and sums (bf16 products are exact in fp32 and
+// each output element adds its 32 products in the same order) with register r
+// of block (a, b) in lane l holding C[16a + l%16][16b + 4(l/16) + r]: four
+// consecutive columns of one row. With C16 (C 16-byte aligned, N a multiple of
+// 8) pairs of values become bf16 pairs in one v_cvt_pk_bf16_f32 (round to
+// nearest even, NaN quieted with sign and upper payload kept: the same bits as
+// f32_to_bf16_rne for every one of the 2^32 inputs, checked exhaustively on the
+// GPU), and v_permlane16_swap_b32 trades the halves of blocks b and b+1 between
+// lane rows g and g^1 of 16, so that each lane holds 8 consecutive columns of
+// one row: one 16-byte store per two blocks, 32 per lane instead of 256 2-byte
+// stores (8192^3: 733 -> 720 us; 4096 x 8192 x 1024: 71 -> 62 us). Otherwise
+// 2-byte stores of any alignment.
+template <bool C16>
+__device__ __forceinline__ void store_c_tr(const f32x4 (&acc)[8][8], const __amdgpu_buffer_rsrc_t rC,
+                                           int N, int wi, int wj, int lane)
+{
+    const int row = wi * 128 + (lane & 15), g = lane >> 4;
+    if constexpr (C16) {
+        const int coff = (row * N + wj * 128 + 16 * (g & 1) + 8 * (g >> 1)) * 2;
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; b += 2) {
+                const f32x2 x0 = {acc[a][b][0], acc[a][b][1]}, x1 = {acc[a][b][2], acc[a][b][3]};
+                const f32x2 y0 = {acc[a][b + 1][0], acc[a][b + 1][1]}, y1 = {acc[a][b + 1][2], acc[a][b + 1][3]};
+                // rows g even keep block b's pair and receive the next row's;
+                // rows g odd receive the previous row's pair of block b + 1
+                const auto s0 = __builtin_amdgcn_permlane16_swap(
+                    __builtin_bit_cast(unsigned, __builtin_convertvector(x0, bf16x2)),
+                    __builtin_bit_cast(unsigned, __builtin_convertvector(y0, bf16x2)), false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(
+                    __builtin_bit_cast(unsigned, __builtin_convertvector(x1, bf16x2)),
+                    __builtin_bit_cast(unsigned, __builtin_convertvector(y1, bf16x2)), false, false);
+                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rC, coff, (a * 16 * N + b * 16) * 2, 0);
+            }
+    } else {
+        const int coff = (row * N + wj * 128 + 4 * g) * 2;
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[a][b][r]), rC, coff,
+                                                          (a * 16 * N + b * 16 + r) * 2, 0);
+    }
+}
+
+template <bool C16>
 __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned short *__restrict__ A,
                                                              const unsigned short *__restrict__ B,
                                                              unsigned short *__restrict__ C, int M,
@@ -525,7 +582,7 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{};
     auto mf = [&](int set, int a, int b) __attribute__((always_inline)) {
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[set][a], bf[set][b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[set][b], af[set][a], acc[a][b], 0, 0, 0);
     };
 
     const int stages = Kd / D_TK;
@@ -568,21 +625,19 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
         stage(1, min((s + 3) * D_TK, last));
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    // C through a buffer descriptor on the tile's first element: one per-lane
-    // offset register, the block and row offsets as scalar offsets (256 N
-    // bytes from the base fit 31 bits: checked by the launcher). D register r
-    // of a 16x16 block: row 4 (l / 16) + r, column l % 16.
-    const __amdgpu_buffer_rsrc_t rC =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
-    const int coff = ((wi * 128 + 4 * (lane >> 4)) * N + wj * 128 + (lane & 15)) * 2;
+    // the accumulators named as accumulation registers where the loop ends:
+    // without this the compiler keeps some of them in architectural registers
+    // for the epilogue's conversions and copies them around every loop pass
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[a][b][r]), rC, coff,
-                                                      ((a * 16 + r) * N + b * 16) * 2, 0);
+        for (int b = 0; b < 8; ++b) asm volatile("" : "+a"(acc[a][b]));
+    // C through a buffer descriptor on the tile's first element: one per-lane
+    // offset register, the block and row offsets as scalar offsets (256 N
+    // bytes from the base fit 31 bits: checked by the launcher)
+    const __amdgpu_buffer_rsrc_t rC =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
+    store_c_tr<C16>(acc, rC, N, wi, wj, lane);
 }
 
 // ------------------------------------------- 4-wave direct-to-LDS kernel, B stored [Kd, N]
@@ -623,7 +678,8 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
 // same bits. Measured at 8192^3: 718-733 us (1500-1531 TFLOP/s) against
 // 759-768 us for the 32x32x16 form of this kernel on the same GPUs (which
 // holds a lower clock), level with it from kk = 1024 to 1152 and 3-6% faster
-// from 2048.
+// from 2048. Like the kernel above, its MFMAs take B's fragment first and C
+// leaves in 16-byte stores (store_c_tr).
 
 __device__ __forceinline__ bf16x8 lds_read_b128(unsigned addr)
 {
@@ -652,6 +708,7 @@ __device__ __forceinline__ i16x4 lds_read_tr_b64(unsigned addr)
                  : "+v"(af[S][0]), "+v"(af[S][1]), "+v"(af[S][2]), "+v"(af[S][3]),             \
                    "+v"(af[S][4]), "+v"(af[S][5]), "+v"(af[S][6]), "+v"(af[S][7]), "+v"(bq[Q]))
 
+template <bool C16>
 __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned short *__restrict__ A,
                                                               const unsigned short *__restrict__ B,
                                                               unsigned short *__restrict__ C, int M,
@@ -756,7 +813,7 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned sho
             if (i >= 2 && i < 32 && (i - 2) % 3 == 0) dtl(buf ^ 1, k1, 6 + (i - 2) / 3);
             if (i >= 112 && (i - 112) % 3 == 0) dtl(buf, k2, (i - 112) / 3);
             asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-                         : "+a"(acc[j][b]) : "v"(af[ks][j]), "v"(bq[G]));
+                         : "+a"(acc[j][b]) : "v"(bq[G]), "v"(af[ks][j]));
             W4_FENCE();
         }
         if (G == 13) {
@@ -795,20 +852,11 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned sho
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bq[1]));
     __builtin_amdgcn_s_waitcnt(0x0F70);
     DN_ACC_FENCE();
-    // C through a buffer descriptor on the tile's first element. D register r
-    // of a 16x16 block: row 4 (l / 16) + r, column l % 16.
+    // C through a buffer descriptor on the tile's first element
     const __amdgpu_buffer_rsrc_t rC =
         __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
     const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const int coff = ((wi * 128 + 4 * (el >> 4)) * N + wj * 128 + (el & 15)) * 2;
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[a][b][r]), rC, coff,
-                                                      ((a * 16 + r) * N + b * 16) * 2, 0);
+    store_c_tr<C16>(acc, rC, N, wi, wj, el);
 }
 #undef DN_ACC_ROW
 #undef DN_ACC_FENCE
@@ -897,17 +945,28 @@ hipError_t launch_layout(const void *a, const void *b, void *c, long long M, lon
     const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
                     Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL &&
                     (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
-    // an even number of k stages: the direct-to-LDS kernels (their C stores
-    // are 16-bit buffer stores of any alignment; 512 N bytes cover a tile's
-    // rows of C)
+    // an even number of k stages: the direct-to-LDS kernels (C in 16-byte
+    // stores where C is 16-byte aligned and N a multiple of 8, else in 2-byte
+    // stores; 512 N bytes cover a tile's rows of C)
+    const bool c16 = ((uintptr_t)c & 15) == 0 && N % 8 == 0;
+    const auto *A = (const unsigned short *)a;
+    const auto *B = (const unsigned short *)b;
+    auto *C = (unsigned short *)c;
+    const dim3 grid((unsigned)(tm * tn));
     if (w4 && BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
-        hipLaunchKernelGGL(gemm_bf16_w4dn_kernel, dim3((unsigned)(tm * tn)), dim3(D_NT), 0, st,
-                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
-                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+        if (c16)
+            hipLaunchKernelGGL(gemm_bf16_w4dn_kernel<true>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
+                               (int)Kd, (int)tm, (int)tn);
+        else
+            hipLaunchKernelGGL(gemm_bf16_w4dn_kernel<false>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
+                               (int)Kd, (int)tm, (int)tn);
     } else if (w4 && !BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
-        hipLaunchKernelGGL(gemm_bf16_w4d_kernel, dim3((unsigned)(tm * tn)), dim3(D_NT), 0, st,
-                           (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
-                           (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
+        if (c16)
+            hipLaunchKernelGGL(gemm_bf16_w4d_kernel<true>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
+                               (int)Kd, (int)tm, (int)tn);
+        else
+            hipLaunchKernelGGL(gemm_bf16_w4d_kernel<false>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
+                               (int)Kd, (int)tm, (int)tn);
     } else if (w4) {
         hipLaunchKernelGGL(gemm_bf16_w4_kernel<BKN>, dim3((unsigned)(tm * tn)), dim3(W4_NT), 0, st,
                            (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,

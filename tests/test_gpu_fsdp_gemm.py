@@ -405,12 +405,13 @@ def _offset_copy(t, off):
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
-@pytest.mark.parametrize("off", [1, 3, 8])
+@pytest.mark.parametrize("off", [1, 3, 4, 8])
 def test_gemm_bf16_output_at_any_element_offset(layout, off):
     """The 4-wave direct-to-LDS kernels (both layouts, an even number of k
     stages) with aligned operands and C at an element offset that
-    is not 16-byte aligned: the same bits as an aligned C, and the elements
-    around C untouched."""
+    is not 16-byte aligned (2-byte stores; 4 elements: 8-byte aligned) or is
+    (8 elements: 16-byte stores): the same bits as C at the start of its
+    allocation, and the elements around C untouched."""
     m = n = 512
     kk = 1024
     say(f"gemm bf16 output offset {layout} off={off}")
