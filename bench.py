@@ -1006,13 +1006,13 @@ def bench_gemm(args):
             "value": res["dp_gemm_bf16"]["tflops"], "results": res,
             "timing": "interleaved rounds of 8 back-to-back calls between two events, "
                       "after ~1 s of warm-up; median per call",
-            "roofline": {"bound": "mfma", "kernel": "gemm_bf16_w4dn_kernel (B stored [k, n], operands loaded straight into LDS, transposing LDS reads, 16x16x32 MFMAs)",
+            "roofline": {"bound": "mfma", "kernel": "gemm_bf16_w4dn_kernel (B stored [k, n], operands loaded straight into LDS, transposing LDS reads, 16x16x32 MFMAs, C in 16-byte stores)",
                          "achieved": res["dp_gemm_bf16"]["tflops"],
                          "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": res["dp_gemm_bf16"]["frac_of_peak"], "traffic": None},
             "roofline_b_nk": {"bound": "mfma",
                               "kernel": "gemm_bf16_w4d_kernel (B stored [n, k], operands loaded "
-                                        "straight into LDS, 16x16x32 MFMAs)",
+                                        "straight into LDS, 16x16x32 MFMAs, C in 16-byte stores)",
                               "achieved": res["dp_gemm_bf16_b_nk"]["tflops"],
                               "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": res["dp_gemm_bf16_b_nk"]["frac_of_peak"], "traffic": None},
