@@ -297,6 +297,7 @@ constexpr int W4_HP = TM / W4_RPP;          // passes per operand tile (8)
 constexpr int W4_KS = W4_TK / 16;           // MFMA k steps per stage (4)
 constexpr int W4_B = 4;                     // 32x32 MFMA blocks per wave side (128 = 4 x 32)
 constexpr long long kW4MinK = 1024;         // shortest k range given to the 4-wave kernel
+constexpr long long kNtcMinK = 8192;        // k range from which C leaves in nontemporal stores
 static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of MFMAs");
 
 // keeps the compiler's scheduler from moving instructions across it, so the
@@ -487,8 +488,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // lane rows g and g^1 of 16, so that each lane holds 8 consecutive columns of
 // one row: one 16-byte store per two blocks, 32 per lane instead of 256 2-byte
 // stores (8192^3: 733 -> 720 us; 4096 x 8192 x 1024: 71 -> 62 us). Otherwise
-// 2-byte stores of any alignment.
-template <bool C16>
+// 2-byte stores of any alignment. NTC marks the 16-byte stores nontemporal:
+// faster where the k range is long (8192^3: 1.1-2.2% for both layouts), slower
+// where C's writes weigh more (kk = 4096: +1-1.7% for B [k, n]; kk = 2048: +6%;
+// kk = 1024: +11%), so the launcher sets it from kk = 8192.
+template <bool C16, bool NTC>
 __device__ __forceinline__ void store_c_tr(const f32x4 (&acc)[8][8], const __amdgpu_buffer_rsrc_t rC,
                                            int N, int wi, int wj, int lane)
 {
@@ -510,7 +514,7 @@ __device__ __forceinline__ void store_c_tr(const f32x4 (&acc)[8][8], const __amd
                     __builtin_bit_cast(unsigned, __builtin_convertvector(x1, bf16x2)),
                     __builtin_bit_cast(unsigned, __builtin_convertvector(y1, bf16x2)), false, false);
                 const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rC, coff, (a * 16 * N + b * 16) * 2, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rC, coff, (a * 16 * N + b * 16) * 2, NTC ? 2 : 0);
             }
     } else {
         const int coff = (row * N + wj * 128 + 4 * g) * 2;
@@ -525,7 +529,7 @@ __device__ __forceinline__ void store_c_tr(const f32x4 (&acc)[8][8], const __amd
     }
 }
 
-template <bool C16>
+template <bool C16, bool NTC>
 __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned short *__restrict__ A,
                                                              const unsigned short *__restrict__ B,
                                                              unsigned short *__restrict__ C, int M,
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4d_kernel(const unsigned shor
     // bytes from the base fit 31 bits: checked by the launcher)
     const __amdgpu_buffer_rsrc_t rC =
         __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
-    store_c_tr<C16>(acc, rC, N, wi, wj, lane);
+    store_c_tr<C16, NTC>(acc, rC, N, wi, wj, lane);
 }
 
 // ------------------------------------------- 4-wave direct-to-LDS kernel, B stored [Kd, N]
@@ -708,7 +712,7 @@ __device__ __forceinline__ i16x4 lds_read_tr_b64(unsigned addr)
                  : "+v"(af[S][0]), "+v"(af[S][1]), "+v"(af[S][2]), "+v"(af[S][3]),             \
                    "+v"(af[S][4]), "+v"(af[S][5]), "+v"(af[S][6]), "+v"(af[S][7]), "+v"(bq[Q]))
 
-template <bool C16>
+template <bool C16, bool NTC>
 __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned short *__restrict__ A,
                                                               const unsigned short *__restrict__ B,
                                                               unsigned short *__restrict__ C, int M,
@@ -856,7 +860,7 @@ __global__ __launch_bounds__(D_NT) void gemm_bf16_w4dn_kernel(const unsigned sho
     const __amdgpu_buffer_rsrc_t rC =
         __builtin_amdgcn_make_buffer_rsrc((void *)(C + m0 * N + n0), (short)0, 0x7fffffff, 0x00020000);
     const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    store_c_tr<C16>(acc, rC, N, wi, wj, el);
+    store_c_tr<C16, NTC>(acc, rC, N, wi, wj, el);
 }
 #undef DN_ACC_ROW
 #undef DN_ACC_FENCE
@@ -946,27 +950,21 @@ hipError_t launch_layout(const void *a, const void *b, void *c, long long M, lon
                     Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL &&
                     (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
     // an even number of k stages: the direct-to-LDS kernels (C in 16-byte
-    // stores where C is 16-byte aligned and N a multiple of 8, else in 2-byte
-    // stores; 512 N bytes cover a tile's rows of C)
-    const bool c16 = ((uintptr_t)c & 15) == 0 && N % 8 == 0;
+    // stores where C is 16-byte aligned and N a multiple of 8, nontemporal from
+    // kk = 8192, else in 2-byte stores; 512 N bytes cover a tile's rows of C)
+    const bool c16 = ((uintptr_t)c & 15) == 0 && N % 8 == 0, ntc = Kd >= kNtcMinK;
     const auto *A = (const unsigned short *)a;
     const auto *B = (const unsigned short *)b;
     auto *C = (unsigned short *)c;
     const dim3 grid((unsigned)(tm * tn));
     if (w4 && BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
-        if (c16)
-            hipLaunchKernelGGL(gemm_bf16_w4dn_kernel<true>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
-                               (int)Kd, (int)tm, (int)tn);
-        else
-            hipLaunchKernelGGL(gemm_bf16_w4dn_kernel<false>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
-                               (int)Kd, (int)tm, (int)tn);
+        auto *kern = c16 ? (ntc ? gemm_bf16_w4dn_kernel<true, true> : gemm_bf16_w4dn_kernel<true, false>)
+                         : gemm_bf16_w4dn_kernel<false, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
     } else if (w4 && !BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
-        if (c16)
-            hipLaunchKernelGGL(gemm_bf16_w4d_kernel<true>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
-                               (int)Kd, (int)tm, (int)tn);
-        else
-            hipLaunchKernelGGL(gemm_bf16_w4d_kernel<false>, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N,
-                               (int)Kd, (int)tm, (int)tn);
+        auto *kern = c16 ? (ntc ? gemm_bf16_w4d_kernel<true, true> : gemm_bf16_w4d_kernel<true, false>)
+                         : gemm_bf16_w4d_kernel<false, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
     } else if (w4) {
         hipLaunchKernelGGL(gemm_bf16_w4_kernel<BKN>, dim3((unsigned)(tm * tn)), dim3(W4_NT), 0, st,
                            (const unsigned short *)a, (const unsigned short *)b, (unsigned short *)c,
