@@ -25,7 +25,7 @@
 // Five designs over a tile of C:
 //
 // * gemm_bf16_w4d_kernel (the default for B stored [N, Kd] where M and N are
-//   multiples of 256 and Kd a multiple of 128, at least 1024): the operands go
+//   multiples of 256 and Kd a multiple of 128, at least 256): the operands go
 //   from global memory straight into LDS, 4 waves of 128x128 with 16x16x32
 //   MFMAs; described at the kernel.
 //
@@ -84,6 +84,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Padded LDS row of an n-contiguous B stage: 256 + 32 elements = 576 bytes, so
@@ -296,7 +298,8 @@ constexpr int W4_RPP = W4_NT / W4_CH;       // rows loaded per pass (32)
 constexpr int W4_HP = TM / W4_RPP;          // passes per operand tile (8)
 constexpr int W4_KS = W4_TK / 16;           // MFMA k steps per stage (4)
 constexpr int W4_B = 4;                     // 32x32 MFMA blocks per wave side (128 = 4 x 32)
-constexpr long long kW4MinK = 1024;         // shortest k range given to the 4-wave kernel
+constexpr long long kW4MinK = 1024;         // shortest k range given to the register-staged 4-wave kernel
+constexpr long long kDirectMinK = 256;      // shortest k range given to the direct-to-LDS kernels
 constexpr long long kNtcMinK = 8192;        // k range from which C leaves in nontemporal stores
 static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of MFMAs");
 
@@ -470,8 +473,6 @@ constexpr int D_NT = 256, D_TK = 64;
 constexpr int D_ELEMS = TM * D_TK;          // one operand's stage: 16,384 bf16 = 32 KiB
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // C of one wave's 128x128 block (rows wi*128.., columns wj*128.. of the tile at
@@ -939,29 +940,34 @@ hipError_t launch_layout(const void *a, const void *b, void *c, long long M, lon
     if (M > 0x7fffffffLL || N > 0x7fffffffLL || Kd > 0x7fffffffLL) return hipErrorInvalidValue;
     const long long tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
     if (tm * tn > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // the 4-wave kernel: whole tiles only, byte offsets from its buffer
+    // the 4-wave kernels: whole tiles only, byte offsets from their buffer
     // descriptors' bases (a tile's 256 rows of A, 512 * Kd bytes; an
     // n-contiguous B's Kd rows, 2 * Kd * N bytes) within 31 bits, and a k range
     // long enough that the main loop outweighs the per-tile prologue and
     // epilogue, which one wave per SIMD cannot overlap with another workgroup's
-    // MFMAs (measured: 1.2x the 8-wave kernel at 8192^3, 1.08x at kk = 1536,
-    // 1.02-1.07x at kk = 1024, 0.93x at kk = 512, 0.8x at kk = 256)
-    const bool w4 = variant == kGemmFast && M % TM == 0 && N % TN == 0 && Kd % W4_TK == 0 &&
-                    Kd >= kW4MinK && 512 * Kd < 0x7fffffffLL &&
-                    (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
-    // an even number of k stages: the direct-to-LDS kernels (C in 16-byte
-    // stores where C is 16-byte aligned and N a multiple of 8, nontemporal from
-    // kk = 8192, else in 2-byte stores; 512 N bytes cover a tile's rows of C)
+    // MFMAs. The register-staged kernel from kk = 1024 (measured against the
+    // 8-wave kernel: 1.2x at 8192^3, 1.08x at kk = 1536, 1.02-1.07x at 1024,
+    // 0.93x at 512, 0.8x at 256); the direct-to-LDS kernels (an even number of
+    // k stages) from kk = 256 (at 4096 x 14336: B [k, n] 0.87x the 8-wave
+    // kernel's time at kk = 256, 0.83x at 384, 0.81x at 512; B [n, k] level
+    // at 256, 0.94x at 384, 0.88x at 512; at kk = 128 B [n, k] is 1.12x)
+    const bool whole = variant == kGemmFast && M % TM == 0 && N % TN == 0 && 512 * Kd < 0x7fffffffLL &&
+                       (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
+    const bool w4 = whole && Kd % W4_TK == 0 && Kd >= kW4MinK;
+    const bool direct = whole && Kd % (2 * D_TK) == 0 && Kd >= kDirectMinK && 512 * N < 0x7fffffffLL;
+    // the direct-to-LDS kernels: C in 16-byte stores where C is 16-byte aligned
+    // and N a multiple of 8, nontemporal from kk = 8192, else in 2-byte stores
+    // (512 N bytes cover a tile's rows of C)
     const bool c16 = ((uintptr_t)c & 15) == 0 && N % 8 == 0, ntc = Kd >= kNtcMinK;
     const auto *A = (const unsigned short *)a;
     const auto *B = (const unsigned short *)b;
     auto *C = (unsigned short *)c;
     const dim3 grid((unsigned)(tm * tn));
-    if (w4 && BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
+    if (direct && BKN) {
         auto *kern = c16 ? (ntc ? gemm_bf16_w4dn_kernel<true, true> : gemm_bf16_w4dn_kernel<true, false>)
                          : gemm_bf16_w4dn_kernel<false, false>;
         hipLaunchKernelGGL(kern, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);
-    } else if (w4 && !BKN && Kd % (2 * D_TK) == 0 && 512 * N < 0x7fffffffLL) {
+    } else if (direct && !BKN) {
         auto *kern = c16 ? (ntc ? gemm_bf16_w4d_kernel<true, true> : gemm_bf16_w4d_kernel<true, false>)
                          : gemm_bf16_w4d_kernel<false, false>;
         hipLaunchKernelGGL(kern, grid, dim3(D_NT), 0, st, A, B, C, (int)M, (int)N, (int)Kd, (int)tm, (int)tn);

@@ -346,17 +346,18 @@ def test_gemm_bf16_8192_sampled():
 @pytest.mark.parametrize("m,n,kk", [(256, 256, 2048), (512, 768, 2112), (1024, 256, 4096),
                                     (512, 512, 1024), (256, 768, 1472),
                                     (768, 512, 320), (2048, 2048, 64), (256, 256, 960),
-                                    (264, 280, 1032)])
+                                    (264, 280, 1032), (512, 768, 256), (768, 256, 640),
+                                    (256, 512, 128)])
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
-    """Whole 256x256 tiles with kk a multiple of 64 and >= 1024 run a 4-wave
-    kernel (with an even number of depth-64 stages the direct-to-LDS ones:
-    16x16x32 MFMAs for both, B's fragments assembled with transposing LDS
-    reads for B stored [kk,n]; with an odd number the register-staged one);
+    """Whole 256x256 tiles with an even number of depth-64 k stages and kk >=
+    256 run the direct-to-LDS 4-wave kernels (16x16x32 MFMAs for both, B's
+    fragments assembled with transposing LDS reads for B stored [kk,n]); with
+    an odd number and kk >= 1024 the register-staged 4-wave kernel;
     the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
     B stored [kk,n] (transposing LDS reads) and [n,kk] alike, so all six agree
-    bit for bit (shorter k ranges and edge tiles take the 8-wave kernel on
-    every path). The default result is also checked against the oracle
+    bit for bit (shorter or odd k ranges and edge tiles take the 8-wave kernel
+    on every path). The default result is also checked against the oracle
     (exactly on small-integer inputs, within the fp32 summation bound on N(0,1)
     inputs); an odd number of k stages (2112 = 33 x 64) and grids that are not a
     multiple of 8 tiles are among the cases."""
@@ -406,21 +407,22 @@ def _offset_copy(t, off):
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("off", [1, 3, 4, 8])
-def test_gemm_bf16_output_at_any_element_offset(layout, off):
+@pytest.mark.parametrize("opts", [{}, {"lean": True}, {"share_cu": True}], ids=["w4", "lean", "share_cu"])
+def test_gemm_bf16_output_at_any_element_offset(layout, off, opts):
     """The 4-wave direct-to-LDS kernels (both layouts, an even number of k
-    stages) with aligned operands and C at an element offset that
-    is not 16-byte aligned (2-byte stores; 4 elements: 8-byte aligned) or is
-    (8 elements: 16-byte stores): the same bits as C at the start of its
-    allocation, and the elements around C untouched."""
+    stages) and the 8-wave variants with aligned operands and C at an element
+    offset that is not 16-byte aligned (2-byte stores; 4 elements: 8-byte
+    aligned) or is (8 elements: 16-byte stores): the same bits as C at the
+    start of its allocation, and the elements around C untouched."""
     m = n = 512
     kk = 1024
-    say(f"gemm bf16 output offset {layout} off={off}")
+    say(f"gemm bf16 output offset {layout} off={off} {opts}")
     a, b = gen.gemm_bf16_inputs(13, m, n, kk, device=DEV, b_layout=layout)
     want = run_gemm(a, b, layout)
     c_full = torch.empty((m * n + off + 8,), dtype=torch.bfloat16, device=DEV)
     c_full.view(torch.int16).fill_(0x5A5A)
     c = c_full[off:off + m * n].view(m, n)
-    dps.dp_gemm_bf16_ex(a, b, c, b_layout=layout)
+    dps.dp_gemm_bf16_ex(a, b, c, b_layout=layout, **opts)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(c), _bits(want))
     guard = np.concatenate([to_np(c_full[:off]), to_np(c_full[off + m * n:])])
