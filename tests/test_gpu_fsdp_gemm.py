@@ -347,7 +347,7 @@ def test_gemm_bf16_8192_sampled():
                                     (512, 512, 1024), (256, 768, 1472),
                                     (768, 512, 320), (2048, 2048, 64), (256, 256, 960),
                                     (264, 280, 1032), (512, 768, 256), (768, 256, 640),
-                                    (256, 512, 128)])
+                                    (256, 512, 128), (256, 512, 8192)])
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     """Whole 256x256 tiles with an even number of depth-64 k stages and kk >=
     256 run the direct-to-LDS 4-wave kernels (16x16x32 MFMAs for both, B's
@@ -359,7 +359,8 @@ def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     bit for bit (shorter or odd k ranges and edge tiles take the 8-wave kernel
     on every path). The default result is also checked against the oracle
     (exactly on small-integer inputs, within the fp32 summation bound on N(0,1)
-    inputs); an odd number of k stages (2112 = 33 x 64) and grids that are not a
+    inputs); kk = 8192 (C in nontemporal stores), an odd number of k stages
+    (2112 = 33 x 64) and grids that are not a
     multiple of 8 tiles are among the cases."""
     say(f"gemm bf16 variants {m}x{n}x{kk}")
     a, b_kn = gen.gemm_bf16_inputs(11, m, n, kk, device=DEV, b_layout="kn")
