@@ -969,7 +969,8 @@ def bench_gemm(args):
     (C = A B^T, the direct-to-LDS kernel), and the two 8-wave variants that
     leave room for a sync workgroup on each CU, against the MFMA roofline; the
     vendor library GEMM (torch.matmul, hipBLASLt) on the same operands in both
-    layouts for context. The variants
+    layouts for context; then the same kernels on a short k range (4096 x
+    14336 x 256, a weight-gradient GEMM over 256 tokens). The variants
     are timed in interleaved rounds of 8 back-to-back calls after ~1 s of
     warm-up, so that they see the same clock and power state."""
     import torch
@@ -1017,10 +1018,34 @@ def bench_gemm(args):
                               "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": res["dp_gemm_bf16_b_nk"]["frac_of_peak"], "traffic": None},
             "config": {"workload": "A [8192, 8192], B [8192, 8192] bf16 ~ N(0,1), row-major"}}
+    # a short k range (a weight-gradient GEMM over 256 tokens: 4096 x 14336,
+    # kk = 256), where writing C weighs most: the default (direct-to-LDS) kernel
+    # against the 8-wave one (DP_LAUNCH_LEAN) and the library, both layouts
+    del a, b, b_nk, c
+    ms, ns, ks = 4096, 14336, 256
+    a, b = gen.gemm_bf16_inputs(6, ms, ns, ks, device="cuda")
+    b_nk = b.t().contiguous()
+    c = torch.empty(ms, ns, dtype=torch.bfloat16, device="cuda")
+    fns = {"dp_gemm_bf16": lambda: dps.dp_gemm_bf16(a, b, c),
+           "dp_gemm_bf16_lean": lambda: dps.dp_gemm_bf16_ex(a, b, c, lean=True),
+           "library_torch_matmul": lambda: torch.matmul(a, b, out=c),
+           "dp_gemm_bf16_b_nk": lambda: dps.dp_gemm_bf16_ex(a, b_nk, c, b_layout="nk"),
+           "dp_gemm_bf16_b_nk_lean": lambda: dps.dp_gemm_bf16_ex(a, b_nk, c, b_layout="nk", lean=True),
+           "library_torch_matmul_b_nk": lambda: torch.matmul(a, b_nk.t(), out=c)}
+    times = {name: [] for name in fns}
+    for _ in range(8):
+        for name, fn in fns.items():
+            times[name].extend(_time_batch_ms(fn, batch=8, warm=2, reps=1))
+    line["short_k"] = {"workload": f"A [{ms}, {ks}], B [{ks}, {ns}] (or [{ns}, {ks}]) bf16, C [{ms}, {ns}]",
+                       "results": {name: {"median_us": round(statistics.median(v) * 1e3, 2),
+                                          "tflops": round(2 * ms * ns * ks / (statistics.median(v) * 1e-3) / 1e12, 1)}
+                                   for name, v in times.items()}}
+    del a, b, b_nk, c
     if not args.no_cpu_baseline:
         import numpy as np
         import oracle
         cores = host_cores()
+        a, b = gen.gemm_bf16_inputs(5, m, n, kk, device="cuda")
         ab, bb = bf16_bits(a), bf16_bits(b)
         rng = np.random.default_rng(0)
         rows = rng.integers(0, m, 256).astype(np.int64)

@@ -25,13 +25,13 @@
 // Five designs over a tile of C:
 //
 // * gemm_bf16_w4d_kernel (the default for B stored [N, Kd] where M and N are
-//   multiples of 256 and Kd a multiple of 128, at least 256): the operands go
+//   multiples of 256 and Kd a multiple of 128, at least 384): the operands go
 //   from global memory straight into LDS, 4 waves of 128x128 with 16x16x32
 //   MFMAs; described at the kernel.
 //
-// * gemm_bf16_w4dn_kernel (the same for B stored [Kd, N]): the same loads
-//   into LDS and 16x16x32 MFMAs, B's fragments assembled with transposing LDS
-//   reads; described at the kernel.
+// * gemm_bf16_w4dn_kernel (the same for B stored [Kd, N], Kd at least 256):
+//   the same loads into LDS and 16x16x32 MFMAs, B's fragments assembled with
+//   transposing LDS reads; described at the kernel.
 //
 // * gemm_bf16_w4_kernel (the default where M and N are multiples of 256, Kd a
 //   multiple of 64 and at least 1024, and the direct-to-LDS kernels do not
@@ -299,7 +299,8 @@ constexpr int W4_HP = TM / W4_RPP;          // passes per operand tile (8)
 constexpr int W4_KS = W4_TK / 16;           // MFMA k steps per stage (4)
 constexpr int W4_B = 4;                     // 32x32 MFMA blocks per wave side (128 = 4 x 32)
 constexpr long long kW4MinK = 1024;         // shortest k range given to the register-staged 4-wave kernel
-constexpr long long kDirectMinK = 256;      // shortest k range given to the direct-to-LDS kernels
+constexpr long long kDirectMinK = 256;      // shortest k range given to the direct-to-LDS kernel for B [Kd, N]
+constexpr long long kDirectMinKNk = 384;    // and to the one for B [N, Kd]
 constexpr long long kNtcMinK = 8192;        // k range from which C leaves in nontemporal stores
 static_assert(W4_HP * 2 == W4_KS * W4_B, "one staged 16-byte load per group of MFMAs");
 
@@ -948,13 +949,15 @@ hipError_t launch_layout(const void *a, const void *b, void *c, long long M, lon
     // MFMAs. The register-staged kernel from kk = 1024 (measured against the
     // 8-wave kernel: 1.2x at 8192^3, 1.08x at kk = 1536, 1.02-1.07x at 1024,
     // 0.93x at 512, 0.8x at 256); the direct-to-LDS kernels (an even number of
-    // k stages) from kk = 256 (at 4096 x 14336: B [k, n] 0.87x the 8-wave
-    // kernel's time at kk = 256, 0.83x at 384, 0.81x at 512; B [n, k] level
-    // at 256, 0.94x at 384, 0.88x at 512; at kk = 128 B [n, k] is 1.12x)
+    // k stages) from kk = 256 for B [k, n] (at 4096 x 14336: 0.87-0.90x the
+    // 8-wave kernel's time at kk = 256, 0.83x at 384, 0.81x at 512) and from
+    // kk = 384 for B [n, k] (0.98-1.04x at 256, 0.94x at 384, 0.88x at 512;
+    // 1.12x at 128)
     const bool whole = variant == kGemmFast && M % TM == 0 && N % TN == 0 && 512 * Kd < 0x7fffffffLL &&
                        (BKN ? 2 * Kd * N < 0x7fffffffLL : true);
     const bool w4 = whole && Kd % W4_TK == 0 && Kd >= kW4MinK;
-    const bool direct = whole && Kd % (2 * D_TK) == 0 && Kd >= kDirectMinK && 512 * N < 0x7fffffffLL;
+    const bool direct = whole && Kd % (2 * D_TK) == 0 && Kd >= (BKN ? kDirectMinK : kDirectMinKNk) &&
+                        512 * N < 0x7fffffffLL;
     // the direct-to-LDS kernels: C in 16-byte stores where C is 16-byte aligned
     // and N a multiple of 8, nontemporal from kk = 8192, else in 2-byte stores
     // (512 N bytes cover a tile's rows of C)

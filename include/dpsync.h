@@ -262,8 +262,9 @@ dp_status_t dp_fsdp_layer_static(int k, int64_t m_local, int64_t d, int64_t f,
  *   every shape, layout and variant, so all give the same bits. Rows that are
  *   16-byte aligned (a and b 16-byte aligned, kk a multiple of 8, and n a
  *   multiple of 8 for b [kk,n]) take the staged kernels: m and n multiples of
- *   256 with kk a multiple of 128 and >= 256, or a multiple of 64 and >= 1024,
- *   a 4-wave kernel (one wave per SIMD), other shapes the 8-wave kernel
+ *   256 with kk a multiple of 128 and >= 256 (>= 384 for b [n,kk]), or a
+ *   multiple of 64 and >= 1024, a 4-wave kernel (one wave per SIMD), other
+ *   shapes the 8-wave kernel
  *   (guarded edge tiles where needed); other rows a slower kernel that
  *   gathers operands element by element. c may start at any element; where
  *   it is 16-byte aligned the 4-wave kernels write it in 16-byte stores.

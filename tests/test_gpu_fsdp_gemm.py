@@ -350,9 +350,10 @@ def test_gemm_bf16_8192_sampled():
                                     (256, 512, 128), (256, 512, 8192)])
 def test_gemm_bf16_variants_and_layouts_bit_identical(m, n, kk):
     """Whole 256x256 tiles with an even number of depth-64 k stages and kk >=
-    256 run the direct-to-LDS 4-wave kernels (16x16x32 MFMAs for both, B's
-    fragments assembled with transposing LDS reads for B stored [kk,n]); with
-    an odd number and kk >= 1024 the register-staged 4-wave kernel;
+    256 (B stored [kk,n]) or >= 384 (B stored [n,kk]) run the direct-to-LDS
+    4-wave kernels (16x16x32 MFMAs for both, B's fragments assembled with
+    transposing LDS reads for B stored [kk,n]); with an odd number and kk >=
+    1024 the register-staged 4-wave kernel;
     the 8-wave variants (DP_LAUNCH_LEAN: depth-64 stages,
     DP_LAUNCH_SHARE_CU: depth-32) add the same k steps in the same order, for
     B stored [kk,n] (transposing LDS reads) and [n,kk] alike, so all six agree
